@@ -1,0 +1,137 @@
+"""Pins of the oracle's products: the rotated-activation identity by brute
+force, the Hadamard-column probe, linearity, Parseval, the end-to-end
+quantisation error, and the bf16 variant against its analytic bound."""
+import numpy as np
+import pytest
+
+import cq_inputs
+import oracle
+
+
+def _butterfly(v):
+    v = np.array(v, dtype=np.float64)
+    h = 1
+    while h < v.shape[-1]:
+        for i in range(0, v.shape[-1], 2 * h):
+            a = v[..., i:i + h].copy()
+            b = v[..., i + h:i + 2 * h].copy()
+            v[..., i:i + h] = a + b
+            v[..., i + h:i + 2 * h] = a - b
+        h *= 2
+    return v / np.sqrt(v.shape[-1])
+
+
+def _blob(cfg, bits, rows, cols, kind="empirical"):
+    levels = None if bits == 5 else cq_inputs.codebook(bits, kind)
+    w = cq_inputs.master(cfg, bits, rows, cols)
+    return oracle.quantize(w, bits, levels), levels, w
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+def test_rotated_activation_identity(bits):
+    rows, cols = 6, 300
+    blob, levels, _ = _blob(95, bits, rows, cols)
+    x = cq_inputs.activations(95, bits, 3, cols)
+    y = oracle.matvec(blob, bits, rows, cols, x, levels)
+    # sum_g n_g <c[q_g], H x_g>, with the butterfly rotation and explicit loops
+    packed, norms = oracle.split_blob(blob, bits, rows, cols)
+    kpad = 384
+    vals = oracle.level_values(oracle.unpack_codes(packed, bits, kpad), bits, levels)
+    xp = np.zeros((3, kpad))
+    xp[:, :cols] = x
+    xr = _butterfly(xp.reshape(3, 3, 128))
+    for b in range(3):
+        for r in range(rows):
+            acc = 0.0
+            for g in range(3):
+                acc += float(norms[r, g]) * float(np.dot(vals[r, 128 * g:128 * (g + 1)], xr[b, g]))
+            scale = np.linalg.norm(oracle.dequantize(blob, bits, rows, cols, levels)[r]) * np.linalg.norm(x[b])
+            assert abs(acc - y[b, r]) <= 1e-13 * scale
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+def test_hadamard_column_probe_reads_back_each_index(bits):
+    rows, cols = 5, 256
+    blob, levels, _ = _blob(96, bits, rows, cols)
+    packed, norms = oracle.split_blob(blob, bits, rows, cols)
+    codes = oracle.unpack_codes(packed, bits, 256)
+    vals = oracle.level_values(codes, bits, levels)
+    H = oracle.hadamard()
+    for g in (0, 1):
+        for j in (0, 1, 2, 3, 7, 8, 63, 64, 127):
+            x = np.zeros((1, cols))
+            x[0, 128 * g:128 * (g + 1)] = H @ np.eye(128)[j]
+            y = oracle.matvec(blob, bits, rows, cols, x, levels)[0]
+            expect = norms[:, g].astype(np.float64) * vals[:, 128 * g + j]
+            assert np.allclose(y, expect, rtol=0, atol=1e-14)
+
+
+def test_linearity_zero_and_parseval():
+    rows, cols = 7, 512
+    blob, levels, _ = _blob(97, 2, rows, cols)
+    x1 = cq_inputs.activations(97, 1, 1, cols)
+    x2 = cq_inputs.activations(97, 2, 1, cols)
+    y1 = oracle.matvec(blob, 2, rows, cols, x1, levels)
+    y2 = oracle.matvec(blob, 2, rows, cols, x2, levels)
+    y12 = oracle.matvec(blob, 2, rows, cols, x1.astype(np.float64) + 2 * x2.astype(np.float64), levels)
+    assert np.allclose(y12, y1 + 2 * y2, rtol=0, atol=1e-12)
+    assert np.all(oracle.matvec(blob, 2, rows, cols, np.zeros((1, cols)), levels) == 0)
+    packed, norms = oracle.split_blob(blob, 2, rows, cols)
+    vals = oracle.level_values(oracle.unpack_codes(packed, 2, 512), 2, levels).reshape(rows, 4, 128)
+    w_hat = oracle.dequantize(blob, 2, rows, cols, levels).reshape(rows, 4, 128)
+    assert np.allclose(np.linalg.norm(w_hat, axis=-1),
+                       norms.astype(np.float64) * np.linalg.norm(vals, axis=-1), rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("bits,min_cos", [(2, 0.92), (3, 0.975), (4, 0.993), (5, 0.88)])
+def test_end_to_end_error_matches_quantiser_distortion(bits, min_cos):
+    # y_quantised vs the unquantised product W.x: cosine ~ sqrt(1 - D_L)
+    rows, cols = 256, 1024
+    blob, levels, w = _blob(98, bits, rows, cols, "gaussian" if bits != 5 else "empirical")
+    x = cq_inputs.activations(98, bits, 1, cols)
+    y = oracle.matvec(blob, bits, rows, cols, x, levels)[0]
+    exact = w.astype(np.float64) @ x[0].astype(np.float64)
+    cos = y @ exact / np.linalg.norm(y) / np.linalg.norm(exact)
+    assert min_cos < cos < 0.9999
+
+
+def test_gemm_rows_equal_matvec_and_row_subsets():
+    rows, cols = 9, 256
+    blob, levels, _ = _blob(99, 4, rows, cols)
+    X = cq_inputs.activations(99, 0, 4, cols)
+    C = oracle.gemm(blob, 4, rows, cols, X, levels)
+    for m in range(4):
+        assert np.allclose(C[m], oracle.matvec(blob, 4, rows, cols, X[m:m + 1], levels)[0], rtol=0, atol=1e-15)
+    ids = np.array([0, 4, 8])
+    assert np.allclose(oracle.gemm(blob, 4, rows, cols, X, levels, row_ids=ids), C[:, ids], rtol=0, atol=1e-15)
+
+
+def test_bf16_round_matches_torch():
+    import torch
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(10000) * 10.0 ** rng.integers(-5, 5, 10000)).astype(np.float32)
+    # exact ties: bf16 value + half an ulp
+    base = oracle.bf16_round(x[:100])
+    ties = (base.view(np.uint32) + np.uint32(0x8000)).view(np.float32)
+    x = np.concatenate([x, ties, -ties, [0.0, -0.0, 1.0, 65504.0]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(oracle.bf16_round(x).view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_bf16_variant_within_analytic_bound(bits):
+    rows, cols, M = 16, 512, 8
+    blob, levels, _ = _blob(100, bits, rows, cols)
+    X = cq_inputs.activations(100, bits, M, cols, "f16")
+    C = oracle.gemm(blob, bits, rows, cols, X, levels)
+    Cb = oracle.gemm_bf16(blob, bits, rows, cols, X, levels)
+    wn = np.linalg.norm(oracle.dequantize(blob, bits, rows, cols, levels), axis=1)
+    xn = np.linalg.norm(X.astype(np.float64), axis=1)
+    assert np.all(np.abs(Cb - C) <= 7.8e-3 * np.outer(xn, wn))
+    cos = np.sum(Cb * C) / np.linalg.norm(Cb) / np.linalg.norm(C)
+    assert cos > 0.9999
+
+
+def test_ternary_crumbs_sign_extend():
+    a = float(oracle.ternary_level32())
+    assert oracle.level_values(np.array([0, 1, 2, 3]), 5).tolist() == [0.0, a, -2 * a, -a]
