@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Throughput of the CQ matrix product on one MI355X.
+
+Headline workload: HBM-resident streaming matvec, CQ2 W 65536 x 16384
+(285,212,672 bytes of packed indices + fp16 norms), batch 1, fp32
+activations N(0,1).  One step = cq_rotate_acts(x) + cq_matvec(W, xr), with the
+step's W taken in turn from three copies of the matrix so that no copy is
+re-read while still resident in the 256 MB Infinity Cache.
+
+  value       = packed bytes per step / wall time per step        (GB/s)
+  roofline    = matvec kernel: packed bytes / mean kernel time (HIP events on
+                the launch stream) against 8 TB/s HBM peak
+  cpu_baseline= the float64 oracle (dense dequantisation + product) on row
+                slices of the same matrix, timed on this host
+
+The same JSON line carries secondary figures under "secondary": the other
+widths and batch 8 at the same shape, the 4096 x 16384 x 16384 GEMM on the
+matrix cores (TFLOP/s) and the 16384 x 16384 encoder (GB/s of fp32 input).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only matvec|gemm|encode|all]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+ROWS, COLS = 65536, 16384
+GEMM_M, GEMM_N, GEMM_K = 4096, 16384, 16384
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "matvec_cq2_65536x16384_traffic.json")
+MATVEC_SRC = os.path.join(ROOT, "hadamard_rotated_codebook_amd", "csrc", "matvec.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _events(torch, n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen):
+    rows, cols = master.shape
+    levels = cq_inputs.codebook(bits)
+    W0 = cq.cq_quantize(master, bits, levels)
+    mats = [W0] + [cq.CQMatrix(bits, rows, cols, W0.blob.clone(), levels) for _ in range(2)]
+    x = torch.randn((batch, cols), generator=gen, device=master.device)
+    xr = torch.empty((batch, cols), device=master.device)
+    y = torch.empty((batch, rows), device=master.device)
+    for i in range(warmup):
+        cq.cq_rotate_acts(x, out=xr)
+        cq.cq_matvec(mats[i % 3], xr, out=y)
+    torch.cuda.synchronize()
+    ev = _events(torch, steps)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        cq.cq_rotate_acts(x, out=xr)
+        ev[i][0].record()
+        cq.cq_matvec(mats[i % 3], xr, out=y)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    kern = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
+    nbytes = W0.blob.numel()
+    del mats, W0
+    return {"bits": bits, "batch": batch, "bytes": nbytes, "step_s": wall, "kernel_s": kern,
+            "flop": 2.0 * rows * cols * batch}
+
+
+def bench_gemm(torch, cq, cq_inputs, master, bits, m, steps, warmup, gen):
+    rows, cols = master.shape
+    levels = cq_inputs.codebook(bits)
+    W = cq.cq_quantize(master, bits, levels)
+    X = torch.randn((m, cols), generator=gen, device=master.device).to(torch.bfloat16)
+    xr = cq.cq_rotate_acts(X, torch.bfloat16)
+    C = torch.empty((m, rows), device=master.device)
+    for _ in range(warmup):
+        cq.cq_gemm(W, xr, out=C)
+    torch.cuda.synchronize()
+    ev = _events(torch, steps)
+    for i in range(steps):
+        ev[i][0].record()
+        cq.cq_gemm(W, xr, out=C)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    kern = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
+    flop = 2.0 * m * rows * cols
+    return {"bits": bits, "m": m, "n": rows, "k": cols, "kernel_s": kern, "tflops": flop / kern / 1e12,
+            "frac_bf16_peak": flop / kern / 1e12 / BF16_PEAK_TFLOPS}
+
+
+def bench_encode(torch, cq, cq_inputs, master, bits, steps, warmup):
+    levels = cq_inputs.codebook(bits)
+    out = torch.empty(cq.cq_blob_bytes(bits, *master.shape), dtype=torch.uint8, device=master.device)
+    for _ in range(warmup):
+        cq.cq_quantize(master, bits, levels, out=out)
+    torch.cuda.synchronize()
+    ev = _events(torch, steps)
+    for i in range(steps):
+        ev[i][0].record()
+        cq.cq_quantize(master, bits, levels, out=out)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    kern = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
+    nbytes = master.numel() * 4
+    return {"bits": bits, "rows": master.shape[0], "cols": master.shape[1], "kernel_s": kern,
+            "input_gbs": nbytes / kern / 1e9, "frac_hbm_peak": nbytes / kern / 1e9 / HBM_PEAK_GBS}
+
+
+def cpu_baseline(seconds=12.0, rows_per_slice=256):
+    """The oracle as it stands, on row slices of the headline matrix."""
+    import numpy as np
+    import cq_inputs
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    levels = cq_inputs.codebook(2)
+    x = cq_inputs.activations(4, 0, 1, COLS)
+    done_bytes, spent, s = 0, 0.0, 0
+    while spent < seconds:
+        r0 = (s * rows_per_slice) % ROWS
+        w = cq_inputs.master(4, 0, ROWS, COLS, r0, r0 + rows_per_slice)
+        blob = oracle.quantize(w, 2, levels)  # input preparation, not timed
+        t0 = time.perf_counter()
+        oracle.matvec(blob, 2, rows_per_slice, COLS, x, levels)
+        spent += time.perf_counter() - t0
+        done_bytes += blob.size
+        s += 1
+    return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{s} slices of {rows_per_slice} rows x {COLS} cols of the CQ2 matrix "
+                      f"(float64 dense dequantisation + product), {spent:.1f} s of CPU work"}
+
+
+def stored_traffic():
+    """HBM bytes per matvec launch from the committed rocprofv3 counter runs, if
+    they were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        src = hashlib.sha256(open(MATVEC_SRC, "rb").read()).hexdigest()
+        if t.get("matvec_source_sha256") != src:
+            return None
+        return t.get("traffic_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--only", choices=["all", "matvec", "gemm", "encode"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; there is no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import cq_inputs
+    import hadamard_rotated_codebook_amd as cq
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261202)
+    result = {}
+    secondary = {}
+
+    if args.only in ("all", "matvec"):
+        log("generating the 65536 x 16384 fp32 master on the GPU")
+        master = torch.randn((ROWS, COLS), generator=gen, device=dev).mul_(0.02)
+        head = bench_matvec(torch, cq, cq_inputs, master, 2, 1, args.steps, args.warmup, gen)
+        log(f"CQ2 b1: step {head['step_s']*1e6:.1f} us, matvec kernel {head['kernel_s']*1e6:.1f} us")
+        result["head"] = head
+        if args.only == "all":
+            for bits, batch in [(3, 1), (4, 1), (5, 1), (2, 8)]:
+                r = bench_matvec(torch, cq, cq_inputs, master, bits, batch, max(args.steps // 3, 20),
+                                 args.warmup, gen)
+                key = f"matvec_cq{bits if bits != 5 else 't'}_b{batch}"
+                r["gbs"] = r["bytes"] / r["kernel_s"] / 1e9
+                r["frac_hbm_peak"] = r["gbs"] / HBM_PEAK_GBS
+                if batch > 1:
+                    r["tflops_fp32"] = r["flop"] / r["kernel_s"] / 1e12
+                secondary[key] = r
+                log(key, f"{r['kernel_s']*1e6:.1f} us", f"{r['gbs']:.0f} GB/s")
+        del master
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "gemm", "encode"):
+        log("generating the 16384 x 16384 fp32 master on the GPU")
+        master = torch.randn((GEMM_N, GEMM_K), generator=gen, device=dev).mul_(0.02)
+        if args.only in ("all", "encode"):
+            for bits in (4, 3):
+                r = bench_encode(torch, cq, cq_inputs, master, bits, 10, 2)
+                secondary[f"encode_cq{bits}_16384x16384"] = r
+                log(f"encode cq{bits}: {r['kernel_s']*1e3:.3f} ms, {r['input_gbs']:.0f} GB/s")
+        if args.only in ("all", "gemm"):
+            for bits in (4, 3):
+                r = bench_gemm(torch, cq, cq_inputs, master, bits, GEMM_M, 10, 2, gen)
+                secondary[f"gemm_cq{bits}_4096x16384x16384"] = r
+                log(f"gemm cq{bits}: {r['kernel_s']*1e3:.3f} ms, {r['tflops']:.1f} TFLOP/s")
+        del master
+        torch.cuda.empty_cache()
+
+    line = {"metric": "CQ2 batch-1 matvec GB/s of packed weights (% HBM peak); CQ GEMM TFLOP/s",
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic: seeded N(0,0.02^2) master encoded on the GPU; activations N(0,1)"}
+    if "head" in result:
+        h = result["head"]
+        line["value"] = h["bytes"] / h["step_s"] / 1e9
+        line["ms_per_step"] = h["step_s"] * 1e3
+        line["config"] = {"workload": "HBM-resident CQ2 matvec, W 65536x16384, batch 1, fp32 activations",
+                          "rows": ROWS, "cols": COLS, "bits": 2, "batch": 1, "packed_bytes": h["bytes"]}
+        ach = h["bytes"] / h["kernel_s"] / 1e9
+        line["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": ach / HBM_PEAK_GBS, "traffic": stored_traffic(),
+                            "kernel": "matvec_nibble_kernel<2,1>", "kernel_us": h["kernel_s"] * 1e6}
+    else:
+        line["value"] = None
+        line["ms_per_step"] = None
+        line["config"] = {"workload": f"partial run (--only {args.only})"}
+    if secondary:
+        line["secondary"] = secondary
+    if not args.no_cpu_baseline and args.only in ("all", "matvec"):
+        log("timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+"""Cactus Quants (CQ) matrix products on one AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``libcq.so``, the C-ABI library declared in
+``include/cq.h``.  This module only marshals arguments: it checks tensor
+metadata, passes raw device pointers and the current HIP stream, and turns
+status codes into exceptions.  Every step of the computation runs in the HIP
+kernels of the library; PyTorch supplies device memory and streams.
+
+The library must be built first (``python -m hadamard_rotated_codebook_amd.build``);
+importing this package without it raises ``ImportError`` -- there is no
+fallback path.
+
+Functions carry the C names: ``cq_blob_bytes``, ``cq_workspace_bytes``,
+``cq_rotate_acts``, ``cq_matvec``, ``cq_gemm``, ``cq_quantize``.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = [
+    "LIB_PATH", "CQError", "CQMatrix", "CQ_GROUP", "CQ_MAX_MATVEC_BATCH",
+    "cq_version", "cq_blob_bytes", "cq_workspace_bytes",
+    "cq_rotate_acts", "cq_matvec", "cq_gemm", "cq_quantize",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcq.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run: python -m hadamard_rotated_codebook_amd.build")
+_lib = ctypes.CDLL(LIB_PATH)
+
+CQ_GROUP = 128
+CQ_MAX_MATVEC_BATCH = 8
+_F32, _F16, _BF16 = 0, 1, 2
+_DTYPES = {torch.float32: _F32, torch.float16: _F16, torch.bfloat16: _BF16}
+OP_MATVEC, OP_GEMM = 0, 1
+
+
+class _Matrix(ctypes.Structure):
+    _fields_ = [
+        ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+        ("blob", ctypes.c_void_p), ("blob_bytes", ctypes.c_uint64),
+        ("levels", ctypes.POINTER(ctypes.c_float)),
+    ]
+
+
+_i32, _i64, _u64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
+_MP = ctypes.POINTER(_Matrix)
+_SIGS = {
+    "cq_version": (_i32, []),
+    "cq_status_string": (ctypes.c_char_p, [_i32]),
+    "cq_blob_bytes": (_i32, [_i32, _i32, _i64, _i64, ctypes.POINTER(_u64)]),
+    "cq_workspace_bytes": (_i32, [_i32, _MP, _i64, ctypes.POINTER(_u64)]),
+    "cq_rotate_acts": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _vp]),
+    "cq_matvec": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
+    "cq_gemm": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
+    "cq_quantize": (_i32, [_vp, _i64, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_float), _vp, _u64, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class CQError(RuntimeError):
+    """A libcq call returned a non-zero cq_status."""
+
+    def __init__(self, status):
+        self.status = int(status)
+        super().__init__(f"cq_status {self.status}: {_lib.cq_status_string(self.status).decode()}")
+
+
+def _check(status):
+    if status != 0:
+        raise CQError(status)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr() if t.numel() else 0)
+
+
+def _levels_array(levels):
+    if levels is None:
+        return None, None
+    arr = np.ascontiguousarray(levels, dtype=np.float32)
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def cq_version():
+    return int(_lib.cq_version())
+
+
+def cq_blob_bytes(bits, rows, cols, group=CQ_GROUP):
+    out = _u64(0)
+    _check(_lib.cq_blob_bytes(bits, group, rows, cols, ctypes.byref(out)))
+    return int(out.value)
+
+
+@dataclass
+class CQMatrix:
+    """A CQ matrix: ``blob`` is a uint8 device tensor laid out as in cq.h;
+    ``levels`` the host fp32 codebook (None for the ternary marker 5)."""
+    bits: int
+    rows: int
+    cols: int
+    blob: torch.Tensor
+    levels: Optional[np.ndarray] = None
+    group: int = CQ_GROUP
+
+    def _struct(self):
+        arr, ptr = _levels_array(self.levels)
+        if self.blob.dtype != torch.uint8:
+            raise TypeError("blob must be uint8")
+        m = _Matrix(self.bits, self.group, self.rows, self.cols, _dev(self.blob, "blob"),
+                    self.blob.numel(), ptr)
+        return m, arr  # keep the levels array alive for the call
+
+
+def cq_workspace_bytes(op, W, batch):
+    m, keep = W._struct()
+    out = _u64(0)
+    _check(_lib.cq_workspace_bytes(op, ctypes.byref(m), batch, ctypes.byref(out)))
+    return int(out.value)
+
+
+def _padded(cols):
+    return -(-cols // CQ_GROUP) * CQ_GROUP
+
+
+def cq_rotate_acts(x, out_dtype=torch.float32, out=None):
+    """xr = per-128-group H.x of a [batch, cols] activation; returns [batch, cols_pad]."""
+    if x.dim() != 2:
+        raise ValueError("x must be [batch, cols]")
+    if x.dtype not in _DTYPES:
+        raise TypeError("x must be float32, float16 or bfloat16")
+    b, cols = x.shape
+    if out is None:
+        out = torch.empty((b, _padded(cols)), dtype=out_dtype, device=x.device)
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    if tuple(out.shape) != (b, _padded(cols)):
+        raise ValueError("out must be [batch, cols_pad]")
+    _check(_lib.cq_rotate_acts(_dev(x, "x"), _DTYPES[x.dtype], b, cols, _dev(out, "out"),
+                               _DTYPES[out.dtype], _stream()))
+    return out
+
+
+def cq_matvec(W, xr, out=None, workspace=None):
+    """y[b, r] = sum_g norm * <c[q], xr_g>; xr float32 [batch, cols_pad]; returns float32 [batch, rows]."""
+    if xr.dtype != torch.float32 or xr.dim() != 2 or xr.shape[1] != _padded(W.cols):
+        raise ValueError("xr must be float32 [batch, cols_pad]")
+    b = xr.shape[0]
+    if out is None:
+        out = torch.empty((b, W.rows), dtype=torch.float32, device=xr.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (b, W.rows):
+        raise ValueError("out must be float32 [batch, rows]")
+    m, keep = W._struct()
+    ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.cq_matvec(ctypes.byref(m), _dev(xr, "xr"), b, _dev(out, "out"), ws, wsb, _stream()))
+    return out
+
+
+def cq_gemm(W, xr, out=None, workspace=None):
+    """C[m, r] = sum_k xr[m, k] * bf16(c[q] * norm); xr bfloat16 [m, cols_pad]; returns float32 [m, rows]."""
+    if xr.dtype != torch.bfloat16 or xr.dim() != 2 or xr.shape[1] != _padded(W.cols):
+        raise ValueError("xr must be bfloat16 [m, cols_pad]")
+    mrows = xr.shape[0]
+    if out is None:
+        out = torch.empty((mrows, W.rows), dtype=torch.float32, device=xr.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (mrows, W.rows):
+        raise ValueError("out must be float32 [m, rows]")
+    m, keep = W._struct()
+    ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.cq_gemm(ctypes.byref(m), _dev(xr, "xr"), mrows, _dev(out, "out"), ws, wsb, _stream()))
+    return out
+
+
+def cq_quantize(w, bits, levels=None, group=CQ_GROUP, out=None):
+    """Encode a float32 [rows, cols] device matrix; returns a CQMatrix whose blob is ``out``
+    (allocated when None)."""
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be float32 [rows, cols]")
+    rows, cols = w.shape
+    nbytes = cq_blob_bytes(bits, rows, cols, group)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    if out.dtype != torch.uint8 or out.numel() != nbytes:
+        raise ValueError("out must be a uint8 tensor of cq_blob_bytes() bytes")
+    arr, ptr = _levels_array(levels)
+    _check(_lib.cq_quantize(_dev(w, "w"), rows, cols, bits, group, ptr, _dev(out, "out"), nbytes, _stream()))
+    return CQMatrix(bits, rows, cols, out, arr, group)

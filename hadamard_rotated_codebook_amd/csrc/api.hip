@@ -1,0 +1,227 @@
+// Host side of libcq: argument validation and kernel dispatch for the C ABI
+// declared in include/cq.h.  Every check runs before anything is enqueued, so
+// a rejected call launches nothing and writes nothing.
+#include <cmath>
+#include <cstring>
+
+#include "cq_internal.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
+  if (!na || !nb) return false;
+  uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+cq_status hip_status(hipError_t e) { return e == hipSuccess ? CQ_OK : CQ_ERR_HIP; }
+
+int64_t padded(int64_t cols) { return (cols + CQ_GROUP - 1) / CQ_GROUP * CQ_GROUP; }
+
+// Blob length rows * (cols_pad*b/8 + 2*cols_pad/128) (needle.js tutorial,
+// "Anatomy of a CQ matrix"; the ternary marker stores 2-bit crumbs).
+cq_status blob_bytes_impl(int32_t bits, int32_t group, int64_t rows, int64_t cols, uint64_t *out) {
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 5) return CQ_ERR_BITS;
+  if (group != CQ_GROUP) return CQ_ERR_GROUP;
+  if (rows < 0 || cols < 0 || rows > CQ_MAX_DIM || cols > CQ_MAX_DIM) return CQ_ERR_SHAPE;
+  const uint64_t kpad = static_cast<uint64_t>(padded(cols));
+  const uint64_t row_bytes = kpad * cq::storage_bits(bits) / 8 + kpad / CQ_GROUP * 2;
+  *out = static_cast<uint64_t>(rows) * row_bytes;  // < 2^61 within the limits
+  return CQ_OK;
+}
+
+// Levels of the stored codes; see cq::CodeLevels.
+cq_status code_levels(int bits, const float *levels, cq::CodeLevels *lev) {
+  std::memset(lev, 0, sizeof *lev);
+  if (bits == 5) {
+    if (levels) return CQ_ERR_CODEBOOK;
+    const float a = cq::ternary_level_f32();
+    lev->v[0] = 0.0f;
+    lev->v[1] = a;
+    lev->v[2] = -2.0f * a;
+    lev->v[3] = -a;
+    return CQ_OK;
+  }
+  if (!levels) return CQ_ERR_CODEBOOK;
+  const int n = 1 << bits;
+  for (int i = 0; i < n; ++i) {
+    if (!std::isfinite(levels[i])) return CQ_ERR_CODEBOOK;
+    if (i && !(levels[i] > levels[i - 1])) return CQ_ERR_CODEBOOK;
+    lev->v[i] = levels[i];
+  }
+  return CQ_OK;
+}
+
+cq_status check_matrix(const cq_matrix *W, cq::CodeLevels *lev) {
+  if (!W) return CQ_ERR_NULL;
+  uint64_t need = 0;
+  cq_status st = blob_bytes_impl(W->bits, W->group, W->rows, W->cols, &need);
+  if (st != CQ_OK) return st;
+  if (W->blob_bytes != need) return CQ_ERR_LENGTH;
+  if (need && !W->blob) return CQ_ERR_NULL;
+  if (W->blob && !aligned(W->blob, 16)) return CQ_ERR_ALIGN;
+  return code_levels(W->bits, W->levels, lev);
+}
+
+size_t dtype_size(int32_t dt) { return dt == CQ_F32 ? 4 : 2; }
+
+}  // namespace
+
+namespace cq {
+
+float ternary_level_f32() { return static_cast<float>(1.2240064 / std::sqrt(128.0)); }
+
+}  // namespace cq
+
+extern "C" {
+
+int32_t cq_version(void) { return 10000; }
+
+const char *cq_status_string(cq_status status) {
+  switch (status) {
+    case CQ_OK: return "ok";
+    case CQ_ERR_NULL: return "a required pointer is NULL";
+    case CQ_ERR_BITS: return "bits must be 2, 3, 4 or 5 (ternary marker)";
+    case CQ_ERR_GROUP: return "group must be 128";
+    case CQ_ERR_SHAPE: return "a dimension is negative or above its limit";
+    case CQ_ERR_LENGTH: return "Inconsistent CQ matrix length";
+    case CQ_ERR_CODEBOOK: return "levels must be 2^bits strictly ascending finite floats (NULL for ternary)";
+    case CQ_ERR_DTYPE: return "unsupported element type";
+    case CQ_ERR_WORKSPACE: return "workspace smaller than cq_workspace_bytes()";
+    case CQ_ERR_ALIGN: return "a device pointer is not aligned as documented";
+    case CQ_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case CQ_ERR_OVERLAP: return "an output buffer overlaps an input buffer";
+  }
+  return "unknown status";
+}
+
+cq_status cq_blob_bytes(int32_t bits, int32_t group, int64_t rows, int64_t cols, uint64_t *bytes) {
+  if (!bytes) return CQ_ERR_NULL;
+  uint64_t n = 0;
+  cq_status st = blob_bytes_impl(bits, group, rows, cols, &n);
+  if (st == CQ_OK) *bytes = n;
+  return st;
+}
+
+cq_status cq_workspace_bytes(int32_t op, const cq_matrix *W, int64_t batch, uint64_t *bytes) {
+  if (!bytes) return CQ_ERR_NULL;
+  cq::CodeLevels lev;
+  cq_status st = check_matrix(W, &lev);
+  if (st != CQ_OK) return st;
+  if (op == CQ_OP_MATVEC) {
+    if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+  } else if (op == CQ_OP_GEMM) {
+    if (batch < 0 || batch > CQ_MAX_DIM) return CQ_ERR_SHAPE;
+  } else {
+    return CQ_ERR_SHAPE;
+  }
+  *bytes = 0;  // no kernel of this version needs scratch memory
+  return CQ_OK;
+}
+
+cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t cols, void *xr,
+                         int32_t xr_dtype, void *stream) {
+  if (x_dtype != CQ_F32 && x_dtype != CQ_F16 && x_dtype != CQ_BF16) return CQ_ERR_DTYPE;
+  if (xr_dtype != CQ_F32 && xr_dtype != CQ_BF16) return CQ_ERR_DTYPE;
+  if (batch < 0 || cols < 0 || batch > CQ_MAX_DIM || cols > CQ_MAX_DIM) return CQ_ERR_SHAPE;
+  if (batch == 0 || cols == 0) return CQ_OK;
+  if (!x || !xr) return CQ_ERR_NULL;
+  if (!aligned(x, dtype_size(x_dtype)) || !aligned(xr, 16)) return CQ_ERR_ALIGN;
+  const int64_t kpad = padded(cols);
+  if (overlaps(x, static_cast<uint64_t>(batch) * cols * dtype_size(x_dtype), xr,
+               static_cast<uint64_t>(batch) * kpad * dtype_size(xr_dtype)))
+    return CQ_ERR_OVERLAP;
+  return hip_status(cq::launch_rotate(x, x_dtype, batch, cols, kpad, xr, xr_dtype,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y, void *workspace,
+                    uint64_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  cq::CodeLevels lev;
+  cq_status st = check_matrix(W, &lev);
+  if (st != CQ_OK) return st;
+  if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+  if (batch == 0 || W->rows == 0) return CQ_OK;
+  if (!y) return CQ_ERR_NULL;
+  if (!aligned(y, 4)) return CQ_ERR_ALIGN;
+  const uint64_t ybytes = static_cast<uint64_t>(batch) * W->rows * 4;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t kpad = padded(W->cols);
+  if (kpad == 0) return hip_status(cq::launch_zero_f32(y, batch * W->rows, s));
+  if (!xr) return CQ_ERR_NULL;
+  if (!aligned(xr, 16)) return CQ_ERR_ALIGN;
+  if (overlaps(y, ybytes, xr, static_cast<uint64_t>(batch) * kpad * 4) ||
+      overlaps(y, ybytes, W->blob, W->blob_bytes))
+    return CQ_ERR_OVERLAP;
+  return hip_status(cq::launch_matvec(static_cast<const uint8_t *>(W->blob), W->bits, W->rows, kpad,
+                                      lev, xr, batch, y, s));
+}
+
+cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c, void *workspace,
+                  uint64_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  cq::CodeLevels lev;
+  cq_status st = check_matrix(W, &lev);
+  if (st != CQ_OK) return st;
+  if (m < 0 || m > CQ_MAX_DIM) return CQ_ERR_SHAPE;
+  if (m == 0 || W->rows == 0) return CQ_OK;
+  if (!c) return CQ_ERR_NULL;
+  if (!aligned(c, 4)) return CQ_ERR_ALIGN;
+  const uint64_t cbytes = static_cast<uint64_t>(m) * W->rows * 4;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t kpad = padded(W->cols);
+  if (kpad == 0) return hip_status(cq::launch_zero_f32(c, m * W->rows, s));
+  if (!xr) return CQ_ERR_NULL;
+  if (!aligned(xr, 16)) return CQ_ERR_ALIGN;
+  if (overlaps(c, cbytes, xr, static_cast<uint64_t>(m) * kpad * 2) ||
+      overlaps(c, cbytes, W->blob, W->blob_bytes))
+    return CQ_ERR_OVERLAP;
+  return hip_status(cq::launch_gemm(static_cast<const uint8_t *>(W->blob), W->bits, W->rows, kpad,
+                                    lev, xr, m, c, s));
+}
+
+cq_status cq_quantize(const float *w, int64_t rows, int64_t cols, int32_t bits, int32_t group,
+                      const float *levels, void *blob, uint64_t blob_bytes, void *stream) {
+  uint64_t need = 0;
+  cq_status st = blob_bytes_impl(bits, group, rows, cols, &need);
+  if (st != CQ_OK) return st;
+  cq::CodeLevels lev;
+  st = code_levels(bits, levels, &lev);
+  if (st != CQ_OK) return st;
+  if (blob_bytes != need) return CQ_ERR_LENGTH;
+  if (need == 0) return CQ_OK;
+  if (!w || !blob) return CQ_ERR_NULL;
+  if (!aligned(w, 4) || !aligned(blob, 16)) return CQ_ERR_ALIGN;
+  if (overlaps(blob, need, w, static_cast<uint64_t>(rows) * cols * 4)) return CQ_ERR_OVERLAP;
+
+  // Decision table: exact midpoints of adjacent ascending levels.  For fp32
+  // levels whose magnitudes are within 2^29 of each other the double sum is
+  // exact, so "u > mid" is the exact "nearer to the upper level" test and a
+  // tie keeps the smaller index (OpenNeedle reference notes, CQ quantisation
+  // steps).
+  cq::EncodeTable tab;
+  std::memset(&tab, 0, sizeof tab);
+  if (bits == 5) {
+    const double a = static_cast<double>(cq::ternary_level_f32());
+    tab.nlevels = 3;
+    tab.mid[0] = -a * 0.5;
+    tab.mid[1] = a * 0.5;
+    tab.code_of_index[0] = 3;  // -a -> crumb 11
+    tab.code_of_index[1] = 0;  //  0 -> crumb 00
+    tab.code_of_index[2] = 1;  // +a -> crumb 01
+  } else {
+    tab.nlevels = 1 << bits;
+    for (int j = 0; j + 1 < tab.nlevels; ++j)
+      tab.mid[j] = (static_cast<double>(levels[j]) + static_cast<double>(levels[j + 1])) * 0.5;
+    for (int j = 0; j < tab.nlevels; ++j) tab.code_of_index[j] = static_cast<uint32_t>(j);
+  }
+  return hip_status(cq::launch_quantize(w, rows, cols, padded(cols), bits, tab,
+                                        static_cast<uint8_t *>(blob), static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

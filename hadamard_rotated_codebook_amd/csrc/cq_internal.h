@@ -1,0 +1,52 @@
+// Internal declarations shared by the HIP translation units of libcq.
+// Not part of the public ABI (that is include/cq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cq.h"
+
+namespace cq {
+
+// Level selected by each *stored* code: levels[code] for 2/3/4-bit matrices;
+// for the ternary marker the crumb's sign extension times a, i.e.
+// {0, a, -2a, -a} for crumbs 00, 01, 10, 11.  Passed to kernels by value.
+struct CodeLevels {
+  float v[16];
+};
+
+// Decision thresholds of the encoder: exact midpoints of adjacent ascending
+// levels (held exactly in double), and the stored code of each level index.
+struct EncodeTable {
+  double mid[15];
+  uint32_t code_of_index[16];
+  int32_t nlevels;
+};
+
+// Storage width of one index: 2 for ternary crumbs, else bits.
+inline int storage_bits(int bits) { return bits == 5 ? 2 : bits; }
+
+// fp32 ternary level: a / sqrt(128) with a = 1.2240064, divided in double and
+// rounded once (needle.js tutorial, "Shared codebooks").
+float ternary_level_f32();
+
+// Launchers.  Arguments are already validated; sizes are non-zero unless a
+// launcher documents otherwise.
+hipError_t launch_rotate(const void *x, int x_dtype, int64_t batch, int64_t cols, int64_t kpad,
+                         void *xr, int xr_dtype, hipStream_t s);
+
+hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
+                         const CodeLevels &lev, const float *xr, int64_t batch, float *y,
+                         hipStream_t s);
+
+hipError_t launch_gemm(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
+                       const CodeLevels &lev, const void *xr, int64_t m, float *c, hipStream_t s);
+
+hipError_t launch_quantize(const float *w, int64_t rows, int64_t cols, int64_t kpad, int bits,
+                           const EncodeTable &tab, uint8_t *blob, hipStream_t s);
+
+// Fills n floats with +0.0 (a kernel, so that it can sit in a captured graph).
+hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s);
+
+}  // namespace cq

@@ -1,0 +1,206 @@
+/*
+ * cq.h -- C ABI of the Cactus Quants (CQ) matrix-product library for one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * A CQ matrix W is stored [rows = out, cols = in] in groups of 128 weights
+ * along the input axis.  Each group is an fp16 L2 norm times a unit direction
+ * in the normalised Walsh-Hadamard domain whose coordinates index a codebook,
+ * so that for every output row
+ *
+ *     y[r] = sum_g norm[r][g] * < c[q[r][g]], H . x_g >            (1)
+ *
+ * with H the order-128 Sylvester-Hadamard matrix divided by sqrt(128).
+ * Sources: the Needle ".cact" format post ("Cactus Quants", "How the kernel
+ * reads it"), the needle.js tutorial "The .cact archive and Cactus Quants"
+ * ("Anatomy of a CQ matrix", "Reconstructing one group") and the OpenNeedle
+ * reference notes (CQ quantisation steps; rotated-activation identity).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Pointers named "device" are HIP device pointers owned by the caller; the
+ *    library never frees, keeps or allocates memory, and keeps no state.
+ *  - Pointers named "host" are read during the call only.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued on
+ *    it and the call returns; results are valid once the stream has reached
+ *    that point.
+ *  - Every argument is validated before anything is enqueued.  On an error
+ *    nothing is launched and no output byte is written.  A failed HIP launch
+ *    returns CQ_ERR_HIP.  Nothing aborts the process.
+ *  - All arrays are dense and row-major; sizes are element counts.
+ *  - Calls that share an output buffer on one stream are ordered by it; two
+ *    calls on different streams writing the same buffer race.
+ */
+#ifndef CQ_H
+#define CQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum cq_status {
+  CQ_OK = 0,
+  CQ_ERR_NULL = 1,      /* a required pointer is NULL                           */
+  CQ_ERR_BITS = 2,      /* bits is not 2, 3, 4 or 5                             */
+  CQ_ERR_GROUP = 3,     /* group is not 128                                     */
+  CQ_ERR_SHAPE = 4,     /* a dimension is negative or above its limit          */
+  CQ_ERR_LENGTH = 5,    /* blob_bytes differs from cq_blob_bytes():
+                           "Inconsistent CQ matrix length"                     */
+  CQ_ERR_CODEBOOK = 6,  /* levels missing, not finite or not strictly
+                           ascending; or levels given for the ternary marker   */
+  CQ_ERR_DTYPE = 7,     /* unsupported element type                             */
+  CQ_ERR_WORKSPACE = 8, /* workspace smaller than cq_workspace_bytes()          */
+  CQ_ERR_ALIGN = 9,     /* a device pointer is not aligned as documented        */
+  CQ_ERR_HIP = 10,      /* a HIP runtime call or kernel launch failed           */
+  CQ_ERR_OVERLAP = 11   /* an output buffer overlaps an input buffer            */
+} cq_status;
+
+/* Element types of activation buffers. */
+typedef enum cq_dtype { CQ_F32 = 0, CQ_F16 = 1, CQ_BF16 = 2 } cq_dtype;
+
+/* Largest accepted dimensions (rows, cols, batch of a GEMM). */
+#define CQ_MAX_DIM ((int64_t)1 << 30)
+/* Largest batch of cq_matvec; larger batches are prefill: use cq_gemm. */
+#define CQ_MAX_MATVEC_BATCH 8
+/* The only supported quantisation group. */
+#define CQ_GROUP 128
+
+/*
+ * A CQ matrix as the ".cact" blob stores it (needle.js tutorial, "Anatomy of a
+ * CQ matrix"; OpenNeedle reference notes, file layout):
+ *
+ *   blob = packed index rows, then fp16 norms
+ *   packed row r: cols_pad * b / 8 bytes, cols_pad = ceil(cols/128) * 128,
+ *                 one continuous LSB-first bitstream: index k occupies bits
+ *                 [k*b, (k+1)*b) (2-bit: four per byte, first column in the
+ *                 lowest bits; 4-bit: low nibble first; 3-bit: indices cross
+ *                 byte boundaries)
+ *   norms:        rows * (cols_pad/128) little-endian fp16, [row][group],
+ *                 directly after the last packed row
+ *
+ * b is `bits` for 2/3/4.  bits == 5 is the ternary marker: b = 2 and each
+ * 2-bit crumb sign-extends (00 -> 0, 01 -> +1, 11 -> -1; 10 -> -2, never
+ * written by cq_quantize) and scales the analytic level
+ * a = fp32(1.2240064 / sqrt(128)) (needle.js tutorial, "Shared codebooks").
+ */
+typedef struct cq_matrix {
+  int32_t bits;          /* 2, 3, 4, or 5 (ternary marker)                        */
+  int32_t group;         /* must be 128                                           */
+  int64_t rows;          /* output dimension, 0 <= rows <= CQ_MAX_DIM             */
+  int64_t cols;          /* input dimension, 0 <= cols <= CQ_MAX_DIM              */
+  const void *blob;      /* device, 16-byte aligned; NULL allowed if blob_bytes==0*/
+  uint64_t blob_bytes;   /* must equal cq_blob_bytes(bits, group, rows, cols)     */
+  const float *levels;   /* host: 2^bits strictly ascending finite fp32 levels,
+                            already divided by sqrt(128) (the file's embedded
+                            codebook); must be NULL when bits == 5               */
+} cq_matrix;
+
+/* Version of this ABI (major * 10000 + minor * 100 + patch). */
+int32_t cq_version(void);
+
+/* Static description of a status code; never NULL. */
+const char *cq_status_string(cq_status status);
+
+/*
+ * Byte length of a CQ blob: rows * (cols_pad*b/8 + 2*cols_pad/128)
+ * (needle.js tutorial, "Anatomy of a CQ matrix"; ternary uses b = 2).
+ * Writes *bytes and returns CQ_OK, or returns an error and leaves *bytes.
+ * Host-only; launches nothing.
+ */
+cq_status cq_blob_bytes(int32_t bits, int32_t group, int64_t rows, int64_t cols,
+                        uint64_t *bytes);
+
+/* Operations that may take a workspace. */
+typedef enum cq_op { CQ_OP_MATVEC = 0, CQ_OP_GEMM = 1 } cq_op;
+
+/*
+ * Device workspace (bytes) that `op` needs for `W` and the given batch (M for
+ * the GEMM).  Host-only.  0 means the call takes workspace = NULL.
+ */
+cq_status cq_workspace_bytes(int32_t op, const cq_matrix *W, int64_t batch,
+                             uint64_t *bytes);
+
+/*
+ * Rotate activations once per 128-group (the ".cact" format post, "How the
+ * kernel reads it": each 128-lane group of the activation is rotated with the
+ * same Hadamard transform, shared by all output rows; OpenNeedle reference
+ * notes, rotated-activation identity: dot(w_hat, x) = n * dot(c[q], H x)).
+ *
+ *   xr[b][g*128 + j] = sum_k H[j][k] * x[b][g*128 + k],  x zero-padded
+ *
+ *   x      device [batch][cols] of x_dtype (CQ_F32, CQ_F16, CQ_BF16),
+ *          aligned to its element size
+ *   xr     device [batch][cols_pad] of xr_dtype (CQ_F32 for cq_matvec,
+ *          CQ_BF16 for cq_gemm), 16-byte aligned; must not overlap x
+ *   Computed in fp32 (seven butterfly stages, then one multiply by
+ *   1/sqrt(128)); bf16 output is rounded to nearest even.
+ *   batch, cols in [0, CQ_MAX_DIM]; nothing is launched when either is 0
+ *   (then xr is untouched: it has no elements when batch or cols_pad is 0).
+ */
+cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t cols,
+                         void *xr, int32_t xr_dtype, void *stream);
+
+/*
+ * Decode matrix-vector product, equation (1), fp32 accumulation:
+ *
+ *   y[b][r] = sum_g float(norm[r][g]) * sum_j c[q[r][g*128+j]] * xr[b][g*128+j]
+ *
+ *   W        matrix descriptor (its blob is read, never expanded)
+ *   xr       device fp32 [batch][W.cols_pad], 16-byte aligned, as written by
+ *            cq_rotate_acts(..., CQ_F32, ...)
+ *   batch    0 <= batch <= CQ_MAX_MATVEC_BATCH
+ *   y        device fp32 [batch][W.rows], 4-byte aligned, must not overlap
+ *            xr or the blob; fully overwritten (0 where cols == 0)
+ *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_MATVEC)
+ */
+cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y,
+                    void *workspace, uint64_t workspace_bytes, void *stream);
+
+/*
+ * Prefill product on the bf16 matrix cores, fp32 accumulation:
+ *
+ *   C[m][r] = sum_k Xr[m][k] * V[r][k],  V[r][g*128+j] = bf16(c[q] * float(norm[r][g]))
+ *
+ * (the product c*norm in fp32, then rounded to nearest even bf16; the
+ * dequantised tile is never written to memory).
+ *
+ *   W        matrix descriptor
+ *   xr       device bf16 [m][W.cols_pad], 16-byte aligned, as written by
+ *            cq_rotate_acts(..., CQ_BF16, ...)
+ *   m        0 <= m <= CQ_MAX_DIM
+ *   c        device fp32 [m][W.rows], 4-byte aligned, must not overlap xr
+ *            or the blob; fully overwritten (0 where cols == 0)
+ *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_GEMM)
+ */
+cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c,
+                  void *workspace, uint64_t workspace_bytes, void *stream);
+
+/*
+ * Encoder (OpenNeedle reference notes, CQ quantisation steps; the porting
+ * post's "cq_quantize rounds each group of 128 weights exactly as the
+ * exporter does").  Per row and per 128-group w (zero-padded):
+ *
+ *   r = w . H                     fp32: fp32 rounding of (w . S) * sqrt(1/128)
+ *                                 with w . S summed exactly and one double
+ *                                 multiply (S = +-1 Sylvester matrix)
+ *   n = ||r||_2                   fp32 rounding of the double norm of r
+ *   u = r / max(n, 1e-12f)        IEEE fp32 division
+ *   q_i = argmin_j |u_i - c_j|    ties to the smaller index (exact compare)
+ *   norm = fp16(n)                round to nearest even; > 65504 -> +inf
+ *   ternary (bits 5): q over (-a, 0, +a) stored as crumbs 11, 00, 01
+ *
+ *   w          device fp32 [rows][cols], 4-byte aligned
+ *   bits       2, 3, 4 or 5;   group: 128
+ *   levels     host, as in cq_matrix (NULL for bits 5)
+ *   blob       device, 16-byte aligned, blob_bytes == cq_blob_bytes(...);
+ *              fully overwritten; must not overlap w
+ */
+cq_status cq_quantize(const float *w, int64_t rows, int64_t cols, int32_t bits, int32_t group,
+                      const float *levels, void *blob, uint64_t blob_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CQ_H */

@@ -1,0 +1,169 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/cq.h declares, and its host-side validation rejects bad arguments
+before launching anything.  No call here reaches a kernel launch: every call
+either fails validation or has nothing to do."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import cq_inputs
+import oracle
+from conftest import ROOT
+
+cq = pytest.importorskip("hadamard_rotated_codebook_amd", reason="libcq.so not built")
+lib = cq._lib
+
+OK, NULL, BITS, GROUP, SHAPE, LENGTH, CODEBOOK, DTYPE, WORKSPACE, ALIGN, HIP, OVERLAP = range(12)
+FAKE = 1 << 40  # a 256-byte aligned address that is never dereferenced on the host
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "cq.h")).read()
+    return sorted(set(re.findall(r"^(?:cq_status|int32_t|const char \*)\s*(cq_\w+)\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert set(names) == {"cq_version", "cq_status_string", "cq_blob_bytes", "cq_workspace_bytes",
+                          "cq_rotate_acts", "cq_matvec", "cq_gemm", "cq_quantize"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert cq.cq_version() == 10000
+    for s in range(12):
+        assert lib.cq_status_string(s).decode()
+    assert lib.cq_status_string(LENGTH).decode() == "Inconsistent CQ matrix length"
+    assert lib.cq_status_string(99).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+def test_blob_bytes_matches_oracle(bits):
+    for rows, cols in [(0, 0), (1, 1), (3, 130), (512, 512), (65536, 16384), (7, 1000), (1 << 30, 128)]:
+        assert cq.cq_blob_bytes(bits, rows, cols) == oracle.blob_bytes(bits, 128, rows, cols)
+
+
+def _blob_status(bits, group, rows, cols):
+    out = ctypes.c_uint64(12345)
+    st = lib.cq_blob_bytes(bits, group, rows, cols, ctypes.byref(out))
+    return st, out.value
+
+
+def test_blob_bytes_errors_leave_output_untouched():
+    assert _blob_status(1, 128, 1, 1) == (BITS, 12345)
+    assert _blob_status(6, 128, 1, 1) == (BITS, 12345)
+    assert _blob_status(2, 64, 1, 1) == (GROUP, 12345)
+    assert _blob_status(2, 128, -1, 1) == (SHAPE, 12345)
+    assert _blob_status(2, 128, 1, (1 << 30) + 1) == (SHAPE, 12345)
+    assert lib.cq_blob_bytes(2, 128, 1, 1, None) == NULL
+
+
+_DEFAULT = object()
+
+
+def _matrix(bits=2, rows=4, cols=256, blob=FAKE, nbytes=None, levels=_DEFAULT):
+    if levels is _DEFAULT:
+        levels = None if bits == 5 else cq_inputs.codebook(bits)
+    arr = None if levels is None else np.ascontiguousarray(levels, np.float32)
+    ptr = None if arr is None else arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    nb = oracle.blob_bytes(bits, 128, rows, cols) if nbytes is None else nbytes
+    m = cq._Matrix(bits, 128, rows, cols, ctypes.c_void_p(blob), nb, ptr)
+    return m, arr
+
+
+def _matvec(m, xr=FAKE + (1 << 30), batch=1, y=FAKE + (1 << 31)):
+    return lib.cq_matvec(ctypes.byref(m), ctypes.c_void_p(xr), batch, ctypes.c_void_p(y), None, 0, None)
+
+
+def _gemm(m, xr=FAKE + (1 << 30), mm=8, c=FAKE + (1 << 31)):
+    return lib.cq_gemm(ctypes.byref(m), ctypes.c_void_p(xr), mm, ctypes.c_void_p(c), None, 0, None)
+
+
+def test_matvec_and_gemm_validation():
+    m, k = _matrix(bits=7, nbytes=0, levels=None)
+    assert _matvec(m) == BITS and _gemm(m) == BITS
+    m, k = _matrix(nbytes=oracle.blob_bytes(2, 128, 4, 256) - 1)
+    assert _matvec(m) == LENGTH and _gemm(m) == LENGTH
+    m, k = _matrix(blob=0)
+    assert _matvec(m) == NULL
+    m, k = _matrix(blob=FAKE + 8)
+    assert _matvec(m) == ALIGN
+    m, k = _matrix(levels=np.array([0.1, 0.0, 0.2, 0.3]))
+    assert _matvec(m) == CODEBOOK and _gemm(m) == CODEBOOK
+    m, k = _matrix(levels=np.array([0.0, 0.1, np.nan, 0.3]))
+    assert _matvec(m) == CODEBOOK
+    m, k = _matrix(levels=None)
+    assert _matvec(m) == CODEBOOK
+    m, k = _matrix(bits=5, levels=np.array([-1.0, 0.0, 1.0]))
+    assert _matvec(m) == CODEBOOK
+    m, k = _matrix()
+    assert _matvec(m, batch=9) == SHAPE and _matvec(m, batch=-1) == SHAPE
+    assert _gemm(m, mm=-1) == SHAPE
+    assert _matvec(m, y=0) == NULL and _gemm(m, c=0) == NULL
+    assert _matvec(m, xr=0) == NULL and _gemm(m, xr=0) == NULL
+    assert _matvec(m, xr=FAKE + 4) == ALIGN and _gemm(m, xr=FAKE + 8) == ALIGN
+    assert _matvec(m, y=FAKE + (1 << 31) + 2) == ALIGN
+    # outputs overlapping an input
+    assert _matvec(m, y=FAKE + 64) == OVERLAP
+    assert _matvec(m, y=FAKE + (1 << 30) + 16) == OVERLAP
+    assert _gemm(m, c=FAKE + (1 << 30)) == OVERLAP
+    assert lib.cq_matvec(None, None, 1, None, None, 0, None) == NULL
+
+
+def test_nothing_to_do_returns_ok_without_launching():
+    m, k = _matrix()
+    assert _matvec(m, batch=0) == OK and _gemm(m, mm=0) == OK
+    m, k = _matrix(rows=0, blob=0)
+    assert _matvec(m) == OK and _gemm(m) == OK
+    assert lib.cq_rotate_acts(ctypes.c_void_p(FAKE), 0, 0, 128, ctypes.c_void_p(FAKE), 0, None) == OK
+    assert lib.cq_rotate_acts(ctypes.c_void_p(FAKE), 0, 4, 0, ctypes.c_void_p(FAKE), 0, None) == OK
+    lv = cq_inputs.codebook(2)
+    p = lv.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    assert lib.cq_quantize(None, 0, 128, 2, 128, p, None, 0, None) == OK
+
+
+def test_rotate_validation():
+    x, xr = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + (1 << 30))
+    assert lib.cq_rotate_acts(x, 3, 1, 128, xr, 0, None) == DTYPE
+    assert lib.cq_rotate_acts(x, 0, 1, 128, xr, 1, None) == DTYPE
+    assert lib.cq_rotate_acts(x, 0, -1, 128, xr, 0, None) == SHAPE
+    assert lib.cq_rotate_acts(None, 0, 1, 128, xr, 0, None) == NULL
+    assert lib.cq_rotate_acts(ctypes.c_void_p(FAKE + 2), 0, 1, 128, xr, 0, None) == ALIGN
+    assert lib.cq_rotate_acts(x, 0, 1, 128, ctypes.c_void_p(FAKE + (1 << 30) + 4), 0, None) == ALIGN
+    assert lib.cq_rotate_acts(x, 0, 2, 128, ctypes.c_void_p(FAKE + 512), 0, None) == OVERLAP
+
+
+def test_quantize_validation():
+    lv = cq_inputs.codebook(2)
+    p = lv.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    w, blob = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + (1 << 30))
+    nb = oracle.blob_bytes(2, 128, 4, 256)
+    assert lib.cq_quantize(w, 4, 256, 6, 128, p, blob, nb, None) == BITS
+    assert lib.cq_quantize(w, 4, 256, 2, 64, p, blob, nb, None) == GROUP
+    assert lib.cq_quantize(w, 4, 256, 2, 128, None, blob, nb, None) == CODEBOOK
+    assert lib.cq_quantize(w, 4, 256, 2, 128, p, blob, nb + 1, None) == LENGTH
+    assert lib.cq_quantize(None, 4, 256, 2, 128, p, blob, nb, None) == NULL
+    assert lib.cq_quantize(w, 4, 256, 2, 128, p, ctypes.c_void_p(FAKE + (1 << 30) + 8), nb, None) == ALIGN
+    assert lib.cq_quantize(w, 4, 256, 2, 128, p, ctypes.c_void_p(FAKE + 256), nb, None) == OVERLAP
+    tern = ctypes.cast(None, ctypes.POINTER(ctypes.c_float))
+    nb5 = oracle.blob_bytes(5, 128, 4, 256)
+    assert lib.cq_quantize(w, 4, 256, 5, 128, p, blob, nb5, None) == CODEBOOK
+    assert lib.cq_quantize(w, 4, 256, 5, 128, tern, blob, nb5 - 2, None) == LENGTH
+
+
+def test_workspace_bytes():
+    m, k = _matrix()
+    out = ctypes.c_uint64(7)
+    assert lib.cq_workspace_bytes(0, ctypes.byref(m), 1, ctypes.byref(out)) == OK and out.value == 0
+    assert lib.cq_workspace_bytes(1, ctypes.byref(m), 4096, ctypes.byref(out)) == OK
+    assert lib.cq_workspace_bytes(0, ctypes.byref(m), 9, ctypes.byref(out)) == SHAPE
+    assert lib.cq_workspace_bytes(5, ctypes.byref(m), 1, ctypes.byref(out)) == SHAPE
+
+
+def test_binding_has_the_c_names():
+    for n in ("cq_blob_bytes", "cq_workspace_bytes", "cq_rotate_acts", "cq_matvec", "cq_gemm", "cq_quantize"):
+        assert callable(getattr(cq, n))

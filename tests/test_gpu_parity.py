@@ -1,0 +1,250 @@
+"""GPU parity: every entry point of libcq against the float64 oracle on the
+same seeded inputs, at sizes that span several tiles/phases with ragged tails,
+plus the degenerate cases (empty batch, zero rows, zero cols).
+
+Bars (fixed by the method's acceptance rule):
+  fp32 paths      |y - y_oracle| <= 1e-4 * ||w_hat_row||_2 * ||x||_2, cosine >= 0.99999
+  bf16 MFMA path  |C - C_oracle| <= 1e-2 * ||w_hat_row||_2 * ||x||_2, cosine >= 0.9999
+  encoder         >= 99.99 % identical indices, mismatches within 1e-5 of a
+                  decision boundary; fp16 norms identical
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import cq_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+cq = pytest.importorskip("hadamard_rotated_codebook_amd")
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _levels(bits, kind="empirical"):
+    return None if bits == 5 else cq_inputs.codebook(bits, kind)
+
+
+def _to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(DEV)
+
+
+def _cq_from_oracle(bits, rows, cols, cfg, kind="empirical"):
+    levels = _levels(bits, kind)
+    w = cq_inputs.master(cfg, bits, rows, cols)
+    blob = oracle.quantize(w, bits, levels)
+    return cq.CQMatrix(bits, rows, cols, _to_dev(blob), levels), blob, levels, w
+
+
+def _check_fp32_product(y, ref, w_hat_norms, x_norms, tol=1e-4, min_cos=0.99999):
+    y = y.astype(np.float64)
+    bound = tol * np.outer(x_norms, w_hat_norms)
+    err = np.abs(y - ref)
+    assert np.all(err <= bound), f"max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}"
+    for b in range(ref.shape[0]):
+        if np.linalg.norm(ref[b]) > 0:
+            cos = y[b] @ ref[b] / np.linalg.norm(y[b]) / np.linalg.norm(ref[b])
+            assert cos >= min_cos, cos
+
+
+# ----------------------------------------------------------------- rotation
+
+@pytest.mark.parametrize("xdt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("batch,cols", [(1, 512), (3, 300), (5, 1000), (2, 16384), (7, 127)])
+def test_rotate_acts(xdt, odt, batch, cols):
+    say("rotate", xdt, odt, batch, cols)
+    x = cq_inputs.activations(11, cols, batch, cols, xdt)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[xdt]
+    xr = cq.cq_rotate_acts(_to_dev(x, tdt), odt)
+    torch.cuda.synchronize()
+    got = xr.float().cpu().numpy().astype(np.float64)
+    ref = oracle.rotate_acts(x)
+    kpad = ref.shape[1]
+    gnorm = np.linalg.norm(np.pad(x.astype(np.float64), ((0, 0), (0, kpad - cols))).reshape(batch, -1, 128), axis=-1)
+    gnorm = np.repeat(gnorm, 128, axis=1)
+    bound = 2e-6 * gnorm + (2.0 ** -8 * np.abs(ref) if odt == torch.bfloat16 else 0)
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_rotate_empty_inputs_are_noops():
+    x = torch.zeros((0, 256), device=DEV)
+    assert cq.cq_rotate_acts(x).shape == (0, 256)
+    x = torch.zeros((3, 0), device=DEV)
+    assert cq.cq_rotate_acts(x).shape == (3, 0)
+
+
+# ------------------------------------------------------------------ matvec
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("rows,cols,batch", [
+    (512, 512, 1),       # the single 512x512 matvec workload
+    (1000, 5000, 1),     # ragged rows, partial last phase
+    (300, 9000, 3),      # several phases, batch split 2 + 1
+    (257, 2048, 4),
+    (64, 640, 8),        # batch split 4 + 4
+    (1, 128, 5),
+    (9, 16384, 2),
+])
+def test_matvec(bits, rows, cols, batch):
+    say("matvec", bits, rows, cols, batch)
+    W, blob, levels, _ = _cq_from_oracle(bits, rows, cols, 20 + batch)
+    x = cq_inputs.activations(21, rows, batch, cols)
+    xr = cq.cq_rotate_acts(_to_dev(x))
+    y = cq.cq_matvec(W, xr)
+    torch.cuda.synchronize()
+    ref = oracle.matvec(blob, bits, rows, cols, x, levels)
+    w_hat = np.linalg.norm(oracle.dequantize(blob, bits, rows, cols, levels), axis=1)
+    _check_fp32_product(y.cpu().numpy(), ref, w_hat, np.linalg.norm(x.astype(np.float64), axis=1))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_matvec_hadamard_column_probe(bits):
+    # x_g = H e_j in one group: y_r = norm[r, g] * level(q[r, g, j]) exactly up to
+    # the rotation's rounding -- pins the GPU bit layout index by index
+    rows, cols = 96, 384
+    W, blob, levels, _ = _cq_from_oracle(bits, rows, cols, 30)
+    packed, norms = oracle.split_blob(blob, bits, rows, cols)
+    vals = oracle.level_values(oracle.unpack_codes(packed, bits, cols), bits, levels)
+    H = oracle.hadamard()
+    for g in range(3):
+        for j in range(128):
+            x = np.zeros((1, cols), np.float32)
+            x[0, 128 * g:128 * (g + 1)] = H[:, j]
+            y = cq.cq_matvec(W, cq.cq_rotate_acts(_to_dev(x)))
+            expect = norms[:, g].astype(np.float64) * vals[:, 128 * g + j]
+            got = y.cpu().numpy()[0].astype(np.float64)
+            assert np.allclose(got, expect, rtol=0, atol=1e-6 * np.max(np.abs(expect))), (g, j)
+
+
+def test_matvec_degenerate_shapes():
+    levels = cq_inputs.codebook(2)
+    # cols == 0: every output is an empty sum
+    W = cq.CQMatrix(2, 5, 0, torch.zeros(0, dtype=torch.uint8, device=DEV), levels)
+    y = torch.full((2, 5), 7.0, device=DEV)
+    cq.cq_matvec(W, torch.zeros((2, 0), device=DEV), out=y)
+    assert torch.all(y == 0)
+    # rows == 0 and batch == 0 write nothing
+    W0 = cq.CQMatrix(2, 0, 256, torch.zeros(0, dtype=torch.uint8, device=DEV), levels)
+    assert cq.cq_matvec(W0, torch.zeros((1, 256), device=DEV)).shape == (1, 0)
+    W1, _, _, _ = _cq_from_oracle(2, 4, 256, 31)
+    assert cq.cq_matvec(W1, torch.zeros((0, 256), device=DEV)).shape == (0, 4)
+    # x = 0 gives y = 0
+    y = cq.cq_matvec(W1, cq.cq_rotate_acts(torch.zeros((1, 256), device=DEV)))
+    assert torch.all(y == 0)
+
+
+def test_matvec_ternary_crumb_10_sign_extends():
+    # crumb 0b10 decodes to -2a (never written by the encoder, but defined)
+    rows, cols = 2, 128
+    codes = np.full((rows, cols), 2, np.uint8)
+    norms = np.ones((rows, 1), np.float16)
+    blob = oracle.make_blob(oracle.pack_codes(codes, 5), norms)
+    W = cq.CQMatrix(5, rows, cols, _to_dev(blob), None)
+    x = cq_inputs.activations(32, 0, 1, cols)
+    y = cq.cq_matvec(W, cq.cq_rotate_acts(_to_dev(x))).cpu().numpy()
+    ref = oracle.matvec(blob, 5, rows, cols, x)
+    _check_fp32_product(y, ref, np.linalg.norm(oracle.dequantize(blob, 5, rows, cols), axis=1),
+                        np.linalg.norm(x.astype(np.float64), axis=1))
+
+
+def test_matvec_is_deterministic():
+    W, _, _, _ = _cq_from_oracle(2, 2000, 4096, 33)
+    xr = cq.cq_rotate_acts(_to_dev(cq_inputs.activations(33, 0, 1, 4096)))
+    a = cq.cq_matvec(W, xr).clone()
+    b = cq.cq_matvec(W, xr)
+    assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------- GEMM
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("m,rows,cols", [(1, 1, 128), (7, 100, 1000), (300, 200, 512), (130, 257, 640), (64, 129, 2048)])
+def test_gemm(bits, m, rows, cols):
+    say("gemm", bits, m, rows, cols)
+    W, blob, levels, _ = _cq_from_oracle(bits, rows, cols, 40 + m)
+    X = cq_inputs.activations(41, rows, m, cols, "f16")
+    xr = cq.cq_rotate_acts(_to_dev(X, torch.float16), torch.bfloat16)
+    C = cq.cq_gemm(W, xr)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy().astype(np.float64)
+    w_hat = np.linalg.norm(oracle.dequantize(blob, bits, rows, cols, levels), axis=1)
+    xn = np.linalg.norm(X.astype(np.float64), axis=1)
+    # the dense float64 product, to the bf16 bar
+    _check_fp32_product(got, oracle.gemm(blob, bits, rows, cols, X, levels), w_hat, xn, tol=1e-2, min_cos=0.9999)
+    # the same roundings as the matrix-core path (bf16 operands), much tighter
+    _check_fp32_product(got, oracle.gemm_bf16(blob, bits, rows, cols, X, levels), w_hat, xn, tol=1e-4, min_cos=0.99999)
+
+
+def test_gemm_degenerate_shapes():
+    levels = cq_inputs.codebook(4)
+    W = cq.CQMatrix(4, 6, 0, torch.zeros(0, dtype=torch.uint8, device=DEV), levels)
+    C = torch.full((3, 6), 5.0, device=DEV)
+    cq.cq_gemm(W, torch.zeros((3, 0), dtype=torch.bfloat16, device=DEV), out=C)
+    assert torch.all(C == 0)
+    W1, _, _, _ = _cq_from_oracle(4, 4, 256, 42)
+    assert cq.cq_gemm(W1, torch.zeros((0, 256), dtype=torch.bfloat16, device=DEV)).shape == (0, 4)
+
+
+# ------------------------------------------------------------------ encoder
+
+def _encoder_agreement(bits, w, blob_gpu, levels):
+    rows, cols = w.shape
+    codes_o, norms_o = oracle.encode(w, bits, levels)
+    packed_g, norms_g = oracle.split_blob(blob_gpu, bits, rows, cols)
+    codes_g = oracle.unpack_codes(packed_g, bits, codes_o.shape[1])
+    same = codes_g == codes_o
+    frac = np.mean(same)
+    assert frac >= 0.9999, frac
+    if not np.all(same):
+        # every mismatch must sit within 1e-5 of a decision boundary
+        kpad = codes_o.shape[1]
+        wp = np.zeros((rows, kpad), np.float32)
+        wp[:, :cols] = w
+        r32 = oracle.rotate_fp32(wp.reshape(rows, -1, 128))
+        n32 = np.sqrt(np.sum(r32.astype(np.float64) ** 2, axis=-1)).astype(np.float32)
+        u = (r32 / np.maximum(n32, np.float32(1e-12))[..., None]).reshape(rows, kpad).astype(np.float64)
+        lv = oracle.codebook_for(bits, levels).astype(np.float64)
+        mids = (lv[:-1] + lv[1:]) / 2
+        d = np.min(np.abs(u[~same][:, None] - mids[None, :]), axis=1)
+        assert np.all(d <= 1e-5), np.max(d)
+    assert np.array_equal(norms_g.view(np.uint16), norms_o.view(np.uint16))
+    return frac
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("kind", ["empirical", "gaussian"])
+@pytest.mark.parametrize("rows,cols", [(512, 512), (37, 1000), (3, 16384), (1, 1)])
+def test_quantize(bits, kind, rows, cols):
+    if bits == 5 and kind == "gaussian":
+        pytest.skip("ternary levels are analytic")
+    say("quantize", bits, kind, rows, cols)
+    levels = _levels(bits, kind)
+    w = cq_inputs.master(50, bits, rows, cols)
+    W = cq.cq_quantize(_to_dev(w), bits, levels)
+    torch.cuda.synchronize()
+    blob_g = W.blob.cpu().numpy()
+    assert blob_g.size == oracle.blob_bytes(bits, 128, rows, cols)
+    frac = _encoder_agreement(bits, w, blob_g, levels)
+    say("  identical index fraction", frac)
+
+
+def test_quantize_special_groups():
+    # zero groups, a constant group (exact ties), a huge group (fp16 overflow), tiny values
+    levels = np.array([-0.25, -0.125, 0.125, 0.25], np.float32)
+    w = np.zeros((4, 256), np.float32)
+    w[1, :128] = 0.03
+    w[2, :128] = 1.0e4
+    w[3, :] = 1e-30
+    W = cq.cq_quantize(_to_dev(w), 2, levels)
+    blob_g = W.blob.cpu().numpy()
+    assert np.array_equal(blob_g, oracle.quantize(w, 2, levels))
