@@ -22,7 +22,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "LIB_PATH", "CQError", "CQMatrix", "CQ_GROUP", "CQ_MAX_MATVEC_BATCH",
+    "LIB_PATH", "CQError", "CQMatrix", "CQ_GROUP", "CQ_MAX_MATVEC_BATCH", "workspace_for",
     "cq_version", "cq_blob_bytes", "cq_workspace_bytes",
     "cq_rotate_acts", "cq_matvec", "cq_gemm", "cq_quantize",
 ]
@@ -157,8 +157,28 @@ def cq_rotate_acts(x, out_dtype=torch.float32, out=None):
     return out
 
 
+_WORKSPACES = {}
+
+
+def workspace_for(nbytes, device):
+    """A zero-filled device workspace of at least ``nbytes`` bytes, cached per
+    (device, current stream).  libcq leaves a workspace ready for the next call,
+    so the cached one is reused as is; calls on one stream never overlap."""
+    if nbytes == 0:
+        return None
+    key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def cq_matvec(W, xr, out=None, workspace=None):
-    """y[b, r] = sum_g norm * <c[q], xr_g>; xr float32 [batch, cols_pad]; returns float32 [batch, rows]."""
+    """y[b, r] = sum_g norm * <c[q], xr_g>; xr float32 [batch, cols_pad]; returns float32 [batch, rows].
+
+    ``workspace``: a zero-filled uint8 device tensor of cq_workspace_bytes()
+    bytes, or None to use a cached one for the current stream."""
     if xr.dtype != torch.float32 or xr.dim() != 2 or xr.shape[1] != _padded(W.cols):
         raise ValueError("xr must be float32 [batch, cols_pad]")
     b = xr.shape[0]
@@ -167,6 +187,10 @@ def cq_matvec(W, xr, out=None, workspace=None):
     if out.dtype != torch.float32 or tuple(out.shape) != (b, W.rows):
         raise ValueError("out must be float32 [batch, rows]")
     m, keep = W._struct()
+    if workspace is None and b > 0 and W.rows > 0:
+        need = _u64(0)
+        _check(_lib.cq_workspace_bytes(OP_MATVEC, ctypes.byref(m), b, ctypes.byref(need)))
+        workspace = workspace_for(int(need.value), xr.device)
     ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.cq_matvec(ctypes.byref(m), _dev(xr, "xr"), b, _dev(out, "out"), ws, wsb, _stream()))

@@ -112,12 +112,13 @@ cq_status cq_workspace_bytes(int32_t op, const cq_matrix *W, int64_t batch, uint
   if (st != CQ_OK) return st;
   if (op == CQ_OP_MATVEC) {
     if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+    *bytes = W->rows ? cq::matvec_workspace_bytes(W->bits, W->rows, padded(W->cols), batch) : 0;
   } else if (op == CQ_OP_GEMM) {
     if (batch < 0 || batch > CQ_MAX_DIM) return CQ_ERR_SHAPE;
+    *bytes = 0;
   } else {
     return CQ_ERR_SHAPE;
   }
-  *bytes = 0;  // no kernel of this version needs scratch memory
   return CQ_OK;
 }
 
@@ -139,8 +140,6 @@ cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t 
 
 cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y, void *workspace,
                     uint64_t workspace_bytes, void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   cq::CodeLevels lev;
   cq_status st = check_matrix(W, &lev);
   if (st != CQ_OK) return st;
@@ -154,11 +153,18 @@ cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y
   if (kpad == 0) return hip_status(cq::launch_zero_f32(y, batch * W->rows, s));
   if (!xr) return CQ_ERR_NULL;
   if (!aligned(xr, 16)) return CQ_ERR_ALIGN;
-  if (overlaps(y, ybytes, xr, static_cast<uint64_t>(batch) * kpad * 4) ||
-      overlaps(y, ybytes, W->blob, W->blob_bytes))
+  const uint64_t need = cq::matvec_workspace_bytes(W->bits, W->rows, kpad, batch);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return CQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return CQ_ERR_ALIGN;
+  }
+  const uint64_t xbytes = static_cast<uint64_t>(batch) * kpad * 4;
+  if (overlaps(y, ybytes, xr, xbytes) || overlaps(y, ybytes, W->blob, W->blob_bytes) ||
+      overlaps(workspace, need, y, ybytes) || overlaps(workspace, need, xr, xbytes) ||
+      overlaps(workspace, need, W->blob, W->blob_bytes))
     return CQ_ERR_OVERLAP;
   return hip_status(cq::launch_matvec(static_cast<const uint8_t *>(W->blob), W->bits, W->rows, kpad,
-                                      lev, xr, batch, y, s));
+                                      lev, xr, batch, y, need ? workspace : nullptr, s));
 }
 
 cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c, void *workspace,

@@ -117,6 +117,12 @@ typedef enum cq_op { CQ_OP_MATVEC = 0, CQ_OP_GEMM = 1 } cq_op;
 /*
  * Device workspace (bytes) that `op` needs for `W` and the given batch (M for
  * the GEMM).  Host-only.  0 means the call takes workspace = NULL.
+ *
+ * A workspace is device memory owned by the caller, 16-byte aligned.  It must
+ * be zero-filled before its first use; every call that completes leaves it
+ * all zeros again (it holds per-call partial sums and completion counters).
+ * Calls that may run at the same time must not share a workspace.  One
+ * workspace sized for the largest matrix and batch serves all smaller calls.
  */
 cq_status cq_workspace_bytes(int32_t op, const cq_matrix *W, int64_t batch,
                              uint64_t *bytes);
@@ -152,7 +158,11 @@ cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t 
  *   batch    0 <= batch <= CQ_MAX_MATVEC_BATCH
  *   y        device fp32 [batch][W.rows], 4-byte aligned, must not overlap
  *            xr or the blob; fully overwritten (0 where cols == 0)
- *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_MATVEC)
+ *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_MATVEC),
+ *            see cq_workspace_bytes (NULL, 0 when that is 0); must not
+ *            overlap any other buffer of the call
+ *   Results do not depend on scheduling: the partial sums of the K slices are
+ *   added in a fixed order.
  */
 cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y,
                     void *workspace, uint64_t workspace_bytes, void *stream);

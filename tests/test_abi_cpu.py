@@ -155,6 +155,26 @@ def test_quantize_validation():
     assert lib.cq_quantize(w, 4, 256, 5, 128, tern, blob, nb5 - 2, None) == LENGTH
 
 
+def test_matvec_workspace_rules():
+    # K beyond one LDS slice needs a workspace: partial sums per slice + counters
+    m, k = _matrix(rows=1000, cols=16384)
+    need = ctypes.c_uint64()
+    assert lib.cq_workspace_bytes(0, ctypes.byref(m), 1, ctypes.byref(need)) == OK
+    nslice = 4  # 4096 columns of 2-bit tables per slice
+    assert need.value >= nslice * 1000 * 4
+    ws = FAKE + (1 << 32)
+    call = lambda w, n: lib.cq_matvec(ctypes.byref(m), ctypes.c_void_p(FAKE + (1 << 30)), 1,
+                                      ctypes.c_void_p(FAKE + (1 << 31)), ctypes.c_void_p(w), n, None)
+    assert call(0, 0) == WORKSPACE
+    assert call(ws, need.value - 1) == WORKSPACE
+    assert call(ws + 4, need.value) == ALIGN
+    assert call(FAKE + (1 << 31) + 64, need.value) == OVERLAP  # workspace on top of y
+    # batch chunks of up to 4 vectors share one workspace
+    need8 = ctypes.c_uint64()
+    assert lib.cq_workspace_bytes(0, ctypes.byref(m), 8, ctypes.byref(need8)) == OK
+    assert need8.value >= 4 * need.value - 4096
+
+
 def test_workspace_bytes():
     m, k = _matrix()
     out = ctypes.c_uint64(7)
@@ -162,6 +182,15 @@ def test_workspace_bytes():
     assert lib.cq_workspace_bytes(1, ctypes.byref(m), 4096, ctypes.byref(out)) == OK
     assert lib.cq_workspace_bytes(0, ctypes.byref(m), 9, ctypes.byref(out)) == SHAPE
     assert lib.cq_workspace_bytes(5, ctypes.byref(m), 1, ctypes.byref(out)) == SHAPE
+    # empty K or no rows: nothing is launched, so no workspace (and no division by zero)
+    for rows, cols in ((5, 0), (0, 256), (0, 0)):
+        e, _ = _matrix(rows=rows, cols=cols)
+        out.value = 7
+        assert lib.cq_workspace_bytes(0, ctypes.byref(e), 8, ctypes.byref(out)) == OK and out.value == 0
+    # a K split over several slices needs counters and partial sums
+    big, _ = _matrix(rows=65536, cols=16384)
+    assert lib.cq_workspace_bytes(0, ctypes.byref(big), 1, ctypes.byref(out)) == OK
+    assert out.value > 0 and out.value % 16 == 0
 
 
 def test_binding_has_the_c_names():

@@ -157,9 +157,33 @@ def test_matvec_ternary_crumb_10_sign_extends():
                         np.linalg.norm(x.astype(np.float64), axis=1))
 
 
+def test_matvec_workspace_reuse_across_shapes():
+    # one zero-filled workspace serves calls with different slice counts and
+    # row-block counts: each call must leave its counters at zero
+    shapes = [(4, 3000, 16384, 1), (2, 700, 16384, 3), (3, 5000, 9000, 1), (5, 64, 16384, 8), (4, 3000, 16384, 1)]
+    ws = torch.zeros(1 << 24, dtype=torch.uint8, device=DEV)
+    for bits, rows, cols, batch in shapes:
+        W, blob, levels, _ = _cq_from_oracle(bits, rows, cols, 34)
+        x = cq_inputs.activations(34, rows, batch, cols)
+        y = cq.cq_matvec(W, cq.cq_rotate_acts(_to_dev(x)), workspace=ws)
+        ref = oracle.matvec(blob, bits, rows, cols, x, levels)
+        w_hat = np.linalg.norm(oracle.dequantize(blob, bits, rows, cols, levels), axis=1)
+        _check_fp32_product(y.cpu().numpy(), ref, w_hat, np.linalg.norm(x.astype(np.float64), axis=1))
+
+
+def test_matvec_rejects_small_workspace():
+    W, _, _, _ = _cq_from_oracle(2, 100, 16384, 35)
+    xr = torch.zeros((1, 16384), device=DEV)
+    need = cq.cq_workspace_bytes(0, W, 1)
+    assert need > 0
+    with pytest.raises(cq.CQError) as e:
+        cq.cq_matvec(W, xr, workspace=torch.zeros(need - 16, dtype=torch.uint8, device=DEV))
+    assert e.value.status == 8
+
+
 def test_matvec_is_deterministic():
-    W, _, _, _ = _cq_from_oracle(2, 2000, 4096, 33)
-    xr = cq.cq_rotate_acts(_to_dev(cq_inputs.activations(33, 0, 1, 4096)))
+    W, _, _, _ = _cq_from_oracle(2, 2000, 16384, 33)
+    xr = cq.cq_rotate_acts(_to_dev(cq_inputs.activations(33, 0, 1, 16384)))
     a = cq.cq_matvec(W, xr).clone()
     b = cq.cq_matvec(W, xr)
     assert torch.equal(a, b)
