@@ -161,15 +161,15 @@ _WORKSPACES = {}
 
 
 def workspace_for(nbytes, device):
-    """A zero-filled device workspace of at least ``nbytes`` bytes, cached per
-    (device, current stream).  libcq leaves a workspace ready for the next call,
-    so the cached one is reused as is; calls on one stream never overlap."""
+    """A device workspace of at least ``nbytes`` bytes, cached per (device,
+    current stream).  libcq needs no particular contents in it, and calls on
+    one stream never overlap, so the cached one is reused as is."""
     if nbytes == 0:
         return None
     key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws
 
@@ -177,8 +177,8 @@ def workspace_for(nbytes, device):
 def cq_matvec(W, xr, out=None, workspace=None):
     """y[b, r] = sum_g norm * <c[q], xr_g>; xr float32 [batch, cols_pad]; returns float32 [batch, rows].
 
-    ``workspace``: a zero-filled uint8 device tensor of cq_workspace_bytes()
-    bytes, or None to use a cached one for the current stream."""
+    ``workspace``: a uint8 device tensor of at least cq_workspace_bytes()
+    bytes (any contents), or None to use a cached one for the current stream."""
     if xr.dtype != torch.float32 or xr.dim() != 2 or xr.shape[1] != _padded(W.cols):
         raise ValueError("xr must be float32 [batch, cols_pad]")
     b = xr.shape[0]

@@ -24,6 +24,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Keep single-lane atomics as written: the wave-combining rewrite waits for
+    # the atomic's return at once, which drains the matvec's load pipeline.
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

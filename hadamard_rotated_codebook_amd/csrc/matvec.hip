@@ -1,391 +1,441 @@
 // Decode matrix-vector product y = W . x for a CQ matrix (equation (1) of
 // include/cq.h), computed as sum_g norm_g * <c[q_g], H x_g> on the rotated
 // activation xr (OpenNeedle reference notes, rotated-activation identity; the
-// ".cact" format post, "How the kernel reads it": the kernel never expands the
-// stored indices and no weight is materialised).
+// ".cact" format post, "How the kernel reads it": the stored indices are looked
+// up, never expanded, and no weight is materialised).
 //
-// Design (HBM-bound at batch 1):
-//  * K is cut into slices whose lookup tables fill 128 KB of LDS.  A
-//    persistent 512-thread workgroup per CU owns one slice, builds its tables
-//    once from the rotated activation, and then streams its slice of the packed
-//    bytes of several 256-row blocks.  The workgroups of the other slices run
-//    at the same time on other CUs and read the other parts of the same rows,
-//    so every packed row is fetched whole from HBM within a short window (a
-//    slice-by-slice walk of K inside one workgroup leaves 1 KB holes in each
-//    4 KB row and measured ~35 % slower).
-//  * 2-bit rows (CQ2 and ternary crumbs): one 16-entry table per pair of
-//    columns, T[v] = lev[v & 3] * x0 + lev[v >> 2] * x1, so one nibble of
-//    packed data (two weights) costs one LDS read and one add.
-//    4-bit rows: one 16-entry table per column, T[v] = lev[v] * x.
-//  * A lane reads 16 consecutive packed bytes of a row (dwordx4, coalesced).
-//    The nibble -> table address is one v_perm_b32 that drops the data byte
-//    next to a per-lane slot: address = value*stride + lane*4 + block*blk_stride,
-//    so in every LDS read the 64 lanes hit 64 different 4-byte slots (one
-//    table per lane) and the access is bank-conflict free.
-//  * Low nibbles index region 0 (stride 256 B per value), high nibbles region
-//    1 (their value already sits at bits 4..7, so stride 4096 B); both masks
-//    take one AND per dword.
-//  * 3-bit rows: one 8-entry table per column; the 3-bit field is extracted
-//    with v_bfe (indices cross byte boundaries) and placed next to the lane
-//    slot with one shift-or.
-//  * Every lane keeps one partial per row slot; the group norm scales it once
-//    per row, and a halving exchange reduces all row slots of a wave at the
-//    end of a row block.  Loads run kAhead rows ahead of the arithmetic, across
-//    row-block boundaries, from clamped in-bounds addresses (no branches, so
-//    the compiler never has to drain the load queue).
-//  * With more than one slice, each workgroup writes its per-row partials to
-//    the caller's workspace; the last of the slices to finish a row block
-//    (an agent-scope counter, release/acquire fences) adds the partials in
-//    slice order and writes y, then resets the counter: the result does not
-//    depend on which workgroup finishes first.
+// Design (HBM-bound at batch 1 on MI355X):
+//  * Lookup tables are indexed by a whole packed field: one byte for 2-bit rows
+//    (CQ2 and ternary crumbs, 4 weights per lookup) and for 4-bit rows (2
+//    weights), one 6-bit field (2 codes) for 3-bit rows.  An entry is the sum
+//    over the field's codes of level * xr, computed in fp32 and stored as fp16
+//    after scaling by a power of two chosen per K-slice (the largest possible
+//    entry lands in [2^14, 2^15)).  Each entry is rounded once; the product with
+//    the fp16 group norm and every sum are fp32 (v_fma_mix), and the scale is
+//    undone exactly after the row reduction.  Compared with 16-entry tables per
+//    pair of columns this halves the LDS reads per weight, which together with
+//    the VALU work bounded the kernel below HBM speed.
+//  * A 1024-thread workgroup (one per CU: the tables take 128 KB of LDS) owns
+//    one K-slice -- the columns whose tables fill 128 KB: 1024 columns at CQ2,
+//    512 at CQ4, 2048 at CQ3 -- builds its tables once, and streams that slice
+//    of every row of its row blocks.  Each lane owns a fixed run of columns and
+//    a private 4-byte slot in every table row (two fp16 positions per slot), so
+//    the 64 lookups of a wave never collide in an LDS bank.
+//  * Table address: one v_perm_b32 for byte fields (the data byte lands next to
+//    the lane slot and the region bit), v_bfe + v_lshl_or for 6-bit fields; the
+//    half of the slot rides in the LDS instruction's immediate offset.  At CQ2 a
+//    lane spends 4 v_perm, 4 LDS reads and 4 v_fma_mix on 16 weights of a row.
+//  * Rows are read through buffer descriptors rebased per row in scalar
+//    registers.  A row past the end of its block or of the matrix gets a
+//    zero-length descriptor and reads zeros, as do lanes past the end of K (their
+//    offsets are out of range): no clamping and no branches, so the loads can run
+//    AHEAD rows ahead of the arithmetic without the compiler draining them.
+//  * The per-lane partial sums of a wave's 32 row slots are reduced across the 64
+//    lanes with the lane-swap instructions (32- and 16-lane halves) and three DPP
+//    halving steps: VALU only, no LDS traffic.
+//  * Workgroup id -> (slice, row blocks) is XCD-aware.  Consecutive workgroup ids
+//    are dispatched to different XCDs; the mapping gives each XCD every slice of
+//    its row blocks, so all of a row's bytes and its norms (a 128-byte line of
+//    norms spans several slices) go through one L2.
+//  * With more than one slice, the workgroups write per-slice partial sums of
+//    each row to the caller's workspace with plain stores, and a second small
+//    kernel adds the slices of each row in slice order: the result does not
+//    depend on scheduling.  (An in-kernel combine -- agent-scope partial stores
+//    and per-block completion counters, the last arrival adding up -- cost
+//    more than this kernel boundary: the counter protocol stalls the waves and
+//    the coherent stores go to memory one 4-byte write at a time.)
 #include "cq_internal.h"
 
 namespace {
 
-#ifndef CQ_MV_THREADS
-#define CQ_MV_THREADS 512
-#endif
-#ifndef CQ_MV_ROWS_PER_WAVE
-#define CQ_MV_ROWS_PER_WAVE 32
-#endif
 #ifndef CQ_MV_AHEAD
-#define CQ_MV_AHEAD 8
+#define CQ_MV_AHEAD 16
 #endif
-constexpr int kThreads = CQ_MV_THREADS;     // one workgroup per CU (128 KB LDS)
+constexpr int kThreads = 1024;                        // one workgroup per CU
 constexpr int kWaves = kThreads / 64;
-constexpr int kRowsPerWave = CQ_MV_ROWS_PER_WAVE;     // row slots per wave (fully unrolled)
-constexpr int kRowsPerBlock = kWaves * kRowsPerWave;  // rows of one row block (256)
-constexpr int kAhead = CQ_MV_AHEAD;         // rows whose loads are in flight ahead of the arithmetic
-static_assert((kRowsPerWave & (kRowsPerWave - 1)) == 0 && kRowsPerWave <= 64, "row slots: power of two");
-static_assert(kRowsPerWave % kAhead == 0, "prefetch ring must divide the row slots");
+constexpr int kRowsPerWave = 32;                      // row slots per wave (fully unrolled)
+constexpr int kRowsPerBlock = kWaves * kRowsPerWave;  // rows of a full row block (512)
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;     // buffer descriptor: raw, 32-bit data format
+constexpr uint32_t kOutOfRange = 0x7ffff000u;         // a buffer offset past any descriptor's length
+
+// Geometry of a storage width SB (2: CQ2 and ternary crumbs, 3: CQ3, 4: CQ4).
+template <int SB>
+struct Geom {
+  static constexpr int LANE_BYTES = SB == 3 ? 12 : 4;            // packed bytes per lane and row
+  static constexpr int LANE_COLS = LANE_BYTES * 8 / SB;          // 16, 32, 8 columns per lane
+  static constexpr int IDX_BITS = SB == 3 ? 6 : 8;               // bits of a table index
+  static constexpr int ENTRIES = 1 << IDX_BITS;                  // entries per table
+  static constexpr int CODES = IDX_BITS / SB;                    // codes per table index
+  static constexpr int POSITIONS = LANE_COLS / CODES;            // tables per lane: 4, 16, 4
+  static constexpr int REGION = ENTRIES * 256;                   // bytes per pair of positions
+  static constexpr int LDS_BYTES = POSITIONS / 2 * REGION;       // 128 KB
+  static constexpr int SLICE_COLS = 64 * LANE_COLS;              // 1024, 2048, 512
+  static constexpr int SLICE_BYTES = 64 * LANE_BYTES;            // 256, 768, 256
+  static constexpr int SLICE_GROUPS = SLICE_COLS / CQ_GROUP;     // 8, 16, 4
+  static constexpr int LANES_PER_GROUP = CQ_GROUP / LANE_COLS;   // 8, 4, 16
+  static constexpr int AHEAD = SB == 3 ? 8 : CQ_MV_AHEAD;        // rows of loads in flight per wave
+  static constexpr int DWORDS = LANE_BYTES / 4;
+  static constexpr int LOOKUPS = LANE_BYTES * 8 / IDX_BITS;     // table reads per lane and row
+  static_assert(LDS_BYTES == 128 * 1024, "tables fill 128 KB");
+  static_assert(kRowsPerWave % AHEAD == 0 && AHEAD < kRowsPerWave, "prefetch ring: divides the row slots");
+};
 
 struct MvArgs {
   const uint8_t *packed;
   const uint16_t *norms;  // fp16 bits, [rows][ngroups]
-  const float *xr;        // [nb][kpad]
-  float *y;               // [nb][rows]
-  float *partial;         // [nslice][nb][rows] (nslice > 1)
-  uint32_t *counter;      // [nblocks] (nslice > 1), zero between calls
+  const float *xr;        // [kpad]
+  float *y;               // [rows]
+  float *partial;         // [nslice][rows] (nslice > 1)
   int64_t rows, kpad, row_bytes, ngroups;
   int32_t rows_per_block;  // multiple of kWaves, <= kRowsPerBlock
   int32_t nblocks;         // row blocks
   int32_t nslice;          // K slices
   int32_t per_slice;       // workgroups per slice (grid = nslice * per_slice)
+  float lev_absmax;        // largest |level| of the code book
   cq::CodeLevels lev;
 };
 
-__device__ inline float half_to_float(uint16_t h) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+__device__ inline _Float16 lds_half(const uint8_t *lds, uint32_t byte_addr) {
+  return *reinterpret_cast<const _Float16 *>(lds + byte_addr);
 }
 
-__device__ inline float lds_at(const float *lds, uint32_t byte_addr) {
-  return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(lds) + byte_addr);
+__device__ inline __amdgpu_buffer_rsrc_t buffer(uint64_t addr, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(addr), 0, static_cast<int>(nbytes),
+                                           static_cast<int>(kRawBufferWord3));
 }
 
-// Lanes that hold row slot m after reduce_rows: lanes kLanesPerRow*m ... +kLanesPerRow-1.
-constexpr int kLanesPerRow = 64 / kRowsPerWave;
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 
 // Bitwise select (one v_bfi_b32): a where mask is 0, b where it is all ones.
 __device__ inline float pick(float a, float b, uint32_t mask) {
   return __uint_as_float((__float_as_uint(a) & ~mask) | (__float_as_uint(b) & mask));
 }
 
-// Sum kRowsPerWave per-lane partials over the 64 lanes of a wave.  Halving
-// exchange: at lane distance 32, 16, ... each lane keeps half of its values
-// (upper lanes the upper half) and adds the partner's copy of them; the rest of
-// the lane distances then sum the remaining single value.  Afterwards the
-// lanes kLanesPerRow*m .. +kLanesPerRow-1 hold the total of row slot m.
+// One halving step: values i and H+i of each lane pair up with a partner lane
+// (DPP pattern CTRL, partner in the other half selected by `upper`); the lower
+// lanes keep value i, the upper lanes value H+i, each adding the partner's
+// copy of it.
+template <int H, int CTRL>
+__device__ inline void halve(float *v, uint32_t upper) {
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float keep = pick(v[i], v[H + i], upper);
+    const float send = pick(v[H + i], v[i], upper);
+    v[i] = keep + dpp<CTRL>(send);
+  }
+}
+
+// Sum each of the 32 row-slot partials over the 64 lanes of the wave.  After
+// it, lanes 2m and 2m+1 hold the total of row slot m.
 __device__ inline float reduce_rows(float (&v)[kRowsPerWave], int lane) {
+  static_assert(kRowsPerWave == 32, "the swap/DPP schedule is written for 32 row slots");
 #pragma unroll
-  for (int half = kRowsPerWave / 2, dist = 32; half >= 1; half >>= 1, dist >>= 1) {
-    const uint32_t upper = (lane & dist) ? 0xffffffffu : 0u;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float keep = pick(v[i], v[half + i], upper);
-      const float send = pick(v[half + i], v[i], upper);
-      v[i] = keep + __shfl_xor(send, dist);
-    }
+  for (int i = 0; i < 16; ++i) {  // lanes 0-31 <-> 32-63: rows i (low half) and 16+i (high half)
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[16 + i]), false, false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
-  float t = v[0];
 #pragma unroll
-  for (int dist = kLanesPerRow / 2; dist >= 1; dist >>= 1) t += __shfl_xor(t, dist);
-  return t;
+  for (int i = 0; i < 8; ++i) {  // 16-lane rows within each half
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[8 + i]), false, false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  halve<4, 0x128>(v, (lane & 8) ? ~0u : 0u);  // row_ror:8        pairs lane k with k^8 in a row
+  halve<2, 0x141>(v, (lane & 4) ? ~0u : 0u);  // row_half_mirror  pairs k with 7-k in 8 lanes
+  halve<1, 0x4e>(v, (lane & 2) ? ~0u : 0u);   // quad_perm 2301   pairs k with k^2
+  return v[0] + dpp<0xb1>(v[0]);              // quad_perm 1032   pairs k with k^1
 }
 
-// Write a row block's per-row totals: directly to y with one slice, else via
-// the workspace, where the last slice to arrive adds the partials in slice
-// order.  All threads of the workgroup call this (it contains barriers).
-//
-// The partials cross CUs (and XCDs, whose L2s are not coherent with each
-// other for plain stores): they are written and read with agent-scope atomic
-// stores/loads, which bypass the non-coherent cache levels.  Each thread waits
-// for its stores to complete (workgroup-scope release: a counter wait, no
-// cache flush) before the barrier; only then does one thread bump the row
-// block's counter.  The last arriver reads the partials, writes y, and clears
-// the partials and the counter, so the workspace is all zeros between calls.
-template <int NB>
-__device__ void finish_block(const MvArgs &a, int slice, int blk, int64_t r0, int64_t r1, int wave, int lane,
-                             const float (&t)[NB]) {
-  const int64_t r = r0 + wave + static_cast<int64_t>(kWaves) * (lane / kLanesPerRow);
-  const bool writer = lane % kLanesPerRow == 0 && r < r1;
-  if (a.nslice == 1) {
-    if (writer)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) a.y[nb * a.rows + r] = t[nb];
-    return;
-  }
-  if (writer)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      __hip_atomic_store(a.partial + (static_cast<int64_t>(slice) * NB + nb) * a.rows + r, t[nb], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  __shared__ int is_last;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(a.counter + blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = old == static_cast<uint32_t>(a.nslice - 1);
-  }
-  __syncthreads();
-  if (is_last) {
-    const int n = static_cast<int>(r1 - r0);
-    for (int i = threadIdx.x; i < NB * n; i += kThreads) {
-      const int nb = i / n;
-      const int64_t rr = r0 + (i - nb * n);
-      float acc = 0.0f;
-      for (int sl = 0; sl < a.nslice; ++sl) {
-        float *p = a.partial + (static_cast<int64_t>(sl) * NB + nb) * a.rows + rr;
-        acc += __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(p, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      a.y[nb * a.rows + rr] = acc;
-    }
-    if (threadIdx.x == 0) __hip_atomic_store(a.counter + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
+// Store a unit's per-row totals: straight to y with one slice, else to this
+// slice's partial sums [slice][row] in the workspace.
+__device__ inline void store_block(const MvArgs &a, int slice, int64_t r0, int64_t r1, int slot, int lane, float t) {
+  const int64_t r = r0 + slot + static_cast<int64_t>(kWaves) * (lane >> 1);
+  if ((lane & 1) || r >= r1) return;
+  if (a.nslice == 1)
+    a.y[r] = t;
+  else
+    a.partial[static_cast<int64_t>(slice) * a.rows + r] = t;
 }
 
-// ---------------------------------------------------------------------------
-// One kernel for all widths.  SB = 2 or 4: nibble tables; SB = 3: column tables
-// (one batch vector).  NB batch vectors share each packed byte.
-// Table layouts (per lane slot s = lane*4 bytes, nibble value v):
-//  * wide (D*NB == 4, 128 KB): low nibbles at v*256 + s + blk*4096, high nibbles
-//    left in place (value*16) at 64 KB + v*4096 + s + blk*256;
-//  * compact (D*NB <= 2, 32*D*NB KB): both nibbles at v*256 + s + blk*4096, the
-//    high nibble shifted down first (one extra shift per dword).
-template <int SB, int NB, int D>
+// Power-of-two scale that puts the largest possible table entry of this slice
+// in [2^14, 2^15): the exponent k of 2^k (0 when the slice's activations are
+// all zero or not finite; clamped so both 2^k and 2^-k are normal floats).
+__device__ inline int table_exponent(float bound) {
+  if (!(bound > 0.0f) || !(bound <= 3.0e38f)) return 0;
+  int e;
+  (void)frexpf(bound, &e);  // bound < 2^e
+  return max(-100, min(100, 15 - e));
+}
+
+template <int SB>
 __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
-  static_assert(SB != 3 || (NB == 1 && D == 3), "3-bit rows: one batch vector, 12 bytes per lane");
-  static_assert(SB == 3 || D * NB <= 4, "nibble tables fit 128 KB");
-  constexpr bool WIDE = SB != 3 && D * NB == 4;
-  constexpr int LDS_FLOATS = SB == 3 ? 16384 : 8192 * D * NB;
-  __shared__ float lds[LDS_FLOATS];
-  constexpr int LANE_COLS = SB == 3 ? 32 : 4 * D * (8 / SB);  // columns per lane
-  constexpr int SLICE_COLS = 64 * LANE_COLS;
-  constexpr int SLICE_BYTES = SLICE_COLS * SB / 8;
-  constexpr int BLOCKS = 4 * D;                      // nibble tables per lane, region, batch vector
-  constexpr int TPT = SB == 3 ? (LANE_COLS + kWaves - 1) / kWaves : (2 * NB * BLOCKS + kWaves - 1) / kWaves;
-  constexpr int NTAB = SB == 3 ? LANE_COLS : 2 * NB * BLOCKS;  // tables per lane slot
-  constexpr int XPT = SB == 2 ? 2 : 1;               // activations per table
+  using G = Geom<SB>;
+  __shared__ __align__(16) uint8_t lds[G::LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps row addressing scalar
-  const int slice = blockIdx.x % a.nslice;
-  const int first_blk = blockIdx.x / a.nslice;
-  const int64_t c_lane = static_cast<int64_t>(slice) * SLICE_COLS + lane * LANE_COLS;  // lane's first column
+  // XCD-aware id: consecutive ids go to different XCDs (8 of them); renumber so
+  // that each XCD's ids are contiguous, then slices vary fastest.
+  int j = blockIdx.x;
+  if ((gridDim.x & 7) == 0) j = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int slice = j % a.nslice;
+  const int first_blk = j / a.nslice;
+  const int my_blocks = first_blk < a.nblocks ? (a.nblocks - 1 - first_blk) / a.per_slice + 1 : 0;
+
+  // Slice geometry.  Lanes past the end of K (only in the last slice) read
+  // zeros and own all-zero tables.
+  const int64_t c_lane = static_cast<int64_t>(slice) * G::SLICE_COLS + lane * G::LANE_COLS;
   const bool lane_active = c_lane < a.kpad;
-  const uint32_t lane_byte = lane_active ? static_cast<uint32_t>(lane * (LANE_COLS * SB / 8)) : 0u;
-  const uint32_t lane_group = lane_active ? static_cast<uint32_t>(lane * LANE_COLS) >> 7 : 0u;
-  const uint8_t *slice_packed = a.packed + static_cast<int64_t>(slice) * SLICE_BYTES;
-  const uint16_t *slice_norms = a.norms + static_cast<int64_t>(slice) * (SLICE_COLS / 128);
+  const uint32_t chunk_bytes = static_cast<uint32_t>(
+      min(static_cast<int64_t>(G::SLICE_BYTES), a.row_bytes - static_cast<int64_t>(slice) * G::SLICE_BYTES));
+  const uint32_t chunk_norm_bytes = static_cast<uint32_t>(
+      2 * min(static_cast<int64_t>(G::SLICE_GROUPS), a.ngroups - static_cast<int64_t>(slice) * G::SLICE_GROUPS));
+  const uint32_t voff_data = lane_active ? static_cast<uint32_t>(lane * G::LANE_BYTES) : kOutOfRange;
+  const uint32_t voff_norm = lane_active ? static_cast<uint32_t>(lane / G::LANES_PER_GROUP) * 2u : kOutOfRange;
+  const uint64_t slice_packed = reinterpret_cast<uint64_t>(a.packed) + static_cast<uint64_t>(slice) * G::SLICE_BYTES;
+  const uint64_t slice_norms =
+      reinterpret_cast<uint64_t>(a.norms) + static_cast<uint64_t>(slice) * G::SLICE_GROUPS * 2;
 
-  // Lanes past the end of K in the last slice read table slots that nothing
-  // writes; their partials are multiplied by a zero norm, so clear LDS once to
-  // keep those reads finite.
-  for (int i = tid; i < LDS_FLOATS / 4; i += kThreads)
-    reinterpret_cast<float4 *>(lds)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  __syncthreads();
-
-  // Build this slice's tables.  Thread (wave, lane) builds tables
-  // t = wave + kWaves*i in its lane's slot.
-#pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    const int t = wave + kWaves * i;
-    if (t >= NTAB) break;
-    if (SB == 3) {
-      const int64_t c = c_lane + t;
-      const float x0 = c < a.kpad ? a.xr[c] : 0.0f;
-#pragma unroll
-      for (int v = 0; v < 8; ++v) lds[(v * 256u + lane * 4u + t * 2048u) >> 2] = a.lev.v[v] * x0;
+  // Work units: unit u is the 32 rows r0 + (u % kWaves) + kWaves*m, m < 32, of
+  // the workgroup's row block u / kWaves (blocks first_blk, first_blk +
+  // per_slice, ...).  Wave w starts with unit w and then takes the next unit
+  // from an LDS counter, one unit ahead: the issue arbiter favours older waves,
+  // and with a fixed share per wave the youngest waves of a CU finished far
+  // behind the others.  The loads walk the rows of the current unit and then of
+  // the next one AHEAD rows ahead of the arithmetic, with scalar bookkeeping:
+  // rows left in the unit and the two row addresses.
+  const int units = my_blocks * kWaves;
+  __shared__ int next_unit;
+  const uint64_t row_step = static_cast<uint64_t>(kWaves) * a.row_bytes;
+  const uint64_t nrow_step = static_cast<uint64_t>(kWaves) * a.ngroups * 2;
+  int lk = 0, nlive = 0;  // loads issued in the current unit, live rows in it
+  uint64_t lp = 0, lq = 0;
+  auto start_unit = [&](int uu) {
+    const int64_t blk = first_blk + static_cast<int64_t>(uu / kWaves) * a.per_slice;
+    const int64_t r0 = blk * a.rows_per_block;
+    const int64_t lrow = r0 + uu % kWaves;
+    const int64_t lend = uu < units ? min(r0 + a.rows_per_block, a.rows) : 0;
+    nlive = __builtin_amdgcn_readfirstlane(lend > lrow ? static_cast<int>((lend - lrow + kWaves - 1) / kWaves) : 0);
+    lk = 0;
+    lp = slice_packed + static_cast<uint64_t>(lrow) * a.row_bytes;
+    lq = slice_norms + static_cast<uint64_t>(lrow) * a.ngroups * 2;
+  };
+  auto load_next = [&](uint32_t (&d)[G::DWORDS], uint32_t &nraw) {
+    const bool live = lk < nlive;
+    const __amdgpu_buffer_rsrc_t rd = buffer(lp, live ? chunk_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rn = buffer(lq, live ? chunk_norm_bytes : 0u);
+    // Keep every row's two loads in one fixed order, in the prologue as in the
+    // loop: the wait counts at the loop header are merged over both paths, and
+    // a different order there makes the compiler drain the prefetch ring.
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SB == 3) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b96(rd, voff_data, 0, 0);
+      d[0] = v[0];
+      d[1 % G::DWORDS] = v[1];
+      d[2 % G::DWORDS] = v[2];
     } else {
-      const int hi = t & 1, blk = t >> 1, nb = blk / BLOCKS, beta = blk - nb * BLOCKS;
-      const int64_t c = c_lane + (SB == 2 ? 4 * beta + 2 * hi : 2 * beta + hi);
-      float x[XPT];
+      d[0] = __builtin_amdgcn_raw_buffer_load_b32(rd, voff_data, 0, 0);
+    }
+    nraw = __builtin_amdgcn_raw_buffer_load_b16(rn, voff_norm, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    ++lk;
+    lp += row_step;
+    lq += nrow_step;
+  };
+
+  // ---- tables: entry (position p, index v, lane) at byte
+  //      (p >> 1) * REGION + v * 256 + lane * 4 + (p & 1) * 2.
+  // The activation loads go out first, then the first AHEAD rows: the tables
+  // wait only for the activations (loads complete in issue order).
+  float4 xv[G::LANE_COLS / 4];
 #pragma unroll
-      for (int e = 0; e < XPT; ++e) x[e] = c < a.kpad ? a.xr[nb * a.kpad + c + e] : 0.0f;
-      float e16[16];
-      if (SB == 2) {
+  for (int c = 0; c < G::LANE_COLS / 4; ++c) {
+    xv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane_active) xv[c] = *reinterpret_cast<const float4 *>(a.xr + c_lane + 4 * c);
+  }
+  constexpr int XQ = SB == 2 ? 4 : 2;  // activations of this thread's table position
+  const int xpos = SB == 2 ? 4 * (wave >> 2) : (SB == 4 ? 2 * (wave >> 2) : 2 * wave);
+  float xq[XQ];
+  if constexpr (XQ == 4) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane_active) v = *reinterpret_cast<const float4 *>(a.xr + c_lane + xpos);
+    xq[0] = v.x, xq[1 % XQ] = v.y, xq[2 % XQ] = v.z, xq[3 % XQ] = v.w;
+  } else {
+    float2 v = make_float2(0.f, 0.f);
+    if (lane_active) v = *reinterpret_cast<const float2 *>(a.xr + c_lane + xpos);
+    xq[0] = v.x, xq[1] = v.y;
+  }
+  if (tid == 0) next_unit = kWaves;
+
+  constexpr int AH = G::AHEAD;
+  uint32_t dw[AH][G::DWORDS];
+  uint32_t nraw[AH];
+  start_unit(wave);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) e16[v] = a.lev.v[v & 3] * x[0] + a.lev.v[v >> 2] * x[XPT - 1];
-      } else {
+  for (int u = 0; u < AH; ++u) load_next(dw[u], nraw[u]);  // in flight while the tables are built
+
+  float mx = 0.0f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) e16[v] = a.lev.v[v] * x[0];
+  for (int c = 0; c < G::LANE_COLS / 4; ++c)
+    mx = fmaxf(fmaxf(mx, fmaxf(fabsf(xv[c].x), fabsf(xv[c].y))), fmaxf(fabsf(xv[c].z), fabsf(xv[c].w)));
+#pragma unroll
+  for (int dist = 32; dist >= 1; dist >>= 1) mx = fmaxf(mx, __shfl_xor(mx, dist));  // the slice's max |xr|
+  const int kexp = table_exponent(static_cast<float>(G::CODES) * a.lev_absmax * mx);
+  const float scale = ldexpf(1.0f, kexp), unscale = ldexpf(1.0f, -kexp);
+  {
+    // Thread (wave w, lane) builds entries e = 64 w + i, i < 64, of its lane.
+    uint8_t *const slot = lds + lane * 4;
+    if constexpr (SB == 2) {
+      const int p = wave >> 2, c3 = wave & 3;  // c3: the fourth code, fixed for this thread
+      const float x0 = xq[0], x1 = xq[1 % XQ], x2 = xq[2 % XQ], x3 = xq[3 % XQ];
+      float hi[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hi[q] = a.lev.v[q] * x2 + a.lev.v[c3] * x3;
+      uint8_t *const row = slot + (p >> 1) * G::REGION + (p & 1) * 2 + c3 * 64 * 256;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        const float lo = a.lev.v[i & 3] * x0 + a.lev.v[(i >> 2) & 3] * x1;
+        *reinterpret_cast<_Float16 *>(row + i * 256) = static_cast<_Float16>((lo + hi[i >> 4]) * scale);
       }
-      uint32_t off, stride;
-      if (WIDE) {
-        off = hi ? 0x10000u + blk * 256u + lane * 4u : blk * 4096u + lane * 4u;
-        stride = hi ? 4096u : 256u;
-      } else {
-        off = (hi * BLOCKS * NB + blk) * 4096u + lane * 4u;
-        stride = 256u;
-      }
+    } else if constexpr (SB == 4) {
+      const int p = wave >> 2;
+      const float x0 = xq[0], x1 = xq[1];
+      uint8_t *const row = slot + (p >> 1) * G::REGION + (p & 1) * 2 + (wave & 3) * 64 * 256;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) lds[(off + v * stride) >> 2] = e16[v];
+      for (int i = 0; i < 64; ++i) {
+        const int v = (wave & 3) * 64 + i;
+        const float t = a.lev.v[v & 15] * x0 + a.lev.v[v >> 4] * x1;
+        *reinterpret_cast<_Float16 *>(row + i * 256) = static_cast<_Float16>(t * scale);
+      }
+    } else {
+      const int p = wave;
+      const float x0 = xq[0], x1 = xq[1];
+      uint8_t *const row = slot + (p >> 1) * G::REGION + (p & 1) * 2;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        const float t = a.lev.v[i & 7] * x0 + a.lev.v[i >> 3] * x1;
+        *reinterpret_cast<_Float16 *>(row + i * 256) = static_cast<_Float16>(t * scale);
+      }
     }
   }
   __syncthreads();
 
-  // Row streams: this workgroup's row blocks are first_blk, first_blk +
-  // per_slice, ...; row slot m of a block is row r0 + wave + kWaves*m.  Loads
-  // walk that sequence kAhead rows ahead of the arithmetic with wave-uniform
-  // pointers: +kWaves rows per slot, a jump per row block, and a clamp to the
-  // last row (the clamped rows past the end are computed and discarded).
-  const int my_blocks = (a.nblocks - 1 - first_blk) / a.per_slice + 1;  // >= 1: first_blk < nblocks
-  const int64_t slot_stride = static_cast<int64_t>(kWaves) * a.row_bytes;
-  const int64_t nslot_stride = static_cast<int64_t>(kWaves) * a.ngroups;
-  const uint8_t *const last_row = slice_packed + (a.rows - 1) * a.row_bytes;
-  const uint16_t *const last_nrow = slice_norms + (a.rows - 1) * a.ngroups;
-  auto block_row = [&](int bi) {  // row of slot 0 of this wave in the bi-th block
-    return (first_blk + static_cast<int64_t>(bi) * a.per_slice) * a.rows_per_block + wave;
-  };
-  const uint8_t *lp = slice_packed + block_row(0) * a.row_bytes;  // next row to load
-  const uint16_t *lq = slice_norms + block_row(0) * a.ngroups;
-  auto load_next = [&](uint32_t (&dw)[D], uint32_t &nraw) {
-    const uint8_t *p = lp < last_row ? lp : last_row;
-    const uint16_t *q = lq < last_nrow ? lq : last_nrow;
-    const uint8_t *src = p + lane_byte;
-    if (D == 4) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(src);
-      dw[0] = v.x; dw[1 % D] = v.y; dw[2 % D] = v.z; dw[3 % D] = v.w;
-    } else if (D == 3) {
-      const uint32_t *w = reinterpret_cast<const uint32_t *>(src);
-      dw[0] = w[0]; dw[1 % D] = w[1 % D]; dw[2 % D] = w[2 % D];
-    } else if (D == 2) {
-      const uint2 v = *reinterpret_cast<const uint2 *>(src);
-      dw[0] = v.x; dw[1 % D] = v.y;
-    } else {
-      dw[0] = *reinterpret_cast<const uint32_t *>(src);
-    }
-    nraw = q[lane_group];
-    lp += slot_stride;
-    lq += nslot_stride;
-  };
+  auto unit_block = [&](int uu) { return first_blk + static_cast<int64_t>(uu / kWaves) * a.per_slice; };
 
-  const uint32_t base_lo = static_cast<uint32_t>(lane) * 4u;
-  const uint32_t base_hi = static_cast<uint32_t>(lane) * 4u + 0x10000u;
-  uint32_t dw[kAhead][D];
-  uint32_t nraw[kAhead];
-#pragma unroll
-  for (int u = 0; u < kAhead; ++u) load_next(dw[u], nraw[u]);
-
-  for (int bi = 0; bi < my_blocks; ++bi) {
-    const int blk = first_blk + bi * a.per_slice;
-    const int64_t r0 = static_cast<int64_t>(blk) * a.rows_per_block;
+  const uint32_t base0 = static_cast<uint32_t>(lane) * 4u;
+  const uint32_t base1 = base0 + 0x10000u;
+  int u = wave, un = units;
+  uint32_t grabbed = 0;  // lane 0: the unit taken for after this one
+  while (u < units) {
+    const int64_t r0 = unit_block(u) * a.rows_per_block;
     const int64_t r1 = min(r0 + static_cast<int64_t>(a.rows_per_block), a.rows);
-    float racc[NB][kRowsPerWave];
+    // Lookups of row m are issued before the accumulation of row m-1, so the
+    // LDS latency of a row is covered by the next row's address and load work.
+    float racc[kRowsPerWave];
+    _Float16 tv[2][G::LOOKUPS];
+    _Float16 nv[2];
+    auto accumulate = [&](int m) {
+      float acc = 0.0f;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int m = 0; m < kRowsPerWave; ++m) racc[nb][m] = 0.0f;
-
+      for (int k = 0; k < G::LOOKUPS; ++k)
+        acc = fmaf(static_cast<float>(tv[m & 1][k]), static_cast<float>(nv[m & 1]), acc);
+      asm volatile("" : "+v"(acc));  // keep the sums here: sunk to the unit's end they hold every lookup live
+      racc[m] = acc;
+    };
 #pragma unroll
     for (int m = 0; m < kRowsPerWave; ++m) {
-      const int slot = m % kAhead;
-      uint32_t cur[D];
+      const int slot = m % AH;
+      uint32_t cur[G::DWORDS];
 #pragma unroll
-      for (int d = 0; d < D; ++d) cur[d] = dw[slot][d];
-      const uint32_t ncur = nraw[slot];
-      if (m + kAhead == kRowsPerWave) {  // the loads move on to the next row block
-        lp = slice_packed + block_row(bi + 1) * a.row_bytes;
-        lq = slice_norms + block_row(bi + 1) * a.ngroups;
+      for (int d = 0; d < G::DWORDS; ++d) cur[d] = dw[slot][d];
+      nv[m & 1] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(nraw[slot]));
+      if (m == 0 && lane == 0) grabbed = atomicAdd(&next_unit, 1);
+      if (m + AH == kRowsPerWave) {  // the loads move on to the next unit
+        un = __builtin_amdgcn_readfirstlane(grabbed);
+        start_unit(un);
       }
       load_next(dw[slot], nraw[slot]);
-      {
-        const float n = lane_active ? half_to_float(static_cast<uint16_t>(ncur)) : 0.0f;
-        if (SB == 3) {
-          float tv[32];
+      if constexpr (SB == 3) {
 #pragma unroll
-          for (int k = 0; k < 32; ++k) {
-            const int bit = 3 * k, w = bit >> 5, sh = bit & 31;
-            const uint32_t code = sh <= 29 ? __builtin_amdgcn_ubfe(cur[w % D], sh, 3)
-                                           : (__builtin_amdgcn_alignbit(cur[(w + 1) % D], cur[w % D], sh) & 7u);
-            tv[k] = lds_at(lds, ((code << 8) | base_lo) + k * 2048u);
-          }
+        for (int k = 0; k < 16; ++k) {  // 6-bit field k: codes 2k, 2k+1
+          const int bit = 6 * k, w = bit >> 5, sh = bit & 31;
+          const uint32_t f = sh <= 26 ? __builtin_amdgcn_ubfe(cur[w], sh, 6)
+                                      : (__builtin_amdgcn_alignbit(cur[(w + 1) % G::DWORDS], cur[w], sh) & 63u);
+          const uint32_t addr = (f << 8) | (k < 8 ? base0 : base1);
+          tv[m & 1][k] = lds_half(lds, addr + ((k >> 1) & 3) * G::REGION + (k & 1) * 2);
+        }
+      } else {
 #pragma unroll
-          for (int w = 1; w < 32; w <<= 1)
-#pragma unroll
-            for (int i = 0; i + w < 32; i += 2 * w) tv[i] += tv[i + w];
-          racc[0][m] = fmaf(tv[0], n, racc[0][m]);
-        } else {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            // All LDS reads of the row first, then a pairwise sum.
-            float tv[8 * D];
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-              const uint32_t lo = cur[d] & 0x0F0F0F0Fu;
-              const uint32_t hi = WIDE ? (cur[d] & 0xF0F0F0F0u) : ((cur[d] >> 4) & 0x0F0F0F0Fu);
-#pragma unroll
-              for (int jb = 0; jb < 4; ++jb) {
-                const uint32_t sel = 0x0C020400u + (static_cast<uint32_t>(jb) << 8);
-                const uint32_t tb = nb * BLOCKS + 4 * d + jb;
-                tv[8 * d + 2 * jb] = lds_at(lds, __builtin_amdgcn_perm(lo, base_lo, sel) + tb * 4096u);
-                if (WIDE)
-                  tv[8 * d + 2 * jb + 1] = lds_at(lds, __builtin_amdgcn_perm(hi, base_hi, sel) + tb * 256u);
-                else
-                  tv[8 * d + 2 * jb + 1] = lds_at(lds, __builtin_amdgcn_perm(hi, base_lo, sel) + (BLOCKS * NB + tb) * 4096u);
-              }
-            }
-#pragma unroll
-            for (int w = 1; w < 8 * D; w <<= 1)
-#pragma unroll
-              for (int i = 0; i + w < 8 * D; i += 2 * w) tv[i] += tv[i + w];
-            racc[nb][m] = fmaf(tv[0], n, racc[nb][m]);
-          }
+        for (int p = 0; p < 4; ++p) {  // byte p of the lane's dword
+          const uint32_t addr = __builtin_amdgcn_perm(cur[0], p < 2 ? base0 : base1, 0x0C020400u + (p << 8));
+          tv[m & 1][p] = lds_half(lds, addr + (p & 1) * 2);
         }
       }
+      if (m > 0) accumulate(m - 1);
     }
-    float t[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) t[nb] = reduce_rows(racc[nb], lane);
-    finish_block<NB>(a, slice, blk, r0, r1, wave, lane, t);
+    accumulate(kRowsPerWave - 1);
+    const float t = reduce_rows(racc, lane) * unscale;
+    store_block(a, slice, r0, r1, u % kWaves, lane, t);
+    u = un;
   }
 }
 
-#ifndef CQ_MV_D1
-#define CQ_MV_D1 4  // packed dwords per lane and row for one batch vector
-#endif
-
-// Packed dwords per lane and row for a chunk of nb batch vectors.
-int lane_dwords(int sb, int nb) { return sb == 3 ? 3 : (nb == 1 ? CQ_MV_D1 : 4 / nb); }
+// y[r] = sum over slices, in slice order, of partial[slice][r].
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ partial, int64_t rows, int nslice,
+                                                      float *__restrict__ y) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; r < rows; r += stride) {
+    float acc = 0.0f;
+    int s = 0;
+    for (; s + 4 <= nslice; s += 4) {  // four loads in flight, added in order
+      const float v0 = partial[(s + 0) * rows + r], v1 = partial[(s + 1) * rows + r];
+      const float v2 = partial[(s + 2) * rows + r], v3 = partial[(s + 3) * rows + r];
+      acc = (((acc + v0) + v1) + v2) + v3;
+    }
+    for (; s < nslice; ++s) acc += partial[s * rows + r];
+    y[r] = acc;
+  }
+}
 
 // Shape of one launch: slices of K, row blocks and persistent workgroups.
 struct MvShape {
   int32_t nslice, rows_per_block, nblocks, per_slice;
 };
 
-int slice_cols(int sb, int nb) {
-  if (sb == 3) return 64 * 32;
-  return 64 * 4 * lane_dwords(sb, nb) * (8 / sb);
+int slice_cols(int sb) {
+  return sb == 2 ? Geom<2>::SLICE_COLS : (sb == 3 ? Geom<3>::SLICE_COLS : Geom<4>::SLICE_COLS);
 }
 
-// Workgroups that fit on the device at once (persistent grid size).
-int max_grid(int sb, int nb);
+typedef void (*MvKernel)(MvArgs);
 
-MvShape mv_shape(int sb, int nb, int64_t rows, int64_t kpad) {
+MvKernel pick_kernel(int sb) {
+  return sb == 2 ? matvec_kernel<2> : (sb == 3 ? matvec_kernel<3> : matvec_kernel<4>);
+}
+
+int max_grid(int sb) {
+  // Resident workgroups per CU for this kernel, times the CU count of the
+  // current device; computed once per (device, width).
+  static int cache[64][3];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int &c = cache[dev][sb - 2];
+  if (c == 0) {
+    int per_cu = 1, cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(pick_kernel(sb)),
+                                                     kThreads, 0) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    c = per_cu * cus;
+  }
+  return c;
+}
+
+MvShape mv_shape(int sb, int64_t rows, int64_t kpad) {
   MvShape s;
-  const int64_t sc = slice_cols(sb, nb);
-  const int grid_max = max_grid(sb, nb);
+  const int64_t sc = slice_cols(sb);
+  const int grid_max = max_grid(sb);
   s.nslice = static_cast<int32_t>((kpad + sc - 1) / sc);
   // Aim at grid_max busy workgroups: small matrices get small row blocks.
   int64_t rpb = (rows * s.nslice + grid_max - 1) / grid_max;
@@ -400,72 +450,29 @@ MvShape mv_shape(int sb, int nb, int64_t rows, int64_t kpad) {
   return s;
 }
 
-typedef void (*MvKernel)(MvArgs);
-
-MvKernel pick_kernel(int sb, int nb) {
-  const int d = lane_dwords(sb, nb);
-  if (sb == 3) return matvec_kernel<3, 1, 3>;
-  if (sb == 2) {
-    if (nb == 4) return matvec_kernel<2, 4, 1>;
-    if (nb == 2) return matvec_kernel<2, 2, 2>;
-    return d == 4 ? matvec_kernel<2, 1, 4> : (d == 2 ? matvec_kernel<2, 1, 2> : matvec_kernel<2, 1, 1>);
-  }
-  if (nb == 4) return matvec_kernel<4, 4, 1>;
-  if (nb == 2) return matvec_kernel<4, 2, 2>;
-  return d == 4 ? matvec_kernel<4, 1, 4> : (d == 2 ? matvec_kernel<4, 1, 2> : matvec_kernel<4, 1, 1>);
-}
-
-int max_grid(int sb, int nb) {
-  // Resident workgroups per CU for this kernel, times the CU count of the
-  // current device; computed once per (device, width, batch chunk).
-  static int cache[64][3][3];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  const int si = sb == 2 ? 0 : (sb == 3 ? 1 : 2), ni = nb == 1 ? 0 : (nb == 2 ? 1 : 2);
-  int &c = cache[dev][si][ni];
-  if (c == 0) {
-    int per_cu = 1, cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(pick_kernel(sb, nb)),
-                                                     kThreads, 0) != hipSuccess || per_cu < 1)
-      per_cu = 1;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    c = per_cu * cus;
-  }
-  return c;
-}
-
-int nb_chunk(int sb, int64_t left) {
-  if (sb == 3) return 1;
-  return left >= 4 ? 4 : (left >= 2 ? 2 : 1);
+float lev_absmax(int sb, const cq::CodeLevels &lev) {
+  float m = 0.0f;
+  for (int i = 0; i < (1 << sb); ++i) m = fmaxf(m, fabsf(lev.v[i]));
+  return m;
 }
 
 }  // namespace
 
 namespace cq {
 
-// Workspace of one launch: [counters: nblocks x u32, padded to 256 B][partials: nslice x nb x rows f32].
-uint64_t chunk_workspace_bytes(const MvShape &s, int nb, int64_t rows) {
-  if (s.nslice <= 1) return 0;
-  const uint64_t counters = (static_cast<uint64_t>(s.nblocks) * 4 + 255) / 256 * 256;
-  return counters + static_cast<uint64_t>(s.nslice) * nb * rows * 4;
-}
-
+// Workspace of one launch: the per-slice partial sums [nslice][rows] (fp32).
+// The batch vectors run one after another and share it.
 uint64_t matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch) {
-  const int sb = storage_bits(bits);
-  uint64_t need = 0;
-  if (rows <= 0 || kpad <= 0) return 0;  // nothing is launched
-  for (int64_t b = 0; b < batch;) {
-    const int nb = nb_chunk(sb, batch - b);
-    const uint64_t bytes = chunk_workspace_bytes(mv_shape(sb, nb, rows, kpad), nb, rows);
-    if (bytes > need) need = bytes;
-    b += nb;
-  }
-  return need;
+  if (rows <= 0 || kpad <= 0 || batch <= 0) return 0;  // nothing is launched
+  const MvShape s = mv_shape(storage_bits(bits), rows, kpad);
+  if (s.nslice <= 1) return 0;
+  return static_cast<uint64_t>(s.nslice) * rows * 4;
 }
 
 hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
                          const float *xr, int64_t batch, float *y, void *workspace, hipStream_t s) {
   const int sb = storage_bits(bits);
+  const MvShape sh = mv_shape(sb, rows, kpad);
   MvArgs a;
   a.packed = blob;
   a.row_bytes = kpad * sb / 8;
@@ -474,28 +481,26 @@ hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kp
   a.kpad = kpad;
   a.ngroups = kpad / CQ_GROUP;
   a.lev = lev;
-  for (int64_t b = 0; b < batch;) {
-    const int nb = nb_chunk(sb, batch - b);
-    const MvShape sh = mv_shape(sb, nb, rows, kpad);
+  a.lev_absmax = lev_absmax(sb, lev);
+  a.nslice = sh.nslice;
+  a.rows_per_block = sh.rows_per_block;
+  a.nblocks = sh.nblocks;
+  a.per_slice = sh.per_slice;
+  a.partial = sh.nslice > 1 ? static_cast<float *>(workspace) : nullptr;
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(sh.nslice) * sh.per_slice));
+  const int64_t cblocks = (rows + 255) / 256;
+  const unsigned cgrid = static_cast<unsigned>(cblocks < 65536 ? cblocks : 65536);
+  for (int64_t b = 0; b < batch; ++b) {
     a.xr = xr + b * kpad;
     a.y = y + b * rows;
-    a.nslice = sh.nslice;
-    a.rows_per_block = sh.rows_per_block;
-    a.nblocks = sh.nblocks;
-    a.per_slice = sh.per_slice;
-    if (sh.nslice > 1) {
-      const uint64_t counters = (static_cast<uint64_t>(sh.nblocks) * 4 + 255) / 256 * 256;
-      a.counter = static_cast<uint32_t *>(workspace);
-      a.partial = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + counters);
-    } else {
-      a.partial = nullptr;
-      a.counter = nullptr;
-    }
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(sh.nslice) * sh.per_slice));
-    pick_kernel(sb, nb)<<<grid, kThreads, 0, s>>>(a);
-    const hipError_t e = hipGetLastError();
+    pick_kernel(sb)<<<grid, kThreads, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    b += nb;
+    if (sh.nslice > 1) {
+      combine_kernel<<<cgrid, 256, 0, s>>>(a.partial, rows, sh.nslice, a.y);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }

@@ -118,11 +118,10 @@ typedef enum cq_op { CQ_OP_MATVEC = 0, CQ_OP_GEMM = 1 } cq_op;
  * Device workspace (bytes) that `op` needs for `W` and the given batch (M for
  * the GEMM).  Host-only.  0 means the call takes workspace = NULL.
  *
- * A workspace is device memory owned by the caller, 16-byte aligned.  It must
- * be zero-filled before its first use; every call that completes leaves it
- * all zeros again (it holds per-call partial sums and completion counters).
- * Calls that may run at the same time must not share a workspace.  One
- * workspace sized for the largest matrix and batch serves all smaller calls.
+ * A workspace is device memory owned by the caller, 16-byte aligned.  Its
+ * contents on entry do not matter and are left unspecified (it holds the
+ * per-call partial sums of the K slices).  Calls that may run at the same time
+ * must not share a workspace; calls on one stream may.
  */
 cq_status cq_workspace_bytes(int32_t op, const cq_matrix *W, int64_t batch,
                              uint64_t *bytes);
@@ -148,7 +147,7 @@ cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t 
                          void *xr, int32_t xr_dtype, void *stream);
 
 /*
- * Decode matrix-vector product, equation (1), fp32 accumulation:
+ * Decode matrix-vector product, equation (1):
  *
  *   y[b][r] = sum_g float(norm[r][g]) * sum_j c[q[r][g*128+j]] * xr[b][g*128+j]
  *
@@ -161,8 +160,13 @@ cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t 
  *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_MATVEC),
  *            see cq_workspace_bytes (NULL, 0 when that is 0); must not
  *            overlap any other buffer of the call
- *   Results do not depend on scheduling: the partial sums of the K slices are
- *   added in a fixed order.
+ *   Arithmetic: the inner sum is read from lookup tables indexed by a packed
+ *   field (4 codes at 2-bit widths, 2 codes at 3- and 4-bit widths); an entry,
+ *   the sum of its codes' level * xr products, is computed in fp32, scaled by
+ *   a power of two per slice of 512-2048 columns and rounded once to fp16
+ *   (relative error <= 2^-11 per entry).  Products with the fp16 norm and all
+ *   sums are fp32.  Results do not depend on scheduling: the partial sums of
+ *   the K slices are added in a fixed order.
  */
 cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y,
                     void *workspace, uint64_t workspace_bytes, void *stream);
