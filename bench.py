@@ -8,8 +8,11 @@ step's W taken in turn from three copies of the matrix so that no copy is
 re-read while still resident in the 256 MB Infinity Cache.
 
   value       = packed bytes per step / wall time per step        (GB/s)
-  roofline    = matvec kernel: packed bytes / mean kernel time (HIP events on
-                the launch stream) against 8 TB/s HBM peak
+  roofline    = one cq_matvec call (the table-lookup kernel and the small
+                kernel that adds the K-slice partial sums): packed bytes /
+                mean call time (HIP events on the launch stream) against the
+                8 TB/s HBM peak; traffic = HBM bytes per call from the committed
+                rocprofv3 FETCH_SIZE/WRITE_SIZE summary
   cpu_baseline= the float64 oracle (dense dequantisation + product) on row
                 slices of the same matrix, timed on this host
 
@@ -18,6 +21,7 @@ widths and batch 8 at the same shape, the 4096 x 16384 x 16384 GEMM on the
 matrix cores (TFLOP/s) and the 16384 x 16384 encoder (GB/s of fp32 input).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only matvec|gemm|encode|all]
+       python bench.py --calibrate-copy      (counter calibration run)
 """
 import argparse
 import hashlib
@@ -33,7 +37,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 ROWS, COLS = 65536, 16384
 GEMM_M, GEMM_N, GEMM_K = 4096, 16384, 16384
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "matvec_cq2_65536x16384_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "matvec_cq2_65536x16384_traffic.md")
 MATVEC_SRC = os.path.join(ROOT, "hadamard_rotated_codebook_amd", "csrc", "matvec.hip")
 
 
@@ -141,17 +145,33 @@ def cpu_baseline(seconds=12.0, rows_per_slice=256):
 
 
 def stored_traffic():
-    """HBM bytes per matvec launch from the committed rocprofv3 counter runs, if
-    they were taken on the current kernel source; else None."""
+    """HBM bytes per cq_matvec call from the committed rocprofv3 counter summary
+    ("key: value" lines), if it was taken on the current kernel source; else None."""
     try:
+        fields = {}
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
+            for line in f:
+                if ":" in line and not line.startswith(("#", "|", " ")):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
         src = hashlib.sha256(open(MATVEC_SRC, "rb").read()).hexdigest()
-        if t.get("matvec_source_sha256") != src:
+        if fields.get("matvec_source_sha256") != src:
             return None
-        return t.get("traffic_bytes_per_launch")
-    except (OSError, ValueError):
+        return int(fields["traffic_bytes_per_call"])
+    except (OSError, ValueError, KeyError):
         return None
+
+
+def calibrate_copy(torch, repeats=5, nbytes=1 << 30):
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE
+    and WRITE_SIZE counters: each launch reads and writes exactly nbytes."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(repeats):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+                      "launches": repeats}), flush=True)
 
 
 def main():
@@ -161,6 +181,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--only", choices=["all", "matvec", "gemm", "encode"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; there is no multi-GPU path "
@@ -168,6 +190,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
     import cq_inputs
     import hadamard_rotated_codebook_amd as cq
 
@@ -226,7 +251,8 @@ def main():
         ach = h["bytes"] / h["kernel_s"] / 1e9
         line["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": ach / HBM_PEAK_GBS, "traffic": stored_traffic(),
-                            "kernel": "matvec_nibble_kernel<2,1>", "kernel_us": h["kernel_s"] * 1e6}
+                            "kernel": "cq_matvec call: matvec_kernel<2> + combine_kernel",
+                            "kernel_us": h["kernel_s"] * 1e6, "algorithmic_bytes": h["bytes"]}
     else:
         line["value"] = None
         line["ms_per_step"] = None

@@ -99,6 +99,12 @@ __device__ inline _Float16 lds_half(const uint8_t *lds, uint32_t byte_addr) {
   return *reinterpret_cast<const _Float16 *>(lds + byte_addr);
 }
 
+// Two floats rounded to nearest-even fp16, a in the low half.
+__device__ inline uint32_t pack_half2(float a, float b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(a))) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(b))) << 16);
+}
+
 __device__ inline __amdgpu_buffer_rsrc_t buffer(uint64_t addr, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(addr), 0, static_cast<int>(nbytes),
                                            static_cast<int>(kRawBufferWord3));
@@ -198,25 +204,31 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
   const uint64_t slice_norms =
       reinterpret_cast<uint64_t>(a.norms) + static_cast<uint64_t>(slice) * G::SLICE_GROUPS * 2;
 
-  // Work units: unit u is the 32 rows r0 + (u % kWaves) + kWaves*m, m < 32, of
-  // the workgroup's row block u / kWaves (blocks first_blk, first_blk +
-  // per_slice, ...).  Wave w starts with unit w and then takes the next unit
-  // from an LDS counter, one unit ahead: the issue arbiter favours older waves,
-  // and with a fixed share per wave the youngest waves of a CU finished far
-  // behind the others.  The loads walk the rows of the current unit and then of
-  // the next one AHEAD rows ahead of the arithmetic, with scalar bookkeeping:
-  // rows left in the unit and the two row addresses.
-  const int units = my_blocks * kWaves;
-  __shared__ int next_unit;
+  // Work units: unit g of a slice is the 32 rows r0 + (g % kWaves) + kWaves*m,
+  // m < 32, of row block g / kWaves.  Wave w starts with unit first_blk *
+  // kWaves + w; further units of the workgroup's row blocks (first_blk,
+  // first_blk + per_slice, ...) come from an LDS counter, taken one unit ahead
+  // so the loads can run on into them.  The issue arbiter favours older waves;
+  // with a fixed share per wave the youngest waves of a CU finished far behind
+  // the others, and now they simply do fewer units.  (A per-slice counter in
+  // memory shared by all workgroups of a slice measured no better.)  The loads
+  // walk the rows of the current unit and then of the next one AHEAD rows
+  // ahead of the arithmetic, with scalar bookkeeping: rows left in the unit and
+  // the two row addresses.
+  const int nunits = a.nblocks * kWaves;
+  __shared__ int next_local;
+  auto unit_of = [&](int grab) {  // the unit a grab stands for, nunits when none is left
+    const int64_t blk = first_blk + static_cast<int64_t>(grab / kWaves) * a.per_slice;
+    return blk < a.nblocks ? static_cast<int>(blk * kWaves + grab % kWaves) : nunits;
+  };
   const uint64_t row_step = static_cast<uint64_t>(kWaves) * a.row_bytes;
   const uint64_t nrow_step = static_cast<uint64_t>(kWaves) * a.ngroups * 2;
   int lk = 0, nlive = 0;  // loads issued in the current unit, live rows in it
   uint64_t lp = 0, lq = 0;
   auto start_unit = [&](int uu) {
-    const int64_t blk = first_blk + static_cast<int64_t>(uu / kWaves) * a.per_slice;
-    const int64_t r0 = blk * a.rows_per_block;
+    const int64_t r0 = static_cast<int64_t>(uu / kWaves) * a.rows_per_block;
     const int64_t lrow = r0 + uu % kWaves;
-    const int64_t lend = uu < units ? min(r0 + a.rows_per_block, a.rows) : 0;
+    const int64_t lend = uu < nunits ? min(r0 + a.rows_per_block, a.rows) : 0;
     nlive = __builtin_amdgcn_readfirstlane(lend > lrow ? static_cast<int>((lend - lrow + kWaves - 1) / kWaves) : 0);
     lk = 0;
     lp = slice_packed + static_cast<uint64_t>(lrow) * a.row_bytes;
@@ -247,89 +259,104 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
 
   // ---- tables: entry (position p, index v, lane) at byte
   //      (p >> 1) * REGION + v * 256 + lane * 4 + (p & 1) * 2.
-  // The activation loads go out first, then the first AHEAD rows: the tables
-  // wait only for the activations (loads complete in issue order).
+  // The activation loads go out first and are waited for (the slice's max)
+  // before the first rows are requested.
   float4 xv[G::LANE_COLS / 4];
 #pragma unroll
   for (int c = 0; c < G::LANE_COLS / 4; ++c) {
     xv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (lane_active) xv[c] = *reinterpret_cast<const float4 *>(a.xr + c_lane + 4 * c);
   }
-  constexpr int XQ = SB == 2 ? 4 : 2;  // activations of this thread's table position
-  const int xpos = SB == 2 ? 4 * (wave >> 2) : (SB == 4 ? 2 * (wave >> 2) : 2 * wave);
+  // Thread (wave w, lane) builds 32 slots of its lane: the pair of positions
+  // q = w / (16 / PAIRS) (both halves of a slot) at indices v = vb + i, i < 32.
+  constexpr int PAIRS = G::POSITIONS / 2;               // 2, 8, 2 pairs of positions
+  constexpr int XQ = SB == 2 ? 8 : 4;                   // activations of a pair of positions
+  const int q = wave / (kWaves / PAIRS);
+  const int vb = (wave % (kWaves / PAIRS)) * 32;
   float xq[XQ];
-  if constexpr (XQ == 4) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lane_active) v = *reinterpret_cast<const float4 *>(a.xr + c_lane + xpos);
-    xq[0] = v.x, xq[1 % XQ] = v.y, xq[2 % XQ] = v.z, xq[3 % XQ] = v.w;
-  } else {
-    float2 v = make_float2(0.f, 0.f);
-    if (lane_active) v = *reinterpret_cast<const float2 *>(a.xr + c_lane + xpos);
-    xq[0] = v.x, xq[1] = v.y;
-  }
-  if (tid == 0) next_unit = kWaves;
-
-  constexpr int AH = G::AHEAD;
-  uint32_t dw[AH][G::DWORDS];
-  uint32_t nraw[AH];
-  start_unit(wave);
 #pragma unroll
-  for (int u = 0; u < AH; ++u) load_next(dw[u], nraw[u]);  // in flight while the tables are built
+  for (int c = 0; c < XQ; c += 4) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane_active) v = *reinterpret_cast<const float4 *>(a.xr + c_lane + XQ * q + c);
+    xq[c] = v.x, xq[c + 1] = v.y, xq[c + 2] = v.z, xq[c + 3] = v.w;
+  }
+  if (tid == 0) next_local = kWaves;
 
   float mx = 0.0f;
 #pragma unroll
   for (int c = 0; c < G::LANE_COLS / 4; ++c)
     mx = fmaxf(fmaxf(mx, fmaxf(fabsf(xv[c].x), fabsf(xv[c].y))), fmaxf(fabsf(xv[c].z), fabsf(xv[c].w)));
+  // The slice's max |xr|: DPP within 16-lane rows, then the two lane swaps.
+  mx = fmaxf(mx, dpp<0xb1>(mx));   // quad_perm 1032
+  mx = fmaxf(mx, dpp<0x4e>(mx));   // quad_perm 2301
+  mx = fmaxf(mx, dpp<0x141>(mx));  // row_half_mirror
+  mx = fmaxf(mx, dpp<0x128>(mx));  // row_ror:8
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  // Only now the first AHEAD rows: issued together with the activations, the
+  // whole chip's burst of row loads held the activations back by several us.
+  constexpr int AH = G::AHEAD;
+  uint32_t dw[AH][G::DWORDS];
+  uint32_t nraw[AH];
+  const int first_unit = my_blocks > 0 ? first_blk * kWaves + wave : nunits;
+  start_unit(first_unit);
 #pragma unroll
-  for (int dist = 32; dist >= 1; dist >>= 1) mx = fmaxf(mx, __shfl_xor(mx, dist));  // the slice's max |xr|
+  for (int u = 0; u < AH; ++u) load_next(dw[u], nraw[u]);  // in flight while the tables are built
   const int kexp = table_exponent(static_cast<float>(G::CODES) * a.lev_absmax * mx);
   const float scale = ldexpf(1.0f, kexp), unscale = ldexpf(1.0f, -kexp);
   {
-    // Thread (wave w, lane) builds entries e = 64 w + i, i < 64, of its lane.
-    uint8_t *const slot = lds + lane * 4;
+#pragma unroll
+    for (int c = 0; c < XQ; ++c) xq[c] *= scale;  // exact: a power of two
+    uint32_t *const out = reinterpret_cast<uint32_t *>(lds + q * G::REGION + vb * 256 + lane * 4);
+    const float *lev = a.lev.v;
     if constexpr (SB == 2) {
-      const int p = wave >> 2, c3 = wave & 3;  // c3: the fourth code, fixed for this thread
-      const float x0 = xq[0], x1 = xq[1 % XQ], x2 = xq[2 % XQ], x3 = xq[3 % XQ];
-      float hi[4];
+      // position h of the pair: codes (v&3, v>>2&3, v>>4&3, v>>6) of columns 4h..4h+3
+      const int c2hi = (vb >> 5) & 1, c3 = vb >> 6;  // fixed for this thread
+      float hi[2][2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) hi[q] = a.lev.v[q] * x2 + a.lev.v[c3] * x3;
-      uint8_t *const row = slot + (p >> 1) * G::REGION + (p & 1) * 2 + c3 * 64 * 256;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const float lo = a.lev.v[i & 3] * x0 + a.lev.v[(i >> 2) & 3] * x1;
-        *reinterpret_cast<_Float16 *>(row + i * 256) = static_cast<_Float16>((lo + hi[i >> 4]) * scale);
+        for (int b = 0; b < 2; ++b) hi[h][b] = lev[2 * c2hi + b] * xq[4 * h + 2] + lev[c3] * xq[4 * h + 3];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float t0 = lev[i & 3] * xq[0] + lev[(i >> 2) & 3] * xq[1] + hi[0][i >> 4];
+        const float t1 = lev[i & 3] * xq[4] + lev[(i >> 2) & 3] * xq[5] + hi[1][i >> 4];
+        out[i * 64] = pack_half2(t0, t1);
       }
     } else if constexpr (SB == 4) {
-      const int p = wave >> 2;
-      const float x0 = xq[0], x1 = xq[1];
-      uint8_t *const row = slot + (p >> 1) * G::REGION + (p & 1) * 2 + (wave & 3) * 64 * 256;
+      // position h: codes (v&15, v>>4) of columns 2h, 2h+1
 #pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const int v = (wave & 3) * 64 + i;
-        const float t = a.lev.v[v & 15] * x0 + a.lev.v[v >> 4] * x1;
-        *reinterpret_cast<_Float16 *>(row + i * 256) = static_cast<_Float16>(t * scale);
+      for (int i = 0; i < 32; ++i) {
+        const int v = vb + i;
+        const float t0 = lev[v & 15] * xq[0] + lev[v >> 4] * xq[1];
+        const float t1 = lev[v & 15] * xq[2] + lev[v >> 4] * xq[3];
+        out[i * 64] = pack_half2(t0, t1);
       }
     } else {
-      const int p = wave;
-      const float x0 = xq[0], x1 = xq[1];
-      uint8_t *const row = slot + (p >> 1) * G::REGION + (p & 1) * 2;
+      // position h: codes (v&7, v>>3) of columns 2h, 2h+1
 #pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const float t = a.lev.v[i & 7] * x0 + a.lev.v[i >> 3] * x1;
-        *reinterpret_cast<_Float16 *>(row + i * 256) = static_cast<_Float16>(t * scale);
+      for (int i = 0; i < 32; ++i) {
+        const int v = vb + i;
+        const float t0 = lev[v & 7] * xq[0] + lev[v >> 3] * xq[1];
+        const float t1 = lev[v & 7] * xq[2] + lev[v >> 3] * xq[3];
+        out[i * 64] = pack_half2(t0, t1);
       }
     }
   }
   __syncthreads();
 
-  auto unit_block = [&](int uu) { return first_blk + static_cast<int64_t>(uu / kWaves) * a.per_slice; };
-
   const uint32_t base0 = static_cast<uint32_t>(lane) * 4u;
   const uint32_t base1 = base0 + 0x10000u;
-  int u = wave, un = units;
-  uint32_t grabbed = 0;  // lane 0: the unit taken for after this one
-  while (u < units) {
-    const int64_t r0 = unit_block(u) * a.rows_per_block;
+  int u = first_unit, un = nunits;
+  uint32_t grabbed = 0;  // lane 0: the grab for the unit after this one
+  while (u < nunits) {
+    const int64_t r0 = static_cast<int64_t>(u / kWaves) * a.rows_per_block;
     const int64_t r1 = min(r0 + static_cast<int64_t>(a.rows_per_block), a.rows);
     // Lookups of row m are issued before the accumulation of row m-1, so the
     // LDS latency of a row is covered by the next row's address and load work.
@@ -351,9 +378,9 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
 #pragma unroll
       for (int d = 0; d < G::DWORDS; ++d) cur[d] = dw[slot][d];
       nv[m & 1] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(nraw[slot]));
-      if (m == 0 && lane == 0) grabbed = atomicAdd(&next_unit, 1);
+      if (m == 0 && lane == 0) grabbed = static_cast<uint32_t>(atomicAdd(&next_local, 1));
       if (m + AH == kRowsPerWave) {  // the loads move on to the next unit
-        un = __builtin_amdgcn_readfirstlane(grabbed);
+        un = unit_of(static_cast<int>(__builtin_amdgcn_readfirstlane(grabbed)));
         start_unit(un);
       }
       load_next(dw[slot], nraw[slot]);
@@ -385,16 +412,17 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
 // y[r] = sum over slices, in slice order, of partial[slice][r].
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ partial, int64_t rows, int nslice,
                                                       float *__restrict__ y) {
+  constexpr int CH = 16;  // loads in flight per thread
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; r < rows; r += stride) {
     float acc = 0.0f;
-    int s = 0;
-    for (; s + 4 <= nslice; s += 4) {  // four loads in flight, added in order
-      const float v0 = partial[(s + 0) * rows + r], v1 = partial[(s + 1) * rows + r];
-      const float v2 = partial[(s + 2) * rows + r], v3 = partial[(s + 3) * rows + r];
-      acc = (((acc + v0) + v1) + v2) + v3;
+    for (int s0 = 0; s0 < nslice; s0 += CH) {
+      float v[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) v[c] = s0 + c < nslice ? partial[static_cast<int64_t>(s0 + c) * rows + r] : 0.0f;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) acc += v[c];  // slice order (the padding adds +0)
     }
-    for (; s < nslice; ++s) acc += partial[s * rows + r];
     y[r] = acc;
   }
 }

@@ -121,7 +121,7 @@ typedef enum cq_op { CQ_OP_MATVEC = 0, CQ_OP_GEMM = 1 } cq_op;
  * A workspace is device memory owned by the caller, 16-byte aligned.  Its
  * contents on entry do not matter and are left unspecified (it holds the
  * per-call partial sums of the K slices).  Calls that may run at the same time
- * must not share a workspace; calls on one stream may.
+ * must not share a workspace; calls on one stream may, whatever their shapes.
  */
 cq_status cq_workspace_bytes(int32_t op, const cq_matrix *W, int64_t batch,
                              uint64_t *bytes);
