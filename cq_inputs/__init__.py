@@ -17,6 +17,9 @@ Recipe (every draw is reproducible from its key alone):
 * Codebooks: the printed 2-bit header values, and for 3/4-bit the values in
   ``tests/golden/codebooks.json`` (written by a script that runs the oracle's
   empirical Lloyd-Max procedure).
+* Full-size product tests use uniformly random packed bytes and fp16 norms
+  drawn around the norm of a N(0, 0.02^2) group: any bytes are a valid CQ
+  matrix, and the oracle decodes the same bytes.
 """
 
 import json
@@ -96,6 +99,22 @@ def cast(x, dtype):
         import torch
         return torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
     raise ValueError(dtype)
+
+
+def random_bytes(config_id, tensor_id, nbytes):
+    """``nbytes`` uniformly random bytes (uint8); stands in for packed CQ
+    indices at sizes where encoding a master on the CPU would take minutes."""
+    return _gen(config_id, tensor_id, 3, 0).integers(0, 256, size=nbytes, dtype=np.uint8)
+
+
+def random_norms(config_id, tensor_id, n, mean=0.226, sd=0.014):
+    """``n`` positive fp16 values drawn as N(mean, sd^2), returned as uint8
+    bytes (little-endian fp16).  The defaults are the norm statistics of a
+    128-group of N(0, 0.02^2) weights: 0.02 times a chi variable with 128
+    degrees of freedom."""
+    v = _gen(config_id, tensor_id, 4, 0).normal(mean, sd, size=n)
+    v = np.maximum(v, mean / 8).astype(np.float16)
+    return v.view(np.uint8)
 
 
 def sample_rows(config_id, tensor_id, rows, n):

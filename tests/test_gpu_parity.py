@@ -183,6 +183,42 @@ def test_matvec_rejects_small_workspace():
     assert e.value.status == 8
 
 
+def _random_cq(bits, rows, cols, cfg):
+    """A full-size CQ matrix from seeded random bytes (no encoder involved):
+    returns the device matrix and the host blob the oracle decodes."""
+    kpad = oracle.padded_cols(cols)
+    packed = cq_inputs.random_bytes(cfg, bits, rows * kpad * oracle.storage_bits(bits) // 8)
+    norms = cq_inputs.random_norms(cfg, bits, rows * (kpad // 128))
+    blob = np.concatenate([packed, norms])
+    assert blob.size == oracle.blob_bytes(bits, 128, rows, cols)
+    return cq.CQMatrix(bits, rows, cols, _to_dev(blob), _levels(bits)), blob
+
+
+def _row_subset(blob, bits, rows, cols, pick):
+    packed, norms = oracle.split_blob(blob, bits, rows, cols)
+    return oracle.make_blob(packed[pick], norms[pick])
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+def test_matvec_full_size_sampled_rows(bits):
+    # the 65536 x 16384 workload in the launch configuration the benchmark
+    # times; the oracle computes sampled rows one by one
+    rows, cols = 65536, 16384
+    say("matvec full size", bits)
+    W, blob = _random_cq(bits, rows, cols, 60)
+    levels = _levels(bits)
+    pick = cq_inputs.sample_rows(60, bits, rows, 48)
+    sub = _row_subset(blob, bits, rows, cols, pick)
+    w_hat = np.linalg.norm(oracle.dequantize(sub, bits, len(pick), cols, levels), axis=1)
+    for batch in ((1, 8) if bits == 2 else (1,)):
+        x = cq_inputs.activations(60, 100 * batch + bits, batch, cols)
+        y = cq.cq_matvec(W, cq.cq_rotate_acts(_to_dev(x))).cpu().numpy()
+        ref = oracle.matvec(sub, bits, len(pick), cols, x, levels)
+        _check_fp32_product(y[:, pick], ref, w_hat, np.linalg.norm(x.astype(np.float64), axis=1))
+    del W
+    torch.cuda.empty_cache()
+
+
 def test_matvec_is_deterministic():
     W, _, _, _ = _cq_from_oracle(2, 2000, 16384, 33)
     xr = cq.cq_rotate_acts(_to_dev(cq_inputs.activations(33, 0, 1, 16384)))
@@ -209,6 +245,30 @@ def test_gemm(bits, m, rows, cols):
     _check_fp32_product(got, oracle.gemm(blob, bits, rows, cols, X, levels), w_hat, xn, tol=1e-2, min_cos=0.9999)
     # the same roundings as the matrix-core path (bf16 operands), much tighter
     _check_fp32_product(got, oracle.gemm_bf16(blob, bits, rows, cols, X, levels), w_hat, xn, tol=1e-4, min_cos=0.99999)
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_gemm_full_size_sampled(bits):
+    # M = 4096, N = K = 16384: sampled rows of C against the oracle
+    m, rows, cols = 4096, 16384, 16384
+    say("gemm full size", bits)
+    W, blob = _random_cq(bits, rows, cols, 61)
+    levels = _levels(bits)
+    X = cq_inputs.activations(61, bits, m, cols, "bf16")
+    xr = cq.cq_rotate_acts(_to_dev(X, torch.bfloat16), torch.bfloat16)
+    C = cq.cq_gemm(W, xr)
+    pick = cq_inputs.sample_rows(61, bits, rows, 24)
+    mp = cq_inputs.sample_rows(62, bits, m, 12)
+    got = C[torch.from_numpy(mp).to(DEV)][:, torch.from_numpy(pick).to(DEV)].cpu().numpy().astype(np.float64)
+    del C, W, xr
+    torch.cuda.empty_cache()
+    sub = _row_subset(blob, bits, rows, cols, pick)
+    w_hat = np.linalg.norm(oracle.dequantize(sub, bits, len(pick), cols, levels), axis=1)
+    xn = np.linalg.norm(X[mp].astype(np.float64), axis=1)
+    _check_fp32_product(got, oracle.gemm(sub, bits, len(pick), cols, X[mp], levels), w_hat, xn,
+                        tol=1e-2, min_cos=0.9999)
+    _check_fp32_product(got, oracle.gemm_bf16(sub, bits, len(pick), cols, X[mp], levels), w_hat, xn,
+                        tol=1e-4, min_cos=0.99999)
 
 
 def test_gemm_degenerate_shapes():
@@ -261,6 +321,22 @@ def test_quantize(bits, kind, rows, cols):
     blob_g = W.blob.cpu().numpy()
     assert blob_g.size == oracle.blob_bytes(bits, 128, rows, cols)
     frac = _encoder_agreement(bits, w, blob_g, levels)
+    say("  identical index fraction", frac)
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_quantize_full_size_sampled_rows(bits):
+    # the 16384 x 16384 encode: sampled rows of the blob against the oracle encoder
+    rows, cols = 16384, 16384
+    say("quantize full size", bits)
+    levels = _levels(bits)
+    w = cq_inputs.master(63, bits, rows, cols)
+    W = cq.cq_quantize(_to_dev(w), bits, levels)
+    blob_g = W.blob.cpu().numpy()
+    del W
+    torch.cuda.empty_cache()
+    pick = cq_inputs.sample_rows(63, bits, rows, 32)
+    frac = _encoder_agreement(bits, w[pick], _row_subset(blob_g, bits, rows, cols, pick), levels)
     say("  identical index fraction", frac)
 
 
