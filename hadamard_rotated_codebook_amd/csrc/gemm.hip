@@ -3,24 +3,50 @@
 // dequantised in the rotated domain, V[r][g*128+j] = bf16(c[q] * norm[r][g]).
 // By the rotated-activation identity (OpenNeedle reference notes) this is the
 // product with the dense dequantised matrix, without ever applying H to the
-// weights or writing them to memory.
+// weights or writing them to memory (".cact" format post, "How the kernel
+// reads it": no weight is materialised outside the tile being multiplied).
 //
-// Tiling: a 256-thread workgroup (4 waves, 2 x 2) computes a 128 x 128 tile of
-// C.  The K loop steps 64 columns (half a quantisation group).  Each step
-// stages the Xr tile (global -> LDS) and decodes the packed W tile to bf16
-// straight into LDS (8 codes per thread per word), then every wave runs
-// 2 x 4 x 4 v_mfma_f32_16x16x32_bf16 on its 64 x 64 sub-tile, fp32 accumulate.
-// LDS rows are 64 bf16 (128 B); 16-byte chunks are XOR-swizzled by row so
-// that the fragment reads of 16 consecutive rows fall in distinct banks.
+// Design (MFMA-bound at M = 4096, N = K = 16384 on MI355X):
+//  * A 512-thread workgroup (8 waves, 2 along M x 4 along N) computes a
+//    256 x 256 tile of C, 128 x 64 per wave: 8 x 4 blocks of
+//    v_mfma_f32_16x16x32_bf16 with fp32 accumulators (128 VGPRs per lane), two
+//    waves per SIMD so that one's barrier waits and decode hide behind the
+//    other's matrix work.
+//  * K advances 64 columns per stage through double-buffered LDS (2 x 64 KB).
+//    While the matrix cores work on stage s, every thread has in flight the
+//    Xr chunks of stage s+1 and its part of the W codes (and, at group starts,
+//    the norm) of stage s+2 -- two register sets for W, whose loads go to HBM
+//    -- and then writes stage s+1, Xr chunks and decoded W values, into the
+//    other LDS buffer: one barrier per stage.  All loads are unconditional
+//    buffer loads; rows past the end of Xr or W fall outside the tile's buffer
+//    range and read as zeros, so no select ties a load to its issue point.
+//  * Decode: a pair of threads owns a row of the W tile.  Per (row, group) it
+//    builds the table bf16(level[c] * norm) for every code c
+//    (v_cvt_pk_bf16_f32, round to nearest even) as byte planes, and turns
+//    packed codes into bf16 pairs with v_perm_b32 lookups: 1.9 VALU per weight
+//    at 2 bits, 2.5 at 3 bits, 3.6 at 4 bits (two 8-entry halves selected by
+//    the code's top bit).
+//  * LDS rows are 64 bf16 (128 B); 16-byte chunks are XOR-swizzled by row so
+//    that the fragment reads of 16 consecutive rows fall in distinct banks.
+//  * Tiles are ordered in groups of 4 M-tiles, and the ids are renumbered so
+//    that each XCD runs consecutive groups: the 32 workgroups of an XCD share
+//    4 Xr tiles and 8 W tiles through its L2.
+#include <type_traits>
+
 #include "cq_internal.h"
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int kThreads = 256;
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kWavesM = 2;  // waves along M; the waves along N are a template parameter
+constexpr int kGroupM = 4;  // M-tiles per tile group
+#ifndef CQ_GEMM_WN
+#define CQ_GEMM_WN 4
+#endif
 
 struct GemmArgs {
   const uint8_t *packed;
@@ -28,104 +54,288 @@ struct GemmArgs {
   const uint16_t *xr;     // bf16 bits [m][kpad]
   float *c;               // [m][rows]
   int64_t m, rows, kpad, row_bytes, ngroups;
+  int32_t tiles_m, tiles_n;
   cq::CodeLevels lev;
 };
 
-__device__ inline uint32_t bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 __device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
+// Raw buffer resource over nbytes at base: loads at offsets >= nbytes return
+// zero, which is how rows past the end of Xr and W read as zeros.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(nbytes),
+                                           0x00020000);  // word 3: raw, 32-bit data format
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// N consecutive dwords at byte offset off, in as few loads as possible.
+template <int N>
+__device__ inline void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *d) {
+#pragma unroll
+  for (int q = 0; q + 4 <= N; q += 4) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * q, 0, 0);
+    d[q] = v.x, d[q + 1] = v.y, d[q + 2] = v.z, d[q + 3] = v.w;
+  }
+  constexpr int q = N / 4 * 4;
+  if constexpr (N - q == 3) {
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off + 4 * q, 0, 0);
+    d[q] = v.x, d[q + 1] = v.y, d[q + 2] = v.z;
+  } else if constexpr (N - q == 2) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * q, 0, 0);
+    d[q] = v.x, d[q + 1] = v.y;
+  } else if constexpr (N - q == 1) {
+    d[q] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * q, 0, 0);
+  }
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) { return __builtin_amdgcn_perm(hi, lo, sel); }
+
+// b where mask bits are set, a elsewhere (one v_bfi_b32).
+__device__ inline uint32_t select(uint32_t mask, uint32_t b, uint32_t a) { return (b & mask) | (a & ~mask); }
+
+// Decoded values of one (row, group): T[c] = bf16(level[c] * norm), as the
+// low and high byte planes of the bf16 values (4 entries per dword).
 template <int SB>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
-  __shared__ uint4 As[BM * BK / 8];  // [row][chunk] 16-byte chunks
-  __shared__ uint4 Vs[BN * BK / 8];
-  __shared__ float lev[16];
+struct Table {
+  static constexpr int L = 1 << SB;
+  uint32_t lo[L / 4 > 0 ? L / 4 : 1], hi[L / 4 > 0 ? L / 4 : 1];
+  uint32_t pair[2];  // SB == 2: T[0] | T[1] << 16, T[2] | T[3] << 16
+
+  __device__ void build(const cq::CodeLevels &lev, float n) {
+    if constexpr (SB == 2) {
+      pair[0] = pack_bf16x2(lev.v[0] * n, lev.v[1] * n);
+      pair[1] = pack_bf16x2(lev.v[2] * n, lev.v[3] * n);
+    } else {
+#pragma unroll
+      for (int k = 0; k < L / 4; ++k) {
+        const uint32_t p0 = pack_bf16x2(lev.v[4 * k] * n, lev.v[4 * k + 1] * n);
+        const uint32_t p1 = pack_bf16x2(lev.v[4 * k + 2] * n, lev.v[4 * k + 3] * n);
+        lo[k] = perm(p1, p0, 0x06040200u);
+        hi[k] = perm(p1, p0, 0x07050301u);
+      }
+    }
+  }
+};
+
+// 4-bit: the 8 codes of a dword -> 4 dwords of bf16 pairs, codes in order.
+__device__ inline void decode4(const Table<4> &t, uint32_t d, uint32_t *o) {
+  // Even codes (low nibbles) and odd codes (high nibbles), one per byte: the
+  // low three bits select within an 8-entry half, bit 3 selects the half.
+  const uint32_t se = d & 0x07070707u, so = (d >> 4) & 0x07070707u;
+  const uint32_t me = ((d >> 3) & 0x01010101u) * 0xffu, mo = ((d >> 7) & 0x01010101u) * 0xffu;
+  const uint32_t el = select(me, perm(t.lo[3], t.lo[2], se), perm(t.lo[1], t.lo[0], se));
+  const uint32_t eh = select(me, perm(t.hi[3], t.hi[2], se), perm(t.hi[1], t.hi[0], se));
+  const uint32_t ol = select(mo, perm(t.lo[3], t.lo[2], so), perm(t.lo[1], t.lo[0], so));
+  const uint32_t oh = select(mo, perm(t.hi[3], t.hi[2], so), perm(t.hi[1], t.hi[0], so));
+  // low bytes of codes 0,1,2,3 and high bytes of codes 0,1,2,3; then 4..7
+  const uint32_t l03 = perm(ol, el, 0x05010400u), h03 = perm(oh, eh, 0x05010400u);
+  const uint32_t l47 = perm(ol, el, 0x07030602u), h47 = perm(oh, eh, 0x07030602u);
+  o[0] = perm(h03, l03, 0x05010400u);
+  o[1] = perm(h03, l03, 0x07030602u);
+  o[2] = perm(h47, l47, 0x05010400u);
+  o[3] = perm(h47, l47, 0x07030602u);
+}
+
+// 3-bit: 8 codes in the low 24 bits of b -> 4 dwords of bf16 pairs.
+__device__ inline void decode3(const Table<3> &t, uint32_t b, uint32_t *o) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t f = b >> (12 * h);  // four codes in bits 0..11
+    const uint32_t s = (f & 7u) | ((f << 5) & 0x700u) | ((f << 10) & 0x70000u) | ((f << 15) & 0x7000000u);
+    const uint32_t l = perm(t.lo[1], t.lo[0], s), hh = perm(t.hi[1], t.hi[0], s);
+    o[2 * h] = perm(hh, l, 0x05010400u);
+    o[2 * h + 1] = perm(hh, l, 0x07030602u);
+  }
+}
+
+// 2-bit (CQ2 and ternary crumbs): the 16 codes of a dword -> 8 dwords.
+__device__ inline void decode2(const Table<2> &t, uint32_t d, uint32_t *o) {
+  const uint32_t x0 = d & 0x03030303u, x1 = (d >> 2) & 0x03030303u;
+  const uint32_t x2 = (d >> 4) & 0x03030303u, x3 = (d >> 6) & 0x03030303u;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    // codes 4b, 4b+1 sit in byte b of x0, x1; codes 4b+2, 4b+3 in x2, x3
+    const uint32_t sa = perm(x1, x0, 0x04040000u + 0x01010101u * b) * 2u + 0x01000100u;
+    const uint32_t sb = perm(x3, x2, 0x04040000u + 0x01010101u * b) * 2u + 0x01000100u;
+    o[2 * b] = perm(t.pair[1], t.pair[0], sa);
+    o[2 * b + 1] = perm(t.pair[1], t.pair[0], sb);
+  }
+}
+
+template <int SB, int WN>
+__global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) {
+  constexpr int kThreads = 64 * kWavesM * WN;
+  constexpr int TN = BN / WN;                  // wave tile: 128 x TN
+  constexpr int FI = 128 / 16, FJ = TN / 16;   // 16 x 16 blocks per wave
+  constexpr int XPT = BM * 8 / kThreads;       // Xr chunks per thread per stage
+  constexpr int TPR = kThreads / BN;           // threads per W row
+  constexpr int CODES = BK / TPR;              // codes a thread decodes per stage
+  constexpr int CODE_DW = CODES * SB / 32;     // their packed dwords
+  __shared__ uint4 As[2][BM * 8];              // [stage][row][chunk], 16-byte chunks
+  __shared__ uint4 Bs[2][BN * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
-  if (tid < 16) lev[tid] = a.lev.v[tid];
+  const int wm = wave / WN, wn = wave % WN;
 
-  floatx4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // Tile order: groups of kGroupM M-tiles walk all N-tiles; ids renumbered so
+  // that consecutive tiles run on one XCD (ids are dispatched round-robin).
+  const int total = a.tiles_m * a.tiles_n;
+  int t = blockIdx.x;
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+  const int per_group = kGroupM * a.tiles_n;
+  const int first_m = (t / per_group) * kGroupM;
+  const int gsize = min(kGroupM, a.tiles_m - first_m);
+  const int tm = first_m + (t % per_group) % gsize;
+  const int tn = (t % per_group) / gsize;
+  const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
 
-  constexpr uint32_t mask = (1u << SB) - 1u;
-  for (int64_t k0 = 0; k0 < a.kpad; k0 += BK) {
-    __syncthreads();
-    // Stage Xr: 128 rows x 8 chunks.
+  // Global sources of this thread: Xr chunk (tid & 7) of rows (tid >> 3) +
+  // (kThreads / 8) p, and part `half` of row `wr` of the W tile.  Offsets are
+  // relative to the tile's first row and fit 32 bits (the host bounds kpad).
+  const int xch = tid & 7;
+  const int wr = tid / TPR, half = tid % TPR;
+  const int64_t mrows = a.m - m0 < BM ? a.m - m0 : BM, nrows = a.rows - n0 < BN ? a.rows - n0 : BN;
+  const __amdgpu_buffer_rsrc_t xbuf = buffer_rsrc(a.xr + m0 * a.kpad, static_cast<uint32_t>(mrows * a.kpad * 2));
+  const __amdgpu_buffer_rsrc_t wbuf =
+      buffer_rsrc(a.packed + n0 * a.row_bytes, static_cast<uint32_t>(nrows * a.row_bytes));
+  const __amdgpu_buffer_rsrc_t nbuf =
+      buffer_rsrc(a.norms + n0 * a.ngroups, static_cast<uint32_t>(nrows * a.ngroups * 2));
+  const uint32_t xoff = static_cast<uint32_t>((tid >> 3) * a.kpad * 2 + xch * 16);
+  const uint32_t xstep = static_cast<uint32_t>((kThreads / 8) * a.kpad * 2);  // between a thread's rows
+  const uint32_t woff = static_cast<uint32_t>(wr * a.row_bytes + half * (CODES * SB / 8));
+  const uint32_t noff = static_cast<uint32_t>(wr * a.ngroups * 2);
+
+  // The W codes of stage s+2 (from HBM) are loaded while stage s is
+  // multiplied, into one of two register sets; the Xr chunks of stage s+1
+  // (mostly cache hits: every N-tile reads them) into a single set.  Even
+  // stages start a group (BK is half a group), so only set 0 carries a norm
+  // and only its stores build a table.  Rows past the end load zeros: an Xr
+  // row directly, a W row through a zero norm (an all-zero decode table).
+  uint4 xa[XPT];
+  uint32_t wc[2][CODE_DW];
+  uint16_t wn16 = 0;
+  auto load_x = [&](int64_t k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + kThreads * i;
-      const int row = id >> 3, ch = id & 7;
-      const int64_t gm = m0 + row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (gm < a.m) v = *reinterpret_cast<const uint4 *>(a.xr + gm * a.kpad + k0 + ch * 8);
-      As[row * 8 + swz(row, ch)] = v;
+    for (int p = 0; p < XPT; ++p)
+      xa[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            xbuf, xoff + p * xstep + static_cast<uint32_t>(k0 * 2), 0, 0));
+  };
+  auto load_w = [&](int64_t k0, auto set_c) {
+    constexpr int S = decltype(set_c)::value;
+    load_dwords<CODE_DW>(wbuf, woff + static_cast<uint32_t>(k0 * SB / 8), wc[S]);
+    if constexpr (S == 0) wn16 = __builtin_amdgcn_raw_buffer_load_b16(nbuf, noff + static_cast<uint32_t>(k0 / CQ_GROUP * 2), 0, 0);
+  };
+
+  Table<SB> tab;
+  auto store_stage = [&](int buf, auto set_c) {
+    constexpr int S = decltype(set_c)::value;
+    const uint32_t *wcs = wc[S];
+#pragma unroll
+    for (int p = 0; p < XPT; ++p) {
+      const int row = (tid >> 3) + (kThreads / 8) * p;
+      As[buf][row * 8 + swz(row, xch)] = xa[p];
     }
-    // Decode W: 128 rows x 8 words of 8 codes.
-    const int64_t g = k0 >> 7;
+    if constexpr (S == 0) tab.build(a.lev, static_cast<float>(__builtin_bit_cast(_Float16, wn16)));
+    uint32_t o[CODES / 2];
+    if constexpr (SB == 4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + kThreads * i;
-      const int row = id >> 3, wd = id & 7;
-      const int64_t gr = n0 + row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (gr < a.rows) {
-        const uint8_t *src = a.packed + gr * a.row_bytes + ((k0 >> 3) + wd) * SB;
-        uint32_t word;
-        if (SB == 2) word = *reinterpret_cast<const uint16_t *>(src);
-        else if (SB == 4) word = *reinterpret_cast<const uint32_t *>(src);
-        else word = src[0] | (static_cast<uint32_t>(src[1]) << 8) | (static_cast<uint32_t>(src[2]) << 16);
-        const float n = static_cast<float>(__builtin_bit_cast(_Float16, a.norms[gr * a.ngroups + g]));
-        uint32_t h[8];
+      for (int q = 0; q < CODE_DW; ++q) decode4(tab, wcs[q], o + 4 * q);
+    } else if constexpr (SB == 3) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = bf16_bits(lev[(word >> (e * SB)) & mask] * n);
-        v = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+      for (int q = 0; q < CODES / 8; ++q) {  // 24 bits per 8 codes: byte offset 3 q
+        const int bit = 24 * q, w = bit >> 5, sh = bit & 31;
+        const uint32_t b = sh <= 8 ? (wcs[w] >> sh) : __builtin_amdgcn_alignbit(wcs[(w + 1) % CODE_DW], wcs[w], sh);
+        decode3(tab, b & 0xffffffu, o + 4 * q);
       }
-      Vs[row * 8 + swz(row, wd)] = v;
+    } else {
+#pragma unroll
+      for (int q = 0; q < CODE_DW; ++q) decode2(tab, wcs[q], o + 8 * q);
     }
-    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CODES / 8; ++c) {
+      const int ch = half * (CODES / 8) + c;
+      Bs[buf][wr * 8 + swz(wr, ch)] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+    }
+  };
 
+  floatx4 acc[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+  // kpad is a multiple of the group size, so the stage count is even.
+  const int nstages = static_cast<int>(a.kpad / BK);
+  load_x(0);
+  load_w(0, Set0{});
+  load_w(BK, Set1{});
+  store_stage(0, Set0{});
+  __syncthreads();
+  // Stage s: loads of stage s+1 (Xr) and s+2 (W, register set s%2), the matrix
+  // cores on LDS buffer s%2, then stage s+1 (W register set (s+1)%2) into LDS
+  // buffer (s+1)%2.  The loads are unconditional (past the end they reload
+  // the last stage, unused): a load issued on only some paths would make the
+  // compiler count outstanding loads for the shorter path and so wait for the
+  // newer ones too.
+  auto stage = [&](int s, auto par_c) {
+    constexpr int P = decltype(par_c)::value;  // s % 2
+    constexpr int cur = P;
+    load_x(static_cast<int64_t>(s + 1 < nstages ? s + 1 : nstages - 1) * BK);
+    load_w(static_cast<int64_t>(s + 2 < nstages ? s + 2 : nstages - 1) * BK, std::integral_constant<int, P>{});
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       const int ch = kk * 4 + (lane >> 4);
-      bf16x8 af[4], bfr[4];
+      bf16x8 af[FI], bfr[FJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 64 + i * 16 + (lane & 15);
-        af[i] = __builtin_bit_cast(bf16x8, As[row * 8 + swz(row, ch)]);
+      for (int i = 0; i < FI; ++i) {
+        const int row = wm * 128 + i * 16 + (lane & 15);
+        af[i] = __builtin_bit_cast(bf16x8, As[cur][row * 8 + swz(row, ch)]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wn * 64 + j * 16 + (lane & 15);
-        bfr[j] = __builtin_bit_cast(bf16x8, Vs[row * 8 + swz(row, ch)]);
+      for (int j = 0; j < FJ; ++j) {
+        const int row = wn * TN + j * 16 + (lane & 15);
+        bfr[j] = __builtin_bit_cast(bf16x8, Bs[cur][row * 8 + swz(row, ch)]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < FJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      // Fence each 32-wide k step: without it the scheduler loads the next
+      // step's fragments while this step's are live, and the 3- and 4-bit
+      // kernels spill past 256 VGPRs (the scratch reloads then drain vmcnt).
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // After the last stage this fills the idle buffer with data nobody reads;
+    // a conditional store would let the compiler sink the Xr loads into it,
+    // right before their use.
+    store_stage(cur ^ 1, std::integral_constant<int, 1 - P>{});
+    __syncthreads();
+  };
+  for (int s = 0; s < nstages; s += 2) {
+    stage(s, Set0{});
+    stage(s + 1, Set1{});
   }
 
   // C fragment layout: lane l, register e -> row 4*(l/16) + e, column l%16.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < FI; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 64 + j * 16 + (lane & 15);
+    for (int j = 0; j < FJ; ++j) {
+      const int64_t col = n0 + wn * TN + j * 16 + (lane & 15);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t row = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + e;
+        const int64_t row = m0 + wm * 128 + i * 16 + 4 * (lane >> 4) + e;
         if (row < a.m && col < a.rows) a.c[row * a.rows + col] = acc[i][j][e];
       }
     }
@@ -138,6 +348,9 @@ namespace cq {
 
 hipError_t launch_gemm(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
                        const void *xr, int64_t m, float *c, hipStream_t s) {
+  // The stage loop needs whole groups; tile-relative buffer offsets need
+  // 257 rows of Xr (2 kpad bytes each) to fit 32 bits.
+  if (kpad <= 0 || kpad % CQ_GROUP != 0 || kpad > (int64_t{1} << 22)) return hipErrorInvalidValue;
   const int sb = storage_bits(bits);
   GemmArgs a;
   a.packed = blob;
@@ -150,13 +363,16 @@ hipError_t launch_gemm(const uint8_t *blob, int bits, int64_t rows, int64_t kpad
   a.kpad = kpad;
   a.ngroups = kpad / CQ_GROUP;
   a.lev = lev;
-  const int64_t gx = (rows + BN - 1) / BN, gy = (m + BM - 1) / BM;
-  if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidConfiguration;
-  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+  const int64_t tm = (m + BM - 1) / BM, tn = (rows + BN - 1) / BN;
+  if (tm * tn > 0x7fffffff) return hipErrorInvalidConfiguration;
+  a.tiles_m = static_cast<int32_t>(tm);
+  a.tiles_n = static_cast<int32_t>(tn);
+  const dim3 grid(static_cast<unsigned>(tm * tn));
+  constexpr int threads = 64 * kWavesM * CQ_GEMM_WN;
   switch (sb) {
-    case 2: gemm_kernel<2><<<grid, kThreads, 0, s>>>(a); break;
-    case 3: gemm_kernel<3><<<grid, kThreads, 0, s>>>(a); break;
-    default: gemm_kernel<4><<<grid, kThreads, 0, s>>>(a); break;
+    case 2: gemm_kernel<2, CQ_GEMM_WN><<<grid, threads, 0, s>>>(a); break;
+    case 3: gemm_kernel<3, CQ_GEMM_WN><<<grid, threads, 0, s>>>(a); break;
+    default: gemm_kernel<4, CQ_GEMM_WN><<<grid, threads, 0, s>>>(a); break;
   }
   return hipGetLastError();
 }
