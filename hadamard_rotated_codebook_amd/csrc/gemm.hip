@@ -13,13 +13,15 @@
 //    waves per SIMD so that one's barrier waits and decode hide behind the
 //    other's matrix work.
 //  * K advances 64 columns per stage through double-buffered LDS (2 x 64 KB).
-//    While the matrix cores work on stage s, every thread has in flight the
-//    Xr chunks of stage s+1 and its part of the W codes (and, at group starts,
-//    the norm) of stage s+2 -- two register sets for W, whose loads go to HBM
-//    -- and then writes stage s+1, Xr chunks and decoded W values, into the
-//    other LDS buffer: one barrier per stage.  All loads are unconditional
-//    buffer loads; rows past the end of Xr or W fall outside the tile's buffer
-//    range and read as zeros, so no select ties a load to its issue point.
+//    At the start of stage s every thread issues the loads of stage s+2 (Xr
+//    chunks, its part of the W codes and, at group starts, the norm) into one
+//    of two register sets; while the matrix cores work on stage s it writes
+//    stage s+1, Xr chunks and decoded W values, into the other LDS buffer, the
+//    decode interleaved among the MFMAs (sched_group_barrier) so that VALU and
+//    matrix cores overlap: one barrier per stage.  All loads are
+//    unconditional buffer loads; rows past the end of Xr or W fall outside the
+//    tile's buffer range and read as zeros, so no select ties a load to its
+//    issue point.
 //  * Decode: a pair of threads owns a row of the W tile.  Per (row, group) it
 //    builds the table bf16(level[c] * norm) for every code c
 //    (v_cvt_pk_bf16_f32, round to nearest even) as byte planes, and turns
@@ -44,6 +46,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kWavesM = 2;  // waves along M; the waves along N are a template parameter
 constexpr int kGroupM = 4;  // M-tiles per tile group
+constexpr int kValuPerMfma = 2;  // VALU slots after each MFMA in the interleave
 #ifndef CQ_GEMM_WN
 #define CQ_GEMM_WN 4
 #endif
@@ -219,49 +222,54 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
   // stages start a group (BK is half a group), so only set 0 carries a norm
   // and only its stores build a table.  Rows past the end load zeros: an Xr
   // row directly, a W row through a zero norm (an all-zero decode table).
-  uint4 xa[XPT];
+  uint4 xa[2][XPT];
   uint32_t wc[2][CODE_DW];
   uint16_t wn16 = 0;
-  auto load_x = [&](int64_t k0) {
-#pragma unroll
-    for (int p = 0; p < XPT; ++p)
-      xa[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            xbuf, xoff + p * xstep + static_cast<uint32_t>(k0 * 2), 0, 0));
-  };
-  auto load_w = [&](int64_t k0, auto set_c) {
+  auto load = [&](int64_t k0, auto set_c) {
     constexpr int S = decltype(set_c)::value;
     load_dwords<CODE_DW>(wbuf, woff + static_cast<uint32_t>(k0 * SB / 8), wc[S]);
-    if constexpr (S == 0) wn16 = __builtin_amdgcn_raw_buffer_load_b16(nbuf, noff + static_cast<uint32_t>(k0 / CQ_GROUP * 2), 0, 0);
+    if constexpr (S == 0)
+      wn16 = __builtin_amdgcn_raw_buffer_load_b16(nbuf, noff + static_cast<uint32_t>(k0 / CQ_GROUP * 2), 0, 0);
+#pragma unroll
+    for (int p = 0; p < XPT; ++p)
+      xa[S][p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               xbuf, xoff + p * xstep + static_cast<uint32_t>(k0 * 2), 0, 0));
   };
 
+  // Writing the stage held in register set S into LDS buffer buf, in two
+  // parts: part 0 writes the Xr chunks, builds the group's table (set 0: even
+  // stages start a group) and decodes the first half of this thread's codes;
+  // part 1 decodes the second half.  Each half is two 16-byte chunks of W.
   Table<SB> tab;
-  auto store_stage = [&](int buf, auto set_c) {
-    constexpr int S = decltype(set_c)::value;
+  auto store_part = [&](int buf, auto set_c, auto part_c) {
+    constexpr int S = decltype(set_c)::value, PART = decltype(part_c)::value;
     const uint32_t *wcs = wc[S];
+    if constexpr (PART == 0) {
 #pragma unroll
-    for (int p = 0; p < XPT; ++p) {
-      const int row = (tid >> 3) + (kThreads / 8) * p;
-      As[buf][row * 8 + swz(row, xch)] = xa[p];
+      for (int p = 0; p < XPT; ++p) {
+        const int row = (tid >> 3) + (kThreads / 8) * p;
+        As[buf][row * 8 + swz(row, xch)] = xa[S][p];
+      }
+      if constexpr (S == 0) tab.build(a.lev, static_cast<float>(__builtin_bit_cast(_Float16, wn16)));
     }
-    if constexpr (S == 0) tab.build(a.lev, static_cast<float>(__builtin_bit_cast(_Float16, wn16)));
-    uint32_t o[CODES / 2];
+    static_assert(CODES / 8 == 4, "four 8-code chunks per thread and stage");
+    uint32_t o[8];
     if constexpr (SB == 4) {
-#pragma unroll
-      for (int q = 0; q < CODE_DW; ++q) decode4(tab, wcs[q], o + 4 * q);
+      decode4(tab, wcs[2 * PART], o);
+      decode4(tab, wcs[2 * PART + 1], o + 4);
     } else if constexpr (SB == 3) {
 #pragma unroll
-      for (int q = 0; q < CODES / 8; ++q) {  // 24 bits per 8 codes: byte offset 3 q
+      for (int q = 2 * PART; q < 2 * PART + 2; ++q) {  // 24 bits per 8 codes: byte offset 3 q
         const int bit = 24 * q, w = bit >> 5, sh = bit & 31;
         const uint32_t b = sh <= 8 ? (wcs[w] >> sh) : __builtin_amdgcn_alignbit(wcs[(w + 1) % CODE_DW], wcs[w], sh);
-        decode3(tab, b & 0xffffffu, o + 4 * q);
+        decode3(tab, b & 0xffffffu, o + 4 * (q - 2 * PART));
       }
     } else {
-#pragma unroll
-      for (int q = 0; q < CODE_DW; ++q) decode2(tab, wcs[q], o + 8 * q);
+      decode2(tab, wcs[PART], o);
     }
 #pragma unroll
-    for (int c = 0; c < CODES / 8; ++c) {
-      const int ch = half * (CODES / 8) + c;
+    for (int c = 0; c < 2; ++c) {
+      const int ch = half * (CODES / 8) + 2 * PART + c;
       Bs[buf][wr * 8 + swz(wr, ch)] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
     }
   };
@@ -272,54 +280,75 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
 #pragma unroll
     for (int j = 0; j < FJ; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  using Set0 = std::integral_constant<int, 0>;
-  using Set1 = std::integral_constant<int, 1>;
-  // kpad is a multiple of the group size, so the stage count is even.
-  const int nstages = static_cast<int>(a.kpad / BK);
-  load_x(0);
-  load_w(0, Set0{});
-  load_w(BK, Set1{});
-  store_stage(0, Set0{});
-  __syncthreads();
-  // Stage s: loads of stage s+1 (Xr) and s+2 (W, register set s%2), the matrix
-  // cores on LDS buffer s%2, then stage s+1 (W register set (s+1)%2) into LDS
-  // buffer (s+1)%2.  The loads are unconditional (past the end they reload
-  // the last stage, unused): a load issued on only some paths would make the
-  // compiler count outstanding loads for the shorter path and so wait for the
-  // newer ones too.
-  auto stage = [&](int s, auto par_c) {
-    constexpr int P = decltype(par_c)::value;  // s % 2
-    constexpr int cur = P;
-    load_x(static_cast<int64_t>(s + 1 < nstages ? s + 1 : nstages - 1) * BK);
-    load_w(static_cast<int64_t>(s + 2 < nstages ? s + 2 : nstages - 1) * BK, std::integral_constant<int, P>{});
+  // One 32-wide k step on LDS buffer cur: the fragment reads, then part PART
+  // of writing the next stage (register set S) into the other buffer, then
+  // the 32 MFMAs, with the decode and its LDS writes interleaved among them
+  // so that the matrix cores and the VALU work at the same time.
+  auto kstep = [&](auto cur_c, auto kk_c, auto set_c) {
+    constexpr int cur = decltype(cur_c)::value, kk = decltype(kk_c)::value;
+    const int ch = kk * 4 + (lane >> 4);
+    bf16x8 af[FI], bfr[FJ];
 #pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      const int ch = kk * 4 + (lane >> 4);
-      bf16x8 af[FI], bfr[FJ];
+    for (int j = 0; j < FJ; ++j) {
+      const int row = wn * TN + j * 16 + (lane & 15);
+      bfr[j] = __builtin_bit_cast(bf16x8, Bs[cur][row * 8 + swz(row, ch)]);
+    }
 #pragma unroll
-      for (int i = 0; i < FI; ++i) {
-        const int row = wm * 128 + i * 16 + (lane & 15);
-        af[i] = __builtin_bit_cast(bf16x8, As[cur][row * 8 + swz(row, ch)]);
-      }
+    for (int i = 0; i < FI; ++i) {
+      const int row = wm * 128 + i * 16 + (lane & 15);
+      af[i] = __builtin_bit_cast(bf16x8, As[cur][row * 8 + swz(row, ch)]);
+    }
+    store_part(cur ^ 1, set_c, kk_c);
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < FJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    // Order: the B fragments and the first A fragment, then per A fragment
+    // the read of the next one and its FJ MFMAs, each MFMA followed by a few
+    // VALU instructions and every fourth by an LDS write.  A fragments are
+    // read one ahead of use, which keeps few of them live.
+    __builtin_amdgcn_sched_group_barrier(0x100, FJ + 1, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      if (i + 1 < FI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
       for (int j = 0; j < FJ; ++j) {
-        const int row = wn * TN + j * 16 + (lane & 15);
-        bfr[j] = __builtin_bit_cast(bf16x8, Bs[cur][row * 8 + swz(row, ch)]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // VALU
+        if ((i * FJ + j) % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
       }
-#pragma unroll
-      for (int i = 0; i < FI; ++i)
-#pragma unroll
-        for (int j = 0; j < FJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      // Fence each 32-wide k step: without it the scheduler loads the next
-      // step's fragments while this step's are live, and the 3- and 4-bit
-      // kernels spill past 256 VGPRs (the scratch reloads then drain vmcnt).
-      __builtin_amdgcn_sched_barrier(0);
     }
-    // After the last stage this fills the idle buffer with data nobody reads;
-    // a conditional store would let the compiler sink the Xr loads into it,
-    // right before their use.
-    store_stage(cur ^ 1, std::integral_constant<int, 1 - P>{});
+    // Fence: without it the scheduler loads the next step's fragments while
+    // this step's are live, and the 3- and 4-bit kernels spill past 256 VGPRs.
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+  using Part0 = std::integral_constant<int, 0>;
+  using Part1 = std::integral_constant<int, 1>;
+  // kpad is a multiple of the group size, so the stage count is even.
+  const int nstages = static_cast<int>(a.kpad / BK);
+  load(0, Set0{});
+  load(BK, Set1{});
+  store_part(0, Set0{}, Part0{});
+  store_part(0, Set0{}, Part1{});
+  __syncthreads();
+  // Stage s: loads of stage s+2 into register set s%2, then the matrix cores
+  // on LDS buffer s%2 while stage s+1 (register set (s+1)%2) is written into
+  // buffer (s+1)%2.  The loads are unconditional (past the end they reload
+  // the last stage, unused), and so are the writes (after the last stage
+  // they fill the idle buffer): a load or a use on only some paths would make
+  // the compiler wait for the newer loads too, or sink the loads to the use.
+  auto stage = [&](int s, auto par_c) {
+    constexpr int P = decltype(par_c)::value;  // s % 2
+    load(static_cast<int64_t>(s + 2 < nstages ? s + 2 : nstages - 1) * BK, par_c);
+    __builtin_amdgcn_sched_barrier(0);
+    using Cur = std::integral_constant<int, P>;
+    using Next = std::integral_constant<int, 1 - P>;
+    kstep(Cur{}, Part0{}, Next{});
+    kstep(Cur{}, Part1{}, Next{});
     __syncthreads();
   };
   for (int s = 0; s < nstages; s += 2) {
