@@ -36,14 +36,22 @@ float ternary_level_f32();
 hipError_t launch_rotate(const void *x, int x_dtype, int64_t batch, int64_t cols, int64_t kpad,
                          void *xr, int xr_dtype, hipStream_t s);
 
-// Workspace the matvec needs (0 when K fits one slice): per-slice partial sums
-// and one counter per row block.  The counters must be zero before a call and
-// are zero again after it.
+// Workspace the matvec needs (0 when K fits one slice): the per-slice partial
+// sums, any contents on entry.
 uint64_t matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch);
 
+// batch 1: lookup-table kernel; batch 2..8: the matrix-core kernel.
 hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
                          const CodeLevels &lev, const float *xr, int64_t batch, float *y,
                          void *workspace, hipStream_t s);
+
+uint64_t matvec_mma_workspace_bytes(int64_t rows, int64_t kpad, int64_t batch);
+hipError_t launch_matvec_mma(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
+                             const CodeLevels &lev, const float *xr, int64_t batch, float *y,
+                             void *workspace, hipStream_t s);
+
+// y[i] = sum over s < nslice, in order, of partial[s * n + i].
+hipError_t launch_combine(const float *partial, int64_t n, int nslice, float *y, hipStream_t s);
 
 hipError_t launch_gemm(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
                        const CodeLevels &lev, const void *xr, int64_t m, float *c, hipStream_t s);

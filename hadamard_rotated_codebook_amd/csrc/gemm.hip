@@ -35,9 +35,12 @@
 //    4 Xr tiles and 8 W tiles through its L2.
 #include <type_traits>
 
+#include "cq_decode.h"
 #include "cq_internal.h"
 
 namespace {
+
+using namespace cqdev;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -62,116 +65,6 @@ struct GemmArgs {
 };
 
 __device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
-
-// Raw buffer resource over nbytes at base: loads at offsets >= nbytes return
-// zero, which is how rows past the end of Xr and W read as zeros.
-__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(nbytes),
-                                           0x00020000);  // word 3: raw, 32-bit data format
-}
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// N consecutive dwords at byte offset off, in as few loads as possible.
-template <int N>
-__device__ inline void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *d) {
-#pragma unroll
-  for (int q = 0; q + 4 <= N; q += 4) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * q, 0, 0);
-    d[q] = v.x, d[q + 1] = v.y, d[q + 2] = v.z, d[q + 3] = v.w;
-  }
-  constexpr int q = N / 4 * 4;
-  if constexpr (N - q == 3) {
-    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off + 4 * q, 0, 0);
-    d[q] = v.x, d[q + 1] = v.y, d[q + 2] = v.z;
-  } else if constexpr (N - q == 2) {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * q, 0, 0);
-    d[q] = v.x, d[q + 1] = v.y;
-  } else if constexpr (N - q == 1) {
-    d[q] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * q, 0, 0);
-  }
-}
-
-__device__ inline uint32_t pack_bf16x2(float a, float b) {
-  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) { return __builtin_amdgcn_perm(hi, lo, sel); }
-
-// b where mask bits are set, a elsewhere (one v_bfi_b32).
-__device__ inline uint32_t select(uint32_t mask, uint32_t b, uint32_t a) { return (b & mask) | (a & ~mask); }
-
-// Decoded values of one (row, group): T[c] = bf16(level[c] * norm), as the
-// low and high byte planes of the bf16 values (4 entries per dword).
-template <int SB>
-struct Table {
-  static constexpr int L = 1 << SB;
-  uint32_t lo[L / 4 > 0 ? L / 4 : 1], hi[L / 4 > 0 ? L / 4 : 1];
-  uint32_t pair[2];  // SB == 2: T[0] | T[1] << 16, T[2] | T[3] << 16
-
-  __device__ void build(const cq::CodeLevels &lev, float n) {
-    if constexpr (SB == 2) {
-      pair[0] = pack_bf16x2(lev.v[0] * n, lev.v[1] * n);
-      pair[1] = pack_bf16x2(lev.v[2] * n, lev.v[3] * n);
-    } else {
-#pragma unroll
-      for (int k = 0; k < L / 4; ++k) {
-        const uint32_t p0 = pack_bf16x2(lev.v[4 * k] * n, lev.v[4 * k + 1] * n);
-        const uint32_t p1 = pack_bf16x2(lev.v[4 * k + 2] * n, lev.v[4 * k + 3] * n);
-        lo[k] = perm(p1, p0, 0x06040200u);
-        hi[k] = perm(p1, p0, 0x07050301u);
-      }
-    }
-  }
-};
-
-// 4-bit: the 8 codes of a dword -> 4 dwords of bf16 pairs, codes in order.
-__device__ inline void decode4(const Table<4> &t, uint32_t d, uint32_t *o) {
-  // Even codes (low nibbles) and odd codes (high nibbles), one per byte: the
-  // low three bits select within an 8-entry half, bit 3 selects the half.
-  const uint32_t se = d & 0x07070707u, so = (d >> 4) & 0x07070707u;
-  const uint32_t me = ((d >> 3) & 0x01010101u) * 0xffu, mo = ((d >> 7) & 0x01010101u) * 0xffu;
-  const uint32_t el = select(me, perm(t.lo[3], t.lo[2], se), perm(t.lo[1], t.lo[0], se));
-  const uint32_t eh = select(me, perm(t.hi[3], t.hi[2], se), perm(t.hi[1], t.hi[0], se));
-  const uint32_t ol = select(mo, perm(t.lo[3], t.lo[2], so), perm(t.lo[1], t.lo[0], so));
-  const uint32_t oh = select(mo, perm(t.hi[3], t.hi[2], so), perm(t.hi[1], t.hi[0], so));
-  // low bytes of codes 0,1,2,3 and high bytes of codes 0,1,2,3; then 4..7
-  const uint32_t l03 = perm(ol, el, 0x05010400u), h03 = perm(oh, eh, 0x05010400u);
-  const uint32_t l47 = perm(ol, el, 0x07030602u), h47 = perm(oh, eh, 0x07030602u);
-  o[0] = perm(h03, l03, 0x05010400u);
-  o[1] = perm(h03, l03, 0x07030602u);
-  o[2] = perm(h47, l47, 0x05010400u);
-  o[3] = perm(h47, l47, 0x07030602u);
-}
-
-// 3-bit: 8 codes in the low 24 bits of b -> 4 dwords of bf16 pairs.
-__device__ inline void decode3(const Table<3> &t, uint32_t b, uint32_t *o) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t f = b >> (12 * h);  // four codes in bits 0..11
-    const uint32_t s = (f & 7u) | ((f << 5) & 0x700u) | ((f << 10) & 0x70000u) | ((f << 15) & 0x7000000u);
-    const uint32_t l = perm(t.lo[1], t.lo[0], s), hh = perm(t.hi[1], t.hi[0], s);
-    o[2 * h] = perm(hh, l, 0x05010400u);
-    o[2 * h + 1] = perm(hh, l, 0x07030602u);
-  }
-}
-
-// 2-bit (CQ2 and ternary crumbs): the 16 codes of a dword -> 8 dwords.
-__device__ inline void decode2(const Table<2> &t, uint32_t d, uint32_t *o) {
-  const uint32_t x0 = d & 0x03030303u, x1 = (d >> 2) & 0x03030303u;
-  const uint32_t x2 = (d >> 4) & 0x03030303u, x3 = (d >> 6) & 0x03030303u;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    // codes 4b, 4b+1 sit in byte b of x0, x1; codes 4b+2, 4b+3 in x2, x3
-    const uint32_t sa = perm(x1, x0, 0x04040000u + 0x01010101u * b) * 2u + 0x01000100u;
-    const uint32_t sb = perm(x3, x2, 0x04040000u + 0x01010101u * b) * 2u + 0x01000100u;
-    o[2 * b] = perm(t.pair[1], t.pair[0], sa);
-    o[2 * b + 1] = perm(t.pair[1], t.pair[0], sb);
-  }
-}
 
 template <int SB, int WN>
 __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) {
@@ -240,7 +133,7 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
   // parts: part 0 writes the Xr chunks, builds the group's table (set 0: even
   // stages start a group) and decodes the first half of this thread's codes;
   // part 1 decodes the second half.  Each half is two 16-byte chunks of W.
-  Table<SB> tab;
+  Table<SB, __bf16> tab;
   auto store_part = [&](int buf, auto set_c, auto part_c) {
     constexpr int S = decltype(set_c)::value, PART = decltype(part_c)::value;
     const uint32_t *wcs = wc[S];

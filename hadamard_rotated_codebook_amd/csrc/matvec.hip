@@ -488,17 +488,26 @@ float lev_absmax(int sb, const cq::CodeLevels &lev) {
 
 namespace cq {
 
-// Workspace of one launch: the per-slice partial sums [nslice][rows] (fp32).
-// The batch vectors run one after another and share it.
+// Workspace of one call: the per-slice partial sums, [nslice][rows] (fp32)
+// for one vector, [nslice][batch][rows] for the batched kernel.
 uint64_t matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch) {
   if (rows <= 0 || kpad <= 0 || batch <= 0) return 0;  // nothing is launched
+  if (batch > 1) return matvec_mma_workspace_bytes(rows, kpad, batch);
   const MvShape s = mv_shape(storage_bits(bits), rows, kpad);
   if (s.nslice <= 1) return 0;
   return static_cast<uint64_t>(s.nslice) * rows * 4;
 }
 
+hipError_t launch_combine(const float *partial, int64_t n, int nslice, float *y, hipStream_t s) {
+  const int64_t cblocks = (n + 255) / 256;
+  const unsigned cgrid = static_cast<unsigned>(cblocks < 65536 ? cblocks : 65536);
+  combine_kernel<<<cgrid, 256, 0, s>>>(partial, n, nslice, y);
+  return hipGetLastError();
+}
+
 hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
                          const float *xr, int64_t batch, float *y, void *workspace, hipStream_t s) {
+  if (batch > 1) return launch_matvec_mma(blob, bits, rows, kpad, lev, xr, batch, y, workspace, s);
   const int sb = storage_bits(bits);
   const MvShape sh = mv_shape(sb, rows, kpad);
   MvArgs a;

@@ -160,13 +160,20 @@ cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t 
  *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_MATVEC),
  *            see cq_workspace_bytes (NULL, 0 when that is 0); must not
  *            overlap any other buffer of the call
- *   Arithmetic: the inner sum is read from lookup tables indexed by a packed
- *   field (4 codes at 2-bit widths, 2 codes at 3- and 4-bit widths); an entry,
- *   the sum of its codes' level * xr products, is computed in fp32, scaled by
- *   a power of two per slice of 512-2048 columns and rounded once to fp16
- *   (relative error <= 2^-11 per entry).  Products with the fp16 norm and all
- *   sums are fp32.  Results do not depend on scheduling: the partial sums of
- *   the K slices are added in a fixed order.
+ *   Arithmetic, batch 1: the inner sum is read from lookup tables indexed by
+ *   a packed field (4 codes at 2-bit widths, 2 codes at 3- and 4-bit widths);
+ *   an entry, the sum of its codes' level * xr products, is computed in fp32,
+ *   scaled by a power of two per slice of 512-2048 columns and rounded once to
+ *   fp16 (relative error <= 2^-11 per entry).  Products with the fp16 norm and
+ *   all sums are fp32.
+ *   Arithmetic, batch 2..8 (fp16 matrix cores, W read once for the batch):
+ *   each weight is fp16(c[q] * float(norm)) and each activation fp16(xr * 2^e),
+ *   2^e a power of two per batch vector and slice of up to 4096 columns that
+ *   puts the slice's largest |xr| in [2^14, 2^15) (both roundings to nearest
+ *   even, relative error <= 2^-11); products and sums are fp32 and the scale
+ *   is undone exactly.
+ *   Results do not depend on scheduling: the partial sums of the K slices are
+ *   added in a fixed order.
  */
 cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y,
                     void *workspace, uint64_t workspace_bytes, void *stream);

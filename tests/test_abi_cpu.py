@@ -156,7 +156,7 @@ def test_quantize_validation():
 
 
 def test_matvec_workspace_rules():
-    # K beyond one LDS slice needs a workspace: partial sums per slice + counters
+    # K beyond one slice needs a workspace: one partial sum per slice and row
     m, k = _matrix(rows=1000, cols=16384)
     need = ctypes.c_uint64()
     assert lib.cq_workspace_bytes(0, ctypes.byref(m), 1, ctypes.byref(need)) == OK
@@ -169,10 +169,15 @@ def test_matvec_workspace_rules():
     assert call(ws, need.value - 1) == WORKSPACE
     assert call(ws + 4, need.value) == ALIGN
     assert call(FAKE + (1 << 31) + 64, need.value) == OVERLAP  # workspace on top of y
-    # the batch vectors run one after another and share one workspace
-    need8 = ctypes.c_uint64()
-    assert lib.cq_workspace_bytes(0, ctypes.byref(m), 8, ctypes.byref(need8)) == OK
-    assert need8.value == need.value
+    # batches of 2..8 run on the matrix-core kernel: 4096-column slices, one
+    # partial sum per slice, batch vector and row
+    for batch in (2, 5, 8):
+        needb = ctypes.c_uint64()
+        assert lib.cq_workspace_bytes(0, ctypes.byref(m), batch, ctypes.byref(needb)) == OK
+        assert needb.value == 4 * batch * 1000 * 4
+    # K within one slice of that kernel: no workspace
+    m2, _ = _matrix(rows=1000, cols=4096)
+    assert lib.cq_workspace_bytes(0, ctypes.byref(m2), 8, ctypes.byref(needb)) == OK and needb.value == 0
 
 
 def test_workspace_bytes():
@@ -187,7 +192,7 @@ def test_workspace_bytes():
         e, _ = _matrix(rows=rows, cols=cols)
         out.value = 7
         assert lib.cq_workspace_bytes(0, ctypes.byref(e), 8, ctypes.byref(out)) == OK and out.value == 0
-    # a K split over several slices needs counters and partial sums
+    # a K split over several slices needs partial sums
     big, _ = _matrix(rows=65536, cols=16384)
     assert lib.cq_workspace_bytes(0, ctypes.byref(big), 1, ctypes.byref(out)) == OK
     assert out.value > 0 and out.value % 16 == 0
