@@ -232,7 +232,7 @@ def main():
                 log(f"encode cq{bits}: {r['kernel_s']*1e3:.3f} ms, {r['input_gbs']:.0f} GB/s")
         if args.only in ("all", "gemm"):
             for bits in (4, 3):
-                r = bench_gemm(torch, cq, cq_inputs, master, bits, GEMM_M, 10, 2, gen)
+                r = bench_gemm(torch, cq, cq_inputs, master, bits, GEMM_M, 20, 10, gen)
                 secondary[f"gemm_cq{bits}_4096x16384x16384"] = r
                 log(f"gemm cq{bits}: {r['kernel_s']*1e3:.3f} ms, {r['tflops']:.1f} TFLOP/s")
         del master
