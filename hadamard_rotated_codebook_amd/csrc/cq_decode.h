@@ -128,4 +128,66 @@ __device__ inline void decode2(const Table<2, T16> &t, uint32_t d, uint32_t *o) 
   }
 }
 
+
+// Byte-plane tables for every width (2-bit included): lo[k] / hi[k] hold the
+// low / high bytes of entries 4k..4k+3.  The permuted decoders below return
+// the values of 8 codes in an order that saves the final interleave; the
+// consumer applies the same order to the other operand.
+template <int SB, typename T16>
+struct PlaneTable {
+  static constexpr int L = 1 << SB;
+  uint32_t lo[L / 4], hi[L / 4];
+  __device__ void build(const cq::CodeLevels &lev, float n) {
+#pragma unroll
+    for (int k = 0; k < L / 4; ++k) {
+      const uint32_t p0 = pack2<T16>(lev.v[4 * k] * n, lev.v[4 * k + 1] * n);
+      const uint32_t p1 = pack2<T16>(lev.v[4 * k + 2] * n, lev.v[4 * k + 3] * n);
+      lo[k] = perm(p1, p0, 0x06040200u);
+      hi[k] = perm(p1, p0, 0x07050301u);
+    }
+  }
+};
+
+// Slot order of the permuted decoders: position t of an 8-value operand holds
+// code perm_code<SB>(t) of its 8 consecutive codes (3-bit: natural order).
+template <int SB>
+__host__ __device__ constexpr int perm_code(int t) {
+  return SB == 2 ? (t >> 1) + 4 * (t & 1)                          // (0,4) (1,5) (2,6) (3,7)
+       : SB == 4 ? (t & 4) + ((t >> 1) & 1) + 2 * (t & 1)          // (0,2) (1,3) (4,6) (5,7)
+                 : t;
+}
+
+// 2-bit: the 16 codes of dword d.  x_i (i < 4) has codes i, i+4, i+8, i+12 in
+// its bytes; one lookup per plane gives four codes' low or high bytes, and
+// one interleave makes two values (27 instructions per 16 codes less the
+// four selector ORs a single table pair would need: 23).  o[0..3] hold codes 0..7 as the pairs
+// (0,4) (1,5) (2,6) (3,7); o[4..7] codes 8..15 as (8,12) (9,13) (10,14) (11,15).
+template <typename T16>
+__device__ inline void decode2_planes(const PlaneTable<2, T16> &t, uint32_t d, uint32_t *o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = (d >> (2 * i)) & 0x03030303u;
+    // selectors 0..3 pick the second source's bytes: the low plane, then
+    // with the sources swapped the high plane
+    const uint32_t l = perm(t.hi[0], t.lo[0], x), h = perm(t.lo[0], t.hi[0], x);
+    o[i] = perm(h, l, 0x05010400u);
+    o[4 + i] = perm(h, l, 0x07030602u);
+  }
+}
+
+// 4-bit: the 8 codes of dword d, as the pairs (0,2) (1,3) (4,6) (5,7).
+template <typename T16>
+__device__ inline void decode4_planes(const PlaneTable<4, T16> &t, uint32_t d, uint32_t *o) {
+  const uint32_t se = d & 0x07070707u, so = (d >> 4) & 0x07070707u;
+  const uint32_t me = ((d >> 3) & 0x01010101u) * 0xffu, mo = ((d >> 7) & 0x01010101u) * 0xffu;
+  const uint32_t el = select(me, perm(t.lo[3], t.lo[2], se), perm(t.lo[1], t.lo[0], se));
+  const uint32_t eh = select(me, perm(t.hi[3], t.hi[2], se), perm(t.hi[1], t.hi[0], se));
+  const uint32_t ol = select(mo, perm(t.lo[3], t.lo[2], so), perm(t.lo[1], t.lo[0], so));
+  const uint32_t oh = select(mo, perm(t.hi[3], t.hi[2], so), perm(t.hi[1], t.hi[0], so));
+  o[0] = perm(eh, el, 0x05010400u);  // codes 0, 2
+  o[1] = perm(oh, ol, 0x05010400u);  // codes 1, 3
+  o[2] = perm(eh, el, 0x07030602u);  // codes 4, 6
+  o[3] = perm(oh, ol, 0x07030602u);  // codes 5, 7
+}
+
 }  // namespace cqdev

@@ -31,6 +31,8 @@
 //    zeros through the buffer range (a zero norm makes a zero table).
 //  * With more than one K slice the slices' partial sums go to the caller's
 //    workspace and are added in slice order by the combine kernel.
+#include <type_traits>
+
 #include "cq_decode.h"
 #include "cq_internal.h"
 
@@ -100,13 +102,22 @@ __global__ __launch_bounds__(kThreads) void matvec_mma_kernel(MmArgs a) {
     }
     const float scale = ldexpf(1.0f, e);
     if (part == 0 && m < kMaxBatch) unscale[m] = ldexpf(1.0f, -e);
+    // Each block of 8 columns is stored in the decoder's slot order, so that
+    // A and B pair the same k in every MFMA slot.
     _Float16 *dst = xs + m * XS;
-    for (int k = part * 4; k < kMaxSliceCols; k += 32 * 4) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (live && k < ncols) v = *reinterpret_cast<const float4 *>(src + k);
-      const uint32_t lo = pack2<_Float16>(v.x * scale, v.y * scale);
-      const uint32_t hi = pack2<_Float16>(v.z * scale, v.w * scale);
-      *reinterpret_cast<uint2 *>(dst + k) = make_uint2(lo, hi);
+    for (int k = part * 8; k < kMaxSliceCols; k += 32 * 8) {
+      float v[8];
+      float4 u0 = make_float4(0.f, 0.f, 0.f, 0.f), u1 = u0;
+      if (live && k < ncols) {
+        u0 = *reinterpret_cast<const float4 *>(src + k);
+        u1 = *reinterpret_cast<const float4 *>(src + k + 4);
+      }
+      v[0] = u0.x, v[1] = u0.y, v[2] = u0.z, v[3] = u0.w, v[4] = u1.x, v[5] = u1.y, v[6] = u1.z, v[7] = u1.w;
+      uint32_t w[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        w[t] = pack2<_Float16>(v[perm_code<SB>(2 * t)] * scale, v[perm_code<SB>(2 * t + 1)] * scale);
+      *reinterpret_cast<uint4 *>(dst + k) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
   __syncthreads();
@@ -146,7 +157,9 @@ __global__ __launch_bounds__(kThreads) void matvec_mma_kernel(MmArgs a) {
     floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
     auto compute_chunk = [&](int c, auto set_c) {
       constexpr int S = decltype(set_c)::value;
-      Table<SB, _Float16> tab[2];
+      // byte-plane tables and the permuted decoders at 2 and 4 bits
+      using Tab = typename std::conditional<SB == 3, Table<3, _Float16>, PlaneTable<SB, _Float16>>::type;
+      Tab tab[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) tab[b].build(a.lev, static_cast<float>(__builtin_bit_cast(_Float16, nrm[S][b])));
       // A fragments of the chunk's 16 k steps, all read up front (a chunk
@@ -166,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void matvec_mma_kernel(MmArgs a) {
         for (int b = 0; b < 2; ++b) {
           uint32_t o[4];
           if constexpr (SB == 4) {
-            decode4(tab[b], codes[S][b][s], o);
+            decode4_planes(tab[b], codes[S][b][s], o);
           } else if constexpr (SB == 3) {
             const int bit = 24 * s, w = bit >> 5, sh = bit & 31;
             const uint32_t f = sh <= 8 ? (codes[S][b][w] >> sh)
@@ -174,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void matvec_mma_kernel(MmArgs a) {
             decode3(tab[b], f & 0xffffffu, o);
           } else {
             uint32_t o8[8];
-            decode2(tab[b], codes[S][b][s >> 1], o8);
+            decode2_planes(tab[b], codes[S][b][s >> 1], o8);
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = o8[4 * (s & 1) + i];
           }
