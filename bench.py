@@ -57,16 +57,18 @@ def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen):
     x = torch.randn((batch, cols), generator=gen, device=master.device)
     xr = torch.empty((batch, cols), device=master.device)
     y = torch.empty((batch, rows), device=master.device)
+    ws = torch.empty(max(cq.cq_workspace_bytes(cq.OP_MATVEC, mats[0], batch), 16), dtype=torch.uint8,
+                     device=master.device)
     for i in range(warmup):
         cq.cq_rotate_acts(x, out=xr)
-        cq.cq_matvec(mats[i % 3], xr, out=y)
+        cq.cq_matvec(mats[i % 3], xr, out=y, workspace=ws)
     torch.cuda.synchronize()
     ev = _events(torch, steps)
     t0 = time.perf_counter()
     for i in range(steps):
         cq.cq_rotate_acts(x, out=xr)
         ev[i][0].record()
-        cq.cq_matvec(mats[i % 3], xr, out=y)
+        cq.cq_matvec(mats[i % 3], xr, out=y, workspace=ws)
         ev[i][1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps

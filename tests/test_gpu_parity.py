@@ -227,6 +227,84 @@ def test_matvec_is_deterministic():
     assert torch.equal(a, b)
 
 
+def test_needle_decode_sweep_shapes():
+    # the Needle-shaped decode workload at batch 1: 27 layers of Q 512x512,
+    # K and V 256x512, gate and out 512x512 at CQ2 -- one rotated activation
+    # feeds Q/K/V/gate, another feeds out -- and the tied 8192x512 logits at
+    # CQ4; every product against the oracle
+    say("needle decode sweep")
+    cols = 512
+    layer_mats = [("q", 512), ("k", 256), ("v", 256), ("gate", 512), ("out", 512)]
+    for layer in range(27):
+        x_in = cq_inputs.activations(2, 2 * layer, 1, cols)
+        x_out = cq_inputs.activations(2, 2 * layer + 1, 1, cols)
+        xr_in, xr_out = cq.cq_rotate_acts(_to_dev(x_in)), cq.cq_rotate_acts(_to_dev(x_out))
+        for t, (name, rows) in enumerate(layer_mats):
+            W, blob, levels, _ = _cq_from_oracle(2, rows, cols, 1000 + 8 * layer + t)
+            x, xr = (x_out, xr_out) if name == "out" else (x_in, xr_in)
+            y = cq.cq_matvec(W, xr).cpu().numpy()
+            w_hat = np.linalg.norm(oracle.dequantize(blob, 2, rows, cols, levels), axis=1)
+            _check_fp32_product(y, oracle.matvec(blob, 2, rows, cols, x, levels), w_hat,
+                                np.linalg.norm(x.astype(np.float64), axis=1))
+    W, blob, levels, _ = _cq_from_oracle(4, 8192, cols, 1999)
+    x = cq_inputs.activations(2, 99, 1, cols)
+    y = cq.cq_matvec(W, cq.cq_rotate_acts(_to_dev(x))).cpu().numpy()
+    w_hat = np.linalg.norm(oracle.dequantize(blob, 4, 8192, cols, levels), axis=1)
+    _check_fp32_product(y, oracle.matvec(blob, 4, 8192, cols, x, levels), w_hat,
+                        np.linalg.norm(x.astype(np.float64), axis=1))
+
+
+def test_needle_prefill_shapes():
+    # the prefill workload: 2048 fp16 tokens x 512, rotated once to bf16,
+    # through the 512x512 and 256x512 CQ2 and the 8192x512 CQ4 matrices
+    say("needle prefill")
+    cols, m = 512, 2048
+    X = cq_inputs.activations(3, 0, m, cols, "f16")
+    xr = cq.cq_rotate_acts(_to_dev(X, torch.float16), torch.bfloat16)
+    xn = np.linalg.norm(X.astype(np.float64), axis=1)
+    for t, (bits, rows) in enumerate(((2, 512), (2, 256), (4, 8192))):
+        W, blob, levels, _ = _cq_from_oracle(bits, rows, cols, 3000 + t)
+        got = cq.cq_gemm(W, xr).cpu().numpy().astype(np.float64)
+        w_hat = np.linalg.norm(oracle.dequantize(blob, bits, rows, cols, levels), axis=1)
+        _check_fp32_product(got, oracle.gemm(blob, bits, rows, cols, X, levels), w_hat, xn, tol=1e-2, min_cos=0.9999)
+        # the bf16-operand variant: at 16.7 M outputs the tail includes the
+        # few activations whose bf16 rounding differs between the GPU's fp32
+        # rotation and the oracle's float64 one (one bf16 ulp, 2^-8), so the
+        # tight bound is 2e-4 here rather than the 1e-4 of the small cases
+        _check_fp32_product(got, oracle.gemm_bf16(blob, bits, rows, cols, X, levels), w_hat, xn,
+                            tol=2e-4, min_cos=0.99999)
+
+
+def test_matvec_step_replays_in_a_graph():
+    # rotate + matvec captured once in a HIP graph (no memset nodes: every
+    # node is a kernel); each replay, with eager work and synchronisation
+    # between replays, must equal the eager result bit for bit
+    for bits, batch, rows, cols in ((2, 1, 600, 16384), (4, 3, 700, 5000)):
+        W, _, _, _ = _cq_from_oracle(bits, rows, cols, 70 + batch)
+        x = _to_dev(cq_inputs.activations(70, bits, batch, cols))
+        kpad = -(-cols // 128) * 128
+        xr = torch.empty((batch, kpad), device=DEV)
+        y = torch.empty((batch, rows), device=DEV)
+        ws = torch.empty(max(cq.cq_workspace_bytes(cq.OP_MATVEC, W, batch), 16), dtype=torch.uint8, device=DEV)
+        cq.cq_rotate_acts(x, out=xr)
+        cq.cq_matvec(W, xr, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        ref = y.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cq.cq_rotate_acts(x, out=xr)
+            cq.cq_matvec(W, xr, out=y, workspace=ws)
+        for i in range(4):
+            y.fill_(float("nan"))
+            xr.zero_()
+            ws.fill_(0x7F)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, ref), (bits, batch, i)
+        del g
+
+
 # --------------------------------------------------------------------- GEMM
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5])
