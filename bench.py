@@ -49,7 +49,10 @@ def _events(torch, n):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
 
-def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen):
+def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen, fused=True):
+    """One step = the rotation and the product of one batch: cq_rotate_matvec
+    (fused=True) or cq_rotate_acts + cq_matvec.  Three copies of the matrix
+    take turns, so no step finds its matrix in the 256 MB Infinity Cache."""
     rows, cols = master.shape
     levels = cq_inputs.codebook(bits)
     W0 = cq.cq_quantize(master, bits, levels)
@@ -57,26 +60,42 @@ def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen):
     x = torch.randn((batch, cols), generator=gen, device=master.device)
     xr = torch.empty((batch, cols), device=master.device)
     y = torch.empty((batch, rows), device=master.device)
-    ws = torch.empty(max(cq.cq_workspace_bytes(cq.OP_MATVEC, mats[0], batch), 16), dtype=torch.uint8,
+    ws = torch.empty(max(cq.cq_workspace_bytes(cq.OP_ROTATE_MATVEC, mats[0], batch), 16), dtype=torch.uint8,
                      device=master.device)
+
+    def step(i, ev=None):
+        if fused:
+            if ev is not None:
+                ev[0].record()
+            cq.cq_rotate_matvec(mats[i % 3], x, out=y, workspace=ws)
+        else:
+            cq.cq_rotate_acts(x, out=xr)
+            if ev is not None:
+                ev[0].record()
+            cq.cq_matvec(mats[i % 3], xr, out=y, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
     for i in range(warmup):
-        cq.cq_rotate_acts(x, out=xr)
-        cq.cq_matvec(mats[i % 3], xr, out=y, workspace=ws)
+        step(i)
     torch.cuda.synchronize()
-    ev = _events(torch, steps)
+    # the step rate, with nothing else in the stream (event records between
+    # the calls would add their own gaps) ...
     t0 = time.perf_counter()
     for i in range(steps):
-        cq.cq_rotate_acts(x, out=xr)
-        ev[i][0].record()
-        cq.cq_matvec(mats[i % 3], xr, out=y, workspace=ws)
-        ev[i][1].record()
+        step(i)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
+    # ... and, in a second pass, the product call alone between events
+    ev = _events(torch, steps)
+    for i in range(steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
     kern = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
     nbytes = W0.blob.numel()
     del mats, W0
     return {"bits": bits, "batch": batch, "bytes": nbytes, "step_s": wall, "kernel_s": kern,
-            "flop": 2.0 * rows * cols * batch}
+            "flop": 2.0 * rows * cols * batch, "call": "cq_rotate_matvec" if fused else "cq_rotate_acts + cq_matvec"}
 
 
 def bench_gemm(torch, cq, cq_inputs, master, bits, m, steps, warmup, gen):
@@ -211,14 +230,18 @@ def main():
         log(f"CQ2 b1: step {head['step_s']*1e6:.1f} us, matvec kernel {head['kernel_s']*1e6:.1f} us")
         result["head"] = head
         if args.only == "all":
-            for bits, batch in [(3, 1), (4, 1), (5, 1), (2, 8)]:
+            two = bench_matvec(torch, cq, cq_inputs, master, 2, 1, args.steps, args.warmup, gen, fused=False)
+            two["gbs"] = two["bytes"] / two["step_s"] / 1e9
+            secondary["matvec_cq2_b1_two_calls"] = two
+            log(f"CQ2 b1 as rotate + matvec: step {two['step_s']*1e6:.1f} us, matvec {two['kernel_s']*1e6:.1f} us")
+            for bits, batch in [(3, 1), (4, 1), (5, 1), (2, 8), (4, 8)]:
                 r = bench_matvec(torch, cq, cq_inputs, master, bits, batch, max(args.steps // 3, 20),
                                  args.warmup, gen)
                 key = f"matvec_cq{bits if bits != 5 else 't'}_b{batch}"
                 r["gbs"] = r["bytes"] / r["kernel_s"] / 1e9
                 r["frac_hbm_peak"] = r["gbs"] / HBM_PEAK_GBS
                 if batch > 1:
-                    r["tflops_fp32"] = r["flop"] / r["kernel_s"] / 1e12
+                    r["tflops"] = r["flop"] / r["kernel_s"] / 1e12  # fp16 matrix cores, fp32 sums
                 secondary[key] = r
                 log(key, f"{r['kernel_s']*1e6:.1f} us", f"{r['gbs']:.0f} GB/s")
         del master
@@ -253,7 +276,7 @@ def main():
         ach = h["bytes"] / h["kernel_s"] / 1e9
         line["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": ach / HBM_PEAK_GBS, "traffic": stored_traffic(),
-                            "kernel": "cq_matvec call: matvec_kernel<2> + combine_kernel",
+                            "kernel": "cq_rotate_matvec call: matvec_kernel<2, true> + combine_kernel",
                             "kernel_us": h["kernel_s"] * 1e6, "algorithmic_bytes": h["bytes"]}
     else:
         line["value"] = None

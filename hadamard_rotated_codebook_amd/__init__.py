@@ -6,7 +6,7 @@ metadata, passes raw device pointers and the current HIP stream, and turns
 status codes into exceptions.  Every step of the computation runs in the HIP
 kernels of the library; PyTorch supplies device memory and streams.
 
-The library must be built first (``python -m hadamard_rotated_codebook_amd.build``);
+The library must be built first (``python hadamard_rotated_codebook_amd/build.py``);
 importing this package without it raises ``ImportError`` -- there is no
 fallback path.
 
@@ -24,19 +24,19 @@ import torch
 __all__ = [
     "LIB_PATH", "CQError", "CQMatrix", "CQ_GROUP", "CQ_MAX_MATVEC_BATCH", "workspace_for",
     "cq_version", "cq_blob_bytes", "cq_workspace_bytes",
-    "cq_rotate_acts", "cq_matvec", "cq_gemm", "cq_quantize",
+    "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_gemm", "cq_quantize",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcq.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run: python -m hadamard_rotated_codebook_amd.build")
+    raise ImportError(f"{LIB_PATH} is not built; run: python hadamard_rotated_codebook_amd/build.py")
 _lib = ctypes.CDLL(LIB_PATH)
 
 CQ_GROUP = 128
 CQ_MAX_MATVEC_BATCH = 8
 _F32, _F16, _BF16 = 0, 1, 2
 _DTYPES = {torch.float32: _F32, torch.float16: _F16, torch.bfloat16: _BF16}
-OP_MATVEC, OP_GEMM = 0, 1
+OP_MATVEC, OP_GEMM, OP_ROTATE_MATVEC = 0, 1, 2
 
 
 class _Matrix(ctypes.Structure):
@@ -57,6 +57,7 @@ _SIGS = {
     "cq_workspace_bytes": (_i32, [_i32, _MP, _i64, ctypes.POINTER(_u64)]),
     "cq_rotate_acts": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _vp]),
     "cq_matvec": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
+    "cq_rotate_matvec": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_gemm": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_quantize": (_i32, [_vp, _i64, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_float), _vp, _u64, _vp]),
 }
@@ -194,6 +195,27 @@ def cq_matvec(W, xr, out=None, workspace=None):
     ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.cq_matvec(ctypes.byref(m), _dev(xr, "xr"), b, _dev(out, "out"), ws, wsb, _stream()))
+    return out
+
+
+def cq_rotate_matvec(W, x, out=None, workspace=None):
+    """cq_matvec(W, cq_rotate_acts(x)) in one call; x float32 [batch, cols]
+    (not rotated); returns float32 [batch, rows].  ``workspace``: at least
+    cq_workspace_bytes(OP_ROTATE_MATVEC) bytes, or None for a cached one."""
+    if x.dtype != torch.float32 or x.dim() != 2 or x.shape[1] != W.cols:
+        raise ValueError("x must be float32 [batch, cols]")
+    x = x.contiguous()
+    b = x.shape[0]
+    if out is None:
+        out = torch.empty((b, W.rows), dtype=torch.float32, device=x.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (b, W.rows):
+        raise ValueError("out must be float32 [batch, rows]")
+    m, keep = W._struct()
+    if workspace is None and b > 0 and W.rows > 0:
+        workspace = workspace_for(cq_workspace_bytes(OP_ROTATE_MATVEC, W, b), x.device)
+    ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.cq_rotate_matvec(ctypes.byref(m), _dev(x, "x"), b, _dev(out, "out"), ws, wsb, _stream()))
     return out
 
 

@@ -1,6 +1,6 @@
 """Build libcq.so (the C-ABI CQ library) in-tree for gfx950 with hipcc.
 
-Usage:  python -m hadamard_rotated_codebook_amd.build  [--jobs N]
+Usage:  python hadamard_rotated_codebook_amd/build.py  [--jobs N]
 
 Always recompiles every source.  Packed-fp32 instructions are disabled for all
 device code (-target-feature -packed-fp32-ops).

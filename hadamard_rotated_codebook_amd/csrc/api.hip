@@ -113,6 +113,9 @@ cq_status cq_workspace_bytes(int32_t op, const cq_matrix *W, int64_t batch, uint
   if (op == CQ_OP_MATVEC) {
     if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
     *bytes = W->rows ? cq::matvec_workspace_bytes(W->bits, W->rows, padded(W->cols), batch) : 0;
+  } else if (op == CQ_OP_ROTATE_MATVEC) {
+    if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+    *bytes = W->rows ? cq::rotate_matvec_workspace_bytes(W->bits, W->rows, padded(W->cols), batch) : 0;
   } else if (op == CQ_OP_GEMM) {
     if (batch < 0 || batch > CQ_MAX_DIM) return CQ_ERR_SHAPE;
     *bytes = 0;
@@ -165,6 +168,35 @@ cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y
     return CQ_ERR_OVERLAP;
   return hip_status(cq::launch_matvec(static_cast<const uint8_t *>(W->blob), W->bits, W->rows, kpad,
                                       lev, xr, batch, y, need ? workspace : nullptr, s));
+}
+
+cq_status cq_rotate_matvec(const cq_matrix *W, const float *x, int64_t batch, float *y, void *workspace,
+                           uint64_t workspace_bytes, void *stream) {
+  cq::CodeLevels lev;
+  cq_status st = check_matrix(W, &lev);
+  if (st != CQ_OK) return st;
+  if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+  if (batch == 0 || W->rows == 0) return CQ_OK;
+  if (!y) return CQ_ERR_NULL;
+  if (!aligned(y, 4)) return CQ_ERR_ALIGN;
+  const uint64_t ybytes = static_cast<uint64_t>(batch) * W->rows * 4;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t kpad = padded(W->cols);
+  if (kpad == 0) return hip_status(cq::launch_zero_f32(y, batch * W->rows, s));
+  if (!x) return CQ_ERR_NULL;
+  if (!aligned(x, 4)) return CQ_ERR_ALIGN;
+  const uint64_t need = cq::rotate_matvec_workspace_bytes(W->bits, W->rows, kpad, batch);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return CQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return CQ_ERR_ALIGN;
+  }
+  const uint64_t xbytes = static_cast<uint64_t>(batch) * W->cols * 4;
+  if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, W->blob, W->blob_bytes) ||
+      overlaps(workspace, need, y, ybytes) || overlaps(workspace, need, x, xbytes) ||
+      overlaps(workspace, need, W->blob, W->blob_bytes))
+    return CQ_ERR_OVERLAP;
+  return hip_status(cq::launch_rotate_matvec(static_cast<const uint8_t *>(W->blob), W->bits, W->rows, kpad, lev,
+                                             x, W->cols, batch, y, need ? workspace : nullptr, s));
 }
 
 cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c, void *workspace,

@@ -45,6 +45,17 @@ hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kp
                          const CodeLevels &lev, const float *xr, int64_t batch, float *y,
                          void *workspace, hipStream_t s);
 
+// The same product from the activation before rotation (x fp32
+// [batch][cols]), results equal to launch_rotate + launch_matvec.  Batch 1:
+// the lookup-table kernel rotates its slice of x itself, with the butterfly
+// of launch_rotate.  Batch 2..8: launch_rotate into the workspace (after the
+// partial sums), then the matrix-core kernel.
+uint64_t rotate_matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch);
+hipError_t launch_rotate_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
+                                const CodeLevels &lev, const float *x, int64_t cols, int64_t batch,
+                                float *y, void *workspace, hipStream_t s);
+
+// The matrix-core kernel (batch 2..8).
 uint64_t matvec_mma_workspace_bytes(int64_t rows, int64_t kpad, int64_t batch);
 hipError_t launch_matvec_mma(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
                              const CodeLevels &lev, const float *xr, int64_t batch, float *y,

@@ -44,6 +44,7 @@
 //    and per-block completion counters, the last arrival adding up -- cost
 //    more than this kernel boundary: the counter protocol stalls the waves and
 //    the coherent stores go to memory one 4-byte write at a time.)
+#include "cq_fwht.h"
 #include "cq_internal.h"
 
 namespace {
@@ -83,7 +84,10 @@ struct Geom {
 struct MvArgs {
   const uint8_t *packed;
   const uint16_t *norms;  // fp16 bits, [rows][ngroups]
-  const float *xr;        // [kpad]
+  const float *xr;        // [kpad], rotated (unused when the kernel rotates)
+  const float *x;         // [cols], not rotated (used when the kernel rotates)
+  int64_t cols;
+  int32_t xvec;           // x rows may be read 8 floats at a time
   float *y;               // [rows]
   float *partial;         // [nslice][rows] (nslice > 1)
   int64_t rows, kpad, row_bytes, ngroups;
@@ -175,10 +179,13 @@ __device__ inline int table_exponent(float bound) {
   return max(-100, min(100, 15 - e));
 }
 
-template <int SB>
+// ROT: the kernel rotates its slice of x itself (the fused call) instead of
+// reading the rotated activation xr.
+template <int SB, bool ROT>
 __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
   using G = Geom<SB>;
   __shared__ __align__(16) uint8_t lds[G::LDS_BYTES];
+  __shared__ __align__(16) float xrot[ROT ? G::SLICE_COLS : 4];  // the slice's rotated activations
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps row addressing scalar
@@ -261,11 +268,38 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
   //      (p >> 1) * REGION + v * 256 + lane * 4 + (p & 1) * 2.
   // The activation loads go out first and are waited for (the slice's max)
   // before the first rows are requested.
+  // Fused call: the first SLICE_GROUPS * 16 threads (whole waves) rotate the
+  // slice's groups into LDS with the same butterfly as cq_rotate_acts.
+  if constexpr (ROT) {
+    constexpr int NG = G::SLICE_GROUPS;
+    static_assert((NG * 16) % 64 == 0, "whole waves rotate");
+    if (tid < NG * 16) {
+      const int g = tid >> 4, j = tid & 15;
+      float v[8];
+      cqdev::load8_f32(a.x, static_cast<int64_t>(slice) * G::SLICE_COLS + g * CQ_GROUP + j * 8, a.cols,
+                       a.xvec != 0, v);
+      cqdev::fwht128_unscaled(v, j);
+      float4 *dst = reinterpret_cast<float4 *>(xrot + g * CQ_GROUP + j * 8);
+      dst[0] = make_float4(v[0] * cqdev::kInvSqrt128, v[1] * cqdev::kInvSqrt128, v[2] * cqdev::kInvSqrt128,
+                           v[3] * cqdev::kInvSqrt128);
+      dst[1] = make_float4(v[4] * cqdev::kInvSqrt128, v[5] * cqdev::kInvSqrt128, v[6] * cqdev::kInvSqrt128,
+                           v[7] * cqdev::kInvSqrt128);
+    }
+    __syncthreads();
+  }
+  // Four rotated activations at column `col` of the slice.
+  auto xr4 = [&](int col) -> float4 {
+    if constexpr (ROT)
+      return *reinterpret_cast<const float4 *>(xrot + col);
+    else
+      return *reinterpret_cast<const float4 *>(a.xr + static_cast<int64_t>(slice) * G::SLICE_COLS + col);
+  };
+  const int lane_col = lane * G::LANE_COLS;  // c_lane within the slice
   float4 xv[G::LANE_COLS / 4];
 #pragma unroll
   for (int c = 0; c < G::LANE_COLS / 4; ++c) {
     xv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lane_active) xv[c] = *reinterpret_cast<const float4 *>(a.xr + c_lane + 4 * c);
+    if (lane_active) xv[c] = xr4(lane_col + 4 * c);
   }
   // Thread (wave w, lane) builds 32 slots of its lane: the pair of positions
   // q = w / (16 / PAIRS) (both halves of a slot) at indices v = vb + i, i < 32.
@@ -277,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
 #pragma unroll
   for (int c = 0; c < XQ; c += 4) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lane_active) v = *reinterpret_cast<const float4 *>(a.xr + c_lane + XQ * q + c);
+    if (lane_active) v = xr4(lane_col + XQ * q + c);
     xq[c] = v.x, xq[c + 1] = v.y, xq[c + 2] = v.z, xq[c + 3] = v.w;
   }
   if (tid == 0) next_local = kWaves;
@@ -438,8 +472,9 @@ int slice_cols(int sb) {
 
 typedef void (*MvKernel)(MvArgs);
 
-MvKernel pick_kernel(int sb) {
-  return sb == 2 ? matvec_kernel<2> : (sb == 3 ? matvec_kernel<3> : matvec_kernel<4>);
+MvKernel pick_kernel(int sb, bool rot = false) {
+  if (rot) return sb == 2 ? matvec_kernel<2, true> : (sb == 3 ? matvec_kernel<3, true> : matvec_kernel<4, true>);
+  return sb == 2 ? matvec_kernel<2, false> : (sb == 3 ? matvec_kernel<3, false> : matvec_kernel<4, false>);
 }
 
 int max_grid(int sb) {
@@ -498,6 +533,12 @@ uint64_t matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t ba
   return static_cast<uint64_t>(s.nslice) * rows * 4;
 }
 
+uint64_t rotate_matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch) {
+  if (rows <= 0 || kpad <= 0 || batch <= 0) return 0;
+  if (batch == 1) return matvec_workspace_bytes(bits, rows, kpad, 1);
+  return (matvec_mma_workspace_bytes(rows, kpad, batch) + 15) / 16 * 16 + static_cast<uint64_t>(batch) * kpad * 4;
+}
+
 hipError_t launch_combine(const float *partial, int64_t n, int nslice, float *y, hipStream_t s) {
   const int64_t cblocks = (n + 255) / 256;
   const unsigned cgrid = static_cast<unsigned>(cblocks < 65536 ? cblocks : 65536);
@@ -505,15 +546,23 @@ hipError_t launch_combine(const float *partial, int64_t n, int nslice, float *y,
   return hipGetLastError();
 }
 
-hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
-                         const float *xr, int64_t batch, float *y, void *workspace, hipStream_t s) {
-  if (batch > 1) return launch_matvec_mma(blob, bits, rows, kpad, lev, xr, batch, y, workspace, s);
+namespace {
+
+// One lookup-table pass (batch 1): from the rotated xr, or (x != nullptr)
+// rotating x in the kernel.
+hipError_t launch_lut(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
+                      const float *xr, const float *x, int64_t cols, float *y, void *workspace, hipStream_t s) {
   const int sb = storage_bits(bits);
   const MvShape sh = mv_shape(sb, rows, kpad);
   MvArgs a;
   a.packed = blob;
   a.row_bytes = kpad * sb / 8;
   a.norms = reinterpret_cast<const uint16_t *>(blob + rows * a.row_bytes);
+  a.xr = xr;
+  a.x = x;
+  a.cols = cols;
+  a.xvec = x != nullptr && cols % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  a.y = y;
   a.rows = rows;
   a.kpad = kpad;
   a.ngroups = kpad / CQ_GROUP;
@@ -525,21 +574,31 @@ hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kp
   a.per_slice = sh.per_slice;
   a.partial = sh.nslice > 1 ? static_cast<float *>(workspace) : nullptr;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(sh.nslice) * sh.per_slice));
-  const int64_t cblocks = (rows + 255) / 256;
-  const unsigned cgrid = static_cast<unsigned>(cblocks < 65536 ? cblocks : 65536);
-  for (int64_t b = 0; b < batch; ++b) {
-    a.xr = xr + b * kpad;
-    a.y = y + b * rows;
-    pick_kernel(sb)<<<grid, kThreads, 0, s>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (sh.nslice > 1) {
-      combine_kernel<<<cgrid, 256, 0, s>>>(a.partial, rows, sh.nslice, a.y);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
-  return hipSuccess;
+  pick_kernel(sb, x != nullptr)<<<grid, kThreads, 0, s>>>(a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sh.nslice <= 1) return e;
+  return launch_combine(a.partial, rows, sh.nslice, y, s);
+}
+
+}  // namespace
+
+hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
+                         const float *xr, int64_t batch, float *y, void *workspace, hipStream_t s) {
+  if (batch > 1) return launch_matvec_mma(blob, bits, rows, kpad, lev, xr, batch, y, workspace, s);
+  return launch_lut(blob, bits, rows, kpad, lev, xr, nullptr, 0, y, workspace, s);
+}
+
+hipError_t launch_rotate_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
+                                const float *x, int64_t cols, int64_t batch, float *y, void *workspace,
+                                hipStream_t s) {
+  if (batch == 1) return launch_lut(blob, bits, rows, kpad, lev, nullptr, x, cols, y, workspace, s);
+  // Batches: every workgroup of a K slice would redo the slice's rotation, so
+  // it runs once, into the workspace after the partial sums.
+  const uint64_t part = matvec_mma_workspace_bytes(rows, kpad, batch);
+  float *xr = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + (part + 15) / 16 * 16);
+  const hipError_t e = launch_rotate(x, CQ_F32, batch, cols, kpad, xr, CQ_F32, s);
+  if (e != hipSuccess) return e;
+  return launch_matvec_mma(blob, bits, rows, kpad, lev, xr, batch, y, part ? workspace : nullptr, s);
 }
 
 }  // namespace cq

@@ -4,14 +4,15 @@
 // group, computed once and shared by all output rows).
 //
 // Layout: 16 lanes own one group, each lane holds 8 consecutive elements, so a
-// 64-lane wave rotates 4 groups.  Stages of element distance 1, 2, 4 run inside
-// a lane; distances 8..64 are lane distances 1..8, exchanged with DPP/shuffle.
-// Memory-bound: one read of x and one write of xr.
+// 64-lane wave rotates 4 groups (the butterfly is cq_fwht.h's, shared with the
+// products that rotate their own activations).  Memory-bound: one read of x
+// and one write of xr.
+#include "cq_fwht.h"
 #include "cq_internal.h"
 
 namespace {
 
-constexpr float kInvSqrt128 = 0.08838834764831845f;
+using cqdev::kInvSqrt128;
 
 __device__ inline float load_elem(const float *p) { return *p; }
 __device__ inline float load_elem(const _Float16 *p) { return static_cast<float>(*p); }
@@ -68,27 +69,7 @@ __global__ __launch_bounds__(256) void rotate_kernel(const TIn *__restrict__ x, 
     for (int i = 0; i < 8; ++i) v[i] = (valid && col0 + i < cols) ? load_elem(src + i) : 0.0f;
   }
 
-  // In-lane butterflies, element distance 1, 2, 4.
-#pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i & h) continue;
-      const float a = v[i], c = v[i + h];
-      v[i] = a + c;
-      v[i + h] = a - c;
-    }
-  }
-  // Cross-lane butterflies, element distance 8, 16, 32, 64 = lane distance 1..8.
-#pragma unroll
-  for (int d = 1; d < 16; d <<= 1) {
-    const bool upper = (j & d) != 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = __shfl_xor(v[i], d, 16);
-      v[i] = upper ? (p - v[i]) : (v[i] + p);
-    }
-  }
+  cqdev::fwht128_unscaled(v, j);
   if (!valid) return;
   const int64_t out = b * kpad + col0;
   if (OUT_BF16) {

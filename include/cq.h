@@ -112,7 +112,7 @@ cq_status cq_blob_bytes(int32_t bits, int32_t group, int64_t rows, int64_t cols,
                         uint64_t *bytes);
 
 /* Operations that may take a workspace. */
-typedef enum cq_op { CQ_OP_MATVEC = 0, CQ_OP_GEMM = 1 } cq_op;
+typedef enum cq_op { CQ_OP_MATVEC = 0, CQ_OP_GEMM = 1, CQ_OP_ROTATE_MATVEC = 2 } cq_op;
 
 /*
  * Device workspace (bytes) that `op` needs for `W` and the given batch (M for
@@ -120,7 +120,8 @@ typedef enum cq_op { CQ_OP_MATVEC = 0, CQ_OP_GEMM = 1 } cq_op;
  *
  * A workspace is device memory owned by the caller, 16-byte aligned.  Its
  * contents on entry do not matter and are left unspecified (it holds the
- * per-call partial sums of the K slices).  Calls that may run at the same time
+ * per-call partial sums of the K slices and, for CQ_OP_ROTATE_MATVEC at batch
+ * 2..8, the rotated activation).  Calls that may run at the same time
  * must not share a workspace; calls on one stream may, whatever their shapes.
  */
 cq_status cq_workspace_bytes(int32_t op, const cq_matrix *W, int64_t batch,
@@ -177,6 +178,25 @@ cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t 
  */
 cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y,
                     void *workspace, uint64_t workspace_bytes, void *stream);
+
+/*
+ * Decode product from the activation before rotation: the same result as
+ * cq_rotate_acts(x, CQ_F32, ..., xr, CQ_F32) followed by cq_matvec(W, xr, ...),
+ * bit for bit, in one call.  At batch 1 each workgroup of the product rotates
+ * the slice of x it needs (the butterfly of cq_rotate_acts) and no rotated
+ * activation is written to memory; at batch 2..8 the rotation runs once into
+ * the workspace, then the product.
+ *
+ *   W, batch, y, stream: as for cq_matvec
+ *   x        device fp32 [batch][W.cols], 4-byte aligned (16-byte alignment
+ *            and W.cols % 8 == 0 allow vector loads), must not overlap y or
+ *            the workspace; not modified
+ *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_ROTATE_MATVEC)
+ *            (for batch 2..8 it also holds the rotated activation)
+ *   Errors as cq_matvec.
+ */
+cq_status cq_rotate_matvec(const cq_matrix *W, const float *x, int64_t batch, float *y,
+                           void *workspace, uint64_t workspace_bytes, void *stream);
 
 /*
  * Prefill product on the bf16 matrix cores, fp32 accumulation:

@@ -28,7 +28,7 @@ def _declared_functions():
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
     assert set(names) == {"cq_version", "cq_status_string", "cq_blob_bytes", "cq_workspace_bytes",
-                          "cq_rotate_acts", "cq_matvec", "cq_gemm", "cq_quantize"}
+                          "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_gemm", "cq_quantize"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -114,6 +114,35 @@ def test_matvec_and_gemm_validation():
     assert lib.cq_matvec(None, None, 1, None, None, 0, None) == NULL
 
 
+def _rotate_matvec(m, x=FAKE + (1 << 30), batch=1, y=FAKE + (1 << 31), ws=None, wsb=0):
+    return lib.cq_rotate_matvec(ctypes.byref(m), ctypes.c_void_p(x), batch, ctypes.c_void_p(y),
+                                None if ws is None else ctypes.c_void_p(ws), wsb, None)
+
+
+def test_rotate_matvec_validation():
+    # the fused call checks like cq_matvec; x is [batch][cols] fp32 (4-byte aligned)
+    m, k = _matrix(bits=7, nbytes=0, levels=None)
+    assert _rotate_matvec(m) == BITS
+    m, k = _matrix(levels=np.array([0.1, 0.0, 0.2, 0.3]))
+    assert _rotate_matvec(m) == CODEBOOK
+    m, k = _matrix()
+    assert _rotate_matvec(m, batch=9) == SHAPE and _rotate_matvec(m, batch=-1) == SHAPE
+    assert _rotate_matvec(m, batch=0) == OK
+    assert _rotate_matvec(m, x=0) == NULL and _rotate_matvec(m, y=0) == NULL
+    assert _rotate_matvec(m, x=FAKE + (1 << 30) + 2) == ALIGN
+    assert _rotate_matvec(m, y=FAKE + (1 << 31) + 2) == ALIGN
+    assert _rotate_matvec(m, y=FAKE + (1 << 30) + 16) == OVERLAP  # y on top of x
+    assert _rotate_matvec(m, y=FAKE + 64) == OVERLAP  # y on top of the blob
+    big, _ = _matrix(rows=1000, cols=16384)
+    need = ctypes.c_uint64()
+    assert lib.cq_workspace_bytes(0, ctypes.byref(big), 1, ctypes.byref(need)) == OK and need.value > 0
+    assert _rotate_matvec(big) == WORKSPACE
+    assert _rotate_matvec(big, ws=FAKE + (1 << 32), wsb=need.value - 1) == WORKSPACE
+    assert _rotate_matvec(big, ws=FAKE + (1 << 32) + 4, wsb=need.value) == ALIGN
+    assert _rotate_matvec(big, ws=FAKE + (1 << 30), wsb=need.value) == OVERLAP  # workspace on x
+    assert lib.cq_rotate_matvec(None, None, 1, None, None, 0, None) == NULL
+
+
 def test_nothing_to_do_returns_ok_without_launching():
     m, k = _matrix()
     assert _matvec(m, batch=0) == OK and _gemm(m, mm=0) == OK
@@ -187,11 +216,21 @@ def test_workspace_bytes():
     assert lib.cq_workspace_bytes(1, ctypes.byref(m), 4096, ctypes.byref(out)) == OK
     assert lib.cq_workspace_bytes(0, ctypes.byref(m), 9, ctypes.byref(out)) == SHAPE
     assert lib.cq_workspace_bytes(5, ctypes.byref(m), 1, ctypes.byref(out)) == SHAPE
+    assert lib.cq_workspace_bytes(3, ctypes.byref(m), 1, ctypes.byref(out)) == SHAPE
     # empty K or no rows: nothing is launched, so no workspace (and no division by zero)
     for rows, cols in ((5, 0), (0, 256), (0, 0)):
         e, _ = _matrix(rows=rows, cols=cols)
         out.value = 7
         assert lib.cq_workspace_bytes(0, ctypes.byref(e), 8, ctypes.byref(out)) == OK and out.value == 0
+    # the fused call: as cq_matvec at batch 1; at batch 2..8 also the rotated
+    # activation, after the partial sums rounded up to 16 bytes
+    m3, _ = _matrix(rows=1001, cols=16384)
+    for batch in (1, 2, 8):
+        a, b = ctypes.c_uint64(), ctypes.c_uint64()
+        assert lib.cq_workspace_bytes(0, ctypes.byref(m3), batch, ctypes.byref(a)) == OK
+        assert lib.cq_workspace_bytes(2, ctypes.byref(m3), batch, ctypes.byref(b)) == OK
+        assert b.value == (a.value if batch == 1 else -(-a.value // 16) * 16 + batch * 16384 * 4)
+    assert lib.cq_workspace_bytes(2, ctypes.byref(m3), 9, ctypes.byref(out)) == SHAPE
     # a K split over several slices needs partial sums
     big, _ = _matrix(rows=65536, cols=16384)
     assert lib.cq_workspace_bytes(0, ctypes.byref(big), 1, ctypes.byref(out)) == OK
@@ -199,5 +238,6 @@ def test_workspace_bytes():
 
 
 def test_binding_has_the_c_names():
-    for n in ("cq_blob_bytes", "cq_workspace_bytes", "cq_rotate_acts", "cq_matvec", "cq_gemm", "cq_quantize"):
+    for n in ("cq_blob_bytes", "cq_workspace_bytes", "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_gemm",
+              "cq_quantize"):
         assert callable(getattr(cq, n))

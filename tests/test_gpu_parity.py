@@ -227,6 +227,38 @@ def test_matvec_is_deterministic():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("rows,cols,batch", [(700, 16384, 1), (300, 5000, 1), (257, 9000, 3), (129, 1003, 8), (64, 128, 2)])
+def test_rotate_matvec_equals_rotate_then_matvec(bits, rows, cols, batch):
+    # the fused call rotates inside the product's kernels with the same
+    # butterfly: bit-identical to cq_rotate_acts + cq_matvec, and within the
+    # fp32 bar of the oracle (odd cols exercise the unvectorised loads)
+    say("rotate_matvec", bits, rows, cols, batch)
+    W, blob, levels, _ = _cq_from_oracle(bits, rows, cols, 80 + batch)
+    x = cq_inputs.activations(81, rows, batch, cols)
+    xd = _to_dev(x)
+    fused = cq.cq_rotate_matvec(W, xd)
+    two = cq.cq_matvec(W, cq.cq_rotate_acts(xd))
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two)
+    ref = oracle.matvec(blob, bits, rows, cols, x, levels)
+    w_hat = np.linalg.norm(oracle.dequantize(blob, bits, rows, cols, levels), axis=1)
+    _check_fp32_product(fused.cpu().numpy(), ref, w_hat, np.linalg.norm(x.astype(np.float64), axis=1))
+
+
+def test_rotate_matvec_full_size():
+    # the 65536 x 16384 CQ2 workload at batch 1 and 8, in the benchmark's
+    # launch configuration, against the two-call path
+    rows, cols = 65536, 16384
+    say("rotate_matvec full size")
+    W, _ = _random_cq(2, rows, cols, 61)
+    for batch in (1, 8):
+        xd = _to_dev(cq_inputs.activations(61, batch, batch, cols))
+        assert torch.equal(cq.cq_rotate_matvec(W, xd), cq.cq_matvec(W, cq.cq_rotate_acts(xd)))
+    del W
+    torch.cuda.empty_cache()
+
+
 def test_needle_decode_sweep_shapes():
     # the Needle-shaped decode workload at batch 1: 27 layers of Q 512x512,
     # K and V 256x512, gate and out 512x512 at CQ2 -- one rotated activation
