@@ -523,11 +523,22 @@ float lev_absmax(int sb, const cq::CodeLevels &lev) {
 
 namespace cq {
 
+#ifndef CQ_LUT_MIN_WEIGHTS
+#define CQ_LUT_MIN_WEIGHTS (1 << 22)
+#endif
+// The lookup-table kernel serves batch 1 from 2^22 weights up (8192 x 512
+// and larger).  Smaller matrices are launch- and prologue-bound, and the
+// matrix-core kernel's prologue (no 128 KB table to build) is shorter:
+// 9.2 against 11.5 us per 512 x 512 call.
+static bool use_lut(int64_t rows, int64_t kpad, int64_t batch) {
+  return batch == 1 && rows * kpad >= static_cast<int64_t>(CQ_LUT_MIN_WEIGHTS);
+}
+
 // Workspace of one call: the per-slice partial sums, [nslice][rows] (fp32)
-// for one vector, [nslice][batch][rows] for the batched kernel.
+// for the lookup-table kernel, [nslice][batch][rows] for the matrix-core one.
 uint64_t matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch) {
   if (rows <= 0 || kpad <= 0 || batch <= 0) return 0;  // nothing is launched
-  if (batch > 1) return matvec_mma_workspace_bytes(rows, kpad, batch);
+  if (!use_lut(rows, kpad, batch)) return matvec_mma_workspace_bytes(rows, kpad, batch);
   const MvShape s = mv_shape(storage_bits(bits), rows, kpad);
   if (s.nslice <= 1) return 0;
   return static_cast<uint64_t>(s.nslice) * rows * 4;
@@ -535,7 +546,7 @@ uint64_t matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t ba
 
 uint64_t rotate_matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch) {
   if (rows <= 0 || kpad <= 0 || batch <= 0) return 0;
-  if (batch == 1) return matvec_workspace_bytes(bits, rows, kpad, 1);
+  if (use_lut(rows, kpad, batch)) return matvec_workspace_bytes(bits, rows, kpad, 1);
   return (matvec_mma_workspace_bytes(rows, kpad, batch) + 15) / 16 * 16 + static_cast<uint64_t>(batch) * kpad * 4;
 }
 
@@ -584,14 +595,14 @@ hipError_t launch_lut(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
 
 hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
                          const float *xr, int64_t batch, float *y, void *workspace, hipStream_t s) {
-  if (batch > 1) return launch_matvec_mma(blob, bits, rows, kpad, lev, xr, batch, y, workspace, s);
+  if (!use_lut(rows, kpad, batch)) return launch_matvec_mma(blob, bits, rows, kpad, lev, xr, batch, y, workspace, s);
   return launch_lut(blob, bits, rows, kpad, lev, xr, nullptr, 0, y, workspace, s);
 }
 
 hipError_t launch_rotate_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
                                 const float *x, int64_t cols, int64_t batch, float *y, void *workspace,
                                 hipStream_t s) {
-  if (batch == 1) return launch_lut(blob, bits, rows, kpad, lev, nullptr, x, cols, y, workspace, s);
+  if (use_lut(rows, kpad, batch)) return launch_lut(blob, bits, rows, kpad, lev, nullptr, x, cols, y, workspace, s);
   // Batches: every workgroup of a K slice would redo the slice's rotation, so
   // it runs once, into the workspace after the partial sums.
   const uint64_t part = matvec_mma_workspace_bytes(rows, kpad, batch);

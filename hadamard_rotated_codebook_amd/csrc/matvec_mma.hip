@@ -1,4 +1,5 @@
-// Batched decode product (2 <= batch <= 8) on the fp16 matrix cores:
+// Decode product on the fp16 matrix cores, for batches of 2..8 vectors and
+// for small matrices at batch 1 (where the lookup tables' prologue dominates):
 //
 //   y[b][r] = sum_g float(norm[r][g]) * sum_j c[q[r][g*128+j]] * xr[b][g*128+j]
 //
@@ -83,7 +84,9 @@ __global__ __launch_bounds__(kThreads) void matvec_mma_kernel(MmArgs a) {
   {
     const int m = tid >> 5, part = tid & 31;
     const bool live = m < a.batch;
-    for (int k = tid * 4; k < kMaxSliceCols; k += kThreads * 4)
+    // only the chunks the products read are staged (and zeroed in the zero row)
+    const int staged = (ncols + kChunkCols - 1) / kChunkCols * kChunkCols;
+    for (int k = tid * 4; k < staged; k += kThreads * 4)
       *reinterpret_cast<uint2 *>(xs + kMaxBatch * XS + k) = make_uint2(0u, 0u);
     const float *src = a.xr + static_cast<int64_t>(live ? m : 0) * a.kpad + c0;
     float mx = 0.0f;
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void matvec_mma_kernel(MmArgs a) {
     // Each block of 8 columns is stored in the decoder's slot order, so that
     // A and B pair the same k in every MFMA slot.
     _Float16 *dst = xs + m * XS;
-    for (int k = part * 8; k < kMaxSliceCols; k += 32 * 8) {
+    for (int k = part * 8; k < staged; k += 32 * 8) {
       float v[8];
       float4 u0 = make_float4(0.f, 0.f, 0.f, 0.f), u1 = u0;
       if (live && k < ncols) {

@@ -126,13 +126,19 @@ def test_rotate_matvec_validation():
     m, k = _matrix(levels=np.array([0.1, 0.0, 0.2, 0.3]))
     assert _rotate_matvec(m) == CODEBOOK
     m, k = _matrix()
-    assert _rotate_matvec(m, batch=9) == SHAPE and _rotate_matvec(m, batch=-1) == SHAPE
+    need = ctypes.c_uint64()
+    # small matrices take the matrix-core kernel, and the rotated activation
+    # lives in the workspace
+    assert lib.cq_workspace_bytes(2, ctypes.byref(m), 1, ctypes.byref(need)) == OK and need.value >= 256 * 4
+    W0 = dict(ws=FAKE + (1 << 32), wsb=need.value)
+    assert _rotate_matvec(m, batch=9, **W0) == SHAPE and _rotate_matvec(m, batch=-1, **W0) == SHAPE
     assert _rotate_matvec(m, batch=0) == OK
-    assert _rotate_matvec(m, x=0) == NULL and _rotate_matvec(m, y=0) == NULL
-    assert _rotate_matvec(m, x=FAKE + (1 << 30) + 2) == ALIGN
-    assert _rotate_matvec(m, y=FAKE + (1 << 31) + 2) == ALIGN
-    assert _rotate_matvec(m, y=FAKE + (1 << 30) + 16) == OVERLAP  # y on top of x
-    assert _rotate_matvec(m, y=FAKE + 64) == OVERLAP  # y on top of the blob
+    assert _rotate_matvec(m) == WORKSPACE
+    assert _rotate_matvec(m, x=0, **W0) == NULL and _rotate_matvec(m, y=0, **W0) == NULL
+    assert _rotate_matvec(m, x=FAKE + (1 << 30) + 2, **W0) == ALIGN
+    assert _rotate_matvec(m, y=FAKE + (1 << 31) + 2, **W0) == ALIGN
+    assert _rotate_matvec(m, y=FAKE + (1 << 30) + 16, **W0) == OVERLAP  # y on top of x
+    assert _rotate_matvec(m, y=FAKE + 64, **W0) == OVERLAP  # y on top of the blob
     big, _ = _matrix(rows=1000, cols=16384)
     need = ctypes.c_uint64()
     assert lib.cq_workspace_bytes(0, ctypes.byref(big), 1, ctypes.byref(need)) == OK and need.value > 0
