@@ -22,7 +22,7 @@ matrix cores (TFLOP/s), the 16384 x 16384 encoder (GB/s of fp32 input) and
 the Needle-shaped decode sweep (27 layers of 512-wide CQ2 matrices plus the
 8192 x 512 CQ4 logits, per token, eager and replayed from a HIP graph).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only matvec|gemm|encode|all]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only matvec|decode|gemm|encode|all]
        python bench.py --calibrate-copy      (counter calibration run)
 """
 import argparse
@@ -104,9 +104,11 @@ def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen, 
 def bench_needle_decode(torch, cq, cq_inputs, steps, gen):
     """One decode token of a Needle-shaped model at batch 1: per layer one
     activation feeds Q 512x512, K and V 256x512 and gate 512x512, another
-    feeds out 512x512 (all CQ2), then the 8192x512 CQ4 tied logits; each
-    product is one cq_rotate_matvec call (136 per token).  Weights are
-    seeded N(0, 0.02^2) masters encoded on the GPU."""
+    feeds out 512x512 (all CQ2), then the 8192x512 CQ4 tied logits.  Two
+    ways: one cq_rotate_matvec call per product (136 calls a token), and the
+    shared-activation call for Q/K/V/gate (cq_rotate_multi_matvec) plus one
+    call for out (55 calls a token).  Each eager and replayed from a HIP
+    graph.  Weights are seeded N(0, 0.02^2) masters encoded on the GPU."""
     dev = torch.device("cuda:0")
     shapes = [512, 256, 256, 512, 512]
     mats, xs, ys = [], [], []
@@ -122,36 +124,50 @@ def bench_needle_decode(torch, cq, cq_inputs, steps, gen):
     need = max(cq.cq_workspace_bytes(cq.OP_ROTATE_MATVEC, m, 1) for m in mats + [logits])
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
-    def token():
+    def per_call():
         for layer in range(27):
             for t in range(5):
                 x = xs[2 * layer + (1 if t == 4 else 0)]
                 cq.cq_rotate_matvec(mats[5 * layer + t], x, out=ys[5 * layer + t], workspace=ws)
         cq.cq_rotate_matvec(logits, xl, out=yl, workspace=ws)
 
+    def shared():
+        for layer in range(27):
+            cq.cq_rotate_multi_matvec(mats[5 * layer:5 * layer + 4], xs[2 * layer], outs=ys[5 * layer:5 * layer + 4],
+                                      workspace=ws)
+            cq.cq_rotate_matvec(mats[5 * layer + 4], xs[2 * layer + 1], out=ys[5 * layer + 4], workspace=ws)
+        cq.cq_rotate_matvec(logits, xl, out=yl, workspace=ws)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        eager = (time.perf_counter() - t0) / steps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph = (time.perf_counter() - t0) / steps
+        del g
+        return eager, graph
+
     nbytes = sum(m.blob.numel() for m in mats) + logits.blob.numel()
-    for _ in range(3):
-        token()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        token()
-    torch.cuda.synchronize()
-    eager = (time.perf_counter() - t0) / steps
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        token()
-    for _ in range(3):
-        g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        g.replay()
-    torch.cuda.synchronize()
-    graph = (time.perf_counter() - t0) / steps
-    del g
-    return {"matvecs_per_token": 136, "bytes_per_token": nbytes, "eager_us_per_token": eager * 1e6,
-            "graph_us_per_token": graph * 1e6, "graph_gbs": nbytes / graph / 1e9}
+    out = {"bytes_per_token": nbytes}
+    for name, fn, calls in (("per_call", per_call, 136), ("shared_activation", shared, 55)):
+        eager, graph = timed(fn)
+        out[name] = {"calls_per_token": calls, "eager_us_per_token": eager * 1e6, "graph_us_per_token": graph * 1e6,
+                     "graph_gbs": nbytes / graph / 1e9}
+    return out
 
 
 def bench_gemm(torch, cq, cq_inputs, master, bits, m, steps, warmup, gen):
@@ -256,7 +272,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--only", choices=["all", "matvec", "gemm", "encode"], default="all")
+    ap.add_argument("--only", choices=["all", "matvec", "decode", "gemm", "encode"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
@@ -304,10 +320,12 @@ def main():
                 log(key, f"{r['kernel_median_s']*1e6:.1f} us (median)", f"{r['gbs']:.0f} GB/s")
         del master
         torch.cuda.empty_cache()
-        if args.only == "all":
-            r = bench_needle_decode(torch, cq, cq_inputs, 50, gen)
-            secondary["needle_decode_token"] = r
-            log(f"needle decode token: {r['eager_us_per_token']:.0f} us eager, {r['graph_us_per_token']:.0f} us graph")
+    if args.only in ("all", "decode"):
+        r = bench_needle_decode(torch, cq, cq_inputs, 50, gen)
+        secondary["needle_decode_token"] = r
+        for k in ("per_call", "shared_activation"):
+            log(f"needle decode token, {k}: {r[k]['eager_us_per_token']:.0f} us eager, "
+                f"{r[k]['graph_us_per_token']:.0f} us graph")
 
     if args.only in ("all", "gemm", "encode"):
         log("generating the 16384 x 16384 fp32 master on the GPU")

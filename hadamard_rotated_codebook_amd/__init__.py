@@ -11,7 +11,9 @@ importing this package without it raises ``ImportError`` -- there is no
 fallback path.
 
 Functions carry the C names: ``cq_blob_bytes``, ``cq_workspace_bytes``,
-``cq_rotate_acts``, ``cq_matvec``, ``cq_gemm``, ``cq_quantize``.
+``cq_rotate_acts``, ``cq_matvec``, ``cq_rotate_matvec``,
+``cq_rotate_multi_matvec``, ``cq_rotate_multi_workspace_bytes``, ``cq_gemm``,
+``cq_quantize``.
 """
 import ctypes
 import os
@@ -24,7 +26,8 @@ import torch
 __all__ = [
     "LIB_PATH", "CQError", "CQMatrix", "CQ_GROUP", "CQ_MAX_MATVEC_BATCH", "workspace_for",
     "cq_version", "cq_blob_bytes", "cq_workspace_bytes",
-    "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_gemm", "cq_quantize",
+    "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_multi_matvec",
+    "cq_rotate_multi_workspace_bytes", "cq_gemm", "cq_quantize",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcq.so")
@@ -58,6 +61,8 @@ _SIGS = {
     "cq_rotate_acts": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _vp]),
     "cq_matvec": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_rotate_matvec": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
+    "cq_rotate_multi_matvec": (_i32, [_MP, _i32, _vp, _i64, ctypes.POINTER(_vp), _vp, _u64, _vp]),
+    "cq_rotate_multi_workspace_bytes": (_i32, [_MP, _i32, _i64, ctypes.POINTER(_u64)]),
     "cq_gemm": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_quantize": (_i32, [_vp, _i64, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_float), _vp, _u64, _vp]),
 }
@@ -217,6 +222,53 @@ def cq_rotate_matvec(W, x, out=None, workspace=None):
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.cq_rotate_matvec(ctypes.byref(m), _dev(x, "x"), b, _dev(out, "out"), ws, wsb, _stream()))
     return out
+
+
+def _structs(Ws):
+    arr = (_Matrix * max(len(Ws), 1))()
+    keep = []
+    for i, W in enumerate(Ws):
+        m, k = W._struct()
+        arr[i] = m
+        keep.append(k)
+    return arr, keep  # keep the levels arrays alive for the call
+
+
+def cq_rotate_multi_workspace_bytes(Ws, batch):
+    arr, keep = _structs(Ws)
+    out = _u64(0)
+    _check(_lib.cq_rotate_multi_workspace_bytes(arr, len(Ws), batch, ctypes.byref(out)))
+    return int(out.value)
+
+
+def cq_rotate_multi_matvec(Ws, x, outs=None, workspace=None):
+    """[cq_rotate_matvec(W, x) for W in Ws] with the rotation of x shared:
+    x float32 [batch, cols] (not rotated), every W with that cols; returns
+    the list of float32 [batch, W.rows] results.  ``workspace``: at least
+    cq_rotate_multi_workspace_bytes(Ws, batch) bytes, or None for a cached one."""
+    Ws = list(Ws)
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be float32 [batch, cols]")
+    if any(W.cols != x.shape[1] for W in Ws):
+        raise ValueError("every matrix must have x's cols")
+    x = x.contiguous()
+    b = x.shape[0]
+    if outs is None:
+        outs = [torch.empty((b, W.rows), dtype=torch.float32, device=x.device) for W in Ws]
+    outs = list(outs)
+    if len(outs) != len(Ws):
+        raise ValueError("one output per matrix")
+    for W, o in zip(Ws, outs):
+        if o.dtype != torch.float32 or tuple(o.shape) != (b, W.rows):
+            raise ValueError("each out must be float32 [batch, rows]")
+    arr, keep = _structs(Ws)
+    if workspace is None and b > 0 and Ws:
+        workspace = workspace_for(cq_rotate_multi_workspace_bytes(Ws, b), x.device)
+    ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ys = (_vp * max(len(outs), 1))(*[_dev(o, "out").value for o in outs])
+    _check(_lib.cq_rotate_multi_matvec(arr, len(Ws), _dev(x, "x"), b, ys, ws, wsb, _stream()))
+    return outs
 
 
 def cq_gemm(W, xr, out=None, workspace=None):

@@ -199,6 +199,90 @@ cq_status cq_rotate_matvec(const cq_matrix *W, const float *x, int64_t batch, fl
                                              x, W->cols, batch, y, need ? workspace : nullptr, s));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks the matrices of a shared-activation call and fills items (y left
+// NULL); returns the common cols_pad through *kpad.
+cq_status check_multi(const cq_matrix *W, int32_t n, int64_t batch, cq::MultiItem *items, int64_t *kpad) {
+  if (n < 0 || n > CQ_MAX_MULTI) return CQ_ERR_SHAPE;
+  if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+  if (n > 0 && !W) return CQ_ERR_NULL;
+  for (int i = 0; i < n; ++i) {
+    cq_status st = check_matrix(&W[i], &items[i].lev);
+    if (st != CQ_OK) return st;
+    if (W[i].cols != W[0].cols) return CQ_ERR_SHAPE;
+    items[i].blob = static_cast<const uint8_t *>(W[i].blob);
+    items[i].bits = W[i].bits;
+    items[i].rows = W[i].rows;
+    items[i].y = nullptr;
+  }
+  *kpad = n > 0 ? padded(W[0].cols) : 0;
+  return CQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cq_status cq_rotate_multi_workspace_bytes(const cq_matrix *W, int32_t n, int64_t batch, uint64_t *bytes) {
+  if (!bytes) return CQ_ERR_NULL;
+  cq::MultiItem items[CQ_MAX_MULTI];
+  int64_t kpad = 0;
+  cq_status st = check_multi(W, n, batch, items, &kpad);
+  if (st != CQ_OK) return st;
+  *bytes = cq::rotate_multi_workspace_bytes(items, n, kpad, batch);
+  return CQ_OK;
+}
+
+cq_status cq_rotate_multi_matvec(const cq_matrix *W, int32_t n, const float *x, int64_t batch, float *const *y,
+                                 void *workspace, uint64_t workspace_bytes, void *stream) {
+  cq::MultiItem items[CQ_MAX_MULTI];
+  int64_t kpad = 0;
+  cq_status st = check_multi(W, n, batch, items, &kpad);
+  if (st != CQ_OK) return st;
+  if (n == 0 || batch == 0) return CQ_OK;
+  if (!y) return CQ_ERR_NULL;
+  for (int i = 0; i < n; ++i) {
+    if (W[i].rows == 0) continue;
+    if (!y[i]) return CQ_ERR_NULL;
+    if (!aligned(y[i], 4)) return CQ_ERR_ALIGN;
+    items[i].y = y[i];
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kpad == 0) {
+    for (int i = 0; i < n; ++i) {
+      if (W[i].rows == 0) continue;
+      const hipError_t e = cq::launch_zero_f32(y[i], batch * W[i].rows, s);
+      if (e != hipSuccess) return CQ_ERR_HIP;
+    }
+    return CQ_OK;
+  }
+  if (!x) return CQ_ERR_NULL;
+  if (!aligned(x, 4)) return CQ_ERR_ALIGN;
+  const uint64_t need = cq::rotate_multi_workspace_bytes(items, n, kpad, batch);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return CQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return CQ_ERR_ALIGN;
+  }
+  const uint64_t xbytes = static_cast<uint64_t>(batch) * W[0].cols * 4;
+  if (overlaps(workspace, need, x, xbytes)) return CQ_ERR_OVERLAP;
+  for (int i = 0; i < n; ++i) {
+    if (overlaps(workspace, need, W[i].blob, W[i].blob_bytes)) return CQ_ERR_OVERLAP;
+    if (W[i].rows == 0) continue;
+    const uint64_t yb = static_cast<uint64_t>(batch) * W[i].rows * 4;
+    if (overlaps(y[i], yb, x, xbytes) || overlaps(y[i], yb, workspace, need)) return CQ_ERR_OVERLAP;
+    for (int j = 0; j < n; ++j) {
+      if (overlaps(y[i], yb, W[j].blob, W[j].blob_bytes)) return CQ_ERR_OVERLAP;
+      if (j != i && W[j].rows && overlaps(y[i], yb, y[j], static_cast<uint64_t>(batch) * W[j].rows * 4))
+        return CQ_ERR_OVERLAP;
+    }
+  }
+  return hip_status(cq::launch_rotate_multi_matvec(items, n, x, W[0].cols, kpad, batch,
+                                                   need ? workspace : nullptr, s));
+}
+
 cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c, void *workspace,
                   uint64_t workspace_bytes, void *stream) {
   (void)workspace;

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "cq_internal.h"
 
 namespace cqdev {
@@ -188,6 +190,32 @@ __device__ inline void decode4_planes(const PlaneTable<4, T16> &t, uint32_t d, u
   o[1] = perm(oh, ol, 0x05010400u);  // codes 1, 3
   o[2] = perm(eh, el, 0x07030602u);  // codes 4, 6
   o[3] = perm(oh, ol, 0x07030602u);  // codes 5, 7
+}
+
+// Tables of the fp16 matrix-core matvec kernels: byte planes at 2 and 4
+// bits, the plane pairs of Table at 3 bits.
+template <int SB>
+using MmaTable = typename std::conditional<SB == 3, Table<3, _Float16>, PlaneTable<SB, _Float16>>::type;
+
+// B operand of k step s (s < 16) of one (row, group): codes 8s..8s+7 of the
+// group's GROUP_DW code dwords, as four dwords of fp16 pairs in slot order
+// perm_code<SB>.  The decoders work in units of 8 (4-bit), 8 (3-bit, one
+// 24-bit field) or 16 codes (2-bit: half of one dword's decode).
+template <int SB>
+__device__ inline void decode_step(const MmaTable<SB> &tab, const uint32_t *codes, int s, uint32_t (&o)[4]) {
+  if constexpr (SB == 4) {
+    decode4_planes(tab, codes[s], o);
+  } else if constexpr (SB == 3) {
+    constexpr int DW = 3 * 128 / 32;
+    const int bit = 24 * s, w = bit >> 5, sh = bit & 31;
+    const uint32_t f = sh <= 8 ? (codes[w] >> sh) : __builtin_amdgcn_alignbit(codes[(w + 1) % DW], codes[w], sh);
+    decode3(tab, f & 0xffffffu, o);
+  } else {
+    uint32_t o8[8];
+    decode2_planes(tab, codes[s >> 1], o8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = o8[4 * (s & 1) + i];
+  }
 }
 
 }  // namespace cqdev

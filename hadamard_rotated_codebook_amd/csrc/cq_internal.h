@@ -40,26 +40,53 @@ hipError_t launch_rotate(const void *x, int x_dtype, int64_t batch, int64_t cols
 // sums, any contents on entry.
 uint64_t matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch);
 
-// batch 1: lookup-table kernel; batch 2..8: the matrix-core kernel.
+// Batch 1 from 2^22 weights: the lookup-table kernel; otherwise the
+// matrix-core kernel.
 hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
                          const CodeLevels &lev, const float *xr, int64_t batch, float *y,
                          void *workspace, hipStream_t s);
 
 // The same product from the activation before rotation (x fp32
-// [batch][cols]), results equal to launch_rotate + launch_matvec.  Batch 1:
-// the lookup-table kernel rotates its slice of x itself, with the butterfly
-// of launch_rotate.  Batch 2..8: launch_rotate into the workspace (after the
-// partial sums), then the matrix-core kernel.
+// [batch][cols]), results equal to launch_rotate + launch_matvec.  Small
+// matrices: launch_multi_matvec.  Batch 1 on the tables: the lookup-table
+// kernel rotates its slice of x itself, with the butterfly of launch_rotate.
+// Otherwise launch_rotate into the workspace (after the partial sums), then
+// the matrix-core kernel.
 uint64_t rotate_matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch);
 hipError_t launch_rotate_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
                                 const CodeLevels &lev, const float *x, int64_t cols, int64_t batch,
                                 float *y, void *workspace, hipStream_t s);
 
-// The matrix-core kernel (batch 2..8).
+// The matrix-core kernel (batches, and small matrices at batch 1).
 uint64_t matvec_mma_workspace_bytes(int64_t rows, int64_t kpad, int64_t batch);
 hipError_t launch_matvec_mma(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
                              const CodeLevels &lev, const float *xr, int64_t batch, float *y,
                              void *workspace, hipStream_t s);
+
+// One matrix of a shared-activation product: its blob, width, rows, code
+// levels and output y [batch][rows].
+struct MultiItem {
+  const uint8_t *blob;
+  int bits;
+  int64_t rows;
+  CodeLevels lev;
+  float *y;
+};
+
+// The one-launch kernel for products that share x (rotating x itself):
+// batch 1..8 and cols_pad <= 4096.
+bool multi_matvec_fits(int64_t kpad, int64_t batch);
+hipError_t launch_multi_matvec(const MultiItem *items, int n, const float *x, int64_t cols, int64_t kpad,
+                               int64_t batch, hipStream_t s);
+
+// Products of several matrices with one activation x (fp32 [batch][cols],
+// not rotated).  Small matrices (under 2^22 weights, cols_pad <= 4096) go
+// to launch_multi_matvec, one launch per width; the others share one
+// rotation into the workspace (after the largest partial-sum region) and
+// take launch_matvec each.
+uint64_t rotate_multi_workspace_bytes(const MultiItem *items, int n, int64_t kpad, int64_t batch);
+hipError_t launch_rotate_multi_matvec(const MultiItem *items, int n, const float *x, int64_t cols, int64_t kpad,
+                                      int64_t batch, void *workspace, hipStream_t s);
 
 // y[i] = sum over s < nslice, in order, of partial[s * n + i].
 hipError_t launch_combine(const float *partial, int64_t n, int nslice, float *y, hipStream_t s);

@@ -544,8 +544,15 @@ uint64_t matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t ba
   return static_cast<uint64_t>(s.nslice) * rows * 4;
 }
 
+// Small matrices whose K fits one slice take the one-launch kernel that
+// rotates x itself (no workspace).
+static bool use_fused_small(int64_t rows, int64_t kpad, int64_t batch) {
+  return rows * kpad < static_cast<int64_t>(CQ_LUT_MIN_WEIGHTS) && multi_matvec_fits(kpad, batch);
+}
+
 uint64_t rotate_matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch) {
   if (rows <= 0 || kpad <= 0 || batch <= 0) return 0;
+  if (use_fused_small(rows, kpad, batch)) return 0;
   if (use_lut(rows, kpad, batch)) return matvec_workspace_bytes(bits, rows, kpad, 1);
   return (matvec_mma_workspace_bytes(rows, kpad, batch) + 15) / 16 * 16 + static_cast<uint64_t>(batch) * kpad * 4;
 }
@@ -602,6 +609,10 @@ hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kp
 hipError_t launch_rotate_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
                                 const float *x, int64_t cols, int64_t batch, float *y, void *workspace,
                                 hipStream_t s) {
+  if (use_fused_small(rows, kpad, batch)) {
+    const MultiItem item = {blob, bits, rows, lev, y};
+    return launch_multi_matvec(&item, 1, x, cols, kpad, batch, s);
+  }
   if (use_lut(rows, kpad, batch)) return launch_lut(blob, bits, rows, kpad, lev, nullptr, x, cols, y, workspace, s);
   // Batches: every workgroup of a K slice would redo the slice's rotation, so
   // it runs once, into the workspace after the partial sums.
@@ -610,6 +621,53 @@ hipError_t launch_rotate_matvec(const uint8_t *blob, int bits, int64_t rows, int
   const hipError_t e = launch_rotate(x, CQ_F32, batch, cols, kpad, xr, CQ_F32, s);
   if (e != hipSuccess) return e;
   return launch_matvec_mma(blob, bits, rows, kpad, lev, xr, batch, y, part ? workspace : nullptr, s);
+}
+
+uint64_t rotate_multi_workspace_bytes(const MultiItem *items, int n, int64_t kpad, int64_t batch) {
+  if (kpad <= 0 || batch <= 0) return 0;
+  uint64_t part = 0;
+  bool shared = false;
+  for (int i = 0; i < n; ++i) {
+    if (items[i].rows <= 0 || use_fused_small(items[i].rows, kpad, batch)) continue;
+    shared = true;
+    const uint64_t p = matvec_workspace_bytes(items[i].bits, items[i].rows, kpad, batch);
+    if (p > part) part = p;
+  }
+  if (!shared) return 0;
+  return (part + 15) / 16 * 16 + static_cast<uint64_t>(batch) * kpad * 4;
+}
+
+hipError_t launch_rotate_multi_matvec(const MultiItem *items, int n, const float *x, int64_t cols, int64_t kpad,
+                                      int64_t batch, void *workspace, hipStream_t s) {
+  MultiItem small[64];
+  int nsmall = 0;
+  bool shared = false;
+  uint64_t part = 0;
+  for (int i = 0; i < n; ++i) {
+    if (items[i].rows <= 0) continue;
+    if (use_fused_small(items[i].rows, kpad, batch)) {
+      if (nsmall == 64) return hipErrorInvalidValue;
+      small[nsmall++] = items[i];
+    } else {
+      shared = true;
+      const uint64_t p = matvec_workspace_bytes(items[i].bits, items[i].rows, kpad, batch);
+      if (p > part) part = p;
+    }
+  }
+  if (nsmall) {
+    const hipError_t e = launch_multi_matvec(small, nsmall, x, cols, kpad, batch, s);
+    if (e != hipSuccess) return e;
+  }
+  if (!shared) return hipSuccess;
+  // the larger matrices: one rotation, shared through the workspace
+  float *xr = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + (part + 15) / 16 * 16);
+  hipError_t e = launch_rotate(x, CQ_F32, batch, cols, kpad, xr, CQ_F32, s);
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    const MultiItem &it = items[i];
+    if (it.rows <= 0 || use_fused_small(it.rows, kpad, batch)) continue;
+    e = launch_matvec(it.blob, it.bits, it.rows, kpad, it.lev, xr, batch, it.y, part ? workspace : nullptr, s);
+  }
+  return e;
 }
 
 }  // namespace cq

@@ -161,8 +161,7 @@ __global__ __launch_bounds__(kThreads) void matvec_mma_kernel(MmArgs a) {
     auto compute_chunk = [&](int c, auto set_c) {
       constexpr int S = decltype(set_c)::value;
       // byte-plane tables and the permuted decoders at 2 and 4 bits
-      using Tab = typename std::conditional<SB == 3, Table<3, _Float16>, PlaneTable<SB, _Float16>>::type;
-      Tab tab[2];
+      MmaTable<SB> tab[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) tab[b].build(a.lev, static_cast<float>(__builtin_bit_cast(_Float16, nrm[S][b])));
       // A fragments of the chunk's 16 k steps, all read up front (a chunk
@@ -173,27 +172,14 @@ __global__ __launch_bounds__(kThreads) void matvec_mma_kernel(MmArgs a) {
       f16x8 af[CQ_GROUP / 8];
 #pragma unroll
       for (int s = 0; s < CQ_GROUP / 8; ++s) af[s] = *reinterpret_cast<const f16x8 *>(a_chunk + s * 16);
-      // 16 k steps of 8 codes per lane; the decoders work in units of 8
-      // (4-bit), 8 (3-bit, 24-bit fields) or 16 codes (2-bit).
+      // 16 k steps of 8 codes per lane
 #pragma unroll
       for (int s = 0; s < CQ_GROUP / 8; ++s) {
         const f16x8 av = af[s];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           uint32_t o[4];
-          if constexpr (SB == 4) {
-            decode4_planes(tab[b], codes[S][b][s], o);
-          } else if constexpr (SB == 3) {
-            const int bit = 24 * s, w = bit >> 5, sh = bit & 31;
-            const uint32_t f = sh <= 8 ? (codes[S][b][w] >> sh)
-                                       : __builtin_amdgcn_alignbit(codes[S][b][(w + 1) % GROUP_DW], codes[S][b][w], sh);
-            decode3(tab[b], f & 0xffffffu, o);
-          } else {
-            uint32_t o8[8];
-            decode2_planes(tab[b], codes[S][b][s >> 1], o8);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = o8[4 * (s & 1) + i];
-          }
+          decode_step<SB>(tab[b], codes[S][b], s, o);
           const f16x8 bv = __builtin_bit_cast(f16x8, make_uint4(o[0], o[1], o[2], o[3]));
           acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[b], 0, 0, 0);
         }

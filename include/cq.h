@@ -65,6 +65,8 @@ typedef enum cq_dtype { CQ_F32 = 0, CQ_F16 = 1, CQ_BF16 = 2 } cq_dtype;
 #define CQ_MAX_MATVEC_BATCH 8
 /* The only supported quantisation group. */
 #define CQ_GROUP 128
+/* Most matrices in one cq_rotate_multi_matvec call. */
+#define CQ_MAX_MULTI 64
 
 /*
  * A CQ matrix as the ".cact" blob stores it (needle.js tutorial, "Anatomy of a
@@ -161,13 +163,14 @@ cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t 
  *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_MATVEC),
  *            see cq_workspace_bytes (NULL, 0 when that is 0); must not
  *            overlap any other buffer of the call
- *   Arithmetic, batch 1: the inner sum is read from lookup tables indexed by
- *   a packed field (4 codes at 2-bit widths, 2 codes at 3- and 4-bit widths);
- *   an entry, the sum of its codes' level * xr products, is computed in fp32,
- *   scaled by a power of two per slice of 512-2048 columns and rounded once to
- *   fp16 (relative error <= 2^-11 per entry).  Products with the fp16 norm and
- *   all sums are fp32.
- *   Arithmetic, batch 2..8 (fp16 matrix cores, W read once for the batch):
+ *   Arithmetic, batch 1 and rows * cols_pad >= 2^22: the inner sum is read
+ *   from lookup tables indexed by a packed field (4 codes at 2-bit widths, 2
+ *   codes at 3- and 4-bit widths); an entry, the sum of its codes' level * xr
+ *   products, is computed in fp32, scaled by a power of two per slice of
+ *   512-2048 columns and rounded once to fp16 (relative error <= 2^-11 per
+ *   entry).  Products with the fp16 norm and all sums are fp32.
+ *   Arithmetic, batch 2..8 and smaller matrices at batch 1 (fp16 matrix
+ *   cores, W read once for the batch):
  *   each weight is fp16(c[q] * float(norm)) and each activation fp16(xr * 2^e),
  *   2^e a power of two per batch vector and slice of up to 4096 columns that
  *   puts the slice's largest |xr| in [2^14, 2^15) (both roundings to nearest
@@ -182,21 +185,59 @@ cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y
 /*
  * Decode product from the activation before rotation: the same result as
  * cq_rotate_acts(x, CQ_F32, ..., xr, CQ_F32) followed by cq_matvec(W, xr, ...),
- * bit for bit, in one call.  At batch 1 each workgroup of the product rotates
- * the slice of x it needs (the butterfly of cq_rotate_acts) and no rotated
- * activation is written to memory; at batch 2..8 the rotation runs once into
- * the workspace, then the product.
+ * bit for bit, in one call.  Where the product kernel allows it, each of its
+ * workgroups rotates the part of x it needs (the butterfly of
+ * cq_rotate_acts) and no rotated activation is written to memory: matrices
+ * under 2^22 weights with cols_pad <= 4096 (one launch, any batch), and batch
+ * 1 on the lookup tables.  Otherwise the rotation runs once into the
+ * workspace, then the product.
  *
  *   W, batch, y, stream: as for cq_matvec
  *   x        device fp32 [batch][W.cols], 4-byte aligned (16-byte alignment
  *            and W.cols % 8 == 0 allow vector loads), must not overlap y or
  *            the workspace; not modified
  *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_ROTATE_MATVEC)
- *            (for batch 2..8 it also holds the rotated activation)
+ *            (it may also hold the rotated activation)
  *   Errors as cq_matvec.
  */
 cq_status cq_rotate_matvec(const cq_matrix *W, const float *x, int64_t batch, float *y,
                            void *workspace, uint64_t workspace_bytes, void *stream);
+
+/*
+ * Several decode products with one activation: for i < n,
+ *
+ *   y[i] = cq_rotate_matvec(W[i], x)      (same values, bit for bit)
+ *
+ * with the rotation of x shared by all of them (".cact" format post, "How
+ * the kernel reads it": each 128-group of the activation is rotated once and
+ * reused by every row that reads it; OpenNeedle reference notes: Q, K, V and
+ * the gate read the same normalised activation).  Matrices under 2^22
+ * weights with cols_pad <= 4096 run in one launch per storage width (up to 8
+ * matrices a launch), each workgroup rotating x itself; larger ones share a
+ * single rotation into the workspace and take one product each.
+ *
+ *   W        host array of n descriptors, all with the same cols
+ *   n        0 <= n <= CQ_MAX_MULTI (0: nothing is done)
+ *   x        device fp32 [batch][cols], as for cq_rotate_matvec
+ *   batch    0 <= batch <= CQ_MAX_MATVEC_BATCH
+ *   y        host array of n device pointers; y[i] is fp32 [batch][W[i].rows],
+ *            4-byte aligned, fully overwritten; the y[i] must not overlap one
+ *            another, x, any blob or the workspace (y[i] may be NULL when
+ *            W[i].rows == 0)
+ *   workspace, workspace_bytes: at least cq_rotate_multi_workspace_bytes(W, n,
+ *            batch) (NULL, 0 when that is 0; it is 0 when every matrix takes
+ *            the one-launch path)
+ *   Errors: those of cq_rotate_matvec for any W[i]; CQ_ERR_SHAPE for n out of
+ *   range or unequal cols.  Nothing is launched unless every check passes.
+ */
+cq_status cq_rotate_multi_matvec(const cq_matrix *W, int32_t n, const float *x, int64_t batch,
+                                 float *const *y, void *workspace, uint64_t workspace_bytes,
+                                 void *stream);
+
+/* Workspace (bytes) of cq_rotate_multi_matvec for these matrices and batch;
+   checks W, n and batch as that call does.  Host-only. */
+cq_status cq_rotate_multi_workspace_bytes(const cq_matrix *W, int32_t n, int64_t batch,
+                                          uint64_t *bytes);
 
 /*
  * Prefill product on the bf16 matrix cores, fp32 accumulation:

@@ -28,7 +28,8 @@ def _declared_functions():
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
     assert set(names) == {"cq_version", "cq_status_string", "cq_blob_bytes", "cq_workspace_bytes",
-                          "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_gemm", "cq_quantize"}
+                          "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_multi_matvec",
+                          "cq_rotate_multi_workspace_bytes", "cq_gemm", "cq_quantize"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -126,19 +127,22 @@ def test_rotate_matvec_validation():
     m, k = _matrix(levels=np.array([0.1, 0.0, 0.2, 0.3]))
     assert _rotate_matvec(m) == CODEBOOK
     m, k = _matrix()
-    need = ctypes.c_uint64()
-    # small matrices take the matrix-core kernel, and the rotated activation
-    # lives in the workspace
-    assert lib.cq_workspace_bytes(2, ctypes.byref(m), 1, ctypes.byref(need)) == OK and need.value >= 256 * 4
-    W0 = dict(ws=FAKE + (1 << 32), wsb=need.value)
-    assert _rotate_matvec(m, batch=9, **W0) == SHAPE and _rotate_matvec(m, batch=-1, **W0) == SHAPE
+    need = ctypes.c_uint64(7)
+    # a small matrix with K in one slice: one launch that rotates x itself,
+    # no workspace
+    for batch in (1, 8):
+        assert lib.cq_workspace_bytes(2, ctypes.byref(m), batch, ctypes.byref(need)) == OK and need.value == 0
+    assert _rotate_matvec(m, batch=9) == SHAPE and _rotate_matvec(m, batch=-1) == SHAPE
     assert _rotate_matvec(m, batch=0) == OK
-    assert _rotate_matvec(m) == WORKSPACE
-    assert _rotate_matvec(m, x=0, **W0) == NULL and _rotate_matvec(m, y=0, **W0) == NULL
-    assert _rotate_matvec(m, x=FAKE + (1 << 30) + 2, **W0) == ALIGN
-    assert _rotate_matvec(m, y=FAKE + (1 << 31) + 2, **W0) == ALIGN
-    assert _rotate_matvec(m, y=FAKE + (1 << 30) + 16, **W0) == OVERLAP  # y on top of x
-    assert _rotate_matvec(m, y=FAKE + 64, **W0) == OVERLAP  # y on top of the blob
+    assert _rotate_matvec(m, x=0) == NULL and _rotate_matvec(m, y=0) == NULL
+    assert _rotate_matvec(m, x=FAKE + (1 << 30) + 2) == ALIGN
+    assert _rotate_matvec(m, y=FAKE + (1 << 31) + 2) == ALIGN
+    assert _rotate_matvec(m, y=FAKE + (1 << 30) + 16) == OVERLAP  # y on top of x
+    assert _rotate_matvec(m, y=FAKE + 64) == OVERLAP  # y on top of the blob
+    # small but K beyond one slice: the rotated activation goes to the workspace
+    wide, _ = _matrix(rows=4, cols=5000)
+    assert lib.cq_workspace_bytes(2, ctypes.byref(wide), 1, ctypes.byref(need)) == OK and need.value == 5120 * 4 + 2 * 4 * 4
+    assert _rotate_matvec(wide) == WORKSPACE
     big, _ = _matrix(rows=1000, cols=16384)
     need = ctypes.c_uint64()
     assert lib.cq_workspace_bytes(0, ctypes.byref(big), 1, ctypes.byref(need)) == OK and need.value > 0
@@ -147,6 +151,72 @@ def test_rotate_matvec_validation():
     assert _rotate_matvec(big, ws=FAKE + (1 << 32) + 4, wsb=need.value) == ALIGN
     assert _rotate_matvec(big, ws=FAKE + (1 << 30), wsb=need.value) == OVERLAP  # workspace on x
     assert lib.cq_rotate_matvec(None, None, 1, None, None, 0, None) == NULL
+
+
+def _mats(*ms):
+    arr = (cq._Matrix * max(len(ms), 1))()
+    for i, m in enumerate(ms):
+        arr[i] = m
+    return arr
+
+
+def _multi(ms, x=FAKE + (1 << 30), batch=1, ys=None, ws=None, wsb=0, n=None):
+    ys = [FAKE + (1 << 31) + (i << 24) for i in range(len(ms))] if ys is None else ys
+    yarr = (ctypes.c_void_p * max(len(ys), 1))(*ys)
+    return lib.cq_rotate_multi_matvec(_mats(*ms), len(ms) if n is None else n, ctypes.c_void_p(x), batch, yarr,
+                                      None if ws is None else ctypes.c_void_p(ws), wsb, None)
+
+
+def _multi_ws(ms, batch=1, n=None):
+    out = ctypes.c_uint64(7)
+    st = lib.cq_rotate_multi_workspace_bytes(_mats(*ms), len(ms) if n is None else n, batch, ctypes.byref(out))
+    return st, out.value
+
+
+def test_rotate_multi_matvec_validation():
+    # Q/K/V/gate-like: small matrices sharing cols, one launch, no workspace
+    q, kq = _matrix(rows=512, cols=512)
+    kk, kk_ = _matrix(bits=3, rows=256, cols=512)
+    t5, _ = _matrix(bits=5, rows=7, cols=512)
+    assert _multi_ws([q, kk, t5], batch=8) == (OK, 0)
+    assert _multi([q, kk, t5], batch=0) == OK and _multi([], n=0) == OK
+    assert _multi([q, kk], n=-1) == SHAPE and _multi([q], n=65) == SHAPE
+    assert _multi([q, kk], batch=9) == SHAPE and _multi([q, kk], batch=-1) == SHAPE
+    odd, _ = _matrix(rows=4, cols=384)
+    assert _multi([q, odd]) == SHAPE and _multi_ws([q, odd])[0] == SHAPE  # unequal cols
+    bad, _ = _matrix(levels=np.array([0.1, 0.0, 0.2, 0.3]), cols=512)
+    assert _multi([q, bad]) == CODEBOOK and _multi_ws([q, bad])[0] == CODEBOOK
+    short, _ = _matrix(rows=4, cols=512, nbytes=10)
+    assert _multi([short, q]) == LENGTH
+    assert lib.cq_rotate_multi_matvec(None, 2, ctypes.c_void_p(FAKE), 1, None, None, 0, None) == NULL
+    assert lib.cq_rotate_multi_matvec(_mats(q), 1, ctypes.c_void_p(FAKE + (1 << 30)), 1, None, None, 0, None) == NULL
+    assert lib.cq_rotate_multi_workspace_bytes(_mats(q), 1, 1, None) == NULL
+    ys = [FAKE + (1 << 31), FAKE + (1 << 32)]
+    assert _multi([q, kk], ys=[ys[0], 0]) == NULL
+    assert _multi([q, kk], ys=[ys[0], ys[1] + 2]) == ALIGN
+    assert _multi([q, kk], x=0) == NULL and _multi([q, kk], x=FAKE + (1 << 30) + 1) == ALIGN
+    # outputs on top of x, a blob or one another
+    assert _multi([q, kk], ys=[ys[0], FAKE + (1 << 30) + 64]) == OVERLAP
+    assert _multi([q, kk], ys=[ys[0], FAKE + 128]) == OVERLAP
+    assert _multi([q, kk], ys=[ys[0], ys[0] + 512 * 4 - 4]) == OVERLAP
+    # a matrix with no rows needs no output pointer; cols == 0 zeroes outputs
+    empty, _ = _matrix(rows=0, cols=512, blob=0)
+    assert _multi_ws([empty, q]) == (OK, 0)
+    # matrices over 2^22 weights, or K beyond 4096, share one rotation in
+    # the workspace: the largest partial-sum region (16-byte aligned), then
+    # batch x cols_pad floats
+    big, _ = _matrix(rows=1000, cols=16384)
+    wide, _ = _matrix(rows=4, cols=16384)
+    part = 16 * 1000 * 4  # 2-bit tables: 1024 columns a slice
+    assert _multi_ws([wide, big]) == (OK, part + 16384 * 4)
+    big8, _ = _matrix(bits=4, rows=8192, cols=512)  # 2^22 weights: the tables at batch 1
+    st, nb = _multi_ws([q, big8])
+    assert st == OK and nb == 512 * 4
+    assert _multi([q, big8]) == WORKSPACE
+    assert _multi([q, big8], ws=FAKE + (1 << 33), wsb=nb - 1) == WORKSPACE
+    assert _multi([q, big8], ws=FAKE + (1 << 33) + 4, wsb=nb) == ALIGN
+    assert _multi([q, big8], ws=FAKE + (1 << 30), wsb=nb) == OVERLAP  # workspace on x
+    assert _multi([q, big8], ws=FAKE + (1 << 31), wsb=nb) == OVERLAP  # workspace on y[0]
 
 
 def test_nothing_to_do_returns_ok_without_launching():
@@ -244,6 +314,6 @@ def test_workspace_bytes():
 
 
 def test_binding_has_the_c_names():
-    for n in ("cq_blob_bytes", "cq_workspace_bytes", "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_gemm",
-              "cq_quantize"):
+    for n in ("cq_blob_bytes", "cq_workspace_bytes", "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec",
+              "cq_rotate_multi_matvec", "cq_rotate_multi_workspace_bytes", "cq_gemm", "cq_quantize"):
         assert callable(getattr(cq, n))

@@ -259,6 +259,102 @@ def test_rotate_matvec_full_size():
     torch.cuda.empty_cache()
 
 
+def _oracle_check(W, blob, levels, x, y):
+    ref = oracle.matvec(blob, W.bits, W.rows, W.cols, x, levels)
+    w_hat = np.linalg.norm(oracle.dequantize(blob, W.bits, W.rows, W.cols, levels), axis=1)
+    _check_fp32_product(y.cpu().numpy(), ref, w_hat, np.linalg.norm(x.astype(np.float64), axis=1))
+
+
+@pytest.mark.parametrize("batch", [1, 3, 8])
+@pytest.mark.parametrize("cols", [512, 300, 3000, 4096])
+def test_rotate_multi_matvec_one_launch(batch, cols):
+    # small matrices of every width sharing x: one launch per width, the
+    # kernel rotating x itself; ten 2-bit matrices take two launches of at
+    # most eight.  Each output equals the two-call path bit for bit (same
+    # fp16 staging, scale and product order) and the oracle within the fp32 bar.
+    say("multi one launch", batch, cols)
+    specs = [(2, 512), (3, 256), (4, 130), (5, 37), (2, 1)] + [(2, 128 + 17 * i) for i in range(9)]
+    mats = [_random_cq(bits, rows, cols, 500 + i) for i, (bits, rows) in enumerate(specs)]
+    x = cq_inputs.activations(84, cols + batch, batch, cols)
+    xd = _to_dev(x)
+    Ws = [W for W, _ in mats]
+    assert cq.cq_rotate_multi_workspace_bytes(Ws, batch) == 0
+    ys = cq.cq_rotate_multi_matvec(Ws, xd)
+    xr = cq.cq_rotate_acts(xd)
+    for (W, blob), y in zip(mats, ys):
+        assert torch.equal(y, cq.cq_matvec(W, xr)), (W.bits, W.rows)
+        assert torch.equal(y, cq.cq_rotate_matvec(W, xd)), (W.bits, W.rows)
+        _oracle_check(W, blob, _levels(W.bits), x, y)
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+@pytest.mark.parametrize("cols,specs", [
+    (512, [(2, 512), (4, 8192), (2, 256), (5, 300)]),  # 8192 x 512: the lookup tables at batch 1
+    (5000, [(2, 100), (3, 1000), (4, 2000)]),           # K beyond 4096: a shared rotation
+])
+def test_rotate_multi_matvec_mixed_paths(batch, cols, specs):
+    say("multi mixed", batch, cols)
+    mats = [_random_cq(bits, rows, cols, 600 + i) for i, (bits, rows) in enumerate(specs)]
+    x = cq_inputs.activations(85, cols + batch, batch, cols)
+    xd = _to_dev(x)
+    Ws = [W for W, _ in mats]
+    ws = torch.full((max(cq.cq_rotate_multi_workspace_bytes(Ws, batch), 16),), 0x7F, dtype=torch.uint8, device=DEV)
+    ys = cq.cq_rotate_multi_matvec(Ws, xd, workspace=ws)
+    xr = cq.cq_rotate_acts(xd)
+    for (W, blob), y in zip(mats, ys):
+        assert torch.equal(y, cq.cq_matvec(W, xr)), (W.bits, W.rows)
+        _oracle_check(W, blob, _levels(W.bits), x, y)
+
+
+def test_rotate_multi_matvec_degenerate():
+    W1, _ = _random_cq(2, 64, 256, 700)
+    W0 = cq.CQMatrix(2, 0, 256, torch.empty(0, dtype=torch.uint8, device=DEV), _levels(2))
+    x = _to_dev(cq_inputs.activations(86, 0, 2, 256))
+    ys = cq.cq_rotate_multi_matvec([W0, W1], x)
+    assert ys[0].shape == (2, 0) and torch.equal(ys[1], cq.cq_rotate_matvec(W1, x))
+    assert cq.cq_rotate_multi_matvec([], x) == []
+    e = cq.cq_rotate_multi_matvec([W1], x[:0])
+    assert e[0].shape == (0, 64)
+    # cols == 0: every output is zero
+    Wz = cq.CQMatrix(3, 5, 0, torch.empty(0, dtype=torch.uint8, device=DEV), _levels(3))
+    y = torch.full((2, 5), float("nan"), device=DEV)
+    cq.cq_rotate_multi_matvec([Wz], torch.empty((2, 0), device=DEV), outs=[y])
+    assert torch.equal(y, torch.zeros_like(y))
+
+
+def test_needle_layer_multi_and_graph():
+    # a Needle decode layer as the library serves it: Q/K/V/gate in one
+    # shared-activation call, out in its own; against the oracle, then the
+    # pair captured in a HIP graph and replayed (eager work and syncs
+    # between replays) bit for bit
+    say("needle layer multi")
+    cols = 512
+    specs = [(2, 512), (2, 256), (2, 256), (2, 512)]
+    mats = [_cq_from_oracle(bits, rows, cols, 710 + i)[:3] for i, (bits, rows) in enumerate(specs)]
+    Wo, blob_o, lev_o, _ = _cq_from_oracle(2, 512, cols, 719)
+    x_in, x_out = cq_inputs.activations(87, 0, 1, cols), cq_inputs.activations(87, 1, 1, cols)
+    xi, xo = _to_dev(x_in), _to_dev(x_out)
+    ys = cq.cq_rotate_multi_matvec([m[0] for m in mats], xi)
+    yo = cq.cq_rotate_matvec(Wo, xo)
+    for (W, blob, levels), y in zip(mats, ys):
+        _oracle_check(W, blob, levels, x_in, y)
+    _oracle_check(Wo, blob_o, lev_o, x_out, yo)
+    ref = [y.clone() for y in ys] + [yo.clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cq.cq_rotate_multi_matvec([m[0] for m in mats], xi, outs=ys)
+        cq.cq_rotate_matvec(Wo, xo, out=yo)
+    for i in range(4):
+        for y in ys + [yo]:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ys + [yo], ref):
+            assert torch.equal(a, b), i
+    del g
+
+
 def test_needle_decode_sweep_shapes():
     # the Needle-shaped decode workload at batch 1: 27 layers of Q 512x512,
     # K and V 256x512, gate and out 512x512 at CQ2 -- one rotated activation
