@@ -40,24 +40,26 @@ hipError_t launch_rotate(const void *x, int x_dtype, int64_t batch, int64_t cols
 // sums, any contents on entry.
 uint64_t matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch);
 
-// Batch 1 from 2^22 weights: the lookup-table kernel; otherwise the
-// matrix-core kernel.
+// Small matrices (see kSmallMaxWeights): launch_small_matvec; otherwise
+// batch 1 from 2^23 weights up: the lookup-table kernel; otherwise the
+// batched matrix-core kernel.
 hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
                          const CodeLevels &lev, const float *xr, int64_t batch, float *y,
                          void *workspace, hipStream_t s);
 
 // The same product from the activation before rotation (x fp32
 // [batch][cols]), results equal to launch_rotate + launch_matvec.  Small
-// matrices: launch_multi_matvec.  Batch 1 on the tables: the lookup-table
-// kernel rotates its slice of x itself, with the butterfly of launch_rotate.
-// Otherwise launch_rotate into the workspace (after the partial sums), then
-// the matrix-core kernel.
+// matrices: launch_small_matvec rotating x itself.  Batch 1 on the tables:
+// the lookup-table kernel rotates its slice of x itself, with the butterfly
+// of launch_rotate.  Otherwise launch_rotate into the workspace (after the
+// partial sums), then the batched matrix-core kernel.
 uint64_t rotate_matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch);
 hipError_t launch_rotate_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
                                 const CodeLevels &lev, const float *x, int64_t cols, int64_t batch,
                                 float *y, void *workspace, hipStream_t s);
 
-// The matrix-core kernel (batches, and small matrices at batch 1).
+// The batched matrix-core kernel (batch 2..8 beyond the small-matrix
+// kernel's limits; also batch 1 with cols_pad > 4096 under 2^23 weights).
 uint64_t matvec_mma_workspace_bytes(int64_t rows, int64_t kpad, int64_t batch);
 hipError_t launch_matvec_mma(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
                              const CodeLevels &lev, const float *xr, int64_t batch, float *y,
@@ -73,17 +75,26 @@ struct MultiItem {
   float *y;
 };
 
-// The one-launch kernel for products that share x (rotating x itself):
-// batch 1..8 and cols_pad <= 4096.
-bool multi_matvec_fits(int64_t kpad, int64_t batch);
-hipError_t launch_multi_matvec(const MultiItem *items, int n, const float *x, int64_t cols, int64_t kpad,
-                               int64_t batch, hipStream_t s);
+// Matrices of at most this many weights (rows x cols_pad) with cols_pad <=
+// 4096 take the small-matrix kernel.
+#ifndef CQ_SMALL_MAX_WEIGHTS
+#define CQ_SMALL_MAX_WEIGHTS (int64_t{1} << 26)
+#endif
+constexpr int64_t kSmallMaxWeights = CQ_SMALL_MAX_WEIGHTS;
+
+// The small-matrix kernel, one launch per storage width for up to 8
+// matrices sharing x: batch 1..8, cols_pad <= 4096.  rotate: x is the
+// activation [batch][cols] and each workgroup rotates it; otherwise x is xr
+// [batch][kpad] (16-byte aligned) as launch_rotate writes it.  Both give the
+// same values.
+bool small_matvec_fits(int64_t kpad, int64_t batch);
+hipError_t launch_small_matvec(const MultiItem *items, int n, const float *x, bool rotate, int64_t cols,
+                               int64_t kpad, int64_t batch, hipStream_t s);
 
 // Products of several matrices with one activation x (fp32 [batch][cols],
-// not rotated).  Small matrices (under 2^22 weights, cols_pad <= 4096) go
-// to launch_multi_matvec, one launch per width; the others share one
-// rotation into the workspace (after the largest partial-sum region) and
-// take launch_matvec each.
+// not rotated).  Small matrices go to launch_small_matvec (rotating x
+// themselves); the others share one rotation into the workspace (after the
+// largest partial-sum region) and take launch_matvec each.
 uint64_t rotate_multi_workspace_bytes(const MultiItem *items, int n, int64_t kpad, int64_t batch);
 hipError_t launch_rotate_multi_matvec(const MultiItem *items, int n, const float *x, int64_t cols, int64_t kpad,
                                       int64_t batch, void *workspace, hipStream_t s);

@@ -524,12 +524,18 @@ float lev_absmax(int sb, const cq::CodeLevels &lev) {
 namespace cq {
 
 #ifndef CQ_LUT_MIN_WEIGHTS
-#define CQ_LUT_MIN_WEIGHTS (1 << 22)
+#define CQ_LUT_MIN_WEIGHTS (int64_t{1} << 23)
 #endif
-// The lookup-table kernel serves batch 1 from 2^22 weights up (8192 x 512
-// and larger).  Smaller matrices are launch- and prologue-bound, and the
-// matrix-core kernel's prologue (no 128 KB table to build) is shorter:
-// 9.2 against 11.5 us per 512 x 512 call.
+// Kernel choice, from batch-1 and batch-8 timings on MI355X.  With
+// cols_pad <= 4096 the small-matrix kernel is faster up to 64 M weights
+// (batch 1: 8.0 us at 512 x 512 and 14.2 us at 16384 x 4096, against 13.0
+// and 16.4 us on the lookup tables) and slower from 128 M.  With more
+// columns, batch 1 takes the lookup tables from 2^23 weights and the batched
+// matrix-core kernel below.
+static bool use_small(int64_t rows, int64_t kpad, int64_t batch) {
+  return rows * kpad <= kSmallMaxWeights && small_matvec_fits(kpad, batch);
+}
+
 static bool use_lut(int64_t rows, int64_t kpad, int64_t batch) {
   return batch == 1 && rows * kpad >= static_cast<int64_t>(CQ_LUT_MIN_WEIGHTS);
 }
@@ -538,21 +544,16 @@ static bool use_lut(int64_t rows, int64_t kpad, int64_t batch) {
 // for the lookup-table kernel, [nslice][batch][rows] for the matrix-core one.
 uint64_t matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch) {
   if (rows <= 0 || kpad <= 0 || batch <= 0) return 0;  // nothing is launched
+  if (use_small(rows, kpad, batch)) return 0;
   if (!use_lut(rows, kpad, batch)) return matvec_mma_workspace_bytes(rows, kpad, batch);
   const MvShape s = mv_shape(storage_bits(bits), rows, kpad);
   if (s.nslice <= 1) return 0;
   return static_cast<uint64_t>(s.nslice) * rows * 4;
 }
 
-// Small matrices whose K fits one slice take the one-launch kernel that
-// rotates x itself (no workspace).
-static bool use_fused_small(int64_t rows, int64_t kpad, int64_t batch) {
-  return rows * kpad < static_cast<int64_t>(CQ_LUT_MIN_WEIGHTS) && multi_matvec_fits(kpad, batch);
-}
-
 uint64_t rotate_matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch) {
   if (rows <= 0 || kpad <= 0 || batch <= 0) return 0;
-  if (use_fused_small(rows, kpad, batch)) return 0;
+  if (use_small(rows, kpad, batch)) return 0;
   if (use_lut(rows, kpad, batch)) return matvec_workspace_bytes(bits, rows, kpad, 1);
   return (matvec_mma_workspace_bytes(rows, kpad, batch) + 15) / 16 * 16 + static_cast<uint64_t>(batch) * kpad * 4;
 }
@@ -602,6 +603,10 @@ hipError_t launch_lut(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
 
 hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
                          const float *xr, int64_t batch, float *y, void *workspace, hipStream_t s) {
+  if (use_small(rows, kpad, batch)) {
+    const MultiItem item = {blob, bits, rows, lev, y};
+    return launch_small_matvec(&item, 1, xr, false, kpad, kpad, batch, s);
+  }
   if (!use_lut(rows, kpad, batch)) return launch_matvec_mma(blob, bits, rows, kpad, lev, xr, batch, y, workspace, s);
   return launch_lut(blob, bits, rows, kpad, lev, xr, nullptr, 0, y, workspace, s);
 }
@@ -609,9 +614,9 @@ hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kp
 hipError_t launch_rotate_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
                                 const float *x, int64_t cols, int64_t batch, float *y, void *workspace,
                                 hipStream_t s) {
-  if (use_fused_small(rows, kpad, batch)) {
+  if (use_small(rows, kpad, batch)) {
     const MultiItem item = {blob, bits, rows, lev, y};
-    return launch_multi_matvec(&item, 1, x, cols, kpad, batch, s);
+    return launch_small_matvec(&item, 1, x, true, cols, kpad, batch, s);
   }
   if (use_lut(rows, kpad, batch)) return launch_lut(blob, bits, rows, kpad, lev, nullptr, x, cols, y, workspace, s);
   // Batches: every workgroup of a K slice would redo the slice's rotation, so
@@ -628,7 +633,7 @@ uint64_t rotate_multi_workspace_bytes(const MultiItem *items, int n, int64_t kpa
   uint64_t part = 0;
   bool shared = false;
   for (int i = 0; i < n; ++i) {
-    if (items[i].rows <= 0 || use_fused_small(items[i].rows, kpad, batch)) continue;
+    if (items[i].rows <= 0 || use_small(items[i].rows, kpad, batch)) continue;
     shared = true;
     const uint64_t p = matvec_workspace_bytes(items[i].bits, items[i].rows, kpad, batch);
     if (p > part) part = p;
@@ -645,7 +650,7 @@ hipError_t launch_rotate_multi_matvec(const MultiItem *items, int n, const float
   uint64_t part = 0;
   for (int i = 0; i < n; ++i) {
     if (items[i].rows <= 0) continue;
-    if (use_fused_small(items[i].rows, kpad, batch)) {
+    if (use_small(items[i].rows, kpad, batch)) {
       if (nsmall == 64) return hipErrorInvalidValue;
       small[nsmall++] = items[i];
     } else {
@@ -655,7 +660,7 @@ hipError_t launch_rotate_multi_matvec(const MultiItem *items, int n, const float
     }
   }
   if (nsmall) {
-    const hipError_t e = launch_multi_matvec(small, nsmall, x, cols, kpad, batch, s);
+    const hipError_t e = launch_small_matvec(small, nsmall, x, true, cols, kpad, batch, s);
     if (e != hipSuccess) return e;
   }
   if (!shared) return hipSuccess;
@@ -664,7 +669,7 @@ hipError_t launch_rotate_multi_matvec(const MultiItem *items, int n, const float
   hipError_t e = launch_rotate(x, CQ_F32, batch, cols, kpad, xr, CQ_F32, s);
   for (int i = 0; i < n && e == hipSuccess; ++i) {
     const MultiItem &it = items[i];
-    if (it.rows <= 0 || use_fused_small(it.rows, kpad, batch)) continue;
+    if (it.rows <= 0 || use_small(it.rows, kpad, batch)) continue;
     e = launch_matvec(it.blob, it.bits, it.rows, kpad, it.lev, xr, batch, it.y, part ? workspace : nullptr, s);
   }
   return e;

@@ -163,21 +163,24 @@ cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t 
  *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_MATVEC),
  *            see cq_workspace_bytes (NULL, 0 when that is 0); must not
  *            overlap any other buffer of the call
- *   Arithmetic, batch 1 and rows * cols_pad >= 2^22: the inner sum is read
- *   from lookup tables indexed by a packed field (4 codes at 2-bit widths, 2
- *   codes at 3- and 4-bit widths); an entry, the sum of its codes' level * xr
- *   products, is computed in fp32, scaled by a power of two per slice of
- *   512-2048 columns and rounded once to fp16 (relative error <= 2^-11 per
- *   entry).  Products with the fp16 norm and all sums are fp32.
- *   Arithmetic, batch 2..8 and smaller matrices at batch 1 (fp16 matrix
- *   cores, W read once for the batch):
- *   each weight is fp16(c[q] * float(norm)) and each activation fp16(xr * 2^e),
+ *   Kernels: a matrix with cols_pad <= 4096 and at most 2^26 weights
+ *   (rows * cols_pad) takes the small-matrix kernel at every batch; otherwise
+ *   batch 1 from 2^23 weights takes the lookup tables, and the rest the
+ *   batched matrix-core kernel.
+ *   Arithmetic of the lookup tables: the inner sum is read from tables
+ *   indexed by a packed field (4 codes at 2-bit widths, 2 codes at 3- and
+ *   4-bit widths); an entry, the sum of its codes' level * xr products, is
+ *   computed in fp32, scaled by a power of two per slice of 512-2048 columns
+ *   and rounded once to fp16 (relative error <= 2^-11 per entry).  Products
+ *   with the fp16 norm and all sums are fp32.
+ *   Arithmetic of the matrix-core kernels (W read once for the batch): each
+ *   weight is fp16(c[q] * float(norm)) and each activation fp16(xr * 2^e),
  *   2^e a power of two per batch vector and slice of up to 4096 columns that
  *   puts the slice's largest |xr| in [2^14, 2^15) (both roundings to nearest
  *   even, relative error <= 2^-11); products and sums are fp32 and the scale
  *   is undone exactly.
- *   Results do not depend on scheduling: the partial sums of the K slices are
- *   added in a fixed order.
+ *   Results do not depend on scheduling: partial sums (of K slices, or of
+ *   the waves that share a row block) are added in a fixed order.
  */
 cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y,
                     void *workspace, uint64_t workspace_bytes, void *stream);
@@ -187,10 +190,10 @@ cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y
  * cq_rotate_acts(x, CQ_F32, ..., xr, CQ_F32) followed by cq_matvec(W, xr, ...),
  * bit for bit, in one call.  Where the product kernel allows it, each of its
  * workgroups rotates the part of x it needs (the butterfly of
- * cq_rotate_acts) and no rotated activation is written to memory: matrices
- * under 2^22 weights with cols_pad <= 4096 (one launch, any batch), and batch
- * 1 on the lookup tables.  Otherwise the rotation runs once into the
- * workspace, then the product.
+ * cq_rotate_acts) and no rotated activation is written to memory: the
+ * small-matrix kernel (one launch, any batch, no workspace) and the lookup
+ * tables.  Otherwise the rotation runs once into the workspace, then the
+ * product.
  *
  *   W, batch, y, stream: as for cq_matvec
  *   x        device fp32 [batch][W.cols], 4-byte aligned (16-byte alignment
@@ -211,10 +214,10 @@ cq_status cq_rotate_matvec(const cq_matrix *W, const float *x, int64_t batch, fl
  * with the rotation of x shared by all of them (".cact" format post, "How
  * the kernel reads it": each 128-group of the activation is rotated once and
  * reused by every row that reads it; OpenNeedle reference notes: Q, K, V and
- * the gate read the same normalised activation).  Matrices under 2^22
- * weights with cols_pad <= 4096 run in one launch per storage width (up to 8
- * matrices a launch), each workgroup rotating x itself; larger ones share a
- * single rotation into the workspace and take one product each.
+ * the gate read the same normalised activation).  Matrices that take the
+ * small-matrix kernel (see cq_matvec) run in one launch per storage width
+ * (up to 8 matrices a launch), each workgroup rotating x itself; the others
+ * share a single rotation into the workspace and take one product each.
  *
  *   W        host array of n descriptors, all with the same cols
  *   n        0 <= n <= CQ_MAX_MULTI (0: nothing is done)

@@ -202,21 +202,23 @@ def test_rotate_multi_matvec_validation():
     # a matrix with no rows needs no output pointer; cols == 0 zeroes outputs
     empty, _ = _matrix(rows=0, cols=512, blob=0)
     assert _multi_ws([empty, q]) == (OK, 0)
-    # matrices over 2^22 weights, or K beyond 4096, share one rotation in
-    # the workspace: the largest partial-sum region (16-byte aligned), then
-    # batch x cols_pad floats
+    # matrices past the small-matrix kernel (K beyond 4096, or over 2^26
+    # weights) share one rotation in the workspace: the largest partial-sum
+    # region (16-byte aligned), then batch x cols_pad floats
     big, _ = _matrix(rows=1000, cols=16384)
     wide, _ = _matrix(rows=4, cols=16384)
     part = 16 * 1000 * 4  # 2-bit tables: 1024 columns a slice
     assert _multi_ws([wide, big]) == (OK, part + 16384 * 4)
-    big8, _ = _matrix(bits=4, rows=8192, cols=512)  # 2^22 weights: the tables at batch 1
-    st, nb = _multi_ws([q, big8])
-    assert st == OK and nb == 512 * 4
-    assert _multi([q, big8]) == WORKSPACE
-    assert _multi([q, big8], ws=FAKE + (1 << 33), wsb=nb - 1) == WORKSPACE
-    assert _multi([q, big8], ws=FAKE + (1 << 33) + 4, wsb=nb) == ALIGN
-    assert _multi([q, big8], ws=FAKE + (1 << 30), wsb=nb) == OVERLAP  # workspace on x
-    assert _multi([q, big8], ws=FAKE + (1 << 31), wsb=nb) == OVERLAP  # workspace on y[0]
+    q4, _ = _matrix(rows=512, cols=4096)
+    big4, _ = _matrix(rows=16385, cols=4096)  # just over 2^26 weights: the tables at batch 1
+    st, nb = _multi_ws([q4, big4])
+    assert st == OK and nb == 4 * 16385 * 4 + 4096 * 4
+    assert _multi_ws([q4, big4], batch=2) == (OK, 2 * 4096 * 4)  # the batched kernel: one slice
+    assert _multi([q4, big4]) == WORKSPACE
+    assert _multi([q4, big4], ws=FAKE + (1 << 33), wsb=nb - 1) == WORKSPACE
+    assert _multi([q4, big4], ws=FAKE + (1 << 33) + 4, wsb=nb) == ALIGN
+    assert _multi([q4, big4], ws=FAKE + (1 << 30), wsb=nb) == OVERLAP  # workspace on x
+    assert _multi([q4, big4], ws=FAKE + (1 << 31), wsb=nb) == OVERLAP  # workspace on y[0]
 
 
 def test_nothing_to_do_returns_ok_without_launching():
