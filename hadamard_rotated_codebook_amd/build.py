@@ -31,9 +31,14 @@ CFLAGS = [
 ]
 
 
+# Per-file flags.  The small-matrix kernel takes its activation arguments as
+# leading scalars and has the dispatcher preload them into SGPRs.
+EXTRA = {"multi_matvec.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=6"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")

@@ -56,23 +56,29 @@ constexpr int kXPad = 8;                          // fp16 elements of padding pe
 constexpr uint32_t kOutOfRange = 0xffff0000u;     // a buffer offset past any range
 
 struct SmallMat {
-  const uint8_t *packed;
-  const uint16_t *norms;  // fp16 bits [rows][ngroups]
+  const uint8_t *packed;  // packed rows; the fp16 norms [rows][ngroups] follow
   float *y;               // [batch][rows]
   int64_t rows;
+  int64_t wgs;            // workgroups of this matrix
 };
 
+// Grid: x = row tiles (the largest matrix's count), y = matrix.
 struct SmallArgs {
-  int32_t wg0[kMaxMats];  // first workgroup of each matrix (ascending)
   SmallMat mat[kMaxMats];
   cq::CodeLevels lev[kMaxMats];
-  const float *x;  // ROT: x [batch][cols]; otherwise xr [batch][kpad]
-  int64_t cols, kpad, row_bytes, ngroups;
-  int32_t nmat, batch, xvec, ks_shift;  // ksplit = 1 << ks_shift waves per block
 };
 
+// The scalar arguments come first: the compiler asks the dispatcher to
+// preload them into SGPRs (-amdgpu-kernarg-preload-count=6), so the
+// activation loads go out before any argument load returns.
+//   x         ROT: x [batch][cols]; otherwise xr [batch][kpad]
+//   xstride   cols (ROT) or kpad, in floats
+//   xvec      ROT: x rows allow 16-byte loads (cols % 8 == 0, x 16-byte aligned)
+//   ks_shift  ksplit = 1 << ks_shift waves per 16-row block
 template <int SB, bool ROT>
-__global__ __launch_bounds__(kThreads) void small_matvec_kernel(SmallArgs a) {
+__global__ __launch_bounds__(kThreads) void small_matvec_kernel(const float *x, int32_t xstride, int32_t ngroups,
+                                                                int32_t batch, int32_t xvec, int32_t ks_shift,
+                                                                SmallArgs a) {
   constexpr int GROUP_BYTES = CQ_GROUP * SB / 8;  // 32, 48, 64
   constexpr int GROUP_DW = GROUP_BYTES / 4;
   constexpr int XS = kMaxCols + kXPad;            // LDS row stride (fp16 elements)
@@ -82,49 +88,25 @@ __global__ __launch_bounds__(kThreads) void small_matvec_kernel(SmallArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wg = blockIdx.x;
-
-  // ---- this workgroup's matrix: the number of later matrices whose first
-  // workgroup is <= wg (the first workgroups ascend; unused slots repeat
-  // the last matrix)
-  int mi = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxMats; ++i) mi += wg >= a.wg0[i] ? 1 : 0;
-  mi = __builtin_amdgcn_readfirstlane(mi);
-  const SmallMat &mat = a.mat[mi];
-  const uint8_t *packed = mat.packed;
-  const uint16_t *norms = mat.norms;
-  float *y = mat.y;
-  const int64_t rows = mat.rows;
-  const int wg0 = a.wg0[mi];
-  const int ks = a.ks_shift, ksplit = 1 << ks;
-  const int blk = wave >> ks, part = wave & (ksplit - 1);
-  const int64_t r0 = ((static_cast<int64_t>(wg - wg0) << (2 - ks)) + blk) * kBlockRows;
-  const int64_t live_rows = rows - r0 < kBlockRows ? (rows - r0 > 0 ? rows - r0 : 0) : kBlockRows;
-  const __amdgpu_buffer_rsrc_t wbuf =
-      buffer_rsrc(packed + r0 * a.row_bytes, static_cast<uint32_t>(live_rows * a.row_bytes));
-  const __amdgpu_buffer_rsrc_t nbuf =
-      buffer_rsrc(norms + r0 * a.ngroups, static_cast<uint32_t>(live_rows * a.ngroups * 2));
-  const int ngroups = static_cast<int>(a.ngroups);
-  const int nchunks = (ngroups + 3) / 4;
-  const int c_lo = part * nchunks >> ks, c_hi = (part + 1) * nchunks >> ks;
+  const int wg = blockIdx.x, mi = blockIdx.y;
 
   // ---- lane roles: row n of the block; quarter q = group 4c+q of chunk c
   // (for the product and for the staging)
   const int n = lane & 15, q = lane >> 4;
+  const int nchunks = (ngroups + 3) / 4;
 
-  // ---- activation loads of the wave's first batch row (a wave without one
-  // loads row 0 and discards it, so that the loads are unconditional)
-  // Every chunk slot is loaded, in straight-line code (slots at or past
-  // nchunks, and elements past the row, read zeros through the buffer
-  // range), so that the wait before the rotation covers only these loads
-  // and not the codes requested after them.
+  // ---- activation loads of the wave's first batch row, before anything
+  // that depends on the matrix (a wave without a row loads row 0 and
+  // discards it, so that the loads are unconditional).  Every chunk slot is
+  // loaded, in straight-line code (slots at or past nchunks, and elements
+  // past the row, read zeros through the buffer range), so that the wait
+  // before the rotation covers only these loads and not the codes requested
+  // after them.
   float v[kMaxChunks][8];
   auto load_x = [&](int m) {
-    const int64_t stride = ROT ? a.cols : a.kpad;
-    const __amdgpu_buffer_rsrc_t xb = buffer_rsrc(a.x + static_cast<int64_t>(m) * stride,
-                                                  static_cast<uint32_t>(stride * 4));
-    if (!ROT || a.xvec) {
+    const __amdgpu_buffer_rsrc_t xb = buffer_rsrc(x + static_cast<int64_t>(m) * xstride,
+                                                  static_cast<uint32_t>(xstride) * 4u);
+    if (!ROT || xvec) {
       // whole 8-element blocks: xr rows are 16-byte aligned; x rows are when
       // xvec (cols % 8 == 0 and x 16-byte aligned)
 #pragma unroll
@@ -145,13 +127,32 @@ __global__ __launch_bounds__(kThreads) void small_matvec_kernel(SmallArgs a) {
         const int64_t col0 = static_cast<int64_t>(4 * c + q) * CQ_GROUP + 8 * n;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const uint32_t off = c < nchunks && col0 + i < a.cols ? static_cast<uint32_t>((col0 + i) * 4) : kOutOfRange;
+          const uint32_t off = c < nchunks && col0 + i < xstride ? static_cast<uint32_t>((col0 + i) * 4) : kOutOfRange;
           v[c][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xb, off, 0, 0));
         }
       }
     }
   };
-  load_x(wave < a.batch ? wave : 0);
+  load_x(wave < batch ? wave : 0);
+
+  // ---- this workgroup's matrix and row tile (a tile past the matrix's end
+  // reads nothing through its empty buffer ranges and leaves once its
+  // requests are out, so that no argument load waits behind a branch)
+  const SmallMat &mat = a.mat[mi];
+  const uint8_t *packed = mat.packed;
+  float *y = mat.y;
+  const int64_t rows = mat.rows;
+  const int64_t row_bytes = static_cast<int64_t>(ngroups) * GROUP_BYTES;
+  const uint16_t *norms = reinterpret_cast<const uint16_t *>(packed + rows * row_bytes);
+  const int ks = ks_shift, ksplit = 1 << ks;
+  const int blk = wave >> ks, part = wave & (ksplit - 1);
+  const int64_t r0 = ((static_cast<int64_t>(wg) << (2 - ks)) + blk) * kBlockRows;
+  const int64_t live_rows = rows - r0 < kBlockRows ? (rows - r0 > 0 ? rows - r0 : 0) : kBlockRows;
+  const __amdgpu_buffer_rsrc_t wbuf =
+      buffer_rsrc(packed + r0 * row_bytes, static_cast<uint32_t>(live_rows * row_bytes));
+  const __amdgpu_buffer_rsrc_t nbuf =
+      buffer_rsrc(norms + r0 * ngroups, static_cast<uint32_t>(live_rows * ngroups * 2));
+  const int c_lo = part * nchunks >> ks, c_hi = (part + 1) * nchunks >> ks;
 
   uint32_t codes[2][GROUP_DW];  // [set][dword]
   uint16_t nrm[2];
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void small_matvec_kernel(SmallArgs a) {
     constexpr int S = decltype(set_c)::value;
     const int g = 4 * c + q;  // this lane's group
     const bool g_live = g < ngroups && c < c_hi;
-    const uint32_t woff = static_cast<uint32_t>(n * a.row_bytes + g * GROUP_BYTES);
+    const uint32_t woff = static_cast<uint32_t>(n * row_bytes + g * GROUP_BYTES);
     load_dwords<GROUP_DW>(wbuf, g_live ? woff : kOutOfRange, codes[S]);
     const uint32_t noff = static_cast<uint32_t>((n * ngroups + g) * 2);
     nrm[S] = __builtin_amdgcn_raw_buffer_load_b16(nbuf, g_live ? noff : kOutOfRange, 0, 0);
@@ -167,6 +168,7 @@ __global__ __launch_bounds__(kThreads) void small_matvec_kernel(SmallArgs a) {
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
   load_chunk(c_lo, Set0{});
+  if (wg >= mat.wgs) return;
 
   // ---- the activation, fp16 in LDS.  Wave w stages batch rows w and w + 4;
   // lane j of quarter q holds elements 8j..8j+7 of group 4c+q.  Groups past
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void small_matvec_kernel(SmallArgs a) {
   // reads is written.
   for (int k = tid * 4; k < nchunks * kChunkCols; k += kThreads * 4)
     *reinterpret_cast<uint2 *>(xs + kMaxBatch * XS + k) = make_uint2(0u, 0u);
-  for (int m = wave; m < a.batch; m += kWaves) {
+  for (int m = wave; m < batch; m += kWaves) {
     if (m != wave) load_x(m);
     float mx = 0.0f;
 #pragma unroll
@@ -189,8 +191,7 @@ __global__ __launch_bounds__(kThreads) void small_matvec_kernel(SmallArgs a) {
         for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(v[c][i]));
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    mx = wave_max(mx);
     int e = 0;
     if (mx > 0.0f && mx <= 3.0e38f) {
       (void)frexpf(mx, &e);  // mx < 2^e
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void small_matvec_kernel(SmallArgs a) {
 
   // ---- the product; for the A operand, batch row m = lane % 16 (the zero
   // row when m >= batch)
-  const int m_a = (lane & 15) < a.batch ? (lane & 15) : kMaxBatch;
+  const int m_a = (lane & 15) < batch ? (lane & 15) : kMaxBatch;
   const uint32_t a_base = static_cast<uint32_t>(m_a * XS + q * CQ_GROUP) * 2u;  // bytes
   const cq::CodeLevels &lev = a.lev[mi];
 
@@ -265,11 +266,11 @@ __global__ __launch_bounds__(kThreads) void small_matvec_kernel(SmallArgs a) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int m = 4 * q + e;
-    if (m < a.batch && r < rows) y[static_cast<int64_t>(m) * rows + r] = acc[e] * unscale[m];
+    if (m < batch && r < rows) y[static_cast<int64_t>(m) * rows + r] = acc[e] * unscale[m];
   }
 }
 
-typedef void (*SmallKernel)(SmallArgs);
+typedef void (*SmallKernel)(const float *, int32_t, int32_t, int32_t, int32_t, int32_t, SmallArgs);
 
 SmallKernel pick(int sb, bool rot) {
   if (rot) return sb == 2 ? small_matvec_kernel<2, true> : (sb == 3 ? small_matvec_kernel<3, true> : small_matvec_kernel<4, true>);
@@ -293,38 +294,27 @@ hipError_t launch_small_matvec(const MultiItem *items, int n, const float *x, bo
   // one launch per storage width, at most kMaxMats matrices each, in order
   for (int sb = 2; sb <= 4; ++sb) {
     SmallArgs a;
-    int count = 0, wgs = 0;
+    int count = 0;
+    int64_t max_wgs = 0;
     auto flush = [&]() -> hipError_t {
       if (count == 0) return hipSuccess;
-      a.nmat = count;
-      a.x = x;
-      a.cols = cols;
-      a.kpad = kpad;
-      a.row_bytes = kpad * sb / 8;
-      a.ngroups = kpad / CQ_GROUP;
-      a.batch = static_cast<int32_t>(batch);
-      a.xvec = cols % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
-      a.ks_shift = ks_shift;
-      for (int i = count; i < kMaxMats; ++i)
-        a.mat[i] = a.mat[count - 1], a.lev[i] = a.lev[count - 1], a.wg0[i] = a.wg0[count - 1];
-      pick(sb, rotate)<<<dim3(static_cast<unsigned>(wgs)), kThreads, 0, s>>>(a);
+      for (int i = count; i < kMaxMats; ++i) a.mat[i] = a.mat[count - 1], a.lev[i] = a.lev[count - 1];
+      const int32_t xvec = cols % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+      pick(sb, rotate)<<<dim3(static_cast<unsigned>(max_wgs), static_cast<unsigned>(count)), kThreads, 0, s>>>(
+          x, static_cast<int32_t>(rotate ? cols : kpad), static_cast<int32_t>(kpad / CQ_GROUP),
+          static_cast<int32_t>(batch), xvec, ks_shift, a);
       count = 0;
-      wgs = 0;
+      max_wgs = 0;
       return hipGetLastError();
     };
     for (int i = 0; i < n; ++i) {
       const MultiItem &it = items[i];
       if (storage_bits(it.bits) != sb || it.rows <= 0) continue;
       const int64_t t = (it.rows + wg_rows - 1) / wg_rows;
-      if (t > (int64_t{1} << 30) - wgs) return hipErrorInvalidValue;
-      SmallMat &m = a.mat[count];
-      m.packed = it.blob;
-      m.norms = reinterpret_cast<const uint16_t *>(it.blob + it.rows * (kpad * sb / 8));
-      m.y = it.y;
-      m.rows = it.rows;
-      a.wg0[count] = wgs;
+      if (t >= (int64_t{1} << 31)) return hipErrorInvalidValue;
+      a.mat[count] = SmallMat{it.blob, it.y, it.rows, t};
       a.lev[count] = it.lev;
-      wgs += static_cast<int>(t);
+      if (t > max_wgs) max_wgs = t;
       if (++count == kMaxMats) {
         const hipError_t e = flush();
         if (e != hipSuccess) return e;
