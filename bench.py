@@ -17,12 +17,13 @@ re-read while still resident in the 256 MB Infinity Cache.
                 slices of the same matrix, timed on this host
 
 The same JSON line carries secondary figures under "secondary": the other
-widths and batch 8 at the same shape, the 4096 x 16384 x 16384 GEMM on the
+widths and batch 8 at the same shape, the CQ-W2A8 integer product (int8
+activations and code book) at the same shape, the 4096 x 16384 x 16384 GEMM on the
 matrix cores (TFLOP/s), the 16384 x 16384 encoder (GB/s of fp32 input) and
 the Needle-shaped decode sweep (27 layers of 512-wide CQ2 matrices plus the
 8192 x 512 CQ4 logits, per token, eager and replayed from a HIP graph).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only matvec|decode|gemm|encode|all]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only matvec|w2a8|decode|gemm|encode|all]
        python bench.py --calibrate-copy      (counter calibration run)
 """
 import argparse
@@ -51,10 +52,11 @@ def _events(torch, n):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
 
-def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen, fused=True):
+def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen, fused=True, w2a8=False):
     """One step = the rotation and the product of one batch: cq_rotate_matvec
-    (fused=True) or cq_rotate_acts + cq_matvec.  Three copies of the matrix
-    take turns, so no step finds its matrix in the 256 MB Infinity Cache."""
+    (fused=True), cq_rotate_acts + cq_matvec, or the int8 product
+    cq_matvec_w2a8 (w2a8=True).  Three copies of the matrix take turns, so no
+    step finds its matrix in the 256 MB Infinity Cache."""
     rows, cols = master.shape
     levels = cq_inputs.codebook(bits)
     W0 = cq.cq_quantize(master, bits, levels)
@@ -66,7 +68,11 @@ def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen, 
                      device=master.device)
 
     def step(i, ev=None):
-        if fused:
+        if w2a8:
+            if ev is not None:
+                ev[0].record()
+            cq.cq_matvec_w2a8(mats[i % 3], x, out=y)
+        elif fused:
             if ev is not None:
                 ev[0].record()
             cq.cq_rotate_matvec(mats[i % 3], x, out=y, workspace=ws)
@@ -98,7 +104,7 @@ def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen, 
     del mats, W0
     return {"bits": bits, "batch": batch, "bytes": nbytes, "step_s": wall, "kernel_s": sum(times) / steps,
             "kernel_median_s": times[steps // 2], "flop": 2.0 * rows * cols * batch,
-            "call": "cq_rotate_matvec" if fused else "cq_rotate_acts + cq_matvec"}
+            "call": "cq_matvec_w2a8" if w2a8 else ("cq_rotate_matvec" if fused else "cq_rotate_acts + cq_matvec")}
 
 
 def bench_needle_decode(torch, cq, cq_inputs, steps, gen):
@@ -272,7 +278,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--only", choices=["all", "matvec", "decode", "gemm", "encode"], default="all")
+    ap.add_argument("--only", choices=["all", "matvec", "w2a8", "decode", "gemm", "encode"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
@@ -295,9 +301,10 @@ def main():
     result = {}
     secondary = {}
 
-    if args.only in ("all", "matvec"):
+    if args.only in ("all", "matvec", "w2a8"):
         log("generating the 65536 x 16384 fp32 master on the GPU")
         master = torch.randn((ROWS, COLS), generator=gen, device=dev).mul_(0.02)
+    if args.only in ("all", "matvec"):
         head = bench_matvec(torch, cq, cq_inputs, master, 2, 1, args.steps, args.warmup, gen)
         log(f"CQ2 b1: step {head['step_s']*1e6:.1f} us, matvec kernel {head['kernel_s']*1e6:.1f} us")
         result["head"] = head
@@ -318,6 +325,17 @@ def main():
                     r["tflops"] = r["flop"] / r["kernel_median_s"] / 1e12  # fp16 matrix cores, fp32 sums
                 secondary[key] = r
                 log(key, f"{r['kernel_median_s']*1e6:.1f} us (median)", f"{r['gbs']:.0f} GB/s")
+    if args.only in ("all", "w2a8"):
+        # the pages' deployment numerics: int8 activations and code book
+        for bits, batch in [(2, 1), (4, 1), (2, 2)]:
+            r = bench_matvec(torch, cq, cq_inputs, master, bits, batch, max(args.steps // 3, 20),
+                             args.warmup, gen, w2a8=True)
+            key = f"matvec_w2a8_cq{bits}_b{batch}"
+            r["gbs"] = r["bytes"] / r["kernel_median_s"] / 1e9
+            r["frac_hbm_peak"] = r["gbs"] / HBM_PEAK_GBS
+            secondary[key] = r
+            log(key, f"{r['kernel_median_s']*1e6:.1f} us (median)", f"{r['gbs']:.0f} GB/s")
+    if args.only in ("all", "matvec", "w2a8"):
         del master
         torch.cuda.empty_cache()
     if args.only in ("all", "decode"):

@@ -12,8 +12,8 @@ fallback path.
 
 Functions carry the C names: ``cq_blob_bytes``, ``cq_workspace_bytes``,
 ``cq_rotate_acts``, ``cq_matvec``, ``cq_rotate_matvec``,
-``cq_rotate_multi_matvec``, ``cq_rotate_multi_workspace_bytes``, ``cq_gemm``,
-``cq_quantize``.
+``cq_rotate_multi_matvec``, ``cq_rotate_multi_workspace_bytes``,
+``cq_matvec_w2a8``, ``cq_gemm``, ``cq_quantize``.
 """
 import ctypes
 import os
@@ -27,7 +27,7 @@ __all__ = [
     "LIB_PATH", "CQError", "CQMatrix", "CQ_GROUP", "CQ_MAX_MATVEC_BATCH", "workspace_for",
     "cq_version", "cq_blob_bytes", "cq_workspace_bytes",
     "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_multi_matvec",
-    "cq_rotate_multi_workspace_bytes", "cq_gemm", "cq_quantize",
+    "cq_rotate_multi_workspace_bytes", "cq_matvec_w2a8", "cq_gemm", "cq_quantize",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcq.so")
@@ -63,6 +63,7 @@ _SIGS = {
     "cq_rotate_matvec": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_rotate_multi_matvec": (_i32, [_MP, _i32, _vp, _i64, ctypes.POINTER(_vp), _vp, _u64, _vp]),
     "cq_rotate_multi_workspace_bytes": (_i32, [_MP, _i32, _i64, ctypes.POINTER(_u64)]),
+    "cq_matvec_w2a8": (_i32, [_MP, _vp, _i64, _vp, _vp]),
     "cq_gemm": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_quantize": (_i32, [_vp, _i64, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_float), _vp, _u64, _vp]),
 }
@@ -269,6 +270,23 @@ def cq_rotate_multi_matvec(Ws, x, outs=None, workspace=None):
     ys = (_vp * max(len(outs), 1))(*[_dev(o, "out").value for o in outs])
     _check(_lib.cq_rotate_multi_matvec(arr, len(Ws), _dev(x, "x"), b, ys, ws, wsb, _stream()))
     return outs
+
+
+def cq_matvec_w2a8(W, x, out=None):
+    """The CQ-W2A8 product (int8 activations and code book, integer dots, one
+    float multiply per group) of x float32 [batch, cols] (not rotated);
+    returns float32 [batch, rows]."""
+    if x.dtype != torch.float32 or x.dim() != 2 or x.shape[1] != W.cols:
+        raise ValueError("x must be float32 [batch, cols]")
+    x = x.contiguous()
+    b = x.shape[0]
+    if out is None:
+        out = torch.empty((b, W.rows), dtype=torch.float32, device=x.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (b, W.rows):
+        raise ValueError("out must be float32 [batch, rows]")
+    m, keep = W._struct()
+    _check(_lib.cq_matvec_w2a8(ctypes.byref(m), _dev(x, "x"), b, _dev(out, "out"), _stream()))
+    return out
 
 
 def cq_gemm(W, xr, out=None, workspace=None):

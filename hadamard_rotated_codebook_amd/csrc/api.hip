@@ -283,6 +283,44 @@ cq_status cq_rotate_multi_matvec(const cq_matrix *W, int32_t n, const float *x, 
                                                    need ? workspace : nullptr, s));
 }
 
+cq_status cq_matvec_w2a8(const cq_matrix *W, const float *x, int64_t batch, float *y, void *stream) {
+  cq::CodeLevels lev;
+  cq_status st = check_matrix(W, &lev);
+  if (st != CQ_OK) return st;
+  if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+  if (batch == 0 || W->rows == 0) return CQ_OK;
+  const int64_t kpad = padded(W->cols);
+  if (kpad > 0 && !cq::w2a8_fits(kpad, batch)) return CQ_ERR_SHAPE;
+  if (!y) return CQ_ERR_NULL;
+  if (!aligned(y, 4)) return CQ_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kpad == 0) return hip_status(cq::launch_zero_f32(y, batch * W->rows, s));
+  if (!x) return CQ_ERR_NULL;
+  if (!aligned(x, 4)) return CQ_ERR_ALIGN;
+  const uint64_t ybytes = static_cast<uint64_t>(batch) * W->rows * 4;
+  if (overlaps(y, ybytes, x, static_cast<uint64_t>(batch) * W->cols * 4) ||
+      overlaps(y, ybytes, W->blob, W->blob_bytes))
+    return CQ_ERR_OVERLAP;
+  // The int8 code book: maxabs / 127 and round half to even, in fp32 (the
+  // ternary crumbs keep their sign-extended integers, scale a).
+  cq::Int8Codebook cb;
+  std::memset(&cb, 0, sizeof cb);
+  const int nlev = W->bits == 5 ? 4 : 1 << W->bits;
+  int8_t c8[16] = {0};
+  if (W->bits == 5) {
+    c8[0] = 0, c8[1] = 1, c8[2] = -2, c8[3] = -1;
+    cb.sc = cq::ternary_level_f32();
+  } else {
+    float mx = 0.0f;
+    for (int i = 0; i < nlev; ++i) mx = std::fmax(mx, std::fabs(lev.v[i]));
+    cb.sc = mx / 127.0f;
+    for (int i = 0; i < nlev; ++i) c8[i] = static_cast<int8_t>(std::nearbyint(lev.v[i] / cb.sc));
+  }
+  for (int i = 0; i < 16; ++i) cb.c8[i / 4] |= static_cast<uint32_t>(static_cast<uint8_t>(c8[i])) << (8 * (i % 4));
+  return hip_status(cq::launch_w2a8(static_cast<const uint8_t *>(W->blob), W->bits, W->rows, W->cols, kpad, cb, x,
+                                    batch, y, s));
+}
+
 cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c, void *workspace,
                   uint64_t workspace_bytes, void *stream) {
   (void)workspace;

@@ -99,6 +99,20 @@ uint64_t rotate_multi_workspace_bytes(const MultiItem *items, int n, int64_t kpa
 hipError_t launch_rotate_multi_matvec(const MultiItem *items, int n, const float *x, int64_t cols, int64_t kpad,
                                       int64_t batch, void *workspace, hipStream_t s);
 
+// The CQ-W2A8 product: int8 code book (byte c % 4 of c8[c / 4] is the int8
+// value of stored code c) and its scale.
+struct Int8Codebook {
+  uint32_t c8[4];
+  float sc;
+};
+// LDS of one W2A8 workgroup: (batch + 1) x cols_pad int8 activations and the
+// group scales; the kernel takes at most kW2a8MaxLds.
+constexpr uint64_t kW2a8MaxLds = 60 * 1024;
+uint64_t w2a8_lds_bytes(int64_t kpad, int64_t batch);
+bool w2a8_fits(int64_t kpad, int64_t batch);
+hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t cols, int64_t kpad, const Int8Codebook &cb,
+                       const float *x, int64_t batch, float *y, hipStream_t s);
+
 // y[i] = sum over s < nslice, in order, of partial[s * n + i].
 hipError_t launch_combine(const float *partial, int64_t n, int nslice, float *y, hipStream_t s);
 

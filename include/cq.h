@@ -243,6 +243,40 @@ cq_status cq_rotate_multi_workspace_bytes(const cq_matrix *W, int32_t n, int64_t
                                           uint64_t *bytes);
 
 /*
+ * CQ-W2A8 decode product: int8 activations and an int8 code book, integer dot
+ * products, one float multiply per group (".cact" format post, "How the
+ * kernel reads it": the rotated activation group is quantised to int8 with
+ * one scale per group, int8 centroids are looked up by the packed indices,
+ * and each group's dot is multiplied by the weight norm, the activation scale
+ * and the codebook scale; OpenNeedle reference notes, Cactus 2-bit kernel):
+ *
+ *   xr  = H . x per group, fp32 (the butterfly of cq_rotate_acts)
+ *   sx  = fp32(max |xr| over the group / 127)
+ *   xq  = clamp(round_half_even(fp32(xr / sx)), -128, 127)   (0 where sx == 0)
+ *   sc  = fp32(max |level| / 127), c8 = round_half_even(fp32(level / sc));
+ *         ternary: c8 = the crumb's integer (0, 1, -2, -1), sc = the level a
+ *   y[b][r] = sum_g (float(norm[r][g]) * sx[b][g] * sc) * sum_j c8[q] * xq
+ *
+ * The integer sums are exact; the per-group products and the sum over groups
+ * are fp32.  This is the pages' deployment arithmetic, not the fp32-accurate
+ * product of cq_matvec: its error against that product is the int8
+ * quantisation of the activation and the code book (about 1 % of |y|).
+ *
+ *   W        matrix descriptor
+ *   x        device fp32 [batch][W.cols], not rotated, 4-byte aligned (16-byte
+ *            alignment and W.cols % 8 == 0 allow vector loads); not modified
+ *   batch    0 <= batch <= CQ_MAX_MATVEC_BATCH, and
+ *            (batch + 1) * cols_pad + 32 * cols_pad / 128 <= 61440 (one
+ *            workgroup holds the whole quantised activation), e.g. cols_pad
+ *            up to 16384 at batch 1 or 2 and 6528 at batch 8; CQ_ERR_SHAPE
+ *            otherwise
+ *   y        device fp32 [batch][W.rows], 4-byte aligned, must not overlap x
+ *            or the blob; fully overwritten (0 where cols == 0)
+ *   No workspace.  Errors as cq_matvec.
+ */
+cq_status cq_matvec_w2a8(const cq_matrix *W, const float *x, int64_t batch, float *y, void *stream);
+
+/*
  * Prefill product on the bf16 matrix cores, fp32 accumulation:
  *
  *   C[m][r] = sum_k Xr[m][k] * V[r][k],  V[r][g*128+j] = bf16(c[q] * float(norm[r][g]))

@@ -41,7 +41,7 @@ import numpy as np
 from .cq import GROUP, TERNARY_MARKER, codebook_for, padded_cols, split_blob, ternary_level32, unpack_codes
 
 __all__ = ["INV_SQRT_GROUP_F32", "rotate_acts_fp32", "quantize_acts_int8", "codebook_int8",
-           "w2a8_from_quantized", "matvec_w2a8"]
+           "w2a8_group_terms", "w2a8_from_quantized", "matvec_w2a8"]
 
 INV_SQRT_GROUP_F32 = np.float32(1.0 / math.sqrt(GROUP))
 """fp32(1/sqrt(128)), the one scaling multiply of the butterfly (R14)."""
@@ -105,11 +105,10 @@ def codebook_int8(bits, levels=None, group=GROUP):
     return c8, sc
 
 
-def w2a8_from_quantized(blob, bits, rows, cols, xq, sx, levels=None, group=GROUP, row_ids=None):
-    """y[b, r] = sum_g (float(n[r, g]) * sx[b, g] * sc) * sum_k c8[q[r, g, k]] * xq[b, g, k]
-    from already quantised activations: the integer dot exact (int64), the
-    scaling and the sum over groups in float64 [cact-format post, "How the
-    kernel reads it"]."""
+def w2a8_group_terms(blob, bits, rows, cols, xq, sx, levels=None, group=GROUP, row_ids=None):
+    """The per-group terms (float(n[r, g]) * sx[b, g] * sc) * sum_k c8[q[r, g, k]] * xq[b, g, k],
+    float64 [batch, rows, groups]: the integer dot exact (int64), the scaling
+    in float64 [cact-format post, "How the kernel reads it"]."""
     packed, norms = split_blob(blob, bits, rows, cols, group)
     if row_ids is not None:
         packed, norms = packed[row_ids], norms[row_ids]
@@ -125,7 +124,12 @@ def w2a8_from_quantized(blob, bits, rows, cols, xq, sx, levels=None, group=GROUP
         dots[:, :, g] = xq[:, g, :] @ w8[:, g, :].T
     scale = (norms.astype(np.float32).astype(np.float64)[None, :, :]
              * np.asarray(sx, dtype=np.float64).reshape(nb, 1, ng) * float(sc))
-    return np.sum(scale * dots.astype(np.float64), axis=-1)
+    return scale * dots.astype(np.float64)
+
+
+def w2a8_from_quantized(blob, bits, rows, cols, xq, sx, levels=None, group=GROUP, row_ids=None):
+    """y[b, r] = the sum over groups of ``w2a8_group_terms``, float64."""
+    return np.sum(w2a8_group_terms(blob, bits, rows, cols, xq, sx, levels, group, row_ids), axis=-1)
 
 
 def matvec_w2a8(blob, bits, rows, cols, x, levels=None, group=GROUP, row_ids=None):

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     names = _declared_functions()
     assert set(names) == {"cq_version", "cq_status_string", "cq_blob_bytes", "cq_workspace_bytes",
                           "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_multi_matvec",
-                          "cq_rotate_multi_workspace_bytes", "cq_gemm", "cq_quantize"}
+                          "cq_rotate_multi_workspace_bytes", "cq_matvec_w2a8", "cq_gemm", "cq_quantize"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -221,6 +221,37 @@ def test_rotate_multi_matvec_validation():
     assert _multi([q4, big4], ws=FAKE + (1 << 31), wsb=nb) == OVERLAP  # workspace on y[0]
 
 
+def _w2a8(m, x=FAKE + (1 << 30), batch=1, y=FAKE + (1 << 31)):
+    return lib.cq_matvec_w2a8(ctypes.byref(m), ctypes.c_void_p(x), batch, ctypes.c_void_p(y), None)
+
+
+def test_matvec_w2a8_validation():
+    m, k = _matrix(bits=7, nbytes=0, levels=None)
+    assert _w2a8(m) == BITS
+    m, k = _matrix(levels=np.array([0.1, 0.0, 0.2, 0.3]))
+    assert _w2a8(m) == CODEBOOK
+    m, k = _matrix(nbytes=10)
+    assert _w2a8(m) == LENGTH
+    m, k = _matrix()
+    assert _w2a8(m, batch=9) == SHAPE and _w2a8(m, batch=-1) == SHAPE
+    assert _w2a8(m, batch=0) == OK
+    assert _w2a8(m, x=0) == NULL and _w2a8(m, y=0) == NULL
+    assert _w2a8(m, x=FAKE + (1 << 30) + 2) == ALIGN and _w2a8(m, y=FAKE + (1 << 31) + 1) == ALIGN
+    assert _w2a8(m, y=FAKE + (1 << 30) + 8) == OVERLAP and _w2a8(m, y=FAKE + 64) == OVERLAP
+    # the whole quantised activation fits one workgroup: 16384 columns at
+    # batch 1 and 2, not 3; 6528 at batch 8, not 6656
+    wide, _ = _matrix(rows=4, cols=16384)
+    assert _w2a8(wide, batch=3) == SHAPE
+    assert _w2a8(wide, batch=2, y=0) == NULL  # past the shape check
+    b8, _ = _matrix(rows=4, cols=6528)
+    assert _w2a8(b8, batch=8, y=0) == NULL
+    b8x, _ = _matrix(rows=4, cols=6656)
+    assert _w2a8(b8x, batch=8) == SHAPE
+    # nothing to do
+    z, _ = _matrix(rows=0, blob=0)
+    assert _w2a8(z) == OK
+
+
 def test_nothing_to_do_returns_ok_without_launching():
     m, k = _matrix()
     assert _matvec(m, batch=0) == OK and _gemm(m, mm=0) == OK
@@ -317,5 +348,6 @@ def test_workspace_bytes():
 
 def test_binding_has_the_c_names():
     for n in ("cq_blob_bytes", "cq_workspace_bytes", "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec",
-              "cq_rotate_multi_matvec", "cq_rotate_multi_workspace_bytes", "cq_gemm", "cq_quantize"):
+              "cq_rotate_multi_matvec", "cq_rotate_multi_workspace_bytes", "cq_matvec_w2a8", "cq_gemm",
+              "cq_quantize"):
         assert callable(getattr(cq, n))

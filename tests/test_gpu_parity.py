@@ -365,6 +365,78 @@ def test_needle_layer_multi_and_graph():
     del g
 
 
+# ------------------------------------------------------------ W2A8 (int8)
+
+def _check_w2a8(y, blob, bits, rows, cols, x, levels, row_ids=None):
+    # integer dots exact on both sides, same int8 decisions: the GPU's fp32
+    # per-group products and sums are within (groups + 8) * 2^-23 of the sum
+    # of the terms' magnitudes (twice the fp32 accumulation bound)
+    xq, sx = oracle.quantize_acts_int8(oracle.rotate_acts_fp32(x))
+    terms = oracle.w2a8_group_terms(blob, bits, rows, cols, xq, sx, levels, row_ids=row_ids)
+    ref = terms.sum(-1)
+    bound = (terms.shape[-1] + 8) * 2.0 ** -23 * np.abs(terms).sum(-1) + 1e-30
+    err = np.abs(y.astype(np.float64) - ref)
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
+
+
+def test_rotation_is_the_oracle_butterfly_bit_for_bit():
+    # the int8 decisions of W2A8 take the fp32 rotation; the GPU's butterfly
+    # and the oracle's fp32 butterfly must agree in every bit
+    for batch, cols in ((1, 512), (3, 1000), (2, 16384)):
+        x = cq_inputs.activations(90, cols, batch, cols)
+        got = cq.cq_rotate_acts(_to_dev(x)).cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), oracle.rotate_acts_fp32(x).view(np.uint32)), (batch, cols)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("rows,cols,batch", [
+    (512, 512, 1), (300, 1000, 3), (257, 2048, 2), (64, 640, 8), (1, 128, 1),
+    (1000, 16384, 1), (9, 16384, 2), (33, 6528, 8), (130, 5000, 4),
+])
+def test_matvec_w2a8(bits, rows, cols, batch):
+    say("w2a8", bits, rows, cols, batch)
+    W, blob = _random_cq(bits, rows, cols, 91 + batch)
+    levels = _levels(bits)
+    x = cq_inputs.activations(92, rows, batch, cols)
+    y = cq.cq_matvec_w2a8(W, _to_dev(x)).cpu().numpy()
+    _check_w2a8(y, blob, bits, rows, cols, x, levels)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_matvec_w2a8_full_size_sampled_rows(bits):
+    # the 65536 x 16384 workload in the benchmark's launch configuration;
+    # the oracle on sampled rows
+    rows, cols = 65536, 16384
+    say("w2a8 full size", bits)
+    W, blob = _random_cq(bits, rows, cols, 93)
+    levels = _levels(bits)
+    pick = cq_inputs.sample_rows(93, bits, rows, 48)
+    sub = _row_subset(blob, bits, rows, cols, pick)
+    x = cq_inputs.activations(93, bits, 1, cols)
+    y = cq.cq_matvec_w2a8(W, _to_dev(x)).cpu().numpy()
+    _check_w2a8(y[:, pick], sub, bits, len(pick), cols, x, levels)
+    del W
+    torch.cuda.empty_cache()
+
+
+def test_matvec_w2a8_degenerate_and_limits():
+    W, blob = _random_cq(2, 70, 256, 94)
+    x = _to_dev(cq_inputs.activations(94, 0, 2, 256))
+    assert cq.cq_matvec_w2a8(W, x[:0]).shape == (0, 70)
+    # an all-zero activation: every group scale is 0 and so is y
+    assert torch.equal(cq.cq_matvec_w2a8(W, torch.zeros_like(x)), torch.zeros((2, 70), device=DEV))
+    Wz = cq.CQMatrix(4, 3, 0, torch.empty(0, dtype=torch.uint8, device=DEV), _levels(4))
+    y = torch.full((2, 3), float("nan"), device=DEV)
+    cq.cq_matvec_w2a8(Wz, torch.empty((2, 0), device=DEV), out=y)
+    assert torch.equal(y, torch.zeros_like(y))
+    Wb, _ = _random_cq(2, 8, 16384, 95)
+    with pytest.raises(cq.CQError) as e:
+        cq.cq_matvec_w2a8(Wb, torch.zeros((3, 16384), device=DEV))
+    assert e.value.status == 4  # CQ_ERR_SHAPE: the quantised activation exceeds one workgroup's LDS
+    a = cq.cq_matvec_w2a8(W, x).clone()
+    assert torch.equal(a, cq.cq_matvec_w2a8(W, x))  # deterministic
+
+
 def test_needle_decode_sweep_shapes():
     # the Needle-shaped decode workload at batch 1: 27 layers of Q 512x512,
     # K and V 256x512, gate and out 512x512 at CQ2 -- one rotated activation
