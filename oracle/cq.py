@@ -19,7 +19,7 @@ __all__ = [
     "ternary_level32", "codebook_for",
     "rotate_fp32", "nearest_level", "encode", "quantize",
     "pack_codes", "unpack_codes", "make_blob", "split_blob",
-    "level_values", "dequantize", "rotate_acts",
+    "level_values", "dequantize", "gather_rows", "rotate_acts",
     "matvec", "gemm", "bf16_round", "gemm_bf16",
 ]
 
@@ -396,6 +396,23 @@ def dequantize(blob, bits, rows, cols, levels=None, group=GROUP, row_ids=None):
     vals = level_values(unpack_codes(packed, bits, kpad), bits, levels, group)
     rotated = vals.reshape(n, ng, group) * norms.astype(np.float32).astype(np.float64)[..., None]
     return (rotated @ hadamard(group)).reshape(n, kpad)
+
+
+def gather_rows(blob, bits, rows, cols, ids, levels=None, group=GROUP):
+    """Dense rows ``ids`` of the reconstruction, float64 [len(ids), cols].
+
+    A row gather (embedding and engram tables) reconstructs the dense groups
+    of the indexed rows only: rotated = codebook[index] * norm, dense group =
+    rotated . H [needle.js tutorial, "Reconstructing one group" and "Keep the
+    quantized views"; OpenNeedle reference, engine notes].  Reading: an id
+    outside [0, rows) gives a row of NaN (the call refuses to invent a row).
+    """
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    out = np.full((ids.size, cols), np.nan)
+    ok = (ids >= 0) & (ids < rows)
+    if np.any(ok):
+        out[ok] = dequantize(blob, bits, rows, cols, levels, group, row_ids=ids[ok])[:, :cols]
+    return out
 
 
 def _pad(x, group):

@@ -135,3 +135,36 @@ def test_bf16_variant_within_analytic_bound(bits):
 def test_ternary_crumbs_sign_extend():
     a = float(oracle.ternary_level32())
     assert oracle.level_values(np.array([0, 1, 2, 3]), 5).tolist() == [0.0, a, -2 * a, -a]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+def test_gather_rows_by_definition(bits):
+    # each gathered element by explicit loops over the Sylvester matrix:
+    # w_hat[r, 128 g + k] = sum_j c[q[r, 128 g + j]] * n[r, g] * S[j, k] / sqrt(128)
+    rows, cols = 5, 200
+    blob, levels, _ = _blob(96, bits, rows, cols)
+    ids = [4, 0, 4, -1, 5, 2]
+    got = oracle.gather_rows(blob, bits, rows, cols, ids, levels)
+    packed, norms = oracle.split_blob(blob, bits, rows, cols)
+    codes = oracle.unpack_codes(packed, bits, 256)
+    S = oracle.sylvester(128)
+    for i, r in enumerate(ids):
+        if not 0 <= r < rows:
+            assert np.all(np.isnan(got[i]))  # ids outside the matrix give NaN rows
+            continue
+        vals = oracle.level_values(codes[r], bits, levels)
+        for k in range(0, cols, 37):
+            g, kk = divmod(k, 128)
+            want = sum(vals[128 * g + j] * float(np.float32(norms[r, g])) * S[j, kk] for j in range(128))
+            assert abs(got[i, k] - want / np.sqrt(128)) <= 1e-12
+    assert np.array_equal(got[0], got[2])  # a repeated id repeats the row
+
+
+def test_gather_rows_times_x_is_the_matvec():
+    rows, cols = 9, 300
+    blob, levels, _ = _blob(97, 2, rows, cols)
+    x = cq_inputs.activations(97, 0, 2, cols)
+    ids = np.array([8, 3, 3, 0])
+    g = oracle.gather_rows(blob, 2, rows, cols, ids, levels)
+    y = oracle.matvec(blob, 2, rows, cols, x, levels)
+    assert np.allclose(x.astype(np.float64) @ g.T, y[:, ids], rtol=1e-12, atol=1e-12)
