@@ -21,7 +21,8 @@ widths and batch 8 at the same shape, the CQ-W2A8 integer product (int8
 activations and code book) at the same shape, the 4096 x 16384 x 16384 GEMM on the
 matrix cores (TFLOP/s), the 16384 x 16384 encoder (GB/s of fp32 input) and
 the Needle-shaped decode sweep (27 layers of 512-wide CQ2 matrices plus the
-8192 x 512 CQ4 logits, per token, eager and replayed from a HIP graph).
+8192 x 512 CQ4 logits, per token, eager and replayed from a HIP graph), and
+the tied-embedding row gather (2048 ids from the 8192 x 512 CQ4 matrix).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only matvec|w2a8|decode|gemm|encode|all]
        python bench.py --calibrate-copy      (counter calibration run)
@@ -174,6 +175,30 @@ def bench_needle_decode(torch, cq, cq_inputs, steps, gen):
         out[name] = {"calls_per_token": calls, "eager_us_per_token": eager * 1e6, "graph_us_per_token": graph * 1e6,
                      "graph_gbs": nbytes / graph / 1e9}
     return out
+
+
+def bench_gather(torch, cq, cq_inputs, gen, steps=50):
+    """The tied-embedding lookup of a Needle-shaped decode: 2048 token ids
+    gathered from the 8192 x 512 CQ4 matrix as fp32 rows (cq_gather_rows)."""
+    dev = torch.device("cuda:0")
+    w = torch.randn((8192, 512), generator=gen, device=dev).mul_(0.02)
+    W = cq.cq_quantize(w, 4, cq_inputs.codebook(4))
+    ids = torch.randint(0, 8192, (2048,), generator=gen, device=dev)
+    out = torch.empty((2048, 512), device=dev)
+    for _ in range(5):
+        cq.cq_gather_rows(W, ids, out=out)
+    torch.cuda.synchronize()
+    ev = _events(torch, steps)
+    for i in range(steps):
+        ev[i][0].record()
+        cq.cq_gather_rows(W, ids, out=out)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) / 1e3 for a, b in ev)[steps // 2]
+    row_bytes = W.blob.numel() // 8192
+    moved = 2048 * (row_bytes + 512 * 4)  # packed row + norms read, fp32 row written
+    return {"rows": 2048, "cols": 512, "bits": 4, "kernel_median_s": t, "rows_per_s": 2048 / t,
+            "gbs": moved / t / 1e9}
 
 
 def bench_gemm(torch, cq, cq_inputs, master, bits, m, steps, warmup, gen):
@@ -344,6 +369,9 @@ def main():
         for k in ("per_call", "shared_activation"):
             log(f"needle decode token, {k}: {r[k]['eager_us_per_token']:.0f} us eager, "
                 f"{r[k]['graph_us_per_token']:.0f} us graph")
+        r = bench_gather(torch, cq, cq_inputs, gen)
+        secondary["gather_cq4_8192x512_2048_rows"] = r
+        log(f"gather 2048 rows of 8192x512 CQ4: {r['kernel_median_s']*1e6:.1f} us, {r['gbs']:.0f} GB/s")
 
     if args.only in ("all", "gemm", "encode"):
         log("generating the 16384 x 16384 fp32 master on the GPU")

@@ -13,7 +13,7 @@ fallback path.
 Functions carry the C names: ``cq_blob_bytes``, ``cq_workspace_bytes``,
 ``cq_rotate_acts``, ``cq_matvec``, ``cq_rotate_matvec``,
 ``cq_rotate_multi_matvec``, ``cq_rotate_multi_workspace_bytes``,
-``cq_matvec_w2a8``, ``cq_gemm``, ``cq_quantize``.
+``cq_matvec_w2a8``, ``cq_gather_rows``, ``cq_gemm``, ``cq_quantize``.
 """
 import ctypes
 import os
@@ -27,7 +27,7 @@ __all__ = [
     "LIB_PATH", "CQError", "CQMatrix", "CQ_GROUP", "CQ_MAX_MATVEC_BATCH", "workspace_for",
     "cq_version", "cq_blob_bytes", "cq_workspace_bytes",
     "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_multi_matvec",
-    "cq_rotate_multi_workspace_bytes", "cq_matvec_w2a8", "cq_gemm", "cq_quantize",
+    "cq_rotate_multi_workspace_bytes", "cq_matvec_w2a8", "cq_gather_rows", "cq_gemm", "cq_quantize",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcq.so")
@@ -64,6 +64,7 @@ _SIGS = {
     "cq_rotate_multi_matvec": (_i32, [_MP, _i32, _vp, _i64, ctypes.POINTER(_vp), _vp, _u64, _vp]),
     "cq_rotate_multi_workspace_bytes": (_i32, [_MP, _i32, _i64, ctypes.POINTER(_u64)]),
     "cq_matvec_w2a8": (_i32, [_MP, _vp, _i64, _vp, _vp]),
+    "cq_gather_rows": (_i32, [_MP, _vp, _i64, _vp, _i32, _vp]),
     "cq_gemm": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_quantize": (_i32, [_vp, _i64, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_float), _vp, _u64, _vp]),
 }
@@ -286,6 +287,25 @@ def cq_matvec_w2a8(W, x, out=None):
         raise ValueError("out must be float32 [batch, rows]")
     m, keep = W._struct()
     _check(_lib.cq_matvec_w2a8(ctypes.byref(m), _dev(x, "x"), b, _dev(out, "out"), _stream()))
+    return out
+
+
+def cq_gather_rows(W, ids, out_dtype=torch.float32, out=None):
+    """Dense rows ``ids`` (int64 device tensor [n]) of the reconstruction;
+    returns [n, cols] of out_dtype (float32, float16 or bfloat16).  Ids
+    outside the matrix give rows of NaN."""
+    if ids.dtype != torch.int64 or ids.dim() != 1:
+        raise ValueError("ids must be an int64 vector")
+    if out_dtype not in _DTYPES:
+        raise TypeError("out_dtype must be float32, float16 or bfloat16")
+    n = ids.shape[0]
+    if out is None:
+        out = torch.empty((n, W.cols), dtype=out_dtype, device=ids.device)
+    if out.dtype not in _DTYPES or tuple(out.shape) != (n, W.cols):
+        raise ValueError("out must be [n, cols] of float32, float16 or bfloat16")
+    m, keep = W._struct()
+    _check(_lib.cq_gather_rows(ctypes.byref(m), _dev(ids.contiguous(), "ids"), n, _dev(out, "out"),
+                               _DTYPES[out.dtype], _stream()))
     return out
 
 

@@ -321,6 +321,24 @@ cq_status cq_matvec_w2a8(const cq_matrix *W, const float *x, int64_t batch, floa
                                     batch, y, s));
 }
 
+cq_status cq_gather_rows(const cq_matrix *W, const int64_t *ids, int64_t n, void *out, int32_t out_dtype,
+                         void *stream) {
+  cq::CodeLevels lev;
+  cq_status st = check_matrix(W, &lev);
+  if (st != CQ_OK) return st;
+  if (out_dtype != CQ_F32 && out_dtype != CQ_F16 && out_dtype != CQ_BF16) return CQ_ERR_DTYPE;
+  if (n < 0 || n > CQ_MAX_DIM) return CQ_ERR_SHAPE;
+  if (n == 0 || W->cols == 0) return CQ_OK;
+  if (!ids || !out) return CQ_ERR_NULL;
+  if (!aligned(ids, 8) || !aligned(out, dtype_size(out_dtype))) return CQ_ERR_ALIGN;
+  const uint64_t obytes = static_cast<uint64_t>(n) * W->cols * dtype_size(out_dtype);
+  if (overlaps(out, obytes, ids, static_cast<uint64_t>(n) * 8) || overlaps(out, obytes, W->blob, W->blob_bytes))
+    return CQ_ERR_OVERLAP;
+  return hip_status(cq::launch_gather(static_cast<const uint8_t *>(W->blob), W->bits, W->rows, W->cols,
+                                      padded(W->cols), lev, ids, n, out, out_dtype,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c, void *workspace,
                   uint64_t workspace_bytes, void *stream) {
   (void)workspace;

@@ -113,6 +113,12 @@ bool w2a8_fits(int64_t kpad, int64_t batch);
 hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t cols, int64_t kpad, const Int8Codebook &cb,
                        const float *x, int64_t batch, float *y, hipStream_t s);
 
+// Row gather: out[i][k] = w_hat[ids[i]][k] (k < cols) in out_dtype; NaN rows
+// for ids outside [0, rows).
+hipError_t launch_gather(const uint8_t *blob, int bits, int64_t rows, int64_t cols, int64_t kpad,
+                         const CodeLevels &lev, const int64_t *ids, int64_t n, void *out, int out_dtype,
+                         hipStream_t s);
+
 // y[i] = sum over s < nslice, in order, of partial[s * n + i].
 hipError_t launch_combine(const float *partial, int64_t n, int nslice, float *y, hipStream_t s);
 

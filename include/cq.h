@@ -277,6 +277,28 @@ cq_status cq_rotate_multi_workspace_bytes(const cq_matrix *W, int32_t n, int64_t
 cq_status cq_matvec_w2a8(const cq_matrix *W, const float *x, int64_t batch, float *y, void *stream);
 
 /*
+ * Row gather: the dense reconstruction of the indexed rows only (needle.js
+ * tutorial, "Reconstructing one group": a row gather, for embeddings and
+ * engram tables, reconstructs the dense group; "Keep the quantized views":
+ * dequantise only the rows you need):
+ *
+ *   out[i][k] = w_hat[ids[i]][k],  k < W.cols,
+ *   w_hat group = (c[q] * float(norm)) . H   (fp32: the level times the
+ *                 norm, the butterfly of cq_rotate_acts, H being its own inverse)
+ *
+ *   W          matrix descriptor
+ *   ids        device int64 [n], 8-byte aligned; an id outside [0, W.rows)
+ *              gives a row of NaN (nothing outside the blob is read)
+ *   n          0 <= n <= CQ_MAX_DIM (0: nothing is done)
+ *   out        device [n][W.cols] of out_dtype (CQ_F32, CQ_F16 or CQ_BF16,
+ *              rounded to nearest even), aligned to its element size; must not
+ *              overlap ids or the blob; fully overwritten
+ *   Errors as cq_matvec, and CQ_ERR_DTYPE for another out_dtype.
+ */
+cq_status cq_gather_rows(const cq_matrix *W, const int64_t *ids, int64_t n, void *out, int32_t out_dtype,
+                         void *stream);
+
+/*
  * Prefill product on the bf16 matrix cores, fp32 accumulation:
  *
  *   C[m][r] = sum_k Xr[m][k] * V[r][k],  V[r][g*128+j] = bf16(c[q] * float(norm[r][g]))

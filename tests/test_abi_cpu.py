@@ -29,7 +29,8 @@ def test_every_declared_symbol_is_exported():
     names = _declared_functions()
     assert set(names) == {"cq_version", "cq_status_string", "cq_blob_bytes", "cq_workspace_bytes",
                           "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_multi_matvec",
-                          "cq_rotate_multi_workspace_bytes", "cq_matvec_w2a8", "cq_gemm", "cq_quantize"}
+                          "cq_rotate_multi_workspace_bytes", "cq_matvec_w2a8", "cq_gather_rows", "cq_gemm",
+                          "cq_quantize"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -252,6 +253,28 @@ def test_matvec_w2a8_validation():
     assert _w2a8(z) == OK
 
 
+def _gather(m, ids=FAKE + (1 << 30), n=4, out=FAKE + (1 << 31), dt=0):
+    return lib.cq_gather_rows(ctypes.byref(m), ctypes.c_void_p(ids), n, ctypes.c_void_p(out), dt, None)
+
+
+def test_gather_rows_validation():
+    m, k = _matrix(bits=7, nbytes=0, levels=None)
+    assert _gather(m) == BITS
+    m, k = _matrix(levels=np.array([0.1, 0.0, 0.2, 0.3]))
+    assert _gather(m) == CODEBOOK
+    m, k = _matrix()
+    assert _gather(m, dt=3) == DTYPE and _gather(m, dt=-1) == DTYPE
+    assert _gather(m, n=-1) == SHAPE and _gather(m, n=(1 << 30) + 1) == SHAPE
+    assert _gather(m, n=0) == OK
+    assert _gather(m, ids=0) == NULL and _gather(m, out=0) == NULL
+    assert _gather(m, ids=FAKE + (1 << 30) + 4) == ALIGN
+    assert _gather(m, out=FAKE + (1 << 31) + 2) == ALIGN and _gather(m, out=FAKE + (1 << 31) + 1, dt=2) == ALIGN
+    assert _gather(m, out=FAKE + (1 << 30) + 16) == OVERLAP  # out on top of ids
+    assert _gather(m, out=FAKE + 32) == OVERLAP  # out on top of the blob
+    z, _ = _matrix(rows=4, cols=0)
+    assert _gather(z) == OK  # no columns: nothing to write
+
+
 def test_nothing_to_do_returns_ok_without_launching():
     m, k = _matrix()
     assert _matvec(m, batch=0) == OK and _gemm(m, mm=0) == OK
@@ -348,6 +371,6 @@ def test_workspace_bytes():
 
 def test_binding_has_the_c_names():
     for n in ("cq_blob_bytes", "cq_workspace_bytes", "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec",
-              "cq_rotate_multi_matvec", "cq_rotate_multi_workspace_bytes", "cq_matvec_w2a8", "cq_gemm",
-              "cq_quantize"):
+              "cq_rotate_multi_matvec", "cq_rotate_multi_workspace_bytes", "cq_matvec_w2a8", "cq_gather_rows",
+              "cq_gemm", "cq_quantize"):
         assert callable(getattr(cq, n))

@@ -437,6 +437,49 @@ def test_matvec_w2a8_degenerate_and_limits():
     assert torch.equal(a, cq.cq_matvec_w2a8(W, x))  # deterministic
 
 
+# ------------------------------------------------------------- row gather
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("rows,cols", [(8192, 512), (300, 1000), (17, 128), (5, 16384), (40, 77)])
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16, torch.float16])
+def test_gather_rows(bits, rows, cols, odt):
+    # the embedding lookup of a tied CQ matrix: rows by id, repeated and
+    # out-of-range ids included (NaN rows), against the oracle
+    say("gather", bits, rows, cols, odt)
+    W, blob = _random_cq(bits, rows, cols, 97)
+    levels = _levels(bits)
+    rng = np.random.default_rng(bits * 1000 + rows)
+    ids = np.concatenate([rng.integers(0, rows, size=37), [0, rows - 1, rows - 1, -1, rows]])
+    got = cq.cq_gather_rows(W, _to_dev(ids.astype(np.int64)), odt).float().cpu().numpy().astype(np.float64)
+    ref = oracle.gather_rows(blob, bits, rows, cols, ids, levels)
+    bad = (ids < 0) | (ids >= rows)
+    assert np.all(np.isnan(got[bad])) and not np.any(np.isnan(got[~bad]))
+    # fp32: the rounding of the level x norm products and of the butterfly's
+    # sums, within 2^-16 of the group's L1 norm / sqrt(128); 16-bit outputs add
+    # one rounding of the value (2^-8 bf16, 2^-11 fp16)
+    packed, norms = oracle.split_blob(blob, bits, rows, cols)
+    kpad = oracle.padded_cols(cols)
+    vals = oracle.level_values(oracle.unpack_codes(packed[ids[~bad]], bits, kpad), bits, levels)
+    l1 = np.abs(vals).reshape(-1, kpad // 128, 128).sum(-1) * norms[ids[~bad]].astype(np.float64)
+    bound = 2.0 ** -16 * np.repeat(l1, 128, axis=1)[:, :cols] / np.sqrt(128)
+    rel = {torch.float32: 0.0, torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}[odt]
+    bound = bound + rel * np.abs(ref[~bad])
+    assert np.all(np.abs(got[~bad] - ref[~bad]) <= bound + 1e-30)
+
+
+def test_gather_rows_empty_and_consistent_with_the_product():
+    W, blob = _random_cq(4, 64, 300, 98)
+    assert cq.cq_gather_rows(W, torch.empty(0, dtype=torch.int64, device=DEV)).shape == (0, 300)
+    ids = torch.arange(64, dtype=torch.int64, device=DEV)
+    dense = cq.cq_gather_rows(W, ids)
+    x = _to_dev(cq_inputs.activations(98, 0, 2, 300))
+    # the gathered dense matrix reproduces the product of the packed one,
+    # within the matvec's fp32-path bar (1e-4 * |w_hat_row| * |x|)
+    y = cq.cq_matvec(W, cq.cq_rotate_acts(x))
+    bound = 1e-4 * torch.outer(x.norm(dim=1), dense.norm(dim=1))
+    assert torch.all((x @ dense.T - y).abs() <= bound)
+
+
 def test_needle_decode_sweep_shapes():
     # the Needle-shaped decode workload at batch 1: 27 layers of Q 512x512,
     # K and V 256x512, gate and out 512x512 at CQ2 -- one rotated activation
