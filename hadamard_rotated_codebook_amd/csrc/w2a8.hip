@@ -113,6 +113,46 @@ __device__ inline float row16_max(float m) {
   return m;
 }
 
+// The activation into LDS: each (batch row, group) is rotated by 16 lanes
+// (the shared butterfly), its absmax found, its values quantised to int8 and
+// stored in the decoders' slot order (xq [batch][kpad]), and its scale
+// stored at sxs[g * 8 + b].  All threads of the workgroup call it.
+template <int SB, int NT>
+__device__ inline void stage_int8(const float *x, int64_t cols, bool xvec, int batch, int ngroups, uint8_t *xq,
+                                  float *sxs) {
+  const int tid = threadIdx.x, j = tid & 15;
+  const int64_t kpad = static_cast<int64_t>(ngroups) * CQ_GROUP;
+  const int tasks = batch * ngroups;
+  for (int t0 = 0; t0 < tasks; t0 += NT / 16) {  // uniform trip count: all lanes run the exchanges
+    const int task = t0 + (tid >> 4);
+    const bool valid = task < tasks;
+    const int b = valid ? task / ngroups : 0, g = valid ? task % ngroups : 0;
+    float v[8];
+    load8_f32(x + static_cast<int64_t>(b) * cols, static_cast<int64_t>(g) * CQ_GROUP + 8 * j, valid ? cols : 0, xvec,
+              v);
+    fwht128_unscaled(v, j);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] *= kInvSqrt128;
+      m = fmaxf(m, fabsf(v[i]));
+    }
+    m = row16_max(m);
+    const float sx = m / 127.0f;
+    if (valid) {
+      uint8_t *dst = xq + static_cast<int64_t>(b) * kpad + static_cast<int64_t>(g) * CQ_GROUP;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = 8 * j + i;  // element of the group
+        int qv = 0;
+        if (sx > 0.0f) qv = static_cast<int>(fminf(fmaxf(rintf(v[i] / sx), -128.0f), 127.0f));
+        dst[(e & ~15) + code_slot<SB>(e & 15)] = static_cast<uint8_t>(qv);
+      }
+      if (j == 0) sxs[g * 8 + b] = sx;
+    }
+  }
+}
+
 // LDS: int8 activations [kMaxBatch + 1 rows][kpad] (row `batch` is zero for
 // the padding lanes), then the group scales [ngroups][8] (fp32).
 template <int SB>
@@ -169,43 +209,10 @@ __global__ __launch_bounds__(kThreads) void w2a8_kernel(W8Args a) {
   using Set1 = std::integral_constant<int, 1>;
   load_chunk(c_lo, Set0{});
 
-  // ---- the activation: rotate each (batch row, group) with 16 lanes, find
-  // the group's absmax, quantise, store the int8 codes in slot order and the
-  // scale.  The zero row first.
+  // ---- the activation (and the zero row the padding lanes read)
   for (int64_t k = tid * 16; k < kpad; k += kThreads * 16)
     *reinterpret_cast<uint4 *>(xq + batch * kpad + k) = make_uint4(0u, 0u, 0u, 0u);
-  {
-    const int j = lane & 15;
-    const int tasks = batch * ngroups;
-    for (int t0 = 0; t0 < tasks; t0 += kThreads / 16) {  // uniform trip count: all lanes run the exchanges
-      const int task = t0 + (tid >> 4);
-      const bool valid = task < tasks;
-      const int b = valid ? task / ngroups : 0, g = valid ? task % ngroups : 0;
-      float v[8];
-      load8_f32(a.x + static_cast<int64_t>(b) * a.cols, static_cast<int64_t>(g) * CQ_GROUP + 8 * j, valid ? a.cols : 0,
-                a.xvec != 0, v);
-      fwht128_unscaled(v, j);
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[i] *= kInvSqrt128;
-        m = fmaxf(m, fabsf(v[i]));
-      }
-      m = row16_max(m);
-      const float sx = m / 127.0f;
-      if (valid) {
-        uint8_t *dst = xq + static_cast<int64_t>(b) * kpad + static_cast<int64_t>(g) * CQ_GROUP;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int e = 8 * j + i;  // element of the group
-          int qv = 0;
-          if (sx > 0.0f) qv = static_cast<int>(fminf(fmaxf(rintf(v[i] / sx), -128.0f), 127.0f));
-          dst[(e & ~15) + code_slot<SB>(e & 15)] = static_cast<uint8_t>(qv);
-        }
-        if (j == 0) sxs[g * 8 + b] = sx;
-      }
-    }
-  }
+  stage_int8<SB, kThreads>(a.x, a.cols, a.xvec != 0, batch, ngroups, xq, sxs);
   __syncthreads();
 
   // ---- the product
@@ -292,6 +299,213 @@ __global__ __launch_bounds__(kThreads) void w2a8_kernel(W8Args a) {
   }
 }
 
+// ---- the row-streaming kernel: batch 1 or 2 and batch x cols_pad <= 16384.
+// A wave reads whole stretches of a row (16-byte pieces, 1 KB per load
+// instruction at full width), decodes each piece with byte permutes and
+// accumulates it with v_dot4_i32_i8 against the lane's int8 activations,
+// which it holds in registers for the whole kernel.  The pieces of one group
+// sit in adjacent lanes: their integer dots are added across those lanes
+// (exact), and the group's first lane scales the group's dot by norm x
+// activation scale, so every group is rounded once, as in the MFMA kernel.
+// Short rows share a wave: 2^lpr_shift lanes per row, a segmented reduction
+// at the end of each step of rows.
+template <int SB>
+struct RowGeom {
+  static constexpr int PB = SB == 3 ? 12 : 16;  // code bytes per piece (one load)
+  static constexpr int PDW = PB / 4;            // 4, 3, 4
+  static constexpr int CP = PB * 8 / SB;        // codes per piece: 64, 32, 32
+  static constexpr int XDW = CP / 4;            // int8 activation dwords per piece
+  static constexpr int PPG = CQ_GROUP / CP;     // pieces per group: 2, 4, 4
+};
+constexpr int kRowThreads = 256;
+constexpr int kRowMaxXdw = 64;  // activation dwords a lane holds, all batch rows
+
+struct W8RowArgs {
+  const uint8_t *packed;
+  const uint16_t *norms;
+  const float *x;
+  float *y;
+  int64_t rows, cols, row_bytes;
+  int32_t ngroups, npieces, lpr_shift, npl, nsteps, xvec;
+  uint32_t c8[4];
+  float sc;
+};
+
+template <int SB, int B, int NPL>
+__global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
+  using G = RowGeom<SB>;
+  static_assert(B * NPL * G::XDW <= kRowMaxXdw, "activation registers");
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int next_step;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int ngroups = a.ngroups, npieces = a.npieces;
+  const int64_t kpad = static_cast<int64_t>(ngroups) * CQ_GROUP;
+  uint8_t *xq = lds;                                             // [B][kpad]
+  float *sxs = reinterpret_cast<float *>(lds + B * kpad);       // [ngroups][8]
+
+  // steps of rows: this workgroup's contiguous range, handed out to its waves
+  const int spw = (a.nsteps + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
+  const int s_begin = static_cast<int>(blockIdx.x) * spw;
+  const int s_end = min(s_begin + spw, a.nsteps);
+  if (tid == 0) next_step = s_begin;
+  stage_int8<SB, kRowThreads>(a.x, a.cols, a.xvec != 0, B, ngroups, xq, sxs);
+  __syncthreads();
+
+  const int lps = a.lpr_shift, lpr = 1 << lps, li = lane & (lpr - 1), rsub = lane >> lps;
+  const int rs = 64 >> lps;  // rows per step
+  // ---- this lane's activations (pieces li + lpr * i) and their group scales
+  uint32_t xr8[B][NPL][G::XDW];
+  float sxv[B][NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int p = li + lpr * i;
+    const bool live = i < a.npl && p < npieces;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(xq + b * kpad + static_cast<int64_t>(live ? p : 0) * G::CP);
+#pragma unroll
+      for (int w = 0; w < G::XDW; ++w) xr8[b][i][w] = live ? src[w] : 0u;
+      // only the group's first lane scales the group's summed dot
+      sxv[b][i] = live && (p % G::PPG) == 0 ? sxs[(p / G::PPG) * 8 + b] : 0.0f;
+    }
+  }
+  uint32_t tab[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tab[i] = a.c8[i];
+
+  // this lane's byte offsets in a step's code and norm buffers
+  uint32_t coff[NPL], noff[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const uint32_t p = static_cast<uint32_t>(li + lpr * i);
+    const bool live = i < a.npl && p < static_cast<uint32_t>(npieces);
+    coff[i] = live ? static_cast<uint32_t>(rsub * a.row_bytes) + p * G::PB : kOutOfRange;
+    noff[i] = live ? (static_cast<uint32_t>(rsub * ngroups) + p / G::PPG) * 2u : kOutOfRange;
+  }
+  uint32_t codes[2][NPL][G::PDW];
+  uint16_t nrm[2][NPL];
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next_step, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  auto load_step = [&](int st, auto set_c) {
+    constexpr int S = decltype(set_c)::value;
+    const int64_t r0 = static_cast<int64_t>(st) * rs;
+    const int64_t live_rows = st < s_end ? (a.rows - r0 < rs ? a.rows - r0 : rs) : 0;
+    const __amdgpu_buffer_rsrc_t rb =
+        buffer_rsrc(a.packed + r0 * a.row_bytes, static_cast<uint32_t>(live_rows * a.row_bytes));
+    const __amdgpu_buffer_rsrc_t nb =
+        buffer_rsrc(a.norms + r0 * ngroups, static_cast<uint32_t>(live_rows * ngroups * 2));
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      load_dwords<G::PDW>(rb, coff[i], codes[S][i]);
+      nrm[S][i] = __builtin_amdgcn_raw_buffer_load_b16(nb, noff[i], 0, 0);
+    }
+  };
+  auto compute_step = [&](int st, auto set_c) {
+    constexpr int S = decltype(set_c)::value;
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      if (i >= a.npl) break;  // uniform
+      const uint32_t *cd = codes[S][i];
+      int32x4 dq[G::XDW / 4];
+      if constexpr (SB == 2) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) decode2_i8(tab[0], cd[w], dq[w]);
+      } else if constexpr (SB == 4) {
+        decode4_i8(tab, cd[0], cd[1], dq[0]);
+        decode4_i8(tab, cd[2], cd[3], dq[1]);
+      } else {
+        const uint32_t f1 = __builtin_amdgcn_alignbit(cd[1], cd[0], 24);
+        const uint32_t f2 = __builtin_amdgcn_alignbit(cd[2], cd[1], 16);
+        decode3_i8(tab, cd[0], f1, dq[0]);
+        decode3_i8(tab, f2, cd[2] >> 8, dq[1]);
+      }
+      const float nn = static_cast<float>(__builtin_bit_cast(_Float16, nrm[S][i]));
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        int dot = 0;
+#pragma unroll
+        for (int w = 0; w < G::XDW; ++w) dot = __builtin_amdgcn_sdot4(dq[w >> 2][w & 3], static_cast<int>(xr8[b][i][w]), dot, false);
+        dot += __builtin_amdgcn_mov_dpp(dot, 0xb1, 0xf, 0xf, false);                     // xor 1: the group's 2 pieces
+        if constexpr (G::PPG == 4) dot += __builtin_amdgcn_mov_dpp(dot, 0x4e, 0xf, 0xf, false);  // xor 2: its 4
+        acc[b] = fmaf(static_cast<float>(dot), sxv[b][i] * nn, acc[b]);
+      }
+    }
+    // segmented sum over the row's lanes (every lane of the segment gets it)
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      float v = acc[b];
+      if (lps >= 1) v += xor_lane<1>(v);
+      if (lps >= 2) v += xor_lane<2>(v);
+      if (lps >= 3) v += xor_lane<4>(v);
+      if (lps >= 4) v += xor_lane<8>(v);
+      if (lps >= 5) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      }
+      if (lps >= 6) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      }
+      acc[b] = v;
+    }
+    const int64_t r = static_cast<int64_t>(st) * rs + rsub;
+    if (li == 0 && st < s_end && r < a.rows) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) a.y[static_cast<int64_t>(b) * a.rows + r] = acc[b] * a.sc;
+    }
+  };
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+  int s0 = grab();
+  load_step(s0, Set0{});
+  int s1 = grab();
+  load_step(s1, Set1{});
+  while (s0 < s_end || s1 < s_end) {  // grabs only grow: the loop ends once both sets are past the range
+    compute_step(s0, Set0{});
+    s0 = grab();
+    load_step(s0, Set0{});
+    compute_step(s1, Set1{});
+    s1 = grab();
+    load_step(s1, Set1{});
+  }
+}
+
+typedef void (*W8RowKernel)(W8RowArgs);
+
+template <int SB, int B>
+constexpr int row_npl() { return kRowMaxXdw / (B * RowGeom<SB>::XDW); }
+
+template <int SB>
+W8RowKernel pick_row_b(int batch) {
+  return batch == 1 ? w2a8_row_kernel<SB, 1, row_npl<SB, 1>()> : w2a8_row_kernel<SB, 2, row_npl<SB, 2>()>;
+}
+
+int row_max_npl(int sb, int batch) {
+  if (sb == 2) return batch == 1 ? row_npl<2, 1>() : row_npl<2, 2>();
+  if (sb == 3) return batch == 1 ? row_npl<3, 1>() : row_npl<3, 2>();
+  return batch == 1 ? row_npl<4, 1>() : row_npl<4, 2>();
+}
+
+// Resident workgroups per CU of a row kernel at an LDS size, cached per
+// device (a handful of (kernel, size) pairs occur in a process).
+int row_occupancy(const void *k, size_t lds, int dev) {
+  struct Entry { const void *k; size_t lds; int dev, per_cu; };
+  static Entry cache[32];
+  static int used = 0;
+  for (int i = 0; i < used; ++i)
+    if (cache[i].k == k && cache[i].lds == lds && cache[i].dev == dev) return cache[i].per_cu;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kRowThreads, lds) != hipSuccess || per_cu < 1) per_cu = 1;
+  if (used < 32) cache[used++] = Entry{k, lds, dev, per_cu};
+  return per_cu;
+}
+
 typedef void (*W8Kernel)(W8Args);
 
 W8Kernel pick(int sb) {
@@ -306,7 +520,10 @@ uint64_t w2a8_lds_bytes(int64_t kpad, int64_t batch) {
   return static_cast<uint64_t>(batch + 1) * kpad + static_cast<uint64_t>(kpad / CQ_GROUP) * 32;
 }
 
+static bool use_row_kernel(int64_t kpad, int64_t batch) { return batch <= 2 && batch * kpad <= 16384; }
+
 bool w2a8_fits(int64_t kpad, int64_t batch) {
+  if (kpad > 0 && kpad % CQ_GROUP == 0 && batch >= 1 && use_row_kernel(kpad, batch)) return true;
   return kpad > 0 && kpad % CQ_GROUP == 0 && batch >= 1 && batch <= kMaxBatch &&
          w2a8_lds_bytes(kpad, batch) <= kW2a8MaxLds;
 }
@@ -315,6 +532,50 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t cols
                        const float *x, int64_t batch, float *y, hipStream_t s) {
   if (!w2a8_fits(kpad, batch) || rows <= 0) return hipErrorInvalidValue;
   const int sb = storage_bits(bits);
+  static int cu_cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cu_cache[dev] == 0) {
+    int cus = 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    cu_cache[dev] = cus;
+  }
+  if (use_row_kernel(kpad, batch)) {
+    W8RowArgs r;
+    r.packed = blob;
+    r.row_bytes = kpad * sb / 8;
+    r.norms = reinterpret_cast<const uint16_t *>(blob + rows * r.row_bytes);
+    r.x = x;
+    r.y = y;
+    r.rows = rows;
+    r.cols = cols;
+    r.ngroups = static_cast<int32_t>(kpad / CQ_GROUP);
+    const int pb = sb == 3 ? 12 : 16;
+    r.npieces = static_cast<int32_t>(r.row_bytes / pb);
+    int lps = 0;
+    while ((1 << lps) < r.npieces && lps < 6) ++lps;
+    r.lpr_shift = lps;
+    r.npl = (r.npieces + 63) >> 6;
+    if (r.npl < 1) r.npl = 1;
+    const int64_t rs = 64 >> lps;
+    const int64_t nsteps = (rows + rs - 1) / rs;
+    if (nsteps >= (int64_t{1} << 31) || static_cast<int64_t>(rs) * r.row_bytes >= (int64_t{1} << 31))
+      return hipErrorInvalidValue;
+    r.nsteps = static_cast<int32_t>(nsteps);
+    r.xvec = cols % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+    for (int i = 0; i < 4; ++i) r.c8[i] = cb.c8[i];
+    r.sc = cb.sc;
+    const size_t lds = static_cast<size_t>(batch * kpad + (kpad / CQ_GROUP) * 32);
+    const W8RowKernel k = sb == 2 ? pick_row_b<2>(static_cast<int>(batch))
+                                  : (sb == 3 ? pick_row_b<3>(static_cast<int>(batch)) : pick_row_b<4>(static_cast<int>(batch)));
+    if (r.npl > row_max_npl(sb, static_cast<int>(batch))) return hipErrorInvalidValue;
+    // one wave of workgroups: as many as the CUs hold at once (registers and
+    // LDS), each over a contiguous range of row steps
+    const int per_cu = row_occupancy(reinterpret_cast<const void *>(k), lds, dev);
+    const int64_t grid = nsteps < int64_t{per_cu} * cu_cache[dev] ? nsteps : int64_t{per_cu} * cu_cache[dev];
+    k<<<dim3(static_cast<unsigned>(grid)), kRowThreads, lds, s>>>(r);
+    return hipGetLastError();
+  }
   W8Args a;
   a.packed = blob;
   a.row_bytes = kpad * sb / 8;
@@ -340,14 +601,6 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t cols
   const size_t lds = static_cast<size_t>(w2a8_lds_bytes(kpad, batch));
   // about as many workgroups as the CUs hold at once (by LDS, at most 8 per
   // CU): each stages the activation once and loops over tiles
-  static int cu_cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cu_cache[dev] == 0) {
-    int cus = 256;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    cu_cache[dev] = cus;
-  }
   int64_t per_cu = static_cast<int64_t>(160 * 1024) / static_cast<int64_t>(lds + sizeof(float) * 4 * kThreads);
   per_cu = per_cu < 1 ? 1 : (per_cu > 8 ? 8 : per_cu);
   const int64_t grid = ntiles < per_cu * cu_cache[dev] ? ntiles : per_cu * cu_cache[dev];

@@ -392,6 +392,7 @@ def test_rotation_is_the_oracle_butterfly_bit_for_bit():
 @pytest.mark.parametrize("rows,cols,batch", [
     (512, 512, 1), (300, 1000, 3), (257, 2048, 2), (64, 640, 8), (1, 128, 1),
     (1000, 16384, 1), (9, 16384, 2), (33, 6528, 8), (130, 5000, 4),
+    (100, 768, 1), (45, 1536, 2), (77, 4096, 1), (5, 8192, 2),
 ])
 def test_matvec_w2a8(bits, rows, cols, batch):
     say("w2a8", bits, rows, cols, batch)
