@@ -13,7 +13,8 @@ fallback path.
 Functions carry the C names: ``cq_blob_bytes``, ``cq_workspace_bytes``,
 ``cq_rotate_acts``, ``cq_matvec``, ``cq_rotate_matvec``,
 ``cq_rotate_multi_matvec``, ``cq_rotate_multi_workspace_bytes``,
-``cq_matvec_w2a8``, ``cq_gather_rows``, ``cq_gemm``, ``cq_quantize``.
+``cq_quantize_acts_int8``, ``cq_matvec_w2a8_quantized``, ``cq_matvec_w2a8``,
+``cq_gather_rows``, ``cq_gemm``, ``cq_quantize``.
 """
 import ctypes
 import os
@@ -27,7 +28,8 @@ __all__ = [
     "LIB_PATH", "CQError", "CQMatrix", "CQ_GROUP", "CQ_MAX_MATVEC_BATCH", "workspace_for",
     "cq_version", "cq_blob_bytes", "cq_workspace_bytes",
     "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_multi_matvec",
-    "cq_rotate_multi_workspace_bytes", "cq_matvec_w2a8", "cq_gather_rows", "cq_gemm", "cq_quantize",
+    "cq_rotate_multi_workspace_bytes", "cq_quantize_acts_int8", "cq_matvec_w2a8_quantized", "cq_matvec_w2a8",
+    "cq_gather_rows", "cq_gemm", "cq_quantize",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcq.so")
@@ -39,7 +41,7 @@ CQ_GROUP = 128
 CQ_MAX_MATVEC_BATCH = 8
 _F32, _F16, _BF16 = 0, 1, 2
 _DTYPES = {torch.float32: _F32, torch.float16: _F16, torch.bfloat16: _BF16}
-OP_MATVEC, OP_GEMM, OP_ROTATE_MATVEC = 0, 1, 2
+OP_MATVEC, OP_GEMM, OP_ROTATE_MATVEC, OP_W2A8 = 0, 1, 2, 3
 
 
 class _Matrix(ctypes.Structure):
@@ -63,7 +65,9 @@ _SIGS = {
     "cq_rotate_matvec": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_rotate_multi_matvec": (_i32, [_MP, _i32, _vp, _i64, ctypes.POINTER(_vp), _vp, _u64, _vp]),
     "cq_rotate_multi_workspace_bytes": (_i32, [_MP, _i32, _i64, ctypes.POINTER(_u64)]),
-    "cq_matvec_w2a8": (_i32, [_MP, _vp, _i64, _vp, _vp]),
+    "cq_quantize_acts_int8": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "cq_matvec_w2a8_quantized": (_i32, [_MP, _vp, _vp, _i64, _vp, _vp]),
+    "cq_matvec_w2a8": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_gather_rows": (_i32, [_MP, _vp, _i64, _vp, _i32, _vp]),
     "cq_gemm": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_quantize": (_i32, [_vp, _i64, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_float), _vp, _u64, _vp]),
@@ -273,10 +277,52 @@ def cq_rotate_multi_matvec(Ws, x, outs=None, workspace=None):
     return outs
 
 
-def cq_matvec_w2a8(W, x, out=None):
+def cq_quantize_acts_int8(x, xq=None, sx=None):
+    """The rotated activation quantised per 128-group to int8: x float32
+    [batch, cols] (not rotated); returns (xq int8 [batch, cols_pad], sx
+    float32 [batch, cols_pad / 128])."""
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be float32 [batch, cols]")
+    x = x.contiguous()
+    b, cols = x.shape
+    kpad = _padded(cols)
+    if xq is None:
+        xq = torch.empty((b, kpad), dtype=torch.int8, device=x.device)
+    if sx is None:
+        sx = torch.empty((b, kpad // CQ_GROUP), dtype=torch.float32, device=x.device)
+    if xq.dtype != torch.int8 or tuple(xq.shape) != (b, kpad):
+        raise ValueError("xq must be int8 [batch, cols_pad]")
+    if sx.dtype != torch.float32 or tuple(sx.shape) != (b, kpad // CQ_GROUP):
+        raise ValueError("sx must be float32 [batch, cols_pad / 128]")
+    _check(_lib.cq_quantize_acts_int8(_dev(x, "x"), b, cols, _dev(xq, "xq"), _dev(sx, "sx"), _stream()))
+    return xq, sx
+
+
+def cq_matvec_w2a8_quantized(W, xq, sx, out=None):
+    """The CQ-W2A8 product from quantised activations (cq_quantize_acts_int8's
+    xq int8 [batch, cols_pad] and sx float32 [batch, cols_pad / 128]);
+    returns float32 [batch, rows]."""
+    kpad = _padded(W.cols)
+    if xq.dtype != torch.int8 or xq.dim() != 2 or xq.shape[1] != kpad:
+        raise ValueError("xq must be int8 [batch, cols_pad]")
+    b = xq.shape[0]
+    if sx.dtype != torch.float32 or tuple(sx.shape) != (b, kpad // CQ_GROUP):
+        raise ValueError("sx must be float32 [batch, cols_pad / 128]")
+    if out is None:
+        out = torch.empty((b, W.rows), dtype=torch.float32, device=xq.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (b, W.rows):
+        raise ValueError("out must be float32 [batch, rows]")
+    m, keep = W._struct()
+    _check(_lib.cq_matvec_w2a8_quantized(ctypes.byref(m), _dev(xq, "xq"), _dev(sx, "sx"), b, _dev(out, "out"),
+                                         _stream()))
+    return out
+
+
+def cq_matvec_w2a8(W, x, out=None, workspace=None):
     """The CQ-W2A8 product (int8 activations and code book, integer dots, one
     float multiply per group) of x float32 [batch, cols] (not rotated);
-    returns float32 [batch, rows]."""
+    returns float32 [batch, rows].  ``workspace``: at least
+    cq_workspace_bytes(OP_W2A8) bytes, or None for a cached one."""
     if x.dtype != torch.float32 or x.dim() != 2 or x.shape[1] != W.cols:
         raise ValueError("x must be float32 [batch, cols]")
     x = x.contiguous()
@@ -286,7 +332,11 @@ def cq_matvec_w2a8(W, x, out=None):
     if out.dtype != torch.float32 or tuple(out.shape) != (b, W.rows):
         raise ValueError("out must be float32 [batch, rows]")
     m, keep = W._struct()
-    _check(_lib.cq_matvec_w2a8(ctypes.byref(m), _dev(x, "x"), b, _dev(out, "out"), _stream()))
+    if workspace is None and b > 0 and W.rows > 0:
+        workspace = workspace_for(cq_workspace_bytes(OP_W2A8, W, b), x.device)
+    ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.cq_matvec_w2a8(ctypes.byref(m), _dev(x, "x"), b, _dev(out, "out"), ws, wsb, _stream()))
     return out
 
 

@@ -119,6 +119,11 @@ cq_status cq_workspace_bytes(int32_t op, const cq_matrix *W, int64_t batch, uint
   } else if (op == CQ_OP_GEMM) {
     if (batch < 0 || batch > CQ_MAX_DIM) return CQ_ERR_SHAPE;
     *bytes = 0;
+  } else if (op == CQ_OP_W2A8) {
+    if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+    const int64_t kpad = padded(W->cols);
+    if (kpad > 0 && batch > 0 && !cq::w2a8_fits(kpad, batch)) return CQ_ERR_SHAPE;
+    *bytes = W->rows && kpad && batch ? cq::w2a8_workspace_bytes(kpad, batch) : 0;
   } else {
     return CQ_ERR_SHAPE;
   }
@@ -283,26 +288,9 @@ cq_status cq_rotate_multi_matvec(const cq_matrix *W, int32_t n, const float *x, 
                                                    need ? workspace : nullptr, s));
 }
 
-cq_status cq_matvec_w2a8(const cq_matrix *W, const float *x, int64_t batch, float *y, void *stream) {
-  cq::CodeLevels lev;
-  cq_status st = check_matrix(W, &lev);
-  if (st != CQ_OK) return st;
-  if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
-  if (batch == 0 || W->rows == 0) return CQ_OK;
-  const int64_t kpad = padded(W->cols);
-  if (kpad > 0 && !cq::w2a8_fits(kpad, batch)) return CQ_ERR_SHAPE;
-  if (!y) return CQ_ERR_NULL;
-  if (!aligned(y, 4)) return CQ_ERR_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (kpad == 0) return hip_status(cq::launch_zero_f32(y, batch * W->rows, s));
-  if (!x) return CQ_ERR_NULL;
-  if (!aligned(x, 4)) return CQ_ERR_ALIGN;
-  const uint64_t ybytes = static_cast<uint64_t>(batch) * W->rows * 4;
-  if (overlaps(y, ybytes, x, static_cast<uint64_t>(batch) * W->cols * 4) ||
-      overlaps(y, ybytes, W->blob, W->blob_bytes))
-    return CQ_ERR_OVERLAP;
-  // The int8 code book: maxabs / 127 and round half to even, in fp32 (the
-  // ternary crumbs keep their sign-extended integers, scale a).
+// The int8 code book of W: maxabs / 127 and round half to even, in fp32 (the
+// ternary crumbs keep their sign-extended integers, scale a).
+static cq::Int8Codebook int8_codebook(const cq_matrix *W, const cq::CodeLevels &lev) {
   cq::Int8Codebook cb;
   std::memset(&cb, 0, sizeof cb);
   const int nlev = W->bits == 5 ? 4 : 1 << W->bits;
@@ -317,8 +305,85 @@ cq_status cq_matvec_w2a8(const cq_matrix *W, const float *x, int64_t batch, floa
     for (int i = 0; i < nlev; ++i) c8[i] = static_cast<int8_t>(std::nearbyint(lev.v[i] / cb.sc));
   }
   for (int i = 0; i < 16; ++i) cb.c8[i / 4] |= static_cast<uint32_t>(static_cast<uint8_t>(c8[i])) << (8 * (i % 4));
-  return hip_status(cq::launch_w2a8(static_cast<const uint8_t *>(W->blob), W->bits, W->rows, W->cols, kpad, cb, x,
-                                    batch, y, s));
+  return cb;
+}
+
+cq_status cq_quantize_acts_int8(const float *x, int64_t batch, int64_t cols, int8_t *xq, float *sx, void *stream) {
+  if (batch < 0 || cols < 0 || batch > CQ_MAX_DIM || cols > CQ_MAX_DIM) return CQ_ERR_SHAPE;
+  if (batch == 0 || cols == 0) return CQ_OK;
+  if (!x || !xq || !sx) return CQ_ERR_NULL;
+  if (!aligned(x, 4) || !aligned(xq, 16) || !aligned(sx, 4)) return CQ_ERR_ALIGN;
+  const int64_t kpad = padded(cols);
+  const uint64_t xbytes = static_cast<uint64_t>(batch) * cols * 4;
+  const uint64_t qbytes = static_cast<uint64_t>(batch) * kpad;
+  const uint64_t sbytes = static_cast<uint64_t>(batch) * (kpad / CQ_GROUP) * 4;
+  if (overlaps(xq, qbytes, x, xbytes) || overlaps(sx, sbytes, x, xbytes) || overlaps(xq, qbytes, sx, sbytes))
+    return CQ_ERR_OVERLAP;
+  return hip_status(cq::launch_quant_acts_int8(x, batch, cols, kpad, xq, sx, static_cast<hipStream_t>(stream)));
+}
+
+// Checks shared by the two W2A8 products; CQ_OK with *done set when there is
+// nothing to launch (or only the zero fill of y).
+static cq_status check_w2a8(const cq_matrix *W, int64_t batch, float *y, cq::CodeLevels *lev, int64_t *kpad,
+                            bool *done, hipStream_t s) {
+  *done = true;
+  cq_status st = check_matrix(W, lev);
+  if (st != CQ_OK) return st;
+  if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+  if (batch == 0 || W->rows == 0) return CQ_OK;
+  *kpad = padded(W->cols);
+  if (*kpad > 0 && !cq::w2a8_fits(*kpad, batch)) return CQ_ERR_SHAPE;
+  if (!y) return CQ_ERR_NULL;
+  if (!aligned(y, 4)) return CQ_ERR_ALIGN;
+  if (overlaps(y, static_cast<uint64_t>(batch) * W->rows * 4, W->blob, W->blob_bytes)) return CQ_ERR_OVERLAP;
+  if (*kpad == 0) return hip_status(cq::launch_zero_f32(y, batch * W->rows, s));
+  *done = false;
+  return CQ_OK;
+}
+
+cq_status cq_matvec_w2a8_quantized(const cq_matrix *W, const int8_t *xq, const float *sx, int64_t batch, float *y,
+                                   void *stream) {
+  cq::CodeLevels lev;
+  int64_t kpad = 0;
+  bool done = true;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  cq_status st = check_w2a8(W, batch, y, &lev, &kpad, &done, s);
+  if (st != CQ_OK || done) return st;
+  if (!xq || !sx) return CQ_ERR_NULL;
+  if (!aligned(xq, 16) || !aligned(sx, 4)) return CQ_ERR_ALIGN;
+  const uint64_t ybytes = static_cast<uint64_t>(batch) * W->rows * 4;
+  if (overlaps(y, ybytes, xq, static_cast<uint64_t>(batch) * kpad) ||
+      overlaps(y, ybytes, sx, static_cast<uint64_t>(batch) * (kpad / CQ_GROUP) * 4))
+    return CQ_ERR_OVERLAP;
+  return hip_status(cq::launch_w2a8(static_cast<const uint8_t *>(W->blob), W->bits, W->rows, kpad,
+                                    int8_codebook(W, lev), xq, sx, batch, y, s));
+}
+
+cq_status cq_matvec_w2a8(const cq_matrix *W, const float *x, int64_t batch, float *y, void *workspace,
+                         uint64_t workspace_bytes, void *stream) {
+  cq::CodeLevels lev;
+  int64_t kpad = 0;
+  bool done = true;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  cq_status st = check_w2a8(W, batch, y, &lev, &kpad, &done, s);
+  if (st != CQ_OK || done) return st;
+  if (!x) return CQ_ERR_NULL;
+  if (!aligned(x, 4)) return CQ_ERR_ALIGN;
+  const uint64_t need = cq::w2a8_workspace_bytes(kpad, batch);
+  if (!workspace || workspace_bytes < need) return CQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return CQ_ERR_ALIGN;
+  const uint64_t ybytes = static_cast<uint64_t>(batch) * W->rows * 4;
+  const uint64_t xbytes = static_cast<uint64_t>(batch) * W->cols * 4;
+  if (overlaps(y, ybytes, x, xbytes) || overlaps(workspace, need, y, ybytes) ||
+      overlaps(workspace, need, x, xbytes) || overlaps(workspace, need, W->blob, W->blob_bytes))
+    return CQ_ERR_OVERLAP;
+  int8_t *xq = static_cast<int8_t *>(workspace);
+  float *sx = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + (need - static_cast<uint64_t>(batch) *
+                                                                                        (kpad / CQ_GROUP) * 4));
+  hipError_t e = cq::launch_quant_acts_int8(x, batch, W->cols, kpad, xq, sx, s);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(cq::launch_w2a8(static_cast<const uint8_t *>(W->blob), W->bits, W->rows, kpad,
+                                    int8_codebook(W, lev), xq, sx, batch, y, s));
 }
 
 cq_status cq_gather_rows(const cq_matrix *W, const int64_t *ids, int64_t n, void *out, int32_t out_dtype,

@@ -110,8 +110,13 @@ struct Int8Codebook {
 constexpr uint64_t kW2a8MaxLds = 60 * 1024;
 uint64_t w2a8_lds_bytes(int64_t kpad, int64_t batch);
 bool w2a8_fits(int64_t kpad, int64_t batch);
-hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t cols, int64_t kpad, const Int8Codebook &cb,
-                       const float *x, int64_t batch, float *y, hipStream_t s);
+// Quantised activations of cq_matvec_w2a8: int8 [batch][kpad] (column order)
+// then, 256 bytes aligned, the scales fp32 [batch][kpad / 128].
+uint64_t w2a8_workspace_bytes(int64_t kpad, int64_t batch);
+hipError_t launch_quant_acts_int8(const float *x, int64_t batch, int64_t cols, int64_t kpad, int8_t *xq, float *sx,
+                                  hipStream_t s);
+hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const Int8Codebook &cb,
+                       const int8_t *xq, const float *sx, int64_t batch, float *y, hipStream_t s);
 
 // Row gather: out[i][k] = w_hat[ids[i]][k] (k < cols) in out_dtype; NaN rows
 // for ids outside [0, rows).

@@ -26,10 +26,10 @@
 //  * lane (row n, quarter q) owns codes 32q..32q+31 of every group of its row
 //    (8, 12 or 16 contiguous bytes) and decodes them with byte permutes of
 //    the int8 codebook held in registers;
-//  * the workgroup first rotates and quantises the whole activation into LDS
-//    (int8, stored in the decoders' slot order) and the group scales, then
-//    loops over row tiles (a grid of about as many workgroups as fit the
-//    chip, so the staging is paid once per workgroup, not per tile);
+//  * a first kernel rotates and quantises the activation once (int8 in
+//    column order and the group scales, in global memory); each product
+//    workgroup copies it into LDS in the decoders' slot order, then loops
+//    over row tiles (a grid of about as many workgroups as fit the chip);
 //  * chunks of 4 groups, two in flight per wave; with 2+ chunks, 2 or 4 waves
 //    split a block's K and add their accumulators through LDS in wave order.
 #include "cq_decode.h"
@@ -57,10 +57,11 @@ constexpr uint32_t kOutOfRange = 0xffff0000u;  // a buffer offset past any range
 struct W8Args {
   const uint8_t *packed;
   const uint16_t *norms;  // fp16 bits [rows][ngroups]
-  const float *x;         // [batch][cols], not rotated
+  const int8_t *xq;       // [batch][kpad], column order
+  const float *sx;        // [batch][ngroups]
   float *y;               // [batch][rows]
-  int64_t rows, cols, row_bytes;
-  int32_t ngroups, batch, xvec, ks_shift;
+  int64_t rows, row_bytes;
+  int32_t ngroups, batch, ks_shift;
   int32_t ntiles;  // row tiles (16 << (2 - ks_shift) rows each); workgroups loop over them
   uint32_t c8[4];  // int8 value of stored code c in byte c % 4 of c8[c / 4]
   float sc;
@@ -113,43 +114,71 @@ __device__ inline float row16_max(float m) {
   return m;
 }
 
-// The activation into LDS: each (batch row, group) is rotated by 16 lanes
-// (the shared butterfly), its absmax found, its values quantised to int8 and
-// stored in the decoders' slot order (xq [batch][kpad]), and its scale
-// stored at sxs[g * 8 + b].  All threads of the workgroup call it.
-template <int SB, int NT>
-__device__ inline void stage_int8(const float *x, int64_t cols, bool xvec, int batch, int ngroups, uint8_t *xq,
-                                  float *sxs) {
-  const int tid = threadIdx.x, j = tid & 15;
+// The rotated activation quantised to int8, one (batch row, group) per 16
+// lanes: the shared butterfly, the group's absmax, sx = absmax / 127 and
+// q = clamp(rint(xr / sx)) (IEEE division, round half to even), written in
+// column order (8 bytes per lane) with the scale at sx[b][g].
+__global__ __launch_bounds__(kThreads) void quant_acts_kernel(const float *x, int64_t cols, int32_t xvec,
+                                                              int64_t tasks, int32_t ngroups, int8_t *xq, float *sxo) {
+  const int j = threadIdx.x & 15;
+  const int64_t task = static_cast<int64_t>(blockIdx.x) * (kThreads / 16) + (threadIdx.x >> 4);
+  const bool valid = task < tasks;  // every lane runs the exchanges
+  const int64_t b = valid ? task / ngroups : 0, g = valid ? task - b * ngroups : 0;
+  float v[8];
+  load8_f32(x + b * cols, g * CQ_GROUP + 8 * j, valid ? cols : 0, xvec != 0, v);
+  fwht128_unscaled(v, j);
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] *= kInvSqrt128;
+    m = fmaxf(m, fabsf(v[i]));
+  }
+  m = row16_max(m);
+  const float sx = m / 127.0f;
+  if (!valid) return;
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int qv = 0;
+    if (sx > 0.0f) qv = static_cast<int>(fminf(fmaxf(rintf(v[i] / sx), -128.0f), 127.0f));
+    w[i >> 2] |= (static_cast<uint32_t>(qv) & 0xffu) << (8 * (i & 3));
+  }
   const int64_t kpad = static_cast<int64_t>(ngroups) * CQ_GROUP;
-  const int tasks = batch * ngroups;
-  for (int t0 = 0; t0 < tasks; t0 += NT / 16) {  // uniform trip count: all lanes run the exchanges
-    const int task = t0 + (tid >> 4);
-    const bool valid = task < tasks;
-    const int b = valid ? task / ngroups : 0, g = valid ? task % ngroups : 0;
-    float v[8];
-    load8_f32(x + static_cast<int64_t>(b) * cols, static_cast<int64_t>(g) * CQ_GROUP + 8 * j, valid ? cols : 0, xvec,
-              v);
-    fwht128_unscaled(v, j);
-    float m = 0.0f;
+  *reinterpret_cast<uint2 *>(xq + b * kpad + g * CQ_GROUP + 8 * j) = make_uint2(w[0], w[1]);
+  if (j == 0) sxo[task] = sx;
+}
+
+// 16 activation bytes of one 16-code step, column order -> slot order.
+template <int SB>
+__device__ inline uint4 to_slot_order(uint4 v) {
+  if constexpr (SB == 3) {
+    return v;
+  } else {
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[i] *= kInvSqrt128;
-      m = fmaxf(m, fabsf(v[i]));
+    for (int c = 0; c < 16; ++c) {
+      const uint32_t byte = (in[c >> 2] >> (8 * (c & 3))) & 0xffu;
+      const int sl = code_slot<SB>(c);
+      out[sl >> 2] |= byte << (8 * (sl & 3));
     }
-    m = row16_max(m);
-    const float sx = m / 127.0f;
-    if (valid) {
-      uint8_t *dst = xq + static_cast<int64_t>(b) * kpad + static_cast<int64_t>(g) * CQ_GROUP;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int e = 8 * j + i;  // element of the group
-        int qv = 0;
-        if (sx > 0.0f) qv = static_cast<int>(fminf(fmaxf(rintf(v[i] / sx), -128.0f), 127.0f));
-        dst[(e & ~15) + code_slot<SB>(e & 15)] = static_cast<uint8_t>(qv);
-      }
-      if (j == 0) sxs[g * 8 + b] = sx;
-    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+  }
+}
+
+// The quantised activation into LDS: xq [batch][kpad] in slot order and the
+// scales at sxs[g * 8 + b].  All threads of the workgroup call it.
+template <int SB, int NT>
+__device__ inline void fill_int8(const int8_t *xq, const float *sx, int batch, int ngroups, uint8_t *lxq,
+                                 float *sxs) {
+  const int tid = threadIdx.x;
+  const int blocks = batch * ngroups * (CQ_GROUP / 16);
+  const uint4 *src = reinterpret_cast<const uint4 *>(xq);
+  uint4 *dst = reinterpret_cast<uint4 *>(lxq);
+  for (int t = tid; t < blocks; t += NT) dst[t] = to_slot_order<SB>(src[t]);
+  for (int t = tid; t < batch * ngroups; t += NT) {
+    const int b = t / ngroups, g = t - b * ngroups;
+    sxs[g * 8 + b] = sx[t];
   }
 }
 
@@ -212,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void w2a8_kernel(W8Args a) {
   // ---- the activation (and the zero row the padding lanes read)
   for (int64_t k = tid * 16; k < kpad; k += kThreads * 16)
     *reinterpret_cast<uint4 *>(xq + batch * kpad + k) = make_uint4(0u, 0u, 0u, 0u);
-  stage_int8<SB, kThreads>(a.x, a.cols, a.xvec != 0, batch, ngroups, xq, sxs);
+  fill_int8<SB, kThreads>(a.xq, a.sx, batch, ngroups, xq, sxs);
   __syncthreads();
 
   // ---- the product
@@ -308,7 +337,10 @@ __global__ __launch_bounds__(kThreads) void w2a8_kernel(W8Args a) {
 // (exact), and the group's first lane scales the group's dot by norm x
 // activation scale, so every group is rounded once, as in the MFMA kernel.
 // Short rows share a wave: 2^lpr_shift lanes per row, a segmented reduction
-// at the end of each step of rows.
+// at the end of each step of rows.  A workgroup copies the quantised
+// activation into LDS once (slot order), each lane takes its pieces' bytes
+// into registers, and the waves then take steps of rows from an LDS counter
+// over the workgroup's contiguous range, two steps in flight per wave.
 template <int SB>
 struct RowGeom {
   static constexpr int PB = SB == 3 ? 12 : 16;  // code bytes per piece (one load)
@@ -323,10 +355,11 @@ constexpr int kRowMaxXdw = 64;  // activation dwords a lane holds, all batch row
 struct W8RowArgs {
   const uint8_t *packed;
   const uint16_t *norms;
-  const float *x;
+  const int8_t *xq;  // [B][kpad], column order
+  const float *sx;   // [B][ngroups]
   float *y;
-  int64_t rows, cols, row_bytes;
-  int32_t ngroups, npieces, lpr_shift, npl, nsteps, xvec;
+  int64_t rows, row_bytes;
+  int32_t ngroups, npieces, lpr_shift, npl, nsteps;
   uint32_t c8[4];
   float sc;
 };
@@ -348,7 +381,7 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
   const int s_begin = static_cast<int>(blockIdx.x) * spw;
   const int s_end = min(s_begin + spw, a.nsteps);
   if (tid == 0) next_step = s_begin;
-  stage_int8<SB, kRowThreads>(a.x, a.cols, a.xvec != 0, B, ngroups, xq, sxs);
+  fill_int8<SB, kRowThreads>(a.xq, a.sx, B, ngroups, xq, sxs);
   __syncthreads();
 
   const int lps = a.lpr_shift, lpr = 1 << lps, li = lane & (lpr - 1), rsub = lane >> lps;
@@ -382,7 +415,7 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
     coff[i] = live ? static_cast<uint32_t>(rsub * a.row_bytes) + p * G::PB : kOutOfRange;
     noff[i] = live ? (static_cast<uint32_t>(rsub * ngroups) + p / G::PPG) * 2u : kOutOfRange;
   }
-  uint32_t codes[2][NPL][G::PDW];
+  uint32_t codes[2][NPL][G::PDW];  // two steps in flight per wave
   uint16_t nrm[2][NPL];
   auto grab = [&]() {
     int v = 0;
@@ -466,7 +499,9 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
   load_step(s0, Set0{});
   int s1 = grab();
   load_step(s1, Set1{});
-  while (s0 < s_end || s1 < s_end) {  // grabs only grow: the loop ends once both sets are past the range
+  // grabs only grow: the loop ends once both sets are past the range (a set
+  // past it loads nothing and stores nothing)
+  while (s0 < s_end || s1 < s_end) {
     compute_step(s0, Set0{});
     s0 = grab();
     load_step(s0, Set0{});
@@ -528,8 +563,25 @@ bool w2a8_fits(int64_t kpad, int64_t batch) {
          w2a8_lds_bytes(kpad, batch) <= kW2a8MaxLds;
 }
 
-hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t cols, int64_t kpad, const Int8Codebook &cb,
-                       const float *x, int64_t batch, float *y, hipStream_t s) {
+uint64_t w2a8_workspace_bytes(int64_t kpad, int64_t batch) {
+  const uint64_t q = (static_cast<uint64_t>(batch) * kpad + 255) / 256 * 256;
+  return q + static_cast<uint64_t>(batch) * (kpad / CQ_GROUP) * 4;
+}
+
+hipError_t launch_quant_acts_int8(const float *x, int64_t batch, int64_t cols, int64_t kpad, int8_t *xq, float *sx,
+                                  hipStream_t s) {
+  const int64_t ngroups = kpad / CQ_GROUP;
+  const int64_t tasks = batch * ngroups;
+  const int64_t wgs = (tasks + kThreads / 16 - 1) / (kThreads / 16);
+  if (wgs >= (int64_t{1} << 31) || ngroups >= (int64_t{1} << 31)) return hipErrorInvalidValue;
+  const int32_t xvec = cols % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  quant_acts_kernel<<<dim3(static_cast<unsigned>(wgs)), kThreads, 0, s>>>(x, cols, xvec, tasks,
+                                                                          static_cast<int32_t>(ngroups), xq, sx);
+  return hipGetLastError();
+}
+
+hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const Int8Codebook &cb,
+                       const int8_t *xq, const float *sx, int64_t batch, float *y, hipStream_t s) {
   if (!w2a8_fits(kpad, batch) || rows <= 0) return hipErrorInvalidValue;
   const int sb = storage_bits(bits);
   static int cu_cache[64];
@@ -545,10 +597,10 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t cols
     r.packed = blob;
     r.row_bytes = kpad * sb / 8;
     r.norms = reinterpret_cast<const uint16_t *>(blob + rows * r.row_bytes);
-    r.x = x;
+    r.xq = xq;
+    r.sx = sx;
     r.y = y;
     r.rows = rows;
-    r.cols = cols;
     r.ngroups = static_cast<int32_t>(kpad / CQ_GROUP);
     const int pb = sb == 3 ? 12 : 16;
     r.npieces = static_cast<int32_t>(r.row_bytes / pb);
@@ -562,7 +614,6 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t cols
     if (nsteps >= (int64_t{1} << 31) || static_cast<int64_t>(rs) * r.row_bytes >= (int64_t{1} << 31))
       return hipErrorInvalidValue;
     r.nsteps = static_cast<int32_t>(nsteps);
-    r.xvec = cols % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
     for (int i = 0; i < 4; ++i) r.c8[i] = cb.c8[i];
     r.sc = cb.sc;
     const size_t lds = static_cast<size_t>(batch * kpad + (kpad / CQ_GROUP) * 32);
@@ -580,13 +631,12 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t cols
   a.packed = blob;
   a.row_bytes = kpad * sb / 8;
   a.norms = reinterpret_cast<const uint16_t *>(blob + rows * a.row_bytes);
-  a.x = x;
+  a.xq = xq;
+  a.sx = sx;
   a.y = y;
   a.rows = rows;
-  a.cols = cols;
   a.ngroups = static_cast<int32_t>(kpad / CQ_GROUP);
   a.batch = static_cast<int32_t>(batch);
-  a.xvec = cols % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   const int cg = sb == 2 ? chunk_groups<2>() : chunk_groups<4>();
   const int nchunks = (a.ngroups + cg - 1) / cg;
   a.ks_shift = nchunks >= 4 ? 2 : (nchunks >= 2 ? 1 : 0);

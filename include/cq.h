@@ -114,7 +114,7 @@ cq_status cq_blob_bytes(int32_t bits, int32_t group, int64_t rows, int64_t cols,
                         uint64_t *bytes);
 
 /* Operations that may take a workspace. */
-typedef enum cq_op { CQ_OP_MATVEC = 0, CQ_OP_GEMM = 1, CQ_OP_ROTATE_MATVEC = 2 } cq_op;
+typedef enum cq_op { CQ_OP_MATVEC = 0, CQ_OP_GEMM = 1, CQ_OP_ROTATE_MATVEC = 2, CQ_OP_W2A8 = 3 } cq_op;
 
 /*
  * Device workspace (bytes) that `op` needs for `W` and the given batch (M for
@@ -123,7 +123,8 @@ typedef enum cq_op { CQ_OP_MATVEC = 0, CQ_OP_GEMM = 1, CQ_OP_ROTATE_MATVEC = 2 }
  * A workspace is device memory owned by the caller, 16-byte aligned.  Its
  * contents on entry do not matter and are left unspecified (it holds the
  * per-call partial sums of the K slices and, for CQ_OP_ROTATE_MATVEC at batch
- * 2..8, the rotated activation).  Calls that may run at the same time
+ * 2..8, the rotated activation; for CQ_OP_W2A8 the int8 activation and its
+ * group scales).  Calls that may run at the same time
  * must not share a workspace; calls on one stream may, whatever their shapes.
  */
 cq_status cq_workspace_bytes(int32_t op, const cq_matrix *W, int64_t batch,
@@ -243,16 +244,34 @@ cq_status cq_rotate_multi_workspace_bytes(const cq_matrix *W, int32_t n, int64_t
                                           uint64_t *bytes);
 
 /*
- * CQ-W2A8 decode product: int8 activations and an int8 code book, integer dot
- * products, one float multiply per group (".cact" format post, "How the
- * kernel reads it": the rotated activation group is quantised to int8 with
- * one scale per group, int8 centroids are looked up by the packed indices,
- * and each group's dot is multiplied by the weight norm, the activation scale
- * and the codebook scale; OpenNeedle reference notes, Cactus 2-bit kernel):
+ * The activation side of CQ-W2A8 (".cact" format post, "How the kernel reads
+ * it": each rotated 128-group of the activation is quantised to int8 with one
+ * scale; OpenNeedle reference notes, Cactus 2-bit kernel: the scale is the
+ * group's absmax / 127):
  *
  *   xr  = H . x per group, fp32 (the butterfly of cq_rotate_acts)
- *   sx  = fp32(max |xr| over the group / 127)
- *   xq  = clamp(round_half_even(fp32(xr / sx)), -128, 127)   (0 where sx == 0)
+ *   sx[b][g]  = fp32(max |xr| over the group / 127)
+ *   xq[b][k]  = clamp(round_half_even(fp32(xr / sx)), -128, 127)  (0 where sx == 0)
+ *
+ *   x      device fp32 [batch][cols], not rotated, 4-byte aligned (16-byte
+ *          alignment and cols % 8 == 0 allow vector loads); not modified
+ *   batch, cols   0 <= each <= CQ_MAX_DIM (0: nothing is done)
+ *   xq     device int8 [batch][cols_pad], 16-byte aligned, column order
+ *          (the padding columns hold their quantised rotated values)
+ *   sx     device fp32 [batch][cols_pad / 128], 4-byte aligned
+ *   Outputs fully overwritten; none may overlap x or each other
+ *   (CQ_ERR_OVERLAP).  CQ_ERR_SHAPE, CQ_ERR_NULL, CQ_ERR_ALIGN, CQ_ERR_HIP.
+ */
+cq_status cq_quantize_acts_int8(const float *x, int64_t batch, int64_t cols, int8_t *xq, float *sx, void *stream);
+
+/*
+ * CQ-W2A8 decode product from quantised activations: int8 activations and an
+ * int8 code book, integer dot products, one float multiply per group
+ * (".cact" format post, "How the kernel reads it": int8 centroids are looked
+ * up by the packed indices, and each group's dot is multiplied by the weight
+ * norm, the activation scale and the codebook scale; OpenNeedle reference
+ * notes, Cactus 2-bit kernel: the codebook scale is maxabs / 127):
+ *
  *   sc  = fp32(max |level| / 127), c8 = round_half_even(fp32(level / sc));
  *         ternary: c8 = the crumb's integer (0, 1, -2, -1), sc = the level a
  *   y[b][r] = sum_g (float(norm[r][g]) * sx[b][g] * sc) * sum_j c8[q] * xq
@@ -263,18 +282,33 @@ cq_status cq_rotate_multi_workspace_bytes(const cq_matrix *W, int32_t n, int64_t
  * quantisation of the activation and the code book (about 1 % of |y|).
  *
  *   W        matrix descriptor
- *   x        device fp32 [batch][W.cols], not rotated, 4-byte aligned (16-byte
- *            alignment and W.cols % 8 == 0 allow vector loads); not modified
+ *   xq, sx   as written by cq_quantize_acts_int8 for W.cols columns (any
+ *            int8 values and finite scales are accepted); not modified
  *   batch    0 <= batch <= CQ_MAX_MATVEC_BATCH, and
  *            (batch + 1) * cols_pad + 32 * cols_pad / 128 <= 61440 (one
  *            workgroup holds the whole quantised activation), e.g. cols_pad
  *            up to 16384 at batch 1 or 2 and 6528 at batch 8; CQ_ERR_SHAPE
  *            otherwise
- *   y        device fp32 [batch][W.rows], 4-byte aligned, must not overlap x
- *            or the blob; fully overwritten (0 where cols == 0)
- *   No workspace.  Errors as cq_matvec.
+ *   y        device fp32 [batch][W.rows], 4-byte aligned, must not overlap
+ *            xq, sx or the blob; fully overwritten (0 where cols == 0)
+ *   Errors as cq_matvec.
  */
-cq_status cq_matvec_w2a8(const cq_matrix *W, const float *x, int64_t batch, float *y, void *stream);
+cq_status cq_matvec_w2a8_quantized(const cq_matrix *W, const int8_t *xq, const float *sx, int64_t batch, float *y,
+                                   void *stream);
+
+/*
+ * CQ-W2A8 from the fp32 activation: cq_quantize_acts_int8 into the workspace,
+ * then cq_matvec_w2a8_quantized (two kernels on the stream).
+ *
+ *   x        device fp32 [batch][W.cols], not rotated, 4-byte aligned; not
+ *            modified
+ *   batch, y as cq_matvec_w2a8_quantized; y must not overlap x
+ *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_W2A8), not
+ *            overlapping x, y or the blob
+ *   Errors as cq_matvec.
+ */
+cq_status cq_matvec_w2a8(const cq_matrix *W, const float *x, int64_t batch, float *y, void *workspace,
+                         uint64_t workspace_bytes, void *stream);
 
 /*
  * Row gather: the dense reconstruction of the indexed rows only (needle.js

@@ -29,8 +29,8 @@ def test_every_declared_symbol_is_exported():
     names = _declared_functions()
     assert set(names) == {"cq_version", "cq_status_string", "cq_blob_bytes", "cq_workspace_bytes",
                           "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_multi_matvec",
-                          "cq_rotate_multi_workspace_bytes", "cq_matvec_w2a8", "cq_gather_rows", "cq_gemm",
-                          "cq_quantize"}
+                          "cq_rotate_multi_workspace_bytes", "cq_quantize_acts_int8", "cq_matvec_w2a8_quantized",
+                          "cq_matvec_w2a8", "cq_gather_rows", "cq_gemm", "cq_quantize"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -222,35 +222,87 @@ def test_rotate_multi_matvec_validation():
     assert _multi([q4, big4], ws=FAKE + (1 << 31), wsb=nb) == OVERLAP  # workspace on y[0]
 
 
-def _w2a8(m, x=FAKE + (1 << 30), batch=1, y=FAKE + (1 << 31)):
-    return lib.cq_matvec_w2a8(ctypes.byref(m), ctypes.c_void_p(x), batch, ctypes.c_void_p(y), None)
+WS = FAKE + (1 << 33)
 
 
-def test_matvec_w2a8_validation():
+def _w2a8(m, x=FAKE + (1 << 30), batch=1, y=FAKE + (1 << 31), ws=WS, wsb=1 << 20):
+    return lib.cq_matvec_w2a8(ctypes.byref(m), ctypes.c_void_p(x), batch, ctypes.c_void_p(y), ctypes.c_void_p(ws),
+                              wsb, None)
+
+
+def _w2a8q(m, xq=FAKE + (1 << 30), sx=FAKE + (1 << 32), batch=1, y=FAKE + (1 << 31)):
+    return lib.cq_matvec_w2a8_quantized(ctypes.byref(m), ctypes.c_void_p(xq), ctypes.c_void_p(sx), batch,
+                                        ctypes.c_void_p(y), None)
+
+
+def _qacts(x=FAKE + (1 << 30), batch=2, cols=300, xq=FAKE + (1 << 31), sx=FAKE + (1 << 32)):
+    return lib.cq_quantize_acts_int8(ctypes.c_void_p(x), batch, cols, ctypes.c_void_p(xq), ctypes.c_void_p(sx), None)
+
+
+def _w8ws(m, batch):
+    out = ctypes.c_uint64(7)
+    st = lib.cq_workspace_bytes(3, ctypes.byref(m), batch, ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("call", [_w2a8, _w2a8q])
+def test_matvec_w2a8_validation(call):
     m, k = _matrix(bits=7, nbytes=0, levels=None)
-    assert _w2a8(m) == BITS
+    assert call(m) == BITS
     m, k = _matrix(levels=np.array([0.1, 0.0, 0.2, 0.3]))
-    assert _w2a8(m) == CODEBOOK
+    assert call(m) == CODEBOOK
     m, k = _matrix(nbytes=10)
-    assert _w2a8(m) == LENGTH
+    assert call(m) == LENGTH
     m, k = _matrix()
-    assert _w2a8(m, batch=9) == SHAPE and _w2a8(m, batch=-1) == SHAPE
-    assert _w2a8(m, batch=0) == OK
-    assert _w2a8(m, x=0) == NULL and _w2a8(m, y=0) == NULL
-    assert _w2a8(m, x=FAKE + (1 << 30) + 2) == ALIGN and _w2a8(m, y=FAKE + (1 << 31) + 1) == ALIGN
-    assert _w2a8(m, y=FAKE + (1 << 30) + 8) == OVERLAP and _w2a8(m, y=FAKE + 64) == OVERLAP
+    assert call(m, batch=9) == SHAPE and call(m, batch=-1) == SHAPE
+    assert call(m, batch=0) == OK
+    assert call(m, y=0) == NULL
+    assert call(m, y=FAKE + (1 << 31) + 1) == ALIGN
+    assert call(m, y=FAKE + (1 << 30) + 8) == OVERLAP and call(m, y=FAKE + 64) == OVERLAP
     # the whole quantised activation fits one workgroup: 16384 columns at
     # batch 1 and 2, not 3; 6528 at batch 8, not 6656
     wide, _ = _matrix(rows=4, cols=16384)
-    assert _w2a8(wide, batch=3) == SHAPE
-    assert _w2a8(wide, batch=2, y=0) == NULL  # past the shape check
+    assert call(wide, batch=3) == SHAPE
+    assert call(wide, batch=2, y=0) == NULL  # past the shape check
     b8, _ = _matrix(rows=4, cols=6528)
-    assert _w2a8(b8, batch=8, y=0) == NULL
+    assert call(b8, batch=8, y=0) == NULL
     b8x, _ = _matrix(rows=4, cols=6656)
-    assert _w2a8(b8x, batch=8) == SHAPE
+    assert call(b8x, batch=8) == SHAPE
     # nothing to do
     z, _ = _matrix(rows=0, blob=0)
-    assert _w2a8(z) == OK
+    assert call(z) == OK
+
+
+def test_matvec_w2a8_activation_and_workspace_checks():
+    m, k = _matrix()
+    assert _w2a8(m, x=0) == NULL and _w2a8(m, x=FAKE + (1 << 30) + 2) == ALIGN
+    assert _w2a8q(m, xq=0) == NULL and _w2a8q(m, sx=0) == NULL
+    assert _w2a8q(m, xq=FAKE + (1 << 30) + 8) == ALIGN and _w2a8q(m, sx=FAKE + (1 << 32) + 2) == ALIGN
+    assert _w2a8q(m, y=FAKE + (1 << 32) + 4) == OVERLAP  # y on sx
+    # workspace: batch x cols_pad int8, 256-aligned, then the fp32 scales
+    assert _w8ws(m, 1) == (OK, 256 + 2 * 4)
+    assert _w8ws(m, 3) == (OK, 768 + 3 * 2 * 4)
+    assert _w8ws(m, 9)[0] == SHAPE
+    wide, _ = _matrix(rows=4, cols=16384)
+    assert _w8ws(wide, 3)[0] == SHAPE and _w8ws(wide, 2) == (OK, 32768 + 2 * 128 * 4)
+    assert _w8ws(_matrix(rows=0, blob=0)[0], 1) == (OK, 0)
+    assert _w2a8(m, ws=0) == WORKSPACE and _w2a8(m, wsb=263) == WORKSPACE
+    assert _w2a8(m, ws=WS + 8) == ALIGN
+    assert _w2a8(m, ws=FAKE + (1 << 30) + 64) == OVERLAP  # workspace on x
+    assert _w2a8(m, ws=FAKE + (1 << 31)) == OVERLAP  # workspace on y
+    assert _w2a8(m, ws=FAKE + 128) == OVERLAP  # workspace on the blob
+    cz, _ = _matrix(cols=0)
+    assert _w2a8(cz, ws=0, y=0) == NULL  # y still required where cols == 0
+
+
+def test_quantize_acts_int8_validation():
+    assert _qacts(batch=-1) == SHAPE and _qacts(cols=-1) == SHAPE and _qacts(cols=(1 << 30) + 1) == SHAPE
+    assert _qacts(batch=0, x=0) == OK and _qacts(cols=0, xq=0) == OK
+    assert _qacts(x=0) == NULL and _qacts(xq=0) == NULL and _qacts(sx=0) == NULL
+    assert _qacts(x=FAKE + (1 << 30) + 2) == ALIGN and _qacts(xq=FAKE + (1 << 31) + 4) == ALIGN
+    assert _qacts(sx=FAKE + (1 << 32) + 1) == ALIGN
+    assert _qacts(xq=FAKE + (1 << 30) + 16) == OVERLAP  # xq on x
+    assert _qacts(sx=FAKE + (1 << 31) + 512) == OVERLAP  # sx on xq (2 x 384 bytes)
 
 
 def _gather(m, ids=FAKE + (1 << 30), n=4, out=FAKE + (1 << 31), dt=0):
@@ -348,7 +400,7 @@ def test_workspace_bytes():
     assert lib.cq_workspace_bytes(1, ctypes.byref(m), 4096, ctypes.byref(out)) == OK
     assert lib.cq_workspace_bytes(0, ctypes.byref(m), 9, ctypes.byref(out)) == SHAPE
     assert lib.cq_workspace_bytes(5, ctypes.byref(m), 1, ctypes.byref(out)) == SHAPE
-    assert lib.cq_workspace_bytes(3, ctypes.byref(m), 1, ctypes.byref(out)) == SHAPE
+    assert lib.cq_workspace_bytes(4, ctypes.byref(m), 1, ctypes.byref(out)) == SHAPE
     # empty K or no rows: nothing is launched, so no workspace (and no division by zero)
     for rows, cols in ((5, 0), (0, 256), (0, 0)):
         e, _ = _matrix(rows=rows, cols=cols)
@@ -371,6 +423,7 @@ def test_workspace_bytes():
 
 def test_binding_has_the_c_names():
     for n in ("cq_blob_bytes", "cq_workspace_bytes", "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec",
-              "cq_rotate_multi_matvec", "cq_rotate_multi_workspace_bytes", "cq_matvec_w2a8", "cq_gather_rows",
+              "cq_rotate_multi_matvec", "cq_rotate_multi_workspace_bytes", "cq_quantize_acts_int8",
+              "cq_matvec_w2a8_quantized", "cq_matvec_w2a8", "cq_gather_rows",
               "cq_gemm", "cq_quantize"):
         assert callable(getattr(cq, n))

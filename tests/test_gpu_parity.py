@@ -388,6 +388,46 @@ def test_rotation_is_the_oracle_butterfly_bit_for_bit():
         assert np.array_equal(got.view(np.uint32), oracle.rotate_acts_fp32(x).view(np.uint32)), (batch, cols)
 
 
+@pytest.mark.parametrize("batch,cols,offset", [
+    (1, 16384, 0), (3, 1000, 0), (11, 300, 1), (8, 6528, 0), (2, 128, 1), (1, 1, 0),
+])
+def test_quantize_acts_int8_is_the_oracle_bit_for_bit(batch, cols, offset):
+    # the int8 activations and their scales: every byte and every bit of the
+    # scales as the oracle's (same fp32 rotation, IEEE division, half-even);
+    # offset 1 makes x unaligned for vector loads
+    say("quantize acts int8", batch, cols, offset)
+    x = cq_inputs.activations(96, cols, batch, cols)
+    x[0, : min(cols, 128)] = 0.0  # an all-zero group: scale 0, codes 0
+    if batch > 2:
+        x[2, :5] *= 1e4  # a group dominated by a few values
+    buf = torch.zeros(batch * cols + offset, dtype=torch.float32, device=DEV)
+    xd = buf[offset:].view(batch, cols)
+    xd.copy_(_to_dev(x))
+    xq, sx = cq.cq_quantize_acts_int8(xd)
+    want_q, want_sx = oracle.quantize_acts_int8(oracle.rotate_acts_fp32(x))
+    assert np.array_equal(xq.cpu().numpy().astype(np.int64), want_q)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), want_sx.view(np.uint32))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("rows,cols,batch", [(700, 2048, 1), (129, 8192, 2), (64, 640, 8), (300, 16384, 1)])
+def test_matvec_w2a8_quantized_any_int8(bits, rows, cols, batch):
+    # the product alone on int8 activations the oracle draws (the full range,
+    # -128 included) and arbitrary positive scales; same inputs on both sides
+    say("w2a8 quantized", bits, rows, cols, batch)
+    W, blob = _random_cq(bits, rows, cols, 97 + batch)
+    levels = _levels(bits)
+    kpad = oracle.padded_cols(cols)
+    rng = np.random.default_rng(rows + bits)
+    xq = rng.integers(-128, 128, size=(batch, kpad)).astype(np.int8)
+    sx = rng.uniform(1e-3, 2e-2, size=(batch, kpad // 128)).astype(np.float32)
+    y = cq.cq_matvec_w2a8_quantized(W, _to_dev(xq), _to_dev(sx)).cpu().numpy()
+    terms = oracle.w2a8_group_terms(blob, bits, rows, cols, xq, sx, levels)
+    bound = (terms.shape[-1] + 8) * 2.0 ** -23 * np.abs(terms).sum(-1) + 1e-30
+    err = np.abs(y.astype(np.float64) - terms.sum(-1))
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 5])
 @pytest.mark.parametrize("rows,cols,batch", [
     (512, 512, 1), (300, 1000, 3), (257, 2048, 2), (64, 640, 8), (1, 128, 1),
