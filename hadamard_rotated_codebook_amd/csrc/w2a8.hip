@@ -364,10 +364,12 @@ struct W8RowArgs {
   float sc;
 };
 
-template <int SB, int B, int NPL>
+// XREG: the lane's activation bytes live in registers (B * NPL * XDW <= 64
+// dwords); otherwise each piece reads them from LDS.
+template <int SB, int B, int NPL, bool XREG>
 __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
   using G = RowGeom<SB>;
-  static_assert(B * NPL * G::XDW <= kRowMaxXdw, "activation registers");
+  static_assert(!XREG || B * NPL * G::XDW <= kRowMaxXdw, "activation registers");
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int next_step;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
   const int lps = a.lpr_shift, lpr = 1 << lps, li = lane & (lpr - 1), rsub = lane >> lps;
   const int rs = 64 >> lps;  // rows per step
   // ---- this lane's activations (pieces li + lpr * i) and their group scales
-  uint32_t xr8[B][NPL][G::XDW];
+  uint32_t xr8[XREG ? B : 1][XREG ? NPL : 1][G::XDW];
   float sxv[B][NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
@@ -395,9 +397,12 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
     const bool live = i < a.npl && p < npieces;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(xq + b * kpad + static_cast<int64_t>(live ? p : 0) * G::CP);
+      if constexpr (XREG) {
+        const uint32_t *src =
+            reinterpret_cast<const uint32_t *>(xq + b * kpad + static_cast<int64_t>(live ? p : 0) * G::CP);
 #pragma unroll
-      for (int w = 0; w < G::XDW; ++w) xr8[b][i][w] = live ? src[w] : 0u;
+        for (int w = 0; w < G::XDW; ++w) xr8[b][i][w] = live ? src[w] : 0u;
+      }
       // only the group's first lane scales the group's summed dot
       sxv[b][i] = live && (p % G::PPG) == 0 ? sxs[(p / G::PPG) * 8 + b] : 0.0f;
     }
@@ -462,8 +467,21 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         int dot = 0;
+        if constexpr (XREG) {
 #pragma unroll
-        for (int w = 0; w < G::XDW; ++w) dot = __builtin_amdgcn_sdot4(dq[w >> 2][w & 3], static_cast<int>(xr8[b][i][w]), dot, false);
+          for (int w = 0; w < G::XDW; ++w)
+            dot = __builtin_amdgcn_sdot4(dq[w >> 2][w & 3], static_cast<int>(xr8[b][i][w]), dot, false);
+        } else {
+          // a group's lanes are all live or all past K; the latter read piece 0
+          const int p = li + lpr * i;
+          const int32x4 *src = reinterpret_cast<const int32x4 *>(xq + b * kpad + (p < npieces ? p : 0) * G::CP);
+#pragma unroll
+          for (int w4 = 0; w4 < G::XDW / 4; ++w4) {
+            const int32x4 xv = src[w4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) dot = __builtin_amdgcn_sdot4(dq[w4][w], xv[w], dot, false);
+          }
+        }
         dot += __builtin_amdgcn_mov_dpp(dot, 0xb1, 0xf, 0xf, false);                     // xor 1: the group's 2 pieces
         if constexpr (G::PPG == 4) dot += __builtin_amdgcn_mov_dpp(dot, 0x4e, 0xf, 0xf, false);  // xor 2: its 4
         acc[b] = fmaf(static_cast<float>(dot), sxv[b][i] * nn, acc[b]);
@@ -513,18 +531,32 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
 
 typedef void (*W8RowKernel)(W8RowArgs);
 
+// Pieces per lane: with the activation in registers, as many as 64 dwords
+// hold; from LDS, enough for 16384 columns.
 template <int SB, int B>
-constexpr int row_npl() { return kRowMaxXdw / (B * RowGeom<SB>::XDW); }
-
+constexpr int row_npl_reg() { return kRowMaxXdw / (B * RowGeom<SB>::XDW); }
 template <int SB>
-W8RowKernel pick_row_b(int batch) {
-  return batch == 1 ? w2a8_row_kernel<SB, 1, row_npl<SB, 1>()> : w2a8_row_kernel<SB, 2, row_npl<SB, 2>()>;
+constexpr int row_npl_lds() { return 16384 * SB / 8 / RowGeom<SB>::PB / 64; }
+
+constexpr int kRowMaxBatch = 4;
+
+// The row kernel for (storage bits, batch, pieces per lane): registers when
+// they hold the lane's activations, else LDS; nullptr past its limits.
+template <int SB>
+W8RowKernel pick_row_sb(int batch, int npl) {
+  if (batch == 1 && npl <= row_npl_reg<SB, 1>()) return w2a8_row_kernel<SB, 1, row_npl_reg<SB, 1>(), true>;
+  if (batch == 2 && npl <= row_npl_reg<SB, 2>()) return w2a8_row_kernel<SB, 2, row_npl_reg<SB, 2>(), true>;
+  if (npl > row_npl_lds<SB>()) return nullptr;
+  switch (batch) {  // batch 1 always fits registers
+    case 2: return w2a8_row_kernel<SB, 2, row_npl_lds<SB>(), false>;
+    case 3: return w2a8_row_kernel<SB, 3, row_npl_lds<SB>(), false>;
+    case 4: return w2a8_row_kernel<SB, 4, row_npl_lds<SB>(), false>;
+    default: return nullptr;
+  }
 }
 
-int row_max_npl(int sb, int batch) {
-  if (sb == 2) return batch == 1 ? row_npl<2, 1>() : row_npl<2, 2>();
-  if (sb == 3) return batch == 1 ? row_npl<3, 1>() : row_npl<3, 2>();
-  return batch == 1 ? row_npl<4, 1>() : row_npl<4, 2>();
+W8RowKernel pick_row(int sb, int batch, int npl) {
+  return sb == 2 ? pick_row_sb<2>(batch, npl) : (sb == 3 ? pick_row_sb<3>(batch, npl) : pick_row_sb<4>(batch, npl));
 }
 
 // Resident workgroups per CU of a row kernel at an LDS size, cached per
@@ -555,7 +587,14 @@ uint64_t w2a8_lds_bytes(int64_t kpad, int64_t batch) {
   return static_cast<uint64_t>(batch + 1) * kpad + static_cast<uint64_t>(kpad / CQ_GROUP) * 32;
 }
 
-static bool use_row_kernel(int64_t kpad, int64_t batch) { return batch <= 2 && batch * kpad <= 16384; }
+// LDS of a row-kernel workgroup: the batch's int8 activations and the scales.
+static uint64_t row_lds_bytes(int64_t kpad, int64_t batch) {
+  return static_cast<uint64_t>(batch) * kpad + static_cast<uint64_t>(kpad / CQ_GROUP) * 32;
+}
+
+static bool use_row_kernel(int64_t kpad, int64_t batch) {
+  return batch <= kRowMaxBatch && kpad <= 16384 && row_lds_bytes(kpad, batch) <= kW2a8MaxLds;
+}
 
 bool w2a8_fits(int64_t kpad, int64_t batch) {
   if (kpad > 0 && kpad % CQ_GROUP == 0 && batch >= 1 && use_row_kernel(kpad, batch)) return true;
@@ -592,7 +631,11 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t kpad
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
     cu_cache[dev] = cus;
   }
-  if (use_row_kernel(kpad, batch)) {
+  // Batch 1-2 and 3 at two bits stream rows (measured faster at 65536 x
+  // 16384 and 131072 x 8192); larger batches share the decode over the
+  // matrix cores unless their activation does not fit that kernel's LDS.
+  const bool mfma_fits = batch <= kMaxBatch && w2a8_lds_bytes(kpad, batch) <= kW2a8MaxLds;
+  if (use_row_kernel(kpad, batch) && (batch <= 2 || (batch == 3 && sb == 2) || !mfma_fits)) {
     W8RowArgs r;
     r.packed = blob;
     r.row_bytes = kpad * sb / 8;
@@ -616,10 +659,9 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t kpad
     r.nsteps = static_cast<int32_t>(nsteps);
     for (int i = 0; i < 4; ++i) r.c8[i] = cb.c8[i];
     r.sc = cb.sc;
-    const size_t lds = static_cast<size_t>(batch * kpad + (kpad / CQ_GROUP) * 32);
-    const W8RowKernel k = sb == 2 ? pick_row_b<2>(static_cast<int>(batch))
-                                  : (sb == 3 ? pick_row_b<3>(static_cast<int>(batch)) : pick_row_b<4>(static_cast<int>(batch)));
-    if (r.npl > row_max_npl(sb, static_cast<int>(batch))) return hipErrorInvalidValue;
+    const size_t lds = static_cast<size_t>(row_lds_bytes(kpad, batch));
+    const W8RowKernel k = pick_row(sb, static_cast<int>(batch), r.npl);
+    if (!k) return hipErrorInvalidValue;
     // one wave of workgroups: as many as the CUs hold at once (registers and
     // LDS), each over a contiguous range of row steps
     const int per_cu = row_occupancy(reinterpret_cast<const void *>(k), lds, dev);

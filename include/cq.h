@@ -284,11 +284,12 @@ cq_status cq_quantize_acts_int8(const float *x, int64_t batch, int64_t cols, int
  *   W        matrix descriptor
  *   xq, sx   as written by cq_quantize_acts_int8 for W.cols columns (any
  *            int8 values and finite scales are accepted); not modified
- *   batch    0 <= batch <= CQ_MAX_MATVEC_BATCH, and
- *            (batch + 1) * cols_pad + 32 * cols_pad / 128 <= 61440 (one
- *            workgroup holds the whole quantised activation), e.g. cols_pad
- *            up to 16384 at batch 1 or 2 and 6528 at batch 8; CQ_ERR_SHAPE
- *            otherwise
+ *   batch    0 <= batch <= CQ_MAX_MATVEC_BATCH, and one workgroup holds
+ *            the whole quantised activation: with P = 32 * cols_pad / 128,
+ *            batch * cols_pad + P <= 61440 for batch <= 4 and cols_pad <=
+ *            16384, or (batch + 1) * cols_pad + P <= 61440; e.g. cols_pad up
+ *            to 27264 at batch 1, 16384 at batch 2 and 3, 14336 at batch 4,
+ *            6528 at batch 8; CQ_ERR_SHAPE otherwise
  *   y        device fp32 [batch][W.rows], 4-byte aligned, must not overlap
  *            xq, sx or the blob; fully overwritten (0 where cols == 0)
  *   Errors as cq_matvec.

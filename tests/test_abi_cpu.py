@@ -259,11 +259,16 @@ def test_matvec_w2a8_validation(call):
     assert call(m, y=0) == NULL
     assert call(m, y=FAKE + (1 << 31) + 1) == ALIGN
     assert call(m, y=FAKE + (1 << 30) + 8) == OVERLAP and call(m, y=FAKE + 64) == OVERLAP
-    # the whole quantised activation fits one workgroup: 16384 columns at
-    # batch 1 and 2, not 3; 6528 at batch 8, not 6656
+    # the whole quantised activation fits one workgroup: 16384 columns up
+    # to batch 3, not 4; 14336 at batch 4, not 14464; 27264 at batch 1, not
+    # 27392; 6528 at batch 8, not 6656
     wide, _ = _matrix(rows=4, cols=16384)
-    assert call(wide, batch=3) == SHAPE
-    assert call(wide, batch=2, y=0) == NULL  # past the shape check
+    assert call(wide, batch=4) == SHAPE
+    assert call(wide, batch=3, y=0) == NULL  # past the shape check
+    assert call(_matrix(rows=4, cols=14336)[0], batch=4, y=0) == NULL
+    assert call(_matrix(rows=4, cols=14464)[0], batch=4) == SHAPE
+    assert call(_matrix(rows=4, cols=27264)[0], batch=1, y=0) == NULL
+    assert call(_matrix(rows=4, cols=27392)[0], batch=1) == SHAPE
     b8, _ = _matrix(rows=4, cols=6528)
     assert call(b8, batch=8, y=0) == NULL
     b8x, _ = _matrix(rows=4, cols=6656)
@@ -284,7 +289,7 @@ def test_matvec_w2a8_activation_and_workspace_checks():
     assert _w8ws(m, 3) == (OK, 768 + 3 * 2 * 4)
     assert _w8ws(m, 9)[0] == SHAPE
     wide, _ = _matrix(rows=4, cols=16384)
-    assert _w8ws(wide, 3)[0] == SHAPE and _w8ws(wide, 2) == (OK, 32768 + 2 * 128 * 4)
+    assert _w8ws(wide, 4)[0] == SHAPE and _w8ws(wide, 2) == (OK, 32768 + 2 * 128 * 4)
     assert _w8ws(_matrix(rows=0, blob=0)[0], 1) == (OK, 0)
     assert _w2a8(m, ws=0) == WORKSPACE and _w2a8(m, wsb=263) == WORKSPACE
     assert _w2a8(m, ws=WS + 8) == ALIGN

@@ -433,6 +433,7 @@ def test_matvec_w2a8_quantized_any_int8(bits, rows, cols, batch):
     (512, 512, 1), (300, 1000, 3), (257, 2048, 2), (64, 640, 8), (1, 128, 1),
     (1000, 16384, 1), (9, 16384, 2), (33, 6528, 8), (130, 5000, 4),
     (100, 768, 1), (45, 1536, 2), (77, 4096, 1), (5, 8192, 2),
+    (20, 16384, 3), (17, 14336, 4), (3, 27264, 1),
 ])
 def test_matvec_w2a8(bits, rows, cols, batch):
     say("w2a8", bits, rows, cols, batch)
@@ -472,7 +473,7 @@ def test_matvec_w2a8_degenerate_and_limits():
     assert torch.equal(y, torch.zeros_like(y))
     Wb, _ = _random_cq(2, 8, 16384, 95)
     with pytest.raises(cq.CQError) as e:
-        cq.cq_matvec_w2a8(Wb, torch.zeros((3, 16384), device=DEV))
+        cq.cq_matvec_w2a8(Wb, torch.zeros((4, 16384), device=DEV))
     assert e.value.status == 4  # CQ_ERR_SHAPE: the quantised activation exceeds one workgroup's LDS
     a = cq.cq_matvec_w2a8(W, x).clone()
     assert torch.equal(a, cq.cq_matvec_w2a8(W, x))  # deterministic
