@@ -45,9 +45,10 @@ def _gen(*key):
 
 def codebook(bits, kind="empirical"):
     """fp32 ascending levels for CQ ``bits`` (2, 3, 4); ``None`` for the
-    ternary marker 5, whose levels are analytic.  ``kind`` is "empirical"
-    (exporter procedure) or "gaussian" (analytic Lloyd-Max / sqrt(128))."""
-    if bits == 5:
+    ternary marker 5 and binary 1, whose levels are analytic.  ``kind`` is
+    "empirical" (exporter procedure) or "gaussian" (analytic Lloyd-Max /
+    sqrt(128))."""
+    if bits in (1, 5):
         return None
     if bits == 2 and kind == "empirical":
         return np.array(CQ2_PRINTED, dtype=np.float32)

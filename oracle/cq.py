@@ -12,11 +12,11 @@ import math
 import numpy as np
 
 __all__ = [
-    "GROUP", "TERNARY_MARKER", "TERNARY_LEVEL",
+    "GROUP", "TERNARY_MARKER", "TERNARY_LEVEL", "BINARY_MARKER",
     "sylvester", "hadamard", "storage_bits", "bits_per_weight",
     "padded_cols", "blob_bytes",
     "gaussian_lloyd_max", "ternary_level", "lloyd_max_empirical",
-    "ternary_level32", "codebook_for",
+    "ternary_level32", "binary_level", "binary_level32", "codebook_for",
     "rotate_fp32", "nearest_level", "encode", "quantize",
     "pack_codes", "unpack_codes", "make_blob", "split_blob",
     "level_values", "dequantize", "gather_rows", "rotate_acts",
@@ -34,6 +34,12 @@ reference, file layout]."""
 TERNARY_LEVEL = 1.2240064
 """Analytic ternary level before division by sqrt(group), as printed in
 [needle.js tutorial, "Shared codebooks"]."""
+
+BINARY_MARKER = 1
+"""Record ``bits`` value of binary weights, one bit per weight, eight per
+byte [cact-format post, "Cactus Quants"].  Reading: the pages name binary
+weights and their packing but no marker; 1, the number of bits stored, is
+the plainest."""
 
 
 # --------------------------------------------------------------------------
@@ -67,10 +73,10 @@ def hadamard(n=GROUP):
 # Sizes
 
 def storage_bits(bits):
-    """Bits stored per index: ``bits`` for codebook widths 2/3/4, and 2 for the
-    ternary marker 5, whose values are 2-bit crumbs [cact-format post, "Cactus
-    Quants"; OpenNeedle reference, file layout]."""
-    if bits not in (2, 3, 4, TERNARY_MARKER):
+    """Bits stored per index: ``bits`` for codebook widths 2/3/4 and for binary
+    (1), and 2 for the ternary marker 5, whose values are 2-bit crumbs
+    [cact-format post, "Cactus Quants"; OpenNeedle reference, file layout]."""
+    if bits not in (BINARY_MARKER, 2, 3, 4, TERNARY_MARKER):
         raise ValueError(f"unsupported CQ bits {bits}")
     return 2 if bits == TERNARY_MARKER else bits
 
@@ -175,19 +181,45 @@ def ternary_level32(group=GROUP):
     return np.float32(TERNARY_LEVEL / math.sqrt(group))
 
 
+def binary_level():
+    """Positive level of the 2-level Lloyd-Max quantiser of N(0, 1), float64.
+
+    The pages say binary weights have a closed-form centroid and store no
+    codebook for them [cact-format post, "Five regions", "Cactus Quants"].
+    Reading: with the threshold at 0 (the midpoint of -c and +c) each level is
+    the mean of its half of N(0, 1), E[Z | Z > 0] = sqrt(2/pi).
+    """
+    return math.sqrt(2.0 / math.pi)
+
+
+def binary_level32(group=GROUP):
+    """fp32 binary level sqrt(2/pi) / sqrt(group): the unit-sphere coordinates
+    of a 128-group are N(0, 1/group) (the same division as the ternary and
+    Lloyd-Max levels).  Reading: divide in float64, then round once to fp32."""
+    return np.float32(binary_level() / math.sqrt(group))
+
+
 def codebook_for(bits, levels=None, group=GROUP):
     """The fp32 ascending levels an index selects.
 
     Widths 2/3/4 take the caller's 4/8/16 levels (the file's embedded codebook
     is authoritative [OpenNeedle reference, codebook generation]).  The ternary
     marker uses the analytic {-a, 0, +a}/sqrt(group) and takes no levels
-    [needle.js tutorial, "Shared codebooks"].
+    [needle.js tutorial, "Shared codebooks"]; binary uses {-c, +c} of
+    ``binary_level32`` and takes none either.
     """
     if bits == TERNARY_MARKER:
         if levels is not None:
             raise ValueError("ternary levels are analytic; pass levels=None")
         a = ternary_level32(group)
         return np.array([-a, 0.0, a], dtype=np.float32)
+    if bits == BINARY_MARKER:
+        # Reading: code 0 selects -c and code 1 selects +c (ascending, as the
+        # codes of the other widths index ascending levels).
+        if levels is not None:
+            raise ValueError("binary levels are analytic; pass levels=None")
+        c = binary_level32(group)
+        return np.array([-c, c], dtype=np.float32)
     storage_bits(bits)
     lv = np.asarray(levels, dtype=np.float32)
     if lv.shape != (1 << bits,):
@@ -316,6 +348,9 @@ def unpack_codes(packed, bits, k):
     * 4-bit: byte = row[col >> 1]; code = (byte >> ((col & 1)*4)) & 15
     * 3-bit: bit = 3*col; window = row[bit>>3] | row[(bit>>3)+1] << 8;
       code = (window >> (bit & 7)) & 7
+    * 1-bit (reading: the same LSB-first stream at eight per byte
+      [cact-format post, "Cactus Quants"]): byte = row[col >> 3];
+      code = (byte >> (col & 7)) & 1
 
     Reading: the 3-bit window's second byte is taken as 0 past the end of the
     row; the last code never needs it, so no byte outside the row is read.
@@ -323,6 +358,8 @@ def unpack_codes(packed, bits, k):
     b = storage_bits(bits)
     p = np.asarray(packed, dtype=np.uint8).astype(np.int64)
     col = np.arange(k)
+    if b == 1:
+        return ((p[:, col >> 3] >> (col & 7)) & 1).astype(np.uint8)
     if b == 2:
         return ((p[:, col >> 2] >> ((col & 3) * 2)) & 3).astype(np.uint8)
     if b == 4:

@@ -51,6 +51,6 @@ def test_workload_sizes():
 
 
 def test_invalid_parameters():
-    for args in [(1, 128, 1, 1), (6, 128, 1, 1), (2, 96, 1, 1), (2, 128, -1, 1)]:
+    for args in [(0, 128, 1, 1), (6, 128, 1, 1), (2, 96, 1, 1), (2, 128, -1, 1)]:
         with pytest.raises(ValueError):
             oracle.blob_bytes(*args)

@@ -120,13 +120,13 @@ def test_product_is_exact_on_the_int8_grid(bits):
     assert np.allclose(got, x_rot @ w_rot.T, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
 def test_product_within_the_quantisation_bound(bits):
     # per group: |<c, xr> - sc sx <c8, q>| <= max|c| * sum|xr - sx q|
     #            + max|c - sc c8| * sx * sum|q| + the fp32 rotation error;
     # summed with the norms, against the exact float64 product
     rows, cols = 24, 1000
-    levels = None if bits == 5 else cq_inputs.codebook(bits)
+    levels = cq_inputs.codebook(bits)
     blob = oracle.quantize(cq_inputs.master(50, bits, rows, cols), bits, levels)
     x = cq_inputs.activations(50, bits, 3, cols)
     got = oracle.matvec_w2a8(blob, bits, rows, cols, x, levels)
@@ -134,7 +134,7 @@ def test_product_within_the_quantisation_bound(bits):
     xr = oracle.rotate_acts_fp32(x).astype(np.float64)
     q, sx = oracle.quantize_acts_int8(oracle.rotate_acts_fp32(x))
     c8, sc = oracle.codebook_int8(bits, levels)
-    lv = (np.array([0.0, 1.0, -2.0, -1.0]) * float(sc)) if bits == 5 else np.asarray(levels, np.float64)
+    lv = (np.array([0.0, 1.0, -2.0, -1.0]) * float(sc)) if bits == 5 else oracle.codebook_for(bits, levels).astype(np.float64)
     cmax, cerr = np.max(np.abs(lv)), np.max(np.abs(lv - c8 * float(sc)))
     s = np.repeat(sx.astype(np.float64), 128, axis=1)
     act_err = np.abs(xr - q * s).reshape(3, 8, 128).sum(-1)             # sum |xr - sx q| per group
