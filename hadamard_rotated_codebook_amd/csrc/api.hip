@@ -21,9 +21,10 @@ cq_status hip_status(hipError_t e) { return e == hipSuccess ? CQ_OK : CQ_ERR_HIP
 int64_t padded(int64_t cols) { return (cols + CQ_GROUP - 1) / CQ_GROUP * CQ_GROUP; }
 
 // Blob length rows * (cols_pad*b/8 + 2*cols_pad/128) (needle.js tutorial,
-// "Anatomy of a CQ matrix"; the ternary marker stores 2-bit crumbs).
+// "Anatomy of a CQ matrix"; the ternary marker stores 2-bit crumbs, binary
+// one bit per weight).
 cq_status blob_bytes_impl(int32_t bits, int32_t group, int64_t rows, int64_t cols, uint64_t *out) {
-  if (bits != 2 && bits != 3 && bits != 4 && bits != 5) return CQ_ERR_BITS;
+  if (bits < 1 || bits > 5) return CQ_ERR_BITS;
   if (group != CQ_GROUP) return CQ_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows > CQ_MAX_DIM || cols > CQ_MAX_DIM) return CQ_ERR_SHAPE;
   const uint64_t kpad = static_cast<uint64_t>(padded(cols));
@@ -42,6 +43,13 @@ cq_status code_levels(int bits, const float *levels, cq::CodeLevels *lev) {
     lev->v[1] = a;
     lev->v[2] = -2.0f * a;
     lev->v[3] = -a;
+    return CQ_OK;
+  }
+  if (bits == 1) {  // code 0 -> -c, code 1 -> +c
+    if (levels) return CQ_ERR_CODEBOOK;
+    const float c = cq::binary_level_f32();
+    lev->v[0] = -c;
+    lev->v[1] = c;
     return CQ_OK;
   }
   if (!levels) return CQ_ERR_CODEBOOK;
@@ -73,6 +81,10 @@ namespace cq {
 
 float ternary_level_f32() { return static_cast<float>(1.2240064 / std::sqrt(128.0)); }
 
+// sqrt(2/pi) / sqrt(128), the mean of the positive half of N(0, 1/128),
+// rounded once to fp32.
+float binary_level_f32() { return static_cast<float>(std::sqrt(2.0 / 3.14159265358979323846) / std::sqrt(128.0)); }
+
 }  // namespace cq
 
 extern "C" {
@@ -83,11 +95,11 @@ const char *cq_status_string(cq_status status) {
   switch (status) {
     case CQ_OK: return "ok";
     case CQ_ERR_NULL: return "a required pointer is NULL";
-    case CQ_ERR_BITS: return "bits must be 2, 3, 4 or 5 (ternary marker)";
+    case CQ_ERR_BITS: return "bits must be 1 (binary), 2, 3, 4 or 5 (ternary marker)";
     case CQ_ERR_GROUP: return "group must be 128";
     case CQ_ERR_SHAPE: return "a dimension is negative or above its limit";
     case CQ_ERR_LENGTH: return "Inconsistent CQ matrix length";
-    case CQ_ERR_CODEBOOK: return "levels must be 2^bits strictly ascending finite floats (NULL for ternary)";
+    case CQ_ERR_CODEBOOK: return "levels must be 2^bits strictly ascending finite floats (NULL for binary and ternary)";
     case CQ_ERR_DTYPE: return "unsupported element type";
     case CQ_ERR_WORKSPACE: return "workspace smaller than cq_workspace_bytes()";
     case CQ_ERR_ALIGN: return "a device pointer is not aligned as documented";
@@ -122,7 +134,7 @@ cq_status cq_workspace_bytes(int32_t op, const cq_matrix *W, int64_t batch, uint
   } else if (op == CQ_OP_W2A8) {
     if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
     const int64_t kpad = padded(W->cols);
-    if (kpad > 0 && batch > 0 && !cq::w2a8_fits(kpad, batch)) return CQ_ERR_SHAPE;
+    if (kpad > 0 && batch > 0 && !cq::w2a8_fits(W->bits, kpad, batch)) return CQ_ERR_SHAPE;
     *bytes = W->rows && kpad && batch ? cq::w2a8_workspace_bytes(kpad, batch) : 0;
   } else {
     return CQ_ERR_SHAPE;
@@ -332,7 +344,7 @@ static cq_status check_w2a8(const cq_matrix *W, int64_t batch, float *y, cq::Cod
   if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
   if (batch == 0 || W->rows == 0) return CQ_OK;
   *kpad = padded(W->cols);
-  if (*kpad > 0 && !cq::w2a8_fits(*kpad, batch)) return CQ_ERR_SHAPE;
+  if (*kpad > 0 && !cq::w2a8_fits(W->bits, *kpad, batch)) return CQ_ERR_SHAPE;
   if (!y) return CQ_ERR_NULL;
   if (!aligned(y, 4)) return CQ_ERR_ALIGN;
   if (overlaps(y, static_cast<uint64_t>(batch) * W->rows * 4, W->blob, W->blob_bytes)) return CQ_ERR_OVERLAP;
@@ -411,6 +423,7 @@ cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c, void 
   cq::CodeLevels lev;
   cq_status st = check_matrix(W, &lev);
   if (st != CQ_OK) return st;
+  if (W->bits == 1) return CQ_ERR_BITS;  // no binary decoder on the bf16 matrix cores
   if (m < 0 || m > CQ_MAX_DIM) return CQ_ERR_SHAPE;
   if (m == 0 || W->rows == 0) return CQ_OK;
   if (!c) return CQ_ERR_NULL;
@@ -457,6 +470,11 @@ cq_status cq_quantize(const float *w, int64_t rows, int64_t cols, int32_t bits, 
     tab.code_of_index[0] = 3;  // -a -> crumb 11
     tab.code_of_index[1] = 0;  //  0 -> crumb 00
     tab.code_of_index[2] = 1;  // +a -> crumb 01
+  } else if (bits == 1) {
+    tab.nlevels = 2;
+    tab.mid[0] = 0.0;  // the midpoint of -c and +c
+    tab.code_of_index[0] = 0;
+    tab.code_of_index[1] = 1;
   } else {
     tab.nlevels = 1 << bits;
     for (int j = 0; j + 1 < tab.nlevels; ++j)

@@ -24,12 +24,16 @@ struct EncodeTable {
   int32_t nlevels;
 };
 
-// Storage width of one index: 2 for ternary crumbs, else bits.
+// Storage width of one index: 2 for ternary crumbs, else bits (1 for binary).
 inline int storage_bits(int bits) { return bits == 5 ? 2 : bits; }
 
 // fp32 ternary level: a / sqrt(128) with a = 1.2240064, divided in double and
 // rounded once (needle.js tutorial, "Shared codebooks").
 float ternary_level_f32();
+
+// fp32 binary level sqrt(2/pi) / sqrt(128), computed in double and rounded
+// once; binary code 0 selects -c, code 1 +c.
+float binary_level_f32();
 
 // Launchers.  Arguments are already validated; sizes are non-zero unless a
 // launcher documents otherwise.
@@ -109,7 +113,7 @@ struct Int8Codebook {
 // group scales; the kernel takes at most kW2a8MaxLds.
 constexpr uint64_t kW2a8MaxLds = 60 * 1024;
 uint64_t w2a8_lds_bytes(int64_t kpad, int64_t batch);
-bool w2a8_fits(int64_t kpad, int64_t batch);
+bool w2a8_fits(int bits, int64_t kpad, int64_t batch);
 // Quantised activations of cq_matvec_w2a8: int8 [batch][kpad] (column order)
 // then, 256 bytes aligned, the scales fp32 [batch][kpad / 128].
 uint64_t w2a8_workspace_bytes(int64_t kpad, int64_t batch);

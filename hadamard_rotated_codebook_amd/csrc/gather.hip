@@ -110,7 +110,8 @@ typedef void (*GKernel)(GArgs);
 
 template <int OUT>
 GKernel pick_sb(int sb) {
-  return sb == 2 ? gather_kernel<2, OUT> : (sb == 3 ? gather_kernel<3, OUT> : gather_kernel<4, OUT>);
+  return sb == 1 ? gather_kernel<1, OUT>
+                 : (sb == 2 ? gather_kernel<2, OUT> : (sb == 3 ? gather_kernel<3, OUT> : gather_kernel<4, OUT>));
 }
 
 }  // namespace

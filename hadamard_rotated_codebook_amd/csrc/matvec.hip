@@ -59,11 +59,12 @@ constexpr int kRowsPerBlock = kWaves * kRowsPerWave;  // rows of a full row bloc
 constexpr uint32_t kRawBufferWord3 = 0x00020000u;     // buffer descriptor: raw, 32-bit data format
 constexpr uint32_t kOutOfRange = 0x7ffff000u;         // a buffer offset past any descriptor's length
 
-// Geometry of a storage width SB (2: CQ2 and ternary crumbs, 3: CQ3, 4: CQ4).
+// Geometry of a storage width SB (1: binary, 2: CQ2 and ternary crumbs,
+// 3: CQ3, 4: CQ4).
 template <int SB>
 struct Geom {
   static constexpr int LANE_BYTES = SB == 3 ? 12 : 4;            // packed bytes per lane and row
-  static constexpr int LANE_COLS = LANE_BYTES * 8 / SB;          // 16, 32, 8 columns per lane
+  static constexpr int LANE_COLS = LANE_BYTES * 8 / SB;          // 32, 16, 32, 8 columns per lane
   static constexpr int IDX_BITS = SB == 3 ? 6 : 8;               // bits of a table index
   static constexpr int ENTRIES = 1 << IDX_BITS;                  // entries per table
   static constexpr int CODES = IDX_BITS / SB;                    // codes per table index
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
   // Thread (wave w, lane) builds 32 slots of its lane: the pair of positions
   // q = w / (16 / PAIRS) (both halves of a slot) at indices v = vb + i, i < 32.
   constexpr int PAIRS = G::POSITIONS / 2;               // 2, 8, 2 pairs of positions
-  constexpr int XQ = SB == 2 ? 8 : 4;                   // activations of a pair of positions
+  constexpr int XQ = 2 * G::CODES;                      // activations of a pair of positions
   const int q = wave / (kWaves / PAIRS);
   const int vb = (wave % (kWaves / PAIRS)) * 32;
   float xq[XQ];
@@ -349,7 +350,25 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
     for (int c = 0; c < XQ; ++c) xq[c] *= scale;  // exact: a power of two
     uint32_t *const out = reinterpret_cast<uint32_t *>(lds + q * G::REGION + vb * 256 + lane * 4);
     const float *lev = a.lev.v;
-    if constexpr (SB == 2) {
+    if constexpr (SB == 1) {
+      // position h of the pair: bit m of v selects -c or +c for column 8h + m;
+      // bits 5..7 are fixed for this thread, bits 0..1 and 2..4 are summed
+      // from small tables
+      float a2[2][4], b3[2][8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float fixed = lev[(vb >> 5) & 1] * xq[8 * h + 5] + lev[(vb >> 6) & 1] * xq[8 * h + 6] +
+                            lev[(vb >> 7) & 1] * xq[8 * h + 7];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a2[h][t] = lev[t & 1] * xq[8 * h] + lev[(t >> 1) & 1] * xq[8 * h + 1];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          b3[h][t] = lev[t & 1] * xq[8 * h + 2] + lev[(t >> 1) & 1] * xq[8 * h + 3] +
+                     lev[(t >> 2) & 1] * xq[8 * h + 4] + fixed;
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) out[i * 64] = pack_half2(a2[0][i & 3] + b3[0][i >> 2], a2[1][i & 3] + b3[1][i >> 2]);
+    } else if constexpr (SB == 2) {
       // position h of the pair: codes (v&3, v>>2&3, v>>4&3, v>>6) of columns 4h..4h+3
       const int c2hi = (vb >> 5) & 1, c3 = vb >> 6;  // fixed for this thread
       float hi[2][2];
@@ -467,23 +486,27 @@ struct MvShape {
 };
 
 int slice_cols(int sb) {
-  return sb == 2 ? Geom<2>::SLICE_COLS : (sb == 3 ? Geom<3>::SLICE_COLS : Geom<4>::SLICE_COLS);
+  return sb == 1 ? Geom<1>::SLICE_COLS
+                 : (sb == 2 ? Geom<2>::SLICE_COLS : (sb == 3 ? Geom<3>::SLICE_COLS : Geom<4>::SLICE_COLS));
 }
 
 typedef void (*MvKernel)(MvArgs);
 
 MvKernel pick_kernel(int sb, bool rot = false) {
-  if (rot) return sb == 2 ? matvec_kernel<2, true> : (sb == 3 ? matvec_kernel<3, true> : matvec_kernel<4, true>);
-  return sb == 2 ? matvec_kernel<2, false> : (sb == 3 ? matvec_kernel<3, false> : matvec_kernel<4, false>);
+  if (rot)
+    return sb == 1 ? matvec_kernel<1, true>
+                   : (sb == 2 ? matvec_kernel<2, true> : (sb == 3 ? matvec_kernel<3, true> : matvec_kernel<4, true>));
+  return sb == 1 ? matvec_kernel<1, false>
+                 : (sb == 2 ? matvec_kernel<2, false> : (sb == 3 ? matvec_kernel<3, false> : matvec_kernel<4, false>));
 }
 
 int max_grid(int sb) {
   // Resident workgroups per CU for this kernel, times the CU count of the
   // current device; computed once per (device, width).
-  static int cache[64][3];
+  static int cache[64][4];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int &c = cache[dev][sb - 2];
+  int &c = cache[dev][sb - 1];
   if (c == 0) {
     int per_cu = 1, cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(pick_kernel(sb)),
@@ -531,30 +554,31 @@ namespace cq {
 // (batch 1: 8.0 us at 512 x 512 and 14.2 us at 16384 x 4096, against 13.0
 // and 16.4 us on the lookup tables) and slower from 128 M.  With more
 // columns, batch 1 takes the lookup tables from 2^23 weights and the batched
-// matrix-core kernel below.
-static bool use_small(int64_t rows, int64_t kpad, int64_t batch) {
-  return rows * kpad <= kSmallMaxWeights && small_matvec_fits(kpad, batch);
+// matrix-core kernel below.  Binary matrices always take the lookup tables
+// (8 weights per lookup), one pass per batch row.
+static bool use_small(int bits, int64_t rows, int64_t kpad, int64_t batch) {
+  return bits != 1 && rows * kpad <= kSmallMaxWeights && small_matvec_fits(kpad, batch);
 }
 
-static bool use_lut(int64_t rows, int64_t kpad, int64_t batch) {
-  return batch == 1 && rows * kpad >= static_cast<int64_t>(CQ_LUT_MIN_WEIGHTS);
+static bool use_lut(int bits, int64_t rows, int64_t kpad, int64_t batch) {
+  return bits == 1 || (batch == 1 && rows * kpad >= static_cast<int64_t>(CQ_LUT_MIN_WEIGHTS));
 }
 
 // Workspace of one call: the per-slice partial sums, [nslice][rows] (fp32)
 // for the lookup-table kernel, [nslice][batch][rows] for the matrix-core one.
 uint64_t matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch) {
   if (rows <= 0 || kpad <= 0 || batch <= 0) return 0;  // nothing is launched
-  if (use_small(rows, kpad, batch)) return 0;
-  if (!use_lut(rows, kpad, batch)) return matvec_mma_workspace_bytes(rows, kpad, batch);
-  const MvShape s = mv_shape(storage_bits(bits), rows, kpad);
+  if (use_small(bits, rows, kpad, batch)) return 0;
+  if (!use_lut(bits, rows, kpad, batch)) return matvec_mma_workspace_bytes(rows, kpad, batch);
+  const MvShape s = mv_shape(storage_bits(bits), rows, kpad);  // one [nslice][rows] reused by each batch row
   if (s.nslice <= 1) return 0;
   return static_cast<uint64_t>(s.nslice) * rows * 4;
 }
 
 uint64_t rotate_matvec_workspace_bytes(int bits, int64_t rows, int64_t kpad, int64_t batch) {
   if (rows <= 0 || kpad <= 0 || batch <= 0) return 0;
-  if (use_small(rows, kpad, batch)) return 0;
-  if (use_lut(rows, kpad, batch)) return matvec_workspace_bytes(bits, rows, kpad, 1);
+  if (use_small(bits, rows, kpad, batch)) return 0;
+  if (use_lut(bits, rows, kpad, batch)) return matvec_workspace_bytes(bits, rows, kpad, 1);
   return (matvec_mma_workspace_bytes(rows, kpad, batch) + 15) / 16 * 16 + static_cast<uint64_t>(batch) * kpad * 4;
 }
 
@@ -603,22 +627,30 @@ hipError_t launch_lut(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
 
 hipError_t launch_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
                          const float *xr, int64_t batch, float *y, void *workspace, hipStream_t s) {
-  if (use_small(rows, kpad, batch)) {
+  if (use_small(bits, rows, kpad, batch)) {
     const MultiItem item = {blob, bits, rows, lev, y};
     return launch_small_matvec(&item, 1, xr, false, kpad, kpad, batch, s);
   }
-  if (!use_lut(rows, kpad, batch)) return launch_matvec_mma(blob, bits, rows, kpad, lev, xr, batch, y, workspace, s);
-  return launch_lut(blob, bits, rows, kpad, lev, xr, nullptr, 0, y, workspace, s);
+  if (!use_lut(bits, rows, kpad, batch)) return launch_matvec_mma(blob, bits, rows, kpad, lev, xr, batch, y, workspace, s);
+  hipError_t e = hipSuccess;
+  for (int64_t b = 0; b < batch && e == hipSuccess; ++b)  // stream order: the partial sums are reused
+    e = launch_lut(blob, bits, rows, kpad, lev, xr + b * kpad, nullptr, 0, y + b * rows, workspace, s);
+  return e;
 }
 
 hipError_t launch_rotate_matvec(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const CodeLevels &lev,
                                 const float *x, int64_t cols, int64_t batch, float *y, void *workspace,
                                 hipStream_t s) {
-  if (use_small(rows, kpad, batch)) {
+  if (use_small(bits, rows, kpad, batch)) {
     const MultiItem item = {blob, bits, rows, lev, y};
     return launch_small_matvec(&item, 1, x, true, cols, kpad, batch, s);
   }
-  if (use_lut(rows, kpad, batch)) return launch_lut(blob, bits, rows, kpad, lev, nullptr, x, cols, y, workspace, s);
+  if (use_lut(bits, rows, kpad, batch)) {
+    hipError_t e = hipSuccess;
+    for (int64_t b = 0; b < batch && e == hipSuccess; ++b)
+      e = launch_lut(blob, bits, rows, kpad, lev, nullptr, x + b * cols, cols, y + b * rows, workspace, s);
+    return e;
+  }
   // Batches: every workgroup of a K slice would redo the slice's rotation, so
   // it runs once, into the workspace after the partial sums.
   const uint64_t part = matvec_mma_workspace_bytes(rows, kpad, batch);
@@ -633,7 +665,7 @@ uint64_t rotate_multi_workspace_bytes(const MultiItem *items, int n, int64_t kpa
   uint64_t part = 0;
   bool shared = false;
   for (int i = 0; i < n; ++i) {
-    if (items[i].rows <= 0 || use_small(items[i].rows, kpad, batch)) continue;
+    if (items[i].rows <= 0 || use_small(items[i].bits, items[i].rows, kpad, batch)) continue;
     shared = true;
     const uint64_t p = matvec_workspace_bytes(items[i].bits, items[i].rows, kpad, batch);
     if (p > part) part = p;
@@ -650,7 +682,7 @@ hipError_t launch_rotate_multi_matvec(const MultiItem *items, int n, const float
   uint64_t part = 0;
   for (int i = 0; i < n; ++i) {
     if (items[i].rows <= 0) continue;
-    if (use_small(items[i].rows, kpad, batch)) {
+    if (use_small(items[i].bits, items[i].rows, kpad, batch)) {
       if (nsmall == 64) return hipErrorInvalidValue;
       small[nsmall++] = items[i];
     } else {
@@ -669,7 +701,7 @@ hipError_t launch_rotate_multi_matvec(const MultiItem *items, int n, const float
   hipError_t e = launch_rotate(x, CQ_F32, batch, cols, kpad, xr, CQ_F32, s);
   for (int i = 0; i < n && e == hipSuccess; ++i) {
     const MultiItem &it = items[i];
-    if (it.rows <= 0 || use_small(it.rows, kpad, batch)) continue;
+    if (it.rows <= 0 || use_small(it.bits, it.rows, kpad, batch)) continue;
     e = launch_matvec(it.blob, it.bits, it.rows, kpad, it.lev, xr, batch, it.y, part ? workspace : nullptr, s);
   }
   return e;

@@ -89,7 +89,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
 
   const int64_t row_bytes = kpad * SB / 8;
   uint8_t *dst = blob + r * row_bytes + g * (16 * SB) + j * SB;
-  if (SB == 2) {
+  if (SB == 1) {
+    dst[0] = static_cast<uint8_t>(word);
+  } else if (SB == 2) {
     *reinterpret_cast<uint16_t *>(dst) = static_cast<uint16_t>(word);
   } else if (SB == 4) {
     *reinterpret_cast<uint32_t *>(dst) = word;
@@ -125,6 +127,7 @@ namespace cq {
 hipError_t launch_quantize(const float *w, int64_t rows, int64_t cols, int64_t kpad, int bits,
                            const EncodeTable &tab, uint8_t *blob, hipStream_t s) {
   switch (storage_bits(bits)) {
+    case 1: return launch_sb<1>(w, rows, cols, kpad, tab, blob, s);
     case 2: return launch_sb<2>(w, rows, cols, kpad, tab, blob, s);
     case 3: return launch_sb<3>(w, rows, cols, kpad, tab, blob, s);
     default: return launch_sb<4>(w, rows, cols, kpad, tab, blob, s);

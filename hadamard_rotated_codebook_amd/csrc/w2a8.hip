@@ -67,15 +67,27 @@ struct W8Args {
   float sc;
 };
 
-// Slot of code c (0..15) of a 16-code step in the decoders' output order.
+// Slot of code c of a decoder block (16 codes; 32 at one bit) in the
+// decoders' output order.
 template <int SB>
 __device__ constexpr int code_slot(int c) {
-  return SB == 2 ? 4 * (c & 3) + (c >> 2)                          // dword i: codes i, 4+i, 8+i, 12+i
+  return SB == 1 ? 4 * (c & 7) + (c >> 3)                          // dword k: codes k, 8+k, 16+k, 24+k
+       : SB == 2 ? 4 * (c & 3) + (c >> 2)                          // dword i: codes i, 4+i, 8+i, 12+i
        : SB == 4 ? 4 * (2 * (c >> 3) + (c & 1)) + ((c & 7) >> 1)  // dwords: even codes, odd codes of each 8
                  : c;                                              // 3-bit: natural order
 }
+template <int SB>
+constexpr int slot_block() { return SB == 1 ? 32 : 16; }
 
 // Decoders: 16 codes -> 4 dwords of int8 (slot order code_slot).
+// 1-bit: the 32 codes of dword d -> 8 dwords; selector k takes bit k of each
+// byte, which picks byte 0 (code 0) or byte 1 (code 1) of the table.
+__device__ inline void decode1_i8(uint32_t t, uint32_t d, int32x4 &o0, int32x4 &o1) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o0[k] = static_cast<int>(perm(0u, t, (d >> k) & 0x01010101u));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o1[k] = static_cast<int>(perm(0u, t, (d >> (k + 4)) & 0x01010101u));
+}
 // 2-bit: the 16 codes of dword d.
 __device__ inline void decode2_i8(uint32_t t, uint32_t d, int32x4 &o) {
 #pragma unroll
@@ -148,21 +160,30 @@ __global__ __launch_bounds__(kThreads) void quant_acts_kernel(const float *x, in
   if (j == 0) sxo[task] = sx;
 }
 
-// 16 activation bytes of one 16-code step, column order -> slot order.
+// The activation bytes of one decoder block (N = 16 or 32 codes, N / 16
+// uint4), column order -> slot order.
 template <int SB>
-__device__ inline uint4 to_slot_order(uint4 v) {
+__device__ inline void to_slot_order(const uint4 *src, uint4 *dst) {
+  constexpr int N = slot_block<SB>();
   if constexpr (SB == 3) {
-    return v;
+    dst[0] = src[0];
   } else {
-    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-    uint32_t out[4] = {0u, 0u, 0u, 0u};
+    uint32_t in[N / 4], out[N / 4];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
+    for (int q = 0; q < N / 16; ++q) {
+      const uint4 v = src[q];
+      in[4 * q] = v.x, in[4 * q + 1] = v.y, in[4 * q + 2] = v.z, in[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) out[i] = 0u;
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
       const uint32_t byte = (in[c >> 2] >> (8 * (c & 3))) & 0xffu;
       const int sl = code_slot<SB>(c);
       out[sl >> 2] |= byte << (8 * (sl & 3));
     }
-    return make_uint4(out[0], out[1], out[2], out[3]);
+#pragma unroll
+    for (int q = 0; q < N / 16; ++q) dst[q] = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
   }
 }
 
@@ -172,10 +193,11 @@ template <int SB, int NT>
 __device__ inline void fill_int8(const int8_t *xq, const float *sx, int batch, int ngroups, uint8_t *lxq,
                                  float *sxs) {
   const int tid = threadIdx.x;
-  const int blocks = batch * ngroups * (CQ_GROUP / 16);
+  constexpr int Q = slot_block<SB>() / 16;  // uint4 per decoder block
+  const int blocks = batch * ngroups * (CQ_GROUP / slot_block<SB>());
   const uint4 *src = reinterpret_cast<const uint4 *>(xq);
   uint4 *dst = reinterpret_cast<uint4 *>(lxq);
-  for (int t = tid; t < blocks; t += NT) dst[t] = to_slot_order<SB>(src[t]);
+  for (int t = tid; t < blocks; t += NT) to_slot_order<SB>(src + Q * t, dst + Q * t);
   for (int t = tid; t < batch * ngroups; t += NT) {
     const int b = t / ngroups, g = t - b * ngroups;
     sxs[g * 8 + b] = sx[t];
@@ -344,10 +366,10 @@ __global__ __launch_bounds__(kThreads) void w2a8_kernel(W8Args a) {
 template <int SB>
 struct RowGeom {
   static constexpr int PB = SB == 3 ? 12 : 16;  // code bytes per piece (one load)
-  static constexpr int PDW = PB / 4;            // 4, 3, 4
-  static constexpr int CP = PB * 8 / SB;        // codes per piece: 64, 32, 32
+  static constexpr int PDW = PB / 4;            // 4, 4, 3, 4
+  static constexpr int CP = PB * 8 / SB;        // codes per piece: 128, 64, 32, 32
   static constexpr int XDW = CP / 4;            // int8 activation dwords per piece
-  static constexpr int PPG = CQ_GROUP / CP;     // pieces per group: 2, 4, 4
+  static constexpr int PPG = CQ_GROUP / CP;     // pieces per group: 1, 2, 4, 4
 };
 constexpr int kRowThreads = 256;
 constexpr int kRowMaxXdw = 64;  // activation dwords a lane holds, all batch rows
@@ -451,7 +473,10 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
       if (i >= a.npl) break;  // uniform
       const uint32_t *cd = codes[S][i];
       int32x4 dq[G::XDW / 4];
-      if constexpr (SB == 2) {
+      if constexpr (SB == 1) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) decode1_i8(tab[0], cd[w], dq[2 * w], dq[2 * w + 1]);
+      } else if constexpr (SB == 2) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) decode2_i8(tab[0], cd[w], dq[w]);
       } else if constexpr (SB == 4) {
@@ -482,7 +507,7 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
             for (int w = 0; w < 4; ++w) dot = __builtin_amdgcn_sdot4(dq[w4][w], xv[w], dot, false);
           }
         }
-        dot += __builtin_amdgcn_mov_dpp(dot, 0xb1, 0xf, 0xf, false);                     // xor 1: the group's 2 pieces
+        if constexpr (G::PPG >= 2) dot += __builtin_amdgcn_mov_dpp(dot, 0xb1, 0xf, 0xf, false);  // xor 1: 2 pieces
         if constexpr (G::PPG == 4) dot += __builtin_amdgcn_mov_dpp(dot, 0x4e, 0xf, 0xf, false);  // xor 2: its 4
         acc[b] = fmaf(static_cast<float>(dot), sxv[b][i] * nn, acc[b]);
       }
@@ -556,7 +581,8 @@ W8RowKernel pick_row_sb(int batch, int npl) {
 }
 
 W8RowKernel pick_row(int sb, int batch, int npl) {
-  return sb == 2 ? pick_row_sb<2>(batch, npl) : (sb == 3 ? pick_row_sb<3>(batch, npl) : pick_row_sb<4>(batch, npl));
+  return sb == 1 ? pick_row_sb<1>(batch, npl)
+                 : (sb == 2 ? pick_row_sb<2>(batch, npl) : (sb == 3 ? pick_row_sb<3>(batch, npl) : pick_row_sb<4>(batch, npl)));
 }
 
 // Resident workgroups per CU of a row kernel at an LDS size, cached per
@@ -596,9 +622,10 @@ static bool use_row_kernel(int64_t kpad, int64_t batch) {
   return batch <= kRowMaxBatch && kpad <= 16384 && row_lds_bytes(kpad, batch) <= kW2a8MaxLds;
 }
 
-bool w2a8_fits(int64_t kpad, int64_t batch) {
+bool w2a8_fits(int bits, int64_t kpad, int64_t batch) {
   if (kpad > 0 && kpad % CQ_GROUP == 0 && batch >= 1 && use_row_kernel(kpad, batch)) return true;
-  return kpad > 0 && kpad % CQ_GROUP == 0 && batch >= 1 && batch <= kMaxBatch &&
+  // the matrix-core kernel has no binary decoder
+  return bits != 1 && kpad > 0 && kpad % CQ_GROUP == 0 && batch >= 1 && batch <= kMaxBatch &&
          w2a8_lds_bytes(kpad, batch) <= kW2a8MaxLds;
 }
 
@@ -621,7 +648,7 @@ hipError_t launch_quant_acts_int8(const float *x, int64_t batch, int64_t cols, i
 
 hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t kpad, const Int8Codebook &cb,
                        const int8_t *xq, const float *sx, int64_t batch, float *y, hipStream_t s) {
-  if (!w2a8_fits(kpad, batch) || rows <= 0) return hipErrorInvalidValue;
+  if (!w2a8_fits(bits, kpad, batch) || rows <= 0) return hipErrorInvalidValue;
   const int sb = storage_bits(bits);
   static int cu_cache[64];
   int dev = 0;
@@ -634,7 +661,7 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t kpad
   // Batch 1-2 and 3 at two bits stream rows (measured faster at 65536 x
   // 16384 and 131072 x 8192); larger batches share the decode over the
   // matrix cores unless their activation does not fit that kernel's LDS.
-  const bool mfma_fits = batch <= kMaxBatch && w2a8_lds_bytes(kpad, batch) <= kW2a8MaxLds;
+  const bool mfma_fits = sb != 1 && batch <= kMaxBatch && w2a8_lds_bytes(kpad, batch) <= kW2a8MaxLds;
   if (use_row_kernel(kpad, batch) && (batch <= 2 || (batch == 3 && sb == 2) || !mfma_fits)) {
     W8RowArgs r;
     r.packed = blob;

@@ -42,13 +42,14 @@ extern "C" {
 typedef enum cq_status {
   CQ_OK = 0,
   CQ_ERR_NULL = 1,      /* a required pointer is NULL                           */
-  CQ_ERR_BITS = 2,      /* bits is not 2, 3, 4 or 5                             */
+  CQ_ERR_BITS = 2,      /* bits is not 1, 2, 3, 4 or 5, or the call does not
+                           take binary matrices (cq_gemm)                      */
   CQ_ERR_GROUP = 3,     /* group is not 128                                     */
   CQ_ERR_SHAPE = 4,     /* a dimension is negative or above its limit          */
   CQ_ERR_LENGTH = 5,    /* blob_bytes differs from cq_blob_bytes():
                            "Inconsistent CQ matrix length"                     */
   CQ_ERR_CODEBOOK = 6,  /* levels missing, not finite or not strictly
-                           ascending; or levels given for the ternary marker   */
+                           ascending; or levels given for binary or ternary    */
   CQ_ERR_DTYPE = 7,     /* unsupported element type                             */
   CQ_ERR_WORKSPACE = 8, /* workspace smaller than cq_workspace_bytes()          */
   CQ_ERR_ALIGN = 9,     /* a device pointer is not aligned as documented        */
@@ -77,7 +78,8 @@ typedef enum cq_dtype { CQ_F32 = 0, CQ_F16 = 1, CQ_BF16 = 2 } cq_dtype;
  *                 one continuous LSB-first bitstream: index k occupies bits
  *                 [k*b, (k+1)*b) (2-bit: four per byte, first column in the
  *                 lowest bits; 4-bit: low nibble first; 3-bit: indices cross
- *                 byte boundaries)
+ *                 byte boundaries; 1-bit: eight per byte, first column in
+ *                 the lowest bit)
  *   norms:        rows * (cols_pad/128) little-endian fp16, [row][group],
  *                 directly after the last packed row
  *
@@ -85,9 +87,14 @@ typedef enum cq_dtype { CQ_F32 = 0, CQ_F16 = 1, CQ_BF16 = 2 } cq_dtype;
  * 2-bit crumb sign-extends (00 -> 0, 01 -> +1, 11 -> -1; 10 -> -2, never
  * written by cq_quantize) and scales the analytic level
  * a = fp32(1.2240064 / sqrt(128)) (needle.js tutorial, "Shared codebooks").
+ * bits == 1 is binary: b = 1, code 0 selects -c and code 1 selects +c with
+ * the closed-form level c = fp32(sqrt(2/pi) / sqrt(128)), the mean of the
+ * positive half of N(0, 1/128) (".cact" format post, "Cactus Quants": binary
+ * weights pack eight per byte and their centroid is analytic; the marker and
+ * the sign convention are this library's reading).
  */
 typedef struct cq_matrix {
-  int32_t bits;          /* 2, 3, 4, or 5 (ternary marker)                        */
+  int32_t bits;          /* 1 (binary), 2, 3, 4, or 5 (ternary marker)            */
   int32_t group;         /* must be 128                                           */
   int64_t rows;          /* output dimension, 0 <= rows <= CQ_MAX_DIM             */
   int64_t cols;          /* input dimension, 0 <= cols <= CQ_MAX_DIM              */
@@ -95,7 +102,7 @@ typedef struct cq_matrix {
   uint64_t blob_bytes;   /* must equal cq_blob_bytes(bits, group, rows, cols)     */
   const float *levels;   /* host: 2^bits strictly ascending finite fp32 levels,
                             already divided by sqrt(128) (the file's embedded
-                            codebook); must be NULL when bits == 5               */
+                            codebook); must be NULL when bits is 1 or 5          */
 } cq_matrix;
 
 /* Version of this ABI (major * 10000 + minor * 100 + patch). */
@@ -106,8 +113,8 @@ const char *cq_status_string(cq_status status);
 
 /*
  * Byte length of a CQ blob: rows * (cols_pad*b/8 + 2*cols_pad/128)
- * (needle.js tutorial, "Anatomy of a CQ matrix"; ternary uses b = 2).
- * Writes *bytes and returns CQ_OK, or returns an error and leaves *bytes.
+ * (needle.js tutorial, "Anatomy of a CQ matrix"; ternary uses b = 2, binary
+ * b = 1).  Writes *bytes and returns CQ_OK, or returns an error and leaves *bytes.
  * Host-only; launches nothing.
  */
 cq_status cq_blob_bytes(int32_t bits, int32_t group, int64_t rows, int64_t cols,
@@ -167,10 +174,11 @@ cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t 
  *   Kernels: a matrix with cols_pad <= 4096 and at most 2^26 weights
  *   (rows * cols_pad) takes the small-matrix kernel at every batch; otherwise
  *   batch 1 from 2^23 weights takes the lookup tables, and the rest the
- *   batched matrix-core kernel.
+ *   batched matrix-core kernel.  Binary matrices always take the lookup
+ *   tables, one pass per batch vector.
  *   Arithmetic of the lookup tables: the inner sum is read from tables
- *   indexed by a packed field (4 codes at 2-bit widths, 2 codes at 3- and
- *   4-bit widths); an entry, the sum of its codes' level * xr products, is
+ *   indexed by a packed field (8 codes at 1 bit, 4 codes at 2-bit widths, 2
+ *   codes at 3- and 4-bit widths); an entry, the sum of its codes' level * xr products, is
  *   computed in fp32, scaled by a power of two per slice of 512-2048 columns
  *   and rounded once to fp16 (relative error <= 2^-11 per entry).  Products
  *   with the fp16 norm and all sums are fp32.
@@ -289,7 +297,8 @@ cq_status cq_quantize_acts_int8(const float *x, int64_t batch, int64_t cols, int
  *            batch * cols_pad + P <= 61440 for batch <= 4 and cols_pad <=
  *            16384, or (batch + 1) * cols_pad + P <= 61440; e.g. cols_pad up
  *            to 27264 at batch 1, 16384 at batch 2 and 3, 14336 at batch 4,
- *            6528 at batch 8; CQ_ERR_SHAPE otherwise
+ *            6528 at batch 8; binary matrices only the first form (batch
+ *            <= 4, cols_pad <= 16384); CQ_ERR_SHAPE otherwise
  *   y        device fp32 [batch][W.rows], 4-byte aligned, must not overlap
  *            xq, sx or the blob; fully overwritten (0 where cols == 0)
  *   Errors as cq_matvec.
@@ -348,6 +357,7 @@ cq_status cq_gather_rows(const cq_matrix *W, const int64_t *ids, int64_t n, void
  *   c        device fp32 [m][W.rows], 4-byte aligned, must not overlap xr
  *            or the blob; fully overwritten (0 where cols == 0)
  *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_GEMM)
+ *   Errors as cq_matvec; CQ_ERR_BITS for a binary matrix.
  */
 cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c,
                   void *workspace, uint64_t workspace_bytes, void *stream);
@@ -365,10 +375,11 @@ cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c,
  *   q_i = argmin_j |u_i - c_j|    ties to the smaller index (exact compare)
  *   norm = fp16(n)                round to nearest even; > 65504 -> +inf
  *   ternary (bits 5): q over (-a, 0, +a) stored as crumbs 11, 00, 01
+ *   binary (bits 1): q over (-c, +c), i.e. the sign of r (0 -> code 0)
  *
  *   w          device fp32 [rows][cols], 4-byte aligned
- *   bits       2, 3, 4 or 5;   group: 128
- *   levels     host, as in cq_matrix (NULL for bits 5)
+ *   bits       1, 2, 3, 4 or 5;   group: 128
+ *   levels     host, as in cq_matrix (NULL for bits 1 and 5)
  *   blob       device, 16-byte aligned, blob_bytes == cq_blob_bytes(...);
  *              fully overwritten; must not overlap w
  */

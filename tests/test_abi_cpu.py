@@ -43,7 +43,7 @@ def test_version_and_status_strings():
     assert lib.cq_status_string(99).decode() == "unknown status"
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
 def test_blob_bytes_matches_oracle(bits):
     for rows, cols in [(0, 0), (1, 1), (3, 130), (512, 512), (65536, 16384), (7, 1000), (1 << 30, 128)]:
         assert cq.cq_blob_bytes(bits, rows, cols) == oracle.blob_bytes(bits, 128, rows, cols)
@@ -56,7 +56,7 @@ def _blob_status(bits, group, rows, cols):
 
 
 def test_blob_bytes_errors_leave_output_untouched():
-    assert _blob_status(1, 128, 1, 1) == (BITS, 12345)
+    assert _blob_status(0, 128, 1, 1) == (BITS, 12345)
     assert _blob_status(6, 128, 1, 1) == (BITS, 12345)
     assert _blob_status(2, 64, 1, 1) == (GROUP, 12345)
     assert _blob_status(2, 128, -1, 1) == (SHAPE, 12345)
@@ -432,3 +432,26 @@ def test_binding_has_the_c_names():
               "cq_matvec_w2a8_quantized", "cq_matvec_w2a8", "cq_gather_rows",
               "cq_gemm", "cq_quantize"):
         assert callable(getattr(cq, n))
+
+
+def test_binary_matrices():
+    # binary (bits 1): analytic levels, so levels must be NULL
+    m, k = _matrix(bits=1, levels=np.array([-0.1, 0.1]))
+    assert _matvec(m) == CODEBOOK
+    m, k = _matrix(bits=1)
+    assert k is None and m.blob_bytes == 4 * 32 + 4 * 2 * 2
+    assert _matvec(m, y=0) == NULL  # past every matrix check
+    assert _gemm(m) == BITS  # no binary decoder on the bf16 matrix cores
+    # the lookup tables take every batch, one pass per vector: the partial
+    # sums of one pass are the whole workspace
+    big, _ = _matrix(bits=1, rows=65536, cols=16384)
+    out1, out4 = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    assert lib.cq_workspace_bytes(0, ctypes.byref(big), 1, ctypes.byref(out1)) == OK
+    assert lib.cq_workspace_bytes(0, ctypes.byref(big), 4, ctypes.byref(out4)) == OK
+    assert out1.value == out4.value == 8 * 65536 * 4  # 2048-column slices
+    # W2A8: only the row-streaming kernel has a binary decoder
+    wide, _ = _matrix(bits=1, rows=4, cols=16384)
+    assert _w2a8(wide, batch=3, y=0) == NULL
+    assert _w2a8(_matrix(bits=1, rows=4, cols=4096)[0], batch=5) == SHAPE
+    assert _w2a8(_matrix(bits=1, rows=4, cols=27264)[0], batch=1) == SHAPE
+    assert _w2a8(_matrix(bits=2, rows=4, cols=4096)[0], batch=5, y=0) == NULL

@@ -85,7 +85,7 @@ def test_rotate_empty_inputs_are_noops():
 
 # ------------------------------------------------------------------ matvec
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("rows,cols,batch", [
     (512, 512, 1),       # the single 512x512 matvec workload
     (1000, 5000, 1),     # ragged rows, partial last phase
@@ -199,7 +199,7 @@ def _row_subset(blob, bits, rows, cols, pick):
     return oracle.make_blob(packed[pick], norms[pick])
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
 def test_matvec_full_size_sampled_rows(bits):
     # the 65536 x 16384 workload in the launch configuration the benchmark
     # times; the oracle computes sampled rows one by one
@@ -210,7 +210,7 @@ def test_matvec_full_size_sampled_rows(bits):
     pick = cq_inputs.sample_rows(60, bits, rows, 48)
     sub = _row_subset(blob, bits, rows, cols, pick)
     w_hat = np.linalg.norm(oracle.dequantize(sub, bits, len(pick), cols, levels), axis=1)
-    for batch in ((1, 8) if bits == 2 else (1,)):
+    for batch in {2: (1, 8), 1: (1, 3)}.get(bits, (1,)):  # binary batches: one table pass per vector
         x = cq_inputs.activations(60, 100 * batch + bits, batch, cols)
         y = cq.cq_matvec(W, cq.cq_rotate_acts(_to_dev(x))).cpu().numpy()
         ref = oracle.matvec(sub, bits, len(pick), cols, x, levels)
@@ -227,7 +227,7 @@ def test_matvec_is_deterministic():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("rows,cols,batch", [(700, 16384, 1), (300, 5000, 1), (257, 9000, 3), (129, 1003, 8), (64, 128, 2)])
 def test_rotate_matvec_equals_rotate_then_matvec(bits, rows, cols, batch):
     # the fused call rotates inside the product's kernels with the same
@@ -294,6 +294,7 @@ def test_rotate_multi_matvec_one_launch(batch, cols):
     # launch per width
     (512, [(2, 512), (4, 131073), (2, 256), (5, 300)]),
     (5000, [(2, 100), (3, 1000), (4, 2000)]),  # K beyond 4096: all share one rotation
+    (640, [(1, 300), (2, 200), (1, 5000)]),     # binary matrices take the shared rotation
 ])
 def test_rotate_multi_matvec_mixed_paths(batch, cols, specs):
     say("multi mixed", batch, cols)
@@ -409,9 +410,11 @@ def test_quantize_acts_int8_is_the_oracle_bit_for_bit(batch, cols, offset):
     assert np.array_equal(sx.cpu().numpy().view(np.uint32), want_sx.view(np.uint32))
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("rows,cols,batch", [(700, 2048, 1), (129, 8192, 2), (64, 640, 8), (300, 16384, 1)])
 def test_matvec_w2a8_quantized_any_int8(bits, rows, cols, batch):
+    if bits == 1 and batch > 4:
+        pytest.skip("binary matrices take the row-streaming kernel only (batch <= 4)")
     # the product alone on int8 activations the oracle draws (the full range,
     # -128 included) and arbitrary positive scales; same inputs on both sides
     say("w2a8 quantized", bits, rows, cols, batch)
@@ -428,7 +431,7 @@ def test_matvec_w2a8_quantized_any_int8(bits, rows, cols, batch):
     assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("rows,cols,batch", [
     (512, 512, 1), (300, 1000, 3), (257, 2048, 2), (64, 640, 8), (1, 128, 1),
     (1000, 16384, 1), (9, 16384, 2), (33, 6528, 8), (130, 5000, 4),
@@ -436,6 +439,8 @@ def test_matvec_w2a8_quantized_any_int8(bits, rows, cols, batch):
     (20, 16384, 3), (17, 14336, 4), (3, 27264, 1),
 ])
 def test_matvec_w2a8(bits, rows, cols, batch):
+    if bits == 1 and (batch > 4 or cols > 16384):
+        pytest.skip("binary matrices take the row-streaming kernel only")
     say("w2a8", bits, rows, cols, batch)
     W, blob = _random_cq(bits, rows, cols, 91 + batch)
     levels = _levels(bits)
@@ -444,7 +449,7 @@ def test_matvec_w2a8(bits, rows, cols, batch):
     _check_w2a8(y, blob, bits, rows, cols, x, levels)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 4])
 def test_matvec_w2a8_full_size_sampled_rows(bits):
     # the 65536 x 16384 workload in the benchmark's launch configuration;
     # the oracle on sampled rows
@@ -481,7 +486,7 @@ def test_matvec_w2a8_degenerate_and_limits():
 
 # ------------------------------------------------------------- row gather
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("rows,cols", [(8192, 512), (300, 1000), (17, 128), (5, 16384), (40, 77)])
 @pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16, torch.float16])
 def test_gather_rows(bits, rows, cols, odt):
@@ -652,6 +657,10 @@ def test_gemm_degenerate_shapes():
     assert torch.all(C == 0)
     W1, _, _, _ = _cq_from_oracle(4, 4, 256, 42)
     assert cq.cq_gemm(W1, torch.zeros((0, 256), dtype=torch.bfloat16, device=DEV)).shape == (0, 4)
+    Wb, _, _, _ = _cq_from_oracle(1, 4, 256, 43)
+    with pytest.raises(cq.CQError) as e:
+        cq.cq_gemm(Wb, torch.zeros((2, 256), dtype=torch.bfloat16, device=DEV))
+    assert e.value.status == 2  # CQ_ERR_BITS: no binary decoder on the bf16 matrix cores
 
 
 # ------------------------------------------------------------------ encoder
@@ -680,12 +689,12 @@ def _encoder_agreement(bits, w, blob_gpu, levels):
     return frac
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("kind", ["empirical", "gaussian"])
 @pytest.mark.parametrize("rows,cols", [(512, 512), (37, 1000), (3, 16384), (1, 1)])
 def test_quantize(bits, kind, rows, cols):
-    if bits == 5 and kind == "gaussian":
-        pytest.skip("ternary levels are analytic")
+    if bits in (1, 5) and kind == "gaussian":
+        pytest.skip("binary and ternary levels are analytic")
     say("quantize", bits, kind, rows, cols)
     levels = _levels(bits, kind)
     w = cq_inputs.master(50, bits, rows, cols)
