@@ -338,10 +338,10 @@ def main():
             two["gbs"] = two["bytes"] / two["step_s"] / 1e9
             secondary["matvec_cq2_b1_two_calls"] = two
             log(f"CQ2 b1 as rotate + matvec: step {two['step_s']*1e6:.1f} us, matvec {two['kernel_s']*1e6:.1f} us")
-            for bits, batch in [(3, 1), (4, 1), (5, 1), (2, 8), (4, 8)]:
+            for bits, batch in [(3, 1), (4, 1), (5, 1), (1, 1), (2, 8), (4, 8)]:
                 r = bench_matvec(torch, cq, cq_inputs, master, bits, batch, max(args.steps // 3, 20),
                                  args.warmup, gen)
-                key = f"matvec_cq{bits if bits != 5 else 't'}_b{batch}"
+                key = f"matvec_cq{ {5: 't', 1: 'b'}.get(bits, bits) }_b{batch}"
                 # rates from the median call: a stall of the launching thread
                 # shows up in the events of the call it delays
                 r["gbs"] = r["bytes"] / r["kernel_median_s"] / 1e9
@@ -352,10 +352,10 @@ def main():
                 log(key, f"{r['kernel_median_s']*1e6:.1f} us (median)", f"{r['gbs']:.0f} GB/s")
     if args.only in ("all", "w2a8"):
         # the pages' deployment numerics: int8 activations and code book
-        for bits, batch in [(2, 1), (4, 1), (2, 2)]:
+        for bits, batch in [(2, 1), (4, 1), (1, 1), (2, 2)]:
             r = bench_matvec(torch, cq, cq_inputs, master, bits, batch, max(args.steps // 3, 20),
                              args.warmup, gen, w2a8=True)
-            key = f"matvec_w2a8_cq{bits}_b{batch}"
+            key = f"matvec_w2a8_cq{ {1: 'b'}.get(bits, bits) }_b{batch}"
             r["gbs"] = r["bytes"] / r["kernel_median_s"] / 1e9
             r["frac_hbm_peak"] = r["gbs"] / HBM_PEAK_GBS
             secondary[key] = r

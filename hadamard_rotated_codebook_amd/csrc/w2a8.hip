@@ -432,6 +432,24 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
   uint32_t tab[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) tab[i] = a.c8[i];
+  // Binary with the activations in registers: c8[bit] = c0 + (c1 - c0) * bit,
+  // so a group's dot is c0 * sum(x) + (c1 - c0) * sum(bit * x), exactly; the
+  // masked sums take the bit bytes straight into v_dot4 (no table permute),
+  // and sum(x) of each of the lane's groups is taken once here.
+  constexpr bool MASKED = SB == 1 && XREG;
+  const int c0 = static_cast<int8_t>(tab[0] & 0xffu), dc = static_cast<int8_t>((tab[0] >> 8) & 0xffu) - c0;
+  int xsum[MASKED ? B : 1][MASKED ? NPL : 1];
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        int t = 0;
+#pragma unroll
+        for (int w = 0; w < G::XDW; ++w) t = __builtin_amdgcn_sdot4(0x01010101, static_cast<int>(xr8[b][i][w]), t, false);
+        xsum[b][i] = t;
+      }
+  }
 
   // this lane's byte offsets in a step's code and norm buffers
   uint32_t coff[NPL], noff[NPL];
@@ -473,7 +491,13 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
       if (i >= a.npl) break;  // uniform
       const uint32_t *cd = codes[S][i];
       int32x4 dq[G::XDW / 4];
-      if constexpr (SB == 1) {
+      if constexpr (MASKED) {
+        // bit bytes: selector k of code dword w is slot dword 8w + k
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) dq[(8 * w + k) >> 2][k & 3] = static_cast<int>((cd[w] >> k) & 0x01010101u);
+      } else if constexpr (SB == 1) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) decode1_i8(tab[0], cd[w], dq[2 * w], dq[2 * w + 1]);
       } else if constexpr (SB == 2) {
@@ -507,6 +531,7 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
             for (int w = 0; w < 4; ++w) dot = __builtin_amdgcn_sdot4(dq[w4][w], xv[w], dot, false);
           }
         }
+        if constexpr (MASKED) dot = c0 * xsum[b][i] + dc * dot;
         if constexpr (G::PPG >= 2) dot += __builtin_amdgcn_mov_dpp(dot, 0xb1, 0xf, 0xf, false);  // xor 1: 2 pieces
         if constexpr (G::PPG == 4) dot += __builtin_amdgcn_mov_dpp(dot, 0x4e, 0xf, 0xf, false);  // xor 2: its 4
         acc[b] = fmaf(static_cast<float>(dot), sxv[b][i] * nn, acc[b]);
