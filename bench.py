@@ -201,6 +201,69 @@ def bench_gather(torch, cq, cq_inputs, gen, steps=50):
             "gbs": moved / t / 1e9}
 
 
+def bench_small_and_prefill(torch, cq, cq_inputs, gen, steps=100):
+    """The single 512 x 512 CQ2 matvec (batch 1, one cq_rotate_matvec call,
+    eager and replayed from a HIP graph) and the Needle-shaped prefill: 2048
+    tokens x 512 of fp16 activations rotated to bf16 once (cq_rotate_acts),
+    then cq_gemm through the 512 x 512 and 256 x 512 CQ2 projections and the
+    8192 x 512 CQ4 logits, each timed per call from HIP graph replays."""
+    dev = torch.device("cuda:0")
+    out = {}
+    w = torch.randn((512, 512), generator=gen, device=dev).mul_(0.02)
+    W = cq.cq_quantize(w, 2, cq_inputs.codebook(2))
+    x = torch.randn((1, 512), generator=gen, device=dev)
+    y = torch.empty((1, 512), device=dev)
+
+    def eager_median(fn, n):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        ev = _events(torch, n)
+        for i in range(n):
+            ev[i][0].record()
+            fn()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) / 1e3 for a, b in ev)[n // 2]
+
+    def graph_per_call(fn, calls=20, replays=10):
+        # launch gaps of the host removed: the calls replayed from a HIP graph
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(replays):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        del g
+        return t0.elapsed_time(t1) / 1e3 / (calls * replays)
+
+    t_eager = eager_median(lambda: cq.cq_rotate_matvec(W, x, out=y), steps)
+    t_graph = graph_per_call(lambda: cq.cq_rotate_matvec(W, x, out=y))
+    nb = W.blob.numel()
+    out["matvec_cq2_512x512_b1"] = {"bytes": nb, "eager_median_s": t_eager, "graph_s_per_call": t_graph,
+                                    "graph_gbs": nb / t_graph / 1e9}
+    # prefill
+    X = torch.randn((2048, 512), generator=gen, device=dev).half()
+    mats = {"q_512x512_cq2": (2, 512), "kv_256x512_cq2": (2, 256), "logits_8192x512_cq4": (4, 8192)}
+    Ws = {k: cq.cq_quantize(torch.randn((r, 512), generator=gen, device=dev).mul_(0.02), b, cq_inputs.codebook(b))
+          for k, (b, r) in mats.items()}
+    xr = torch.empty((2048, 512), dtype=torch.bfloat16, device=dev)
+    t_rot = graph_per_call(lambda: cq.cq_rotate_acts(X, torch.bfloat16, out=xr))
+    pre = {"rotate_2048x512_s": t_rot}
+    for k, Wk in Ws.items():
+        C = torch.empty((2048, Wk.rows), device=dev)
+        t = graph_per_call(lambda: cq.cq_gemm(Wk, xr, out=C))
+        pre[k] = {"s": t, "tflops": 2.0 * 2048 * Wk.rows * 512 / t / 1e12}
+    out["needle_prefill_2048_tokens"] = pre
+    return out
+
+
 def bench_gemm(torch, cq, cq_inputs, master, bits, m, steps, warmup, gen):
     rows, cols = master.shape
     levels = cq_inputs.codebook(bits)
@@ -372,6 +435,14 @@ def main():
         r = bench_gather(torch, cq, cq_inputs, gen)
         secondary["gather_cq4_8192x512_2048_rows"] = r
         log(f"gather 2048 rows of 8192x512 CQ4: {r['kernel_median_s']*1e6:.1f} us, {r['gbs']:.0f} GB/s")
+        r = bench_small_and_prefill(torch, cq, cq_inputs, gen)
+        secondary.update(r)
+        s5 = r["matvec_cq2_512x512_b1"]
+        log(f"matvec 512x512 CQ2 b1: {s5['eager_median_s']*1e6:.1f} us eager, {s5['graph_s_per_call']*1e6:.2f} us "
+            f"per call in a graph")
+        p = r["needle_prefill_2048_tokens"]
+        log("prefill 2048 tokens: rotate " + f"{p['rotate_2048x512_s']*1e6:.1f} us; " +
+            ", ".join(f"{k} {v['s']*1e6:.1f} us ({v['tflops']:.0f} TFLOP/s)" for k, v in p.items() if k != "rotate_2048x512_s"))
 
     if args.only in ("all", "gemm", "encode"):
         log("generating the 16384 x 16384 fp32 master on the GPU")

@@ -46,7 +46,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BK = 64;
 constexpr int kWavesM = 2;  // waves along M; the waves along N are a template parameter
 constexpr int kGroupM = 4;  // M-tiles per tile group
 constexpr int kValuPerMfma = 2;  // VALU slots after each MFMA in the interleave
@@ -66,11 +66,15 @@ struct GemmArgs {
 
 __device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
-template <int SB, int WN>
+// T: the workgroup's tile is T x T (256, or 128 for products too small to
+// give every CU a 256 x 256 tile); WN waves along N.
+template <int SB, int WN, int T>
 __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) {
+  constexpr int BM = T, BN = T;
   constexpr int kThreads = 64 * kWavesM * WN;
-  constexpr int TN = BN / WN;                  // wave tile: 128 x TN
-  constexpr int FI = 128 / 16, FJ = TN / 16;   // 16 x 16 blocks per wave
+  constexpr int WTM = BM / kWavesM;            // wave tile: WTM x TN
+  constexpr int TN = BN / WN;
+  constexpr int FI = WTM / 16, FJ = TN / 16;   // 16 x 16 blocks per wave
   constexpr int XPT = BM * 8 / kThreads;       // Xr chunks per thread per stage
   constexpr int TPR = kThreads / BN;           // threads per W row
   constexpr int CODES = BK / TPR;              // codes a thread decodes per stage
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
     }
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
-      const int row = wm * 128 + i * 16 + (lane & 15);
+      const int row = wm * WTM + i * 16 + (lane & 15);
       af[i] = __builtin_bit_cast(bf16x8, As[cur][row * 8 + swz(row, ch)]);
     }
     store_part(cur ^ 1, set_c, kk_c);
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
       const int64_t col = n0 + wn * TN + j * 16 + (lane & 15);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t row = m0 + wm * 128 + i * 16 + 4 * (lane >> 4) + e;
+        const int64_t row = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + e;
         if (row < a.m && col < a.rows) a.c[row * a.rows + col] = acc[i][j][e];
       }
     }
@@ -285,16 +289,30 @@ hipError_t launch_gemm(const uint8_t *blob, int bits, int64_t rows, int64_t kpad
   a.kpad = kpad;
   a.ngroups = kpad / CQ_GROUP;
   a.lev = lev;
-  const int64_t tm = (m + BM - 1) / BM, tn = (rows + BN - 1) / BN;
+  // 256 x 256 tiles when they give at least one per CU; otherwise 128 x 128
+  // tiles (4 waves, 64 x 64 each), four times as many workgroups.
+  const int64_t tm256 = (m + 255) / 256, tn256 = (rows + 255) / 256;
+  const bool big = tm256 * tn256 >= 256;
+  const int64_t tile = big ? 256 : 128;
+  const int64_t tm = (m + tile - 1) / tile, tn = (rows + tile - 1) / tile;
   if (tm * tn > 0x7fffffff) return hipErrorInvalidConfiguration;
   a.tiles_m = static_cast<int32_t>(tm);
   a.tiles_n = static_cast<int32_t>(tn);
   const dim3 grid(static_cast<unsigned>(tm * tn));
-  constexpr int threads = 64 * kWavesM * CQ_GEMM_WN;
-  switch (sb) {
-    case 2: gemm_kernel<2, CQ_GEMM_WN><<<grid, threads, 0, s>>>(a); break;
-    case 3: gemm_kernel<3, CQ_GEMM_WN><<<grid, threads, 0, s>>>(a); break;
-    default: gemm_kernel<4, CQ_GEMM_WN><<<grid, threads, 0, s>>>(a); break;
+  if (big) {
+    constexpr int threads = 64 * kWavesM * CQ_GEMM_WN;
+    switch (sb) {
+      case 2: gemm_kernel<2, CQ_GEMM_WN, 256><<<grid, threads, 0, s>>>(a); break;
+      case 3: gemm_kernel<3, CQ_GEMM_WN, 256><<<grid, threads, 0, s>>>(a); break;
+      default: gemm_kernel<4, CQ_GEMM_WN, 256><<<grid, threads, 0, s>>>(a); break;
+    }
+  } else {
+    constexpr int threads = 64 * kWavesM * 2;
+    switch (sb) {
+      case 2: gemm_kernel<2, 2, 128><<<grid, threads, 0, s>>>(a); break;
+      case 3: gemm_kernel<3, 2, 128><<<grid, threads, 0, s>>>(a); break;
+      default: gemm_kernel<4, 2, 128><<<grid, threads, 0, s>>>(a); break;
+    }
   }
   return hipGetLastError();
 }
