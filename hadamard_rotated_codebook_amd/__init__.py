@@ -92,7 +92,9 @@ def _check(status):
 
 
 def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    # the current device's current stream as a raw handle (building a
+    # torch.cuda.Stream object per call costs several microseconds)
+    return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(torch.cuda.current_device()))
 
 
 def _dev(t, name):
@@ -131,20 +133,37 @@ class CQMatrix:
     levels: Optional[np.ndarray] = None
     group: int = CQ_GROUP
 
+    def _key(self):
+        b = self.blob
+        lv = None if self.levels is None else np.asarray(self.levels, dtype=np.float32).tobytes()
+        return (self.bits, self.group, self.rows, self.cols, b.data_ptr(), b.numel(), b.dtype, b.is_cuda,
+                b.is_contiguous(), lv)
+
     def _struct(self):
+        """The C descriptor (and the levels array it points to), rebuilt only
+        when a field, the blob tensor or the level values change."""
+        key = self._key()
+        cached = self.__dict__.get("_c_struct")
+        if cached is not None and cached[0] == key:
+            return cached[1], cached[2]
         arr, ptr = _levels_array(self.levels)
         if self.blob.dtype != torch.uint8:
             raise TypeError("blob must be uint8")
         m = _Matrix(self.bits, self.group, self.rows, self.cols, _dev(self.blob, "blob"),
                     self.blob.numel(), ptr)
-        return m, arr  # keep the levels array alive for the call
+        self.__dict__["_c_struct"] = (key, m, arr)  # arr stays alive with the descriptor
+        self.__dict__["_ws_bytes"] = {}
+        return m, arr
 
 
 def cq_workspace_bytes(op, W, batch):
     m, keep = W._struct()
-    out = _u64(0)
-    _check(_lib.cq_workspace_bytes(op, ctypes.byref(m), batch, ctypes.byref(out)))
-    return int(out.value)
+    memo = W.__dict__["_ws_bytes"]  # reset whenever the descriptor is rebuilt
+    if (op, batch) not in memo:
+        out = _u64(0)
+        _check(_lib.cq_workspace_bytes(op, ctypes.byref(m), batch, ctypes.byref(out)))
+        memo[(op, batch)] = int(out.value)
+    return memo[(op, batch)]
 
 
 def _padded(cols):
