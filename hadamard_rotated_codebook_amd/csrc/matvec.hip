@@ -44,6 +44,8 @@
 //    and per-block completion counters, the last arrival adding up -- cost
 //    more than this kernel boundary: the counter protocol stalls the waves and
 //    the coherent stores go to memory one 4-byte write at a time.)
+#include <atomic>
+
 #include "cq_fwht.h"
 #include "cq_internal.h"
 
@@ -503,10 +505,12 @@ MvKernel pick_kernel(int sb, bool rot = false) {
 int max_grid(int sb) {
   // Resident workgroups per CU for this kernel, times the CU count of the
   // current device; computed once per (device, width).
-  static int cache[64][4];
+  // (atomic: host threads may launch concurrently; a racing first call only
+  // computes the same value twice)
+  static std::atomic<int> cache[64][4];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int &c = cache[dev][sb - 1];
+  int c = cache[dev][sb - 1].load(std::memory_order_relaxed);
   if (c == 0) {
     int per_cu = 1, cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(pick_kernel(sb)),
@@ -514,6 +518,7 @@ int max_grid(int sb) {
       per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
     c = per_cu * cus;
+    cache[dev][sb - 1].store(c, std::memory_order_relaxed);
   }
   return c;
 }

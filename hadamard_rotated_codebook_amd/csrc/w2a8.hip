@@ -32,6 +32,9 @@
 //    over row tiles (a grid of about as many workgroups as fit the chip);
 //  * chunks of 4 groups, two in flight per wave; with 2+ chunks, 2 or 4 waves
 //    split a block's K and add their accumulators through LDS in wave order.
+#include <atomic>
+#include <mutex>
+
 #include "cq_decode.h"
 #include "cq_fwht.h"
 #include "cq_internal.h"
@@ -616,6 +619,8 @@ int row_occupancy(const void *k, size_t lds, int dev) {
   struct Entry { const void *k; size_t lds; int dev, per_cu; };
   static Entry cache[32];
   static int used = 0;
+  static std::mutex mu;  // host threads may launch concurrently
+  std::lock_guard<std::mutex> lock(mu);
   for (int i = 0; i < used; ++i)
     if (cache[i].k == k && cache[i].lds == lds && cache[i].dev == dev) return cache[i].per_cu;
   int per_cu = 0;
@@ -626,8 +631,8 @@ int row_occupancy(const void *k, size_t lds, int dev) {
 
 typedef void (*W8Kernel)(W8Args);
 
-W8Kernel pick(int sb) {
-  return sb == 2 ? w2a8_kernel<2> : (sb == 3 ? w2a8_kernel<3> : w2a8_kernel<4>);
+W8Kernel pick(int sb) {  // no binary decoder here: nullptr for sb 1
+  return sb == 2 ? w2a8_kernel<2> : (sb == 3 ? w2a8_kernel<3> : (sb == 4 ? w2a8_kernel<4> : nullptr));
 }
 
 }  // namespace
@@ -675,13 +680,13 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t kpad
                        const int8_t *xq, const float *sx, int64_t batch, float *y, hipStream_t s) {
   if (!w2a8_fits(bits, kpad, batch) || rows <= 0) return hipErrorInvalidValue;
   const int sb = storage_bits(bits);
-  static int cu_cache[64];
+  static std::atomic<int> cu_cache[64];  // CUs per device, 0 until asked
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cu_cache[dev] == 0) {
-    int cus = 256;
+  int cus = cu_cache[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    cu_cache[dev] = cus;
+    cu_cache[dev].store(cus, std::memory_order_relaxed);
   }
   // Batch 1-2 and 3 at two bits stream rows (measured faster at 65536 x
   // 16384 and 131072 x 8192); larger batches share the decode over the
@@ -717,7 +722,7 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t kpad
     // one wave of workgroups: as many as the CUs hold at once (registers and
     // LDS), each over a contiguous range of row steps
     const int per_cu = row_occupancy(reinterpret_cast<const void *>(k), lds, dev);
-    const int64_t grid = nsteps < int64_t{per_cu} * cu_cache[dev] ? nsteps : int64_t{per_cu} * cu_cache[dev];
+    const int64_t grid = nsteps < int64_t{per_cu} * cus ? nsteps : int64_t{per_cu} * cus;
     k<<<dim3(static_cast<unsigned>(grid)), kRowThreads, lds, s>>>(r);
     return hipGetLastError();
   }
@@ -747,8 +752,10 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t kpad
   // CU): each stages the activation once and loops over tiles
   int64_t per_cu = static_cast<int64_t>(160 * 1024) / static_cast<int64_t>(lds + sizeof(float) * 4 * kThreads);
   per_cu = per_cu < 1 ? 1 : (per_cu > 8 ? 8 : per_cu);
-  const int64_t grid = ntiles < per_cu * cu_cache[dev] ? ntiles : per_cu * cu_cache[dev];
-  pick(sb)<<<dim3(static_cast<unsigned>(grid)), kThreads, lds, s>>>(a);
+  const int64_t grid = ntiles < per_cu * cus ? ntiles : per_cu * cus;
+  const W8Kernel k = pick(sb);
+  if (!k) return hipErrorInvalidValue;
+  k<<<dim3(static_cast<unsigned>(grid)), kThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 

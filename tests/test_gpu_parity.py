@@ -732,3 +732,37 @@ def test_quantize_special_groups():
     W = cq.cq_quantize(_to_dev(w), 2, levels)
     blob_g = W.blob.cpu().numpy()
     assert np.array_equal(blob_g, oracle.quantize(w, 2, levels))
+
+
+def test_concurrent_host_threads_on_their_own_streams():
+    # the launchers' host-side caches are shared by every thread: calls from
+    # several threads at once, each on its own stream, give the results of
+    # the same calls made one by one (every kernel here is deterministic)
+    import threading
+    say("threads")
+    mats = [_random_cq(bits, rows, 4096, 800 + i)[0] for i, (bits, rows) in enumerate([(2, 3000), (4, 700), (1, 5000), (3, 257)])]
+    x = _to_dev(cq_inputs.activations(800, 0, 2, 4096))
+    ref = [(cq.cq_rotate_matvec(W, x).clone(), cq.cq_matvec_w2a8(W, x[:1]).clone()) for W in mats]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                W = mats[i]
+                for _ in range(20):
+                    a = cq.cq_rotate_matvec(W, x)
+                    b = cq.cq_matvec_w2a8(W, x[:1])
+                s.synchronize()
+                if not (torch.equal(a, ref[i][0]) and torch.equal(b, ref[i][1])):
+                    errors.append(i)
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(mats))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
