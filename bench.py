@@ -401,7 +401,7 @@ def main():
             two["gbs"] = two["bytes"] / two["step_s"] / 1e9
             secondary["matvec_cq2_b1_two_calls"] = two
             log(f"CQ2 b1 as rotate + matvec: step {two['step_s']*1e6:.1f} us, matvec {two['kernel_s']*1e6:.1f} us")
-            for bits, batch in [(3, 1), (4, 1), (5, 1), (1, 1), (2, 8), (4, 8)]:
+            for bits, batch in [(3, 1), (4, 1), (5, 1), (1, 1), (2, 8), (4, 8), (1, 8)]:
                 r = bench_matvec(torch, cq, cq_inputs, master, bits, batch, max(args.steps // 3, 20),
                                  args.warmup, gen)
                 key = f"matvec_cq{ {5: 't', 1: 'b'}.get(bits, bits) }_b{batch}"

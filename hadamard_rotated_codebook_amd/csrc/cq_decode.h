@@ -150,11 +150,37 @@ struct PlaneTable {
   }
 };
 
+// Binary (1-bit) values of one (row, group): fp16(-c * norm) and fp16(+c *
+// norm) differ only in the sign bit, so their low bytes are equal.  src
+// holds byte 0 = high byte of the code-0 value, byte 1 = high byte of the
+// code-1 value, byte 2 = the common low byte.
+template <typename T16>
+struct BinTable {
+  uint32_t src;
+  __device__ void build(const cq::CodeLevels &lev, float n) {
+    const uint32_t v0 = pack2<T16>(lev.v[0] * n, lev.v[1] * n);  // code 0 low half, code 1 high half
+    src = perm(0u, v0, 0x0c000301u);                             // bytes: hi(v0), hi(v1), lo(v1), 0
+  }
+};
+
+// 1-bit: the 8 codes of byte b, as the pairs (0,4) (1,5) (2,6) (3,7): for
+// pair t the selector takes the common low byte (index 2) for both halves
+// and the code's high byte (index 0 or 1) from bit t / t + 4 of b.
+template <typename T16>
+__device__ inline void decode1_planes(const BinTable<T16> &t, uint32_t b, uint32_t *o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = (b >> i) & 0x11u;                                       // bits i and i + 4
+    const uint32_t sel = ((x * 0x00100100u) & 0x01000100u) | 0x00020002u;  // x < 2^5: v_mul_u32_u24; bits 8, 24
+    o[i] = perm(0u, t.src, sel);
+  }
+}
+
 // Slot order of the permuted decoders: position t of an 8-value operand holds
 // code perm_code<SB>(t) of its 8 consecutive codes (3-bit: natural order).
 template <int SB>
 __host__ __device__ constexpr int perm_code(int t) {
-  return SB == 2 ? (t >> 1) + 4 * (t & 1)                          // (0,4) (1,5) (2,6) (3,7)
+  return SB <= 2 ? (t >> 1) + 4 * (t & 1)                          // (0,4) (1,5) (2,6) (3,7)
        : SB == 4 ? (t & 4) + ((t >> 1) & 1) + 2 * (t & 1)          // (0,2) (1,3) (4,6) (5,7)
                  : t;
 }
@@ -195,7 +221,9 @@ __device__ inline void decode4_planes(const PlaneTable<4, T16> &t, uint32_t d, u
 // Tables of the fp16 matrix-core matvec kernels: byte planes at 2 and 4
 // bits, the plane pairs of Table at 3 bits.
 template <int SB>
-using MmaTable = typename std::conditional<SB == 3, Table<3, _Float16>, PlaneTable<SB, _Float16>>::type;
+using MmaTable = typename std::conditional<
+    SB == 1, BinTable<_Float16>,
+    typename std::conditional<SB == 3, Table<3, _Float16>, PlaneTable<SB, _Float16>>::type>::type;
 
 // B operand of k step s (s < 16) of one (row, group): codes 8s..8s+7 of the
 // group's GROUP_DW code dwords, as four dwords of fp16 pairs in slot order
@@ -203,7 +231,9 @@ using MmaTable = typename std::conditional<SB == 3, Table<3, _Float16>, PlaneTab
 // 24-bit field) or 16 codes (2-bit: half of one dword's decode).
 template <int SB>
 __device__ inline void decode_step(const MmaTable<SB> &tab, const uint32_t *codes, int s, uint32_t (&o)[4]) {
-  if constexpr (SB == 4) {
+  if constexpr (SB == 1) {
+    decode1_planes(tab, (codes[s >> 2] >> (8 * (s & 3))) & 0xffu, o);
+  } else if constexpr (SB == 4) {
     decode4_planes(tab, codes[s], o);
   } else if constexpr (SB == 3) {
     constexpr int DW = 3 * 128 / 32;

@@ -559,14 +559,15 @@ namespace cq {
 // (batch 1: 8.0 us at 512 x 512 and 14.2 us at 16384 x 4096, against 13.0
 // and 16.4 us on the lookup tables) and slower from 128 M.  With more
 // columns, batch 1 takes the lookup tables from 2^23 weights and the batched
-// matrix-core kernel below.  Binary matrices always take the lookup tables
-// (8 weights per lookup), one pass per batch row.
+// matrix-core kernel below (every width, binary included).
 static bool use_small(int bits, int64_t rows, int64_t kpad, int64_t batch) {
-  return bits != 1 && rows * kpad <= kSmallMaxWeights && small_matvec_fits(kpad, batch);
+  (void)bits;
+  return rows * kpad <= kSmallMaxWeights && small_matvec_fits(kpad, batch);
 }
 
 static bool use_lut(int bits, int64_t rows, int64_t kpad, int64_t batch) {
-  return bits == 1 || (batch == 1 && rows * kpad >= static_cast<int64_t>(CQ_LUT_MIN_WEIGHTS));
+  (void)bits;
+  return batch == 1 && rows * kpad >= static_cast<int64_t>(CQ_LUT_MIN_WEIGHTS);
 }
 
 // Workspace of one call: the per-slice partial sums, [nslice][rows] (fp32)

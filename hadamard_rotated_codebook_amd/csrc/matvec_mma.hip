@@ -271,6 +271,7 @@ hipError_t launch_matvec_mma(const uint8_t *blob, int bits, int64_t rows, int64_
   if (static_cast<int64_t>(kRowsPerWave) * a.row_bytes >= (int64_t{1} << 31)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(sh.nslice) * sh.per_slice));
   switch (sb) {
+    case 1: matvec_mma_kernel<1><<<grid, kThreads, 0, s>>>(a); break;
     case 2: matvec_mma_kernel<2><<<grid, kThreads, 0, s>>>(a); break;
     case 3: matvec_mma_kernel<3><<<grid, kThreads, 0, s>>>(a); break;
     default: matvec_mma_kernel<4><<<grid, kThreads, 0, s>>>(a); break;

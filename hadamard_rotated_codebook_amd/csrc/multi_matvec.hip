@@ -272,10 +272,14 @@ __global__ __launch_bounds__(kThreads) void small_matvec_kernel(const float *x, 
 
 typedef void (*SmallKernel)(const float *, int32_t, int32_t, int32_t, int32_t, int32_t, SmallArgs);
 
-SmallKernel pick(int sb, bool rot) {
-  if (rot) return sb == 2 ? small_matvec_kernel<2, true> : (sb == 3 ? small_matvec_kernel<3, true> : small_matvec_kernel<4, true>);
-  return sb == 2 ? small_matvec_kernel<2, false> : (sb == 3 ? small_matvec_kernel<3, false> : small_matvec_kernel<4, false>);
+template <bool ROT>
+SmallKernel pick_rot(int sb) {
+  return sb == 1 ? small_matvec_kernel<1, ROT>
+                 : (sb == 2 ? small_matvec_kernel<2, ROT>
+                            : (sb == 3 ? small_matvec_kernel<3, ROT> : small_matvec_kernel<4, ROT>));
 }
+
+SmallKernel pick(int sb, bool rot) { return rot ? pick_rot<true>(sb) : pick_rot<false>(sb); }
 
 }  // namespace
 
@@ -292,7 +296,7 @@ hipError_t launch_small_matvec(const MultiItem *items, int n, const float *x, bo
   const int ks_shift = nchunks >= 4 ? 2 : (nchunks >= 2 ? 1 : 0);
   const int64_t wg_rows = static_cast<int64_t>(kBlockRows) * (kWaves >> ks_shift);
   // one launch per storage width, at most kMaxMats matrices each, in order
-  for (int sb = 2; sb <= 4; ++sb) {
+  for (int sb = 1; sb <= 4; ++sb) {
     SmallArgs a;
     int count = 0;
     int64_t max_wgs = 0;

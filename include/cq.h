@@ -174,8 +174,7 @@ cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t 
  *   Kernels: a matrix with cols_pad <= 4096 and at most 2^26 weights
  *   (rows * cols_pad) takes the small-matrix kernel at every batch; otherwise
  *   batch 1 from 2^23 weights takes the lookup tables, and the rest the
- *   batched matrix-core kernel.  Binary matrices always take the lookup
- *   tables, one pass per batch vector.
+ *   batched matrix-core kernel.
  *   Arithmetic of the lookup tables: the inner sum is read from tables
  *   indexed by a packed field (8 codes at 1 bit, 4 codes at 2-bit widths, 2
  *   codes at 3- and 4-bit widths); an entry, the sum of its codes' level * xr products, is

@@ -442,13 +442,13 @@ def test_binary_matrices():
     assert k is None and m.blob_bytes == 4 * 32 + 4 * 2 * 2
     assert _matvec(m, y=0) == NULL  # past every matrix check
     assert _gemm(m) == BITS  # no binary decoder on the bf16 matrix cores
-    # the lookup tables take every batch, one pass per vector: the partial
-    # sums of one pass are the whole workspace
+    # batch 1: the lookup tables on 2048-column slices; batch 4: the matrix
+    # cores on 4096-column slices, partial sums per vector
     big, _ = _matrix(bits=1, rows=65536, cols=16384)
     out1, out4 = ctypes.c_uint64(0), ctypes.c_uint64(0)
     assert lib.cq_workspace_bytes(0, ctypes.byref(big), 1, ctypes.byref(out1)) == OK
     assert lib.cq_workspace_bytes(0, ctypes.byref(big), 4, ctypes.byref(out4)) == OK
-    assert out1.value == out4.value == 8 * 65536 * 4  # 2048-column slices
+    assert out1.value == 8 * 65536 * 4 and out4.value == 4 * 4 * 65536 * 4
     # W2A8: only the row-streaming kernel has a binary decoder
     wide, _ = _matrix(bits=1, rows=4, cols=16384)
     assert _w2a8(wide, batch=3, y=0) == NULL
