@@ -423,7 +423,6 @@ cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c, void 
   cq::CodeLevels lev;
   cq_status st = check_matrix(W, &lev);
   if (st != CQ_OK) return st;
-  if (W->bits == 1) return CQ_ERR_BITS;  // no binary decoder on the bf16 matrix cores
   if (m < 0 || m > CQ_MAX_DIM) return CQ_ERR_SHAPE;
   if (m == 0 || W->rows == 0) return CQ_OK;
   if (!c) return CQ_ERR_NULL;

@@ -176,6 +176,18 @@ __device__ inline void decode1_planes(const BinTable<T16> &t, uint32_t b, uint32
   }
 }
 
+// 1-bit, natural order: the 8 codes of byte b as the pairs (0,1) (2,3) (4,5)
+// (6,7) (the GEMM's B tile keeps k in order).
+template <typename T16>
+__device__ inline void decode1(const BinTable<T16> &t, uint32_t b, uint32_t *o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = (b >> (2 * i)) & 3u;                                  // bits 2i and 2i + 1
+    const uint32_t sel = ((x * 0x00800100u) & 0x01000100u) | 0x00020002u;  // -> bits 8, 24
+    o[i] = perm(0u, t.src, sel);
+  }
+}
+
 // Slot order of the permuted decoders: position t of an 8-value operand holds
 // code perm_code<SB>(t) of its 8 consecutive codes (3-bit: natural order).
 template <int SB>

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
   // parts: part 0 writes the Xr chunks, builds the group's table (set 0: even
   // stages start a group) and decodes the first half of this thread's codes;
   // part 1 decodes the second half.  Each half is two 16-byte chunks of W.
-  Table<SB, __bf16> tab;
+  typename std::conditional<SB == 1, BinTable<__bf16>, Table<SB, __bf16>>::type tab;
   auto store_part = [&](int buf, auto set_c, auto part_c) {
     constexpr int S = decltype(set_c)::value, PART = decltype(part_c)::value;
     const uint32_t *wcs = wc[S];
@@ -151,7 +151,10 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
     }
     static_assert(CODES / 8 == 4, "four 8-code chunks per thread and stage");
     uint32_t o[8];
-    if constexpr (SB == 4) {
+    if constexpr (SB == 1) {  // 16 codes: bytes 2 PART and 2 PART + 1 of the stage's dword
+      decode1(tab, (wcs[0] >> (16 * PART)) & 0xffu, o);
+      decode1(tab, (wcs[0] >> (16 * PART + 8)) & 0xffu, o + 4);
+    } else if constexpr (SB == 4) {
       decode4(tab, wcs[2 * PART], o);
       decode4(tab, wcs[2 * PART + 1], o + 4);
     } else if constexpr (SB == 3) {
@@ -302,6 +305,7 @@ hipError_t launch_gemm(const uint8_t *blob, int bits, int64_t rows, int64_t kpad
   if (big) {
     constexpr int threads = 64 * kWavesM * CQ_GEMM_WN;
     switch (sb) {
+      case 1: gemm_kernel<1, CQ_GEMM_WN, 256><<<grid, threads, 0, s>>>(a); break;
       case 2: gemm_kernel<2, CQ_GEMM_WN, 256><<<grid, threads, 0, s>>>(a); break;
       case 3: gemm_kernel<3, CQ_GEMM_WN, 256><<<grid, threads, 0, s>>>(a); break;
       default: gemm_kernel<4, CQ_GEMM_WN, 256><<<grid, threads, 0, s>>>(a); break;
@@ -309,6 +313,7 @@ hipError_t launch_gemm(const uint8_t *blob, int bits, int64_t rows, int64_t kpad
   } else {
     constexpr int threads = 64 * kWavesM * 2;
     switch (sb) {
+      case 1: gemm_kernel<1, 2, 128><<<grid, threads, 0, s>>>(a); break;
       case 2: gemm_kernel<2, 2, 128><<<grid, threads, 0, s>>>(a); break;
       case 3: gemm_kernel<3, 2, 128><<<grid, threads, 0, s>>>(a); break;
       default: gemm_kernel<4, 2, 128><<<grid, threads, 0, s>>>(a); break;

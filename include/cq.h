@@ -42,8 +42,7 @@ extern "C" {
 typedef enum cq_status {
   CQ_OK = 0,
   CQ_ERR_NULL = 1,      /* a required pointer is NULL                           */
-  CQ_ERR_BITS = 2,      /* bits is not 1, 2, 3, 4 or 5, or the call does not
-                           take binary matrices (cq_gemm)                      */
+  CQ_ERR_BITS = 2,      /* bits is not 1, 2, 3, 4 or 5                          */
   CQ_ERR_GROUP = 3,     /* group is not 128                                     */
   CQ_ERR_SHAPE = 4,     /* a dimension is negative or above its limit          */
   CQ_ERR_LENGTH = 5,    /* blob_bytes differs from cq_blob_bytes():
@@ -356,7 +355,7 @@ cq_status cq_gather_rows(const cq_matrix *W, const int64_t *ids, int64_t n, void
  *   c        device fp32 [m][W.rows], 4-byte aligned, must not overlap xr
  *            or the blob; fully overwritten (0 where cols == 0)
  *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_GEMM)
- *   Errors as cq_matvec; CQ_ERR_BITS for a binary matrix.
+ *   Errors as cq_matvec.
  */
 cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c,
                   void *workspace, uint64_t workspace_bytes, void *stream);

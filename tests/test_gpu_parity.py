@@ -607,7 +607,7 @@ def test_matvec_step_replays_in_a_graph():
 
 # --------------------------------------------------------------------- GEMM
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("m,rows,cols", [(1, 1, 128), (7, 100, 1000), (300, 200, 512), (130, 257, 640), (64, 129, 2048)])
 def test_gemm(bits, m, rows, cols):
     say("gemm", bits, m, rows, cols)
@@ -657,10 +657,6 @@ def test_gemm_degenerate_shapes():
     assert torch.all(C == 0)
     W1, _, _, _ = _cq_from_oracle(4, 4, 256, 42)
     assert cq.cq_gemm(W1, torch.zeros((0, 256), dtype=torch.bfloat16, device=DEV)).shape == (0, 4)
-    Wb, _, _, _ = _cq_from_oracle(1, 4, 256, 43)
-    with pytest.raises(cq.CQError) as e:
-        cq.cq_gemm(Wb, torch.zeros((2, 256), dtype=torch.bfloat16, device=DEV))
-    assert e.value.status == 2  # CQ_ERR_BITS: no binary decoder on the bf16 matrix cores
 
 
 # ------------------------------------------------------------------ encoder
