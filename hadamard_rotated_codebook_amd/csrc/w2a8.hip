@@ -211,9 +211,9 @@ __device__ inline void fill_int8(const int8_t *xq, const float *sx, int batch, i
 // the padding lanes), then the group scales [ngroups][8] (fp32).
 template <int SB>
 __global__ __launch_bounds__(kThreads) void w2a8_kernel(W8Args a) {
-  constexpr int GROUP_BYTES = CQ_GROUP * SB / 8;  // 32, 48, 64
-  constexpr int QB = GROUP_BYTES / 4;              // a quarter's bytes: 8, 12, 16
-  constexpr int QDW = QB / 4;                      // 2, 3, 4
+  constexpr int GROUP_BYTES = CQ_GROUP * SB / 8;  // 16, 32, 48, 64
+  constexpr int QB = GROUP_BYTES / 4;              // a quarter's bytes: 4, 8, 12, 16
+  constexpr int QDW = QB / 4;                      // 1, 2, 3, 4
   extern __shared__ __align__(16) uint8_t lds[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -285,7 +285,9 @@ __global__ __launch_bounds__(kThreads) void w2a8_kernel(W8Args a) {
       if (g >= ngroups) break;  // a partial last chunk (uniform)
       const uint32_t *cd = codes[S][gi];
       int32x4 bq[2];
-      if constexpr (SB == 2) {
+      if constexpr (SB == 1) {  // one 32-code slot block
+        decode1_i8(tab[0], cd[0], bq[0], bq[1]);
+      } else if constexpr (SB == 2) {
         decode2_i8(tab[0], cd[0], bq[0]);
         decode2_i8(tab[0], cd[1], bq[1]);
       } else if constexpr (SB == 4) {
@@ -631,8 +633,8 @@ int row_occupancy(const void *k, size_t lds, int dev) {
 
 typedef void (*W8Kernel)(W8Args);
 
-W8Kernel pick(int sb) {  // no binary decoder here: nullptr for sb 1
-  return sb == 2 ? w2a8_kernel<2> : (sb == 3 ? w2a8_kernel<3> : (sb == 4 ? w2a8_kernel<4> : nullptr));
+W8Kernel pick(int sb) {
+  return sb == 1 ? w2a8_kernel<1> : (sb == 2 ? w2a8_kernel<2> : (sb == 3 ? w2a8_kernel<3> : w2a8_kernel<4>));
 }
 
 }  // namespace
@@ -653,9 +655,9 @@ static bool use_row_kernel(int64_t kpad, int64_t batch) {
 }
 
 bool w2a8_fits(int bits, int64_t kpad, int64_t batch) {
+  (void)bits;  // every width has both kernels
   if (kpad > 0 && kpad % CQ_GROUP == 0 && batch >= 1 && use_row_kernel(kpad, batch)) return true;
-  // the matrix-core kernel has no binary decoder
-  return bits != 1 && kpad > 0 && kpad % CQ_GROUP == 0 && batch >= 1 && batch <= kMaxBatch &&
+  return kpad > 0 && kpad % CQ_GROUP == 0 && batch >= 1 && batch <= kMaxBatch &&
          w2a8_lds_bytes(kpad, batch) <= kW2a8MaxLds;
 }
 
@@ -691,7 +693,7 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t kpad
   // Batch 1-2 and 3 at two bits stream rows (measured faster at 65536 x
   // 16384 and 131072 x 8192); larger batches share the decode over the
   // matrix cores unless their activation does not fit that kernel's LDS.
-  const bool mfma_fits = sb != 1 && batch <= kMaxBatch && w2a8_lds_bytes(kpad, batch) <= kW2a8MaxLds;
+  const bool mfma_fits = batch <= kMaxBatch && w2a8_lds_bytes(kpad, batch) <= kW2a8MaxLds;
   if (use_row_kernel(kpad, batch) && (batch <= 2 || (batch == 3 && sb == 2) || !mfma_fits)) {
     W8RowArgs r;
     r.packed = blob;

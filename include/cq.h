@@ -295,8 +295,7 @@ cq_status cq_quantize_acts_int8(const float *x, int64_t batch, int64_t cols, int
  *            batch * cols_pad + P <= 61440 for batch <= 4 and cols_pad <=
  *            16384, or (batch + 1) * cols_pad + P <= 61440; e.g. cols_pad up
  *            to 27264 at batch 1, 16384 at batch 2 and 3, 14336 at batch 4,
- *            6528 at batch 8; binary matrices only the first form (batch
- *            <= 4, cols_pad <= 16384); CQ_ERR_SHAPE otherwise
+ *            6528 at batch 8; CQ_ERR_SHAPE otherwise
  *   y        device fp32 [batch][W.rows], 4-byte aligned, must not overlap
  *            xq, sx or the blob; fully overwritten (0 where cols == 0)
  *   Errors as cq_matvec.

@@ -449,9 +449,8 @@ def test_binary_matrices():
     assert lib.cq_workspace_bytes(0, ctypes.byref(big), 1, ctypes.byref(out1)) == OK
     assert lib.cq_workspace_bytes(0, ctypes.byref(big), 4, ctypes.byref(out4)) == OK
     assert out1.value == 8 * 65536 * 4 and out4.value == 4 * 4 * 65536 * 4
-    # W2A8: only the row-streaming kernel has a binary decoder
+    # W2A8: the same limits as the other widths (both kernels decode binary)
     wide, _ = _matrix(bits=1, rows=4, cols=16384)
-    assert _w2a8(wide, batch=3, y=0) == NULL
-    assert _w2a8(_matrix(bits=1, rows=4, cols=4096)[0], batch=5) == SHAPE
-    assert _w2a8(_matrix(bits=1, rows=4, cols=27264)[0], batch=1) == SHAPE
-    assert _w2a8(_matrix(bits=2, rows=4, cols=4096)[0], batch=5, y=0) == NULL
+    assert _w2a8(wide, batch=3, y=0) == NULL and _w2a8(wide, batch=4) == SHAPE
+    assert _w2a8(_matrix(bits=1, rows=4, cols=4096)[0], batch=5, y=0) == NULL
+    assert _w2a8(_matrix(bits=1, rows=4, cols=27264)[0], batch=1, y=0) == NULL

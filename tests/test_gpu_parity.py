@@ -413,8 +413,6 @@ def test_quantize_acts_int8_is_the_oracle_bit_for_bit(batch, cols, offset):
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("rows,cols,batch", [(700, 2048, 1), (129, 8192, 2), (64, 640, 8), (300, 16384, 1)])
 def test_matvec_w2a8_quantized_any_int8(bits, rows, cols, batch):
-    if bits == 1 and batch > 4:
-        pytest.skip("binary matrices take the row-streaming kernel only (batch <= 4)")
     # the product alone on int8 activations the oracle draws (the full range,
     # -128 included) and arbitrary positive scales; same inputs on both sides
     say("w2a8 quantized", bits, rows, cols, batch)
@@ -439,8 +437,6 @@ def test_matvec_w2a8_quantized_any_int8(bits, rows, cols, batch):
     (20, 16384, 3), (17, 14336, 4), (3, 27264, 1),
 ])
 def test_matvec_w2a8(bits, rows, cols, batch):
-    if bits == 1 and (batch > 4 or cols > 16384):
-        pytest.skip("binary matrices take the row-streaming kernel only")
     say("w2a8", bits, rows, cols, batch)
     W, blob = _random_cq(bits, rows, cols, 91 + batch)
     levels = _levels(bits)
