@@ -372,7 +372,7 @@ def main():
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; there is no multi-GPU path "
+        print("bench.py: measures one GPU only; there is no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
