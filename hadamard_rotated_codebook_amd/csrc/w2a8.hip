@@ -1,5 +1,5 @@
 // The CQ-W2A8 decode product: int8 activations, int8 codebook, integer dot
-// products on the matrix cores, one float multiply per group:
+// products, one float multiply per group:
 //
 //   y[b][r] = sum_g (float(norm[r][g]) * sx[b][g] * sc) * sum_k c8[q[r][g][k]] * xq[b][g][k]
 //
@@ -15,23 +15,28 @@
 //   sx   = fp32(absmax of the group's xr / 127), an IEEE division;
 //   xq   = clamp(round-half-even(fp32(xr / sx)), -128, 127); 0 when sx == 0;
 //   c8   = round-half-even(fp32(c / sc)), sc = fp32(max|c| / 127), computed on
-//          the host; ternary crumbs use their sign-extended integers, sc = a.
+//          the host; ternary crumbs use their sign-extended integers, sc = a;
+//          binary codes +-127.
 // The integer dots are exact; the per-group scaling and the sums are fp32.
 //
-// Design, per workgroup of 256 threads (4 waves):
-//  * a wave owns a 16-row block; v_mfma_i32_16x16x64_i8 with A = the batch
+// Three kernels:
+//  * quant_acts_kernel rotates and quantises the activation once (int8 in
+//    column order and the group scales, in global memory);
+//  * w2a8_row_kernel (batch 1-2, 3 at two bits, and what the next kernel's
+//    LDS cannot hold) streams whole stretches of rows through v_dot4_i32_i8
+//    (its own notes are below);
+//  * w2a8_kernel (larger batches): per workgroup of 256 threads (4 waves), a
+//    wave owns a 16-row block; v_mfma_i32_16x16x64_i8 with A = the batch
 //    (padding lanes read a zero row) and B = 16 rows x 64 codes of one group,
 //    two steps per group, so the i32 accumulator holds one group and is
-//    scaled into the fp32 sum before the next;
-//  * lane (row n, quarter q) owns codes 32q..32q+31 of every group of its row
-//    (8, 12 or 16 contiguous bytes) and decodes them with byte permutes of
-//    the int8 codebook held in registers;
-//  * a first kernel rotates and quantises the activation once (int8 in
-//    column order and the group scales, in global memory); each product
-//    workgroup copies it into LDS in the decoders' slot order, then loops
-//    over row tiles (a grid of about as many workgroups as fit the chip);
-//  * chunks of 4 groups, two in flight per wave; with 2+ chunks, 2 or 4 waves
-//    split a block's K and add their accumulators through LDS in wave order.
+//    scaled into the fp32 sum before the next.  Lane (row n, quarter q) owns
+//    codes 32q..32q+31 of every group of its row (4 to 16 contiguous bytes)
+//    and decodes them with byte permutes of the int8 codebook held in
+//    registers.  Each workgroup copies the quantised activation into LDS in
+//    the decoders' slot order, then loops over row tiles (a grid of about as
+//    many workgroups as fit the chip).  Chunks of 4 groups, two in flight per
+//    wave; with 2+ chunks, 2 or 4 waves split a block's K and add their
+//    accumulators through LDS in wave order.
 #include <atomic>
 #include <mutex>
 
