@@ -25,6 +25,10 @@
 //    the lane slot and the region bit), v_bfe + v_lshl_or for 6-bit fields; the
 //    half of the slot rides in the LDS instruction's immediate offset.  At CQ2 a
 //    lane spends 4 v_perm, 4 LDS reads and 4 v_fma_mix on 16 weights of a row.
+//  * The group norms of a wave's unit of 32 rows (16 bytes per row at 2 bits,
+//    4 KB apart) come in a few 2-byte loads per lane when the loads move on
+//    to the unit, and are staged in a per-wave LDS buffer: one load per row
+//    cost 11 % of the kernel's time, the unit loads cut that by a third.
 //  * Rows are read through buffer descriptors rebased per row in scalar
 //    registers.  A row past the end of its block or of the matrix gets a
 //    zero-length descriptor and reads zeros, as do lanes past the end of K (their
@@ -80,6 +84,8 @@ struct Geom {
   static constexpr int AHEAD = SB == 3 ? 8 : CQ_MV_AHEAD;        // rows of loads in flight per wave
   static constexpr int DWORDS = LANE_BYTES / 4;
   static constexpr int LOOKUPS = LANE_BYTES * 8 / IDX_BITS;     // table reads per lane and row
+  static constexpr int NORM_BYTES = SLICE_GROUPS * 2;            // a row chunk's norms: 16, 32, 8 (32 at 1 bit)
+  static constexpr int NORM_H = kRowsPerWave * SLICE_GROUPS / 64;  // a lane's norms of a unit: 4, 8, 2 (8)
   static_assert(LDS_BYTES == 128 * 1024, "tables fill 128 KB");
   static_assert(kRowsPerWave % AHEAD == 0 && AHEAD < kRowsPerWave, "prefetch ring: divides the row slots");
 };
@@ -189,6 +195,7 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
   using G = Geom<SB>;
   __shared__ __align__(16) uint8_t lds[G::LDS_BYTES];
   __shared__ __align__(16) float xrot[ROT ? G::SLICE_COLS : 4];  // the slice's rotated activations
+  __shared__ __align__(16) uint16_t nbuf[kWaves][kRowsPerWave * G::SLICE_GROUPS];  // each wave's unit norms
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps row addressing scalar
@@ -209,7 +216,6 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
   const uint32_t chunk_norm_bytes = static_cast<uint32_t>(
       2 * min(static_cast<int64_t>(G::SLICE_GROUPS), a.ngroups - static_cast<int64_t>(slice) * G::SLICE_GROUPS));
   const uint32_t voff_data = lane_active ? static_cast<uint32_t>(lane * G::LANE_BYTES) : kOutOfRange;
-  const uint32_t voff_norm = lane_active ? static_cast<uint32_t>(lane / G::LANES_PER_GROUP) * 2u : kOutOfRange;
   const uint64_t slice_packed = reinterpret_cast<uint64_t>(a.packed) + static_cast<uint64_t>(slice) * G::SLICE_BYTES;
   const uint64_t slice_norms =
       reinterpret_cast<uint64_t>(a.norms) + static_cast<uint64_t>(slice) * G::SLICE_GROUPS * 2;
@@ -234,7 +240,12 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
   const uint64_t row_step = static_cast<uint64_t>(kWaves) * a.row_bytes;
   const uint64_t nrow_step = static_cast<uint64_t>(kWaves) * a.ngroups * 2;
   int lk = 0, nlive = 0;  // loads issued in the current unit, live rows in it
-  uint64_t lp = 0, lq = 0;
+  uint64_t lp = 0;
+  // The norms of a unit's 32 row chunks come in NORM_H 2-byte loads per lane
+  // when the loads move on to the unit (norm j of the unit: row j /
+  // SLICE_GROUPS, group j % SLICE_GROUPS; lane l takes j = 64 h + l), each
+  // checked against the buffer range on its own, so groups past K read zeros.
+  uint32_t nun[G::NORM_H];
   auto start_unit = [&](int uu) {
     const int64_t r0 = static_cast<int64_t>(uu / kWaves) * a.rows_per_block;
     const int64_t lrow = r0 + uu % kWaves;
@@ -242,12 +253,20 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
     nlive = __builtin_amdgcn_readfirstlane(lend > lrow ? static_cast<int>((lend - lrow + kWaves - 1) / kWaves) : 0);
     lk = 0;
     lp = slice_packed + static_cast<uint64_t>(lrow) * a.row_bytes;
-    lq = slice_norms + static_cast<uint64_t>(lrow) * a.ngroups * 2;
+    const uint64_t lq = slice_norms + static_cast<uint64_t>(lrow) * a.ngroups * 2;
+    const uint32_t range = nlive > 0 ? static_cast<uint32_t>((nlive - 1) * nrow_step) + chunk_norm_bytes : 0u;
+    const __amdgpu_buffer_rsrc_t rq = buffer(lq, range);
+#pragma unroll
+    for (int h = 0; h < G::NORM_H; ++h) {
+      const int j = 64 * h + lane, m = j / G::SLICE_GROUPS, gq = j % G::SLICE_GROUPS;
+      const uint32_t off = 2 * gq < static_cast<int>(chunk_norm_bytes) ? static_cast<uint32_t>(m * nrow_step + 2 * gq)
+                                                                       : kOutOfRange;
+      nun[h] = __builtin_amdgcn_raw_buffer_load_b16(rq, off, 0, 0);
+    }
   };
-  auto load_next = [&](uint32_t (&d)[G::DWORDS], uint32_t &nraw) {
+  auto load_next = [&](uint32_t (&d)[G::DWORDS]) {
     const bool live = lk < nlive;
     const __amdgpu_buffer_rsrc_t rd = buffer(lp, live ? chunk_bytes : 0u);
-    const __amdgpu_buffer_rsrc_t rn = buffer(lq, live ? chunk_norm_bytes : 0u);
     // Keep every row's two loads in one fixed order, in the prologue as in the
     // loop: the wait counts at the loop header are merged over both paths, and
     // a different order there makes the compiler drain the prefetch ring.
@@ -260,11 +279,9 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
     } else {
       d[0] = __builtin_amdgcn_raw_buffer_load_b32(rd, voff_data, 0, 0);
     }
-    nraw = __builtin_amdgcn_raw_buffer_load_b16(rn, voff_norm, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     ++lk;
     lp += row_step;
-    lq += nrow_step;
   };
 
   // ---- tables: entry (position p, index v, lane) at byte
@@ -340,11 +357,10 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
   // whole chip's burst of row loads held the activations back by several us.
   constexpr int AH = G::AHEAD;
   uint32_t dw[AH][G::DWORDS];
-  uint32_t nraw[AH];
   const int first_unit = my_blocks > 0 ? first_blk * kWaves + wave : nunits;
   start_unit(first_unit);
 #pragma unroll
-  for (int u = 0; u < AH; ++u) load_next(dw[u], nraw[u]);  // in flight while the tables are built
+  for (int u = 0; u < AH; ++u) load_next(dw[u]);  // in flight while the tables are built
   const int kexp = table_exponent(static_cast<float>(G::CODES) * a.lev_absmax * mx);
   const float scale = ldexpf(1.0f, kexp), unscale = ldexpf(1.0f, -kexp);
   {
@@ -408,6 +424,7 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
 
   const uint32_t base0 = static_cast<uint32_t>(lane) * 4u;
   const uint32_t base1 = base0 + 0x10000u;
+  const int norm_group = lane / G::LANES_PER_GROUP;  // this lane's group within the slice
   int u = first_unit, un = nunits;
   uint32_t grabbed = 0;  // lane 0: the grab for the unit after this one
   while (u < nunits) {
@@ -432,13 +449,17 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
       uint32_t cur[G::DWORDS];
 #pragma unroll
       for (int d = 0; d < G::DWORDS; ++d) cur[d] = dw[slot][d];
-      nv[m & 1] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(nraw[slot]));
+      if (m == 0) {  // this unit's norms into the wave's buffer (written and read as uint16_t)
+#pragma unroll
+        for (int h = 0; h < G::NORM_H; ++h) nbuf[wave][64 * h + lane] = static_cast<uint16_t>(nun[h]);
+      }
+      nv[m & 1] = __builtin_bit_cast(_Float16, nbuf[wave][m * G::SLICE_GROUPS + norm_group]);
       if (m == 0 && lane == 0) grabbed = static_cast<uint32_t>(atomicAdd(&next_local, 1));
       if (m + AH == kRowsPerWave) {  // the loads move on to the next unit
         un = unit_of(static_cast<int>(__builtin_amdgcn_readfirstlane(grabbed)));
         start_unit(un);
       }
-      load_next(dw[slot], nraw[slot]);
+      load_next(dw[slot]);
       if constexpr (SB == 3) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {  // 6-bit field k: codes 2k, 2k+1
@@ -567,7 +588,8 @@ static bool use_small(int bits, int64_t rows, int64_t kpad, int64_t batch) {
 
 static bool use_lut(int bits, int64_t rows, int64_t kpad, int64_t batch) {
   (void)bits;
-  return batch == 1 && rows * kpad >= static_cast<int64_t>(CQ_LUT_MIN_WEIGHTS);
+  // the unit norm offsets (32 rows 16 rows apart) are 32-bit: K below 2^28
+  return batch == 1 && rows * kpad >= static_cast<int64_t>(CQ_LUT_MIN_WEIGHTS) && kpad < (int64_t{1} << 28);
 }
 
 // Workspace of one call: the per-slice partial sums, [nslice][rows] (fp32)
