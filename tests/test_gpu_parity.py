@@ -199,6 +199,21 @@ def _row_subset(blob, bits, rows, cols, pick):
     return oracle.make_blob(packed[pick], norms[pick])
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("batch", [1, 3])
+def test_matvec_very_long_rows(bits, batch):
+    # K = 65613 (a ragged last group): 65 (CQ2) or 129 (CQ4) table slices at batch 1 and
+    # 17 matrix-core slices at batch 3, all added by the combine kernel
+    rows, cols = 200, 65613
+    say("matvec long rows", bits, batch)
+    W, blob, levels, _ = _cq_from_oracle(bits, rows, cols, 140 + batch)
+    x = cq_inputs.activations(140, bits, batch, cols)
+    y = cq.cq_rotate_matvec(W, _to_dev(x)).cpu().numpy()
+    ref = oracle.matvec(blob, bits, rows, cols, x, levels)
+    w_hat = np.linalg.norm(oracle.dequantize(blob, bits, rows, cols, levels), axis=1)
+    _check_fp32_product(y, ref, w_hat, np.linalg.norm(x.astype(np.float64), axis=1))
+
+
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
 def test_matvec_full_size_sampled_rows(bits):
     # the 65536 x 16384 workload in the launch configuration the benchmark
