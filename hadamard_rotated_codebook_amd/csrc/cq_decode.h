@@ -66,6 +66,12 @@ struct Table {
   uint32_t lo[L / 4 > 0 ? L / 4 : 1], hi[L / 4 > 0 ? L / 4 : 1];
   uint32_t pair[2];  // SB == 2: T[0] | T[1] << 16, T[2] | T[3] << 16
 
+  // Byte planes as cq::MmaLevels holds them: d[k] = low bytes, d[L/4 + k] =
+  // high bytes of entries 4k..4k+3.
+  __device__ void load(const uint32_t *d) {
+#pragma unroll
+    for (int k = 0; k < L / 4; ++k) lo[k] = d[k], hi[k] = d[L / 4 + k];
+  }
   __device__ void build(const cq::CodeLevels &lev, float n) {
     if constexpr (SB == 2) {
       pair[0] = pack2<T16>(lev.v[0] * n, lev.v[1] * n);
@@ -139,6 +145,10 @@ template <int SB, typename T16>
 struct PlaneTable {
   static constexpr int L = 1 << SB;
   uint32_t lo[L / 4], hi[L / 4];
+  __device__ void load(const uint32_t *d) {
+#pragma unroll
+    for (int k = 0; k < L / 4; ++k) lo[k] = d[k], hi[k] = d[L / 4 + k];
+  }
   __device__ void build(const cq::CodeLevels &lev, float n) {
 #pragma unroll
     for (int k = 0; k < L / 4; ++k) {
@@ -157,6 +167,7 @@ struct PlaneTable {
 template <typename T16>
 struct BinTable {
   uint32_t src;
+  __device__ void load(const uint32_t *d) { src = d[0]; }
   __device__ void build(const cq::CodeLevels &lev, float n) {
     const uint32_t v0 = pack2<T16>(lev.v[0] * n, lev.v[1] * n);  // code 0 low half, code 1 high half
     src = perm(0u, v0, 0x0c000301u);                             // bytes: hi(v0), hi(v1), lo(v1), 0
@@ -258,6 +269,74 @@ __device__ inline void decode_step(const MmaTable<SB> &tab, const uint32_t *code
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = o8[4 * (s & 1) + i];
   }
+}
+
+// B operand of k step t (t < 4) of one 32-code piece of a group (the codes a
+// lane owns in the matvec kernels: SB dwords): codes 8t..8t+7 of the piece,
+// four dwords of fp16 pairs in slot order perm_code<SB>.
+template <int SB>
+__device__ inline void decode_piece(const MmaTable<SB> &tab, const uint32_t *codes, int t, uint32_t (&o)[4]) {
+  if constexpr (SB == 1) {
+    decode1_planes(tab, (codes[0] >> (8 * t)) & 0xffu, o);
+  } else if constexpr (SB == 4) {
+    decode4_planes(tab, codes[t], o);
+  } else if constexpr (SB == 3) {
+    // 24-bit field t at bit 24t of the three dwords
+    const uint32_t f = t == 0 ? codes[0]
+                     : t == 1 ? __builtin_amdgcn_alignbit(codes[1], codes[0], 24)
+                     : t == 2 ? __builtin_amdgcn_alignbit(codes[2], codes[1], 16)
+                              : codes[2] >> 8;
+    decode3(tab, f & 0xffffffu, o);
+  } else {
+    uint32_t o8[8];
+    decode2_planes(tab, codes[t >> 1], o8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = o8[4 * (t & 1) + i];
+  }
+}
+
+// The pieces of a chunk of four groups, from whole groups: lane quarter q
+// (lanes 16q..16q+15) holds group q of the chunk as four pieces of SB dwords
+// (d[p*SB + i]: piece p), and afterwards holds piece q of every group (d[j*SB
+// + i]: piece q of group j).  A 4x4 transpose across the quarters: the
+// 16-lane swap exchanges quarter bit 0 with piece bit 0, the 32-lane swap
+// quarter bit 1 with piece bit 1.
+template <int SB>
+__device__ inline void quarter_transpose(uint32_t *d) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const auto r = __builtin_amdgcn_permlane16_swap(d[(2 * h) * SB + i], d[(2 * h + 1) * SB + i], false, false);
+      d[(2 * h) * SB + i] = r[0];
+      d[(2 * h + 1) * SB + i] = r[1];
+    }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const auto r = __builtin_amdgcn_permlane32_swap(d[h * SB + i], d[(2 + h) * SB + i], false, false);
+      d[h * SB + i] = r[0];
+      d[(2 + h) * SB + i] = r[1];
+    }
+}
+
+// Every quarter's value v of a 16-lane-quarter-uniform pattern, in every
+// lane: out[j] = v of quarter j (lanes 16j..16j+15 at the same lane % 16).
+__device__ inline void quarter_gather(uint32_t v, uint32_t (&out)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // quarters (q & 1) and (q & 1) + 2
+  const auto lo = __builtin_amdgcn_permlane16_swap(a[0], a[0], false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(a[1], a[1], false, false);
+  out[0] = lo[0], out[1] = lo[1], out[2] = hi[0], out[3] = hi[1];
+}
+
+// Activation operand of the fp16 matrix-core matvec kernels: batch rows
+// 0..7 of the 16 MFMA rows carry fp16(a), rows 8..15 fp16(a - fp16(a)), with
+// a the activation times a power of two; the products with the two rows add
+// up to the product with a to about 2^-22.
+__device__ inline void split_f16(float a, _Float16 &hi, _Float16 &lo) {
+  hi = static_cast<_Float16>(a);
+  lo = static_cast<_Float16>(a - static_cast<float>(hi));
 }
 
 }  // namespace cqdev

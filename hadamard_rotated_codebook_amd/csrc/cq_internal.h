@@ -27,6 +27,22 @@ struct EncodeTable {
 // Storage width of one index: 2 for ternary crumbs, else bits (1 for binary).
 inline int storage_bits(int bits) { return bits == 5 ? 2 : bits; }
 
+// Code levels of the fp16 matrix-core matvec kernels.  The weight operand is
+// the level of each code alone (the group norm is applied in fp32 to each
+// group's sum), scaled by 1 / lscale and held as the sum of two fp16 values,
+// hi = fp16(level / lscale) and lo = fp16(level / lscale - hi), so that the
+// operand carries 22 significant bits.  Binary and ternary levels are
+// integer multiples of one level (+-1; 0, 1, -2, -1), exact in fp16 with
+// lscale = that level, and need no low part.  hi / lo hold the decode tables
+// of the 16-bit values as cq_decode.h's MmaTable loads them (byte planes).
+struct MmaLevels {
+  uint32_t hi[8];
+  uint32_t lo[8];
+  float lscale;
+  int32_t split;  // 1 when some low part is non-zero
+};
+MmaLevels mma_levels(int bits, const CodeLevels &lev);
+
 // fp32 ternary level: a / sqrt(128) with a = 1.2240064, divided in double and
 // rounded once (needle.js tutorial, "Shared codebooks").
 float ternary_level_f32();

@@ -180,12 +180,19 @@ cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t 
  *   computed in fp32, scaled by a power of two per slice of 512-2048 columns
  *   and rounded once to fp16 (relative error <= 2^-11 per entry).  Products
  *   with the fp16 norm and all sums are fp32.
- *   Arithmetic of the matrix-core kernels (W read once for the batch): each
- *   weight is fp16(c[q] * float(norm)) and each activation fp16(xr * 2^e),
- *   2^e a power of two per batch vector and slice of up to 4096 columns that
- *   puts the slice's largest |xr| in [2^14, 2^15) (both roundings to nearest
- *   even, relative error <= 2^-11); products and sums are fp32 and the scale
- *   is undone exactly.
+ *   Arithmetic of the matrix-core kernels (W read once for the batch; the
+ *   fp16 matrix cores with two-part operands): the activation a = xr * 2^e
+ *   (2^e a power of two per batch vector and slice of up to 4096 columns
+ *   that puts the slice's largest |xr| in [2^14, 2^15)) is held as
+ *   hi = fp16(a) plus lo = fp16(a - hi); each code's level, scaled by 2^sl
+ *   (largest |level| in [2^14, 2^15)), is held the same way (binary and
+ *   ternary levels are exact multiples of one level and need no low part);
+ *   the products of the fp16 parts are exact in fp32, each 128-group is
+ *   summed on its own in fp32 and multiplied in fp32 by float(norm) * 2^-sl
+ *   (or by norm * level), and the scales are undone exactly.  Operands
+ *   thus carry 22 significant bits, and no rounding is shared by all weights
+ *   of one code: activations lined up with a weight row, group norms in
+ *   fp16's subnormal range and rows of one group keep fp32 accuracy.
  *   Results do not depend on scheduling: partial sums (of K slices, or of
  *   the waves that share a row block) are added in a fixed order.
  */
