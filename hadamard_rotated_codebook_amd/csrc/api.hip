@@ -75,6 +75,11 @@ cq_status check_matrix(const cq_matrix *W, cq::CodeLevels *lev) {
 
 size_t dtype_size(int32_t dt) { return dt == CQ_F32 ? 4 : 2; }
 
+// The matvec kernels' 32-bit tile offsets bound cols_pad.
+cq_status check_matvec_cols(const cq_matrix *W) {
+  return padded(W->cols) > CQ_MAX_MATVEC_COLS ? CQ_ERR_SHAPE : CQ_OK;
+}
+
 }  // namespace
 
 namespace cq {
@@ -123,13 +128,13 @@ cq_status cq_workspace_bytes(int32_t op, const cq_matrix *W, int64_t batch, uint
   cq_status st = check_matrix(W, &lev);
   if (st != CQ_OK) return st;
   if (op == CQ_OP_MATVEC) {
-    if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+    if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH || check_matvec_cols(W) != CQ_OK) return CQ_ERR_SHAPE;
     *bytes = W->rows ? cq::matvec_workspace_bytes(W->bits, W->rows, padded(W->cols), batch) : 0;
   } else if (op == CQ_OP_ROTATE_MATVEC) {
-    if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+    if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH || check_matvec_cols(W) != CQ_OK) return CQ_ERR_SHAPE;
     *bytes = W->rows ? cq::rotate_matvec_workspace_bytes(W->bits, W->rows, padded(W->cols), batch) : 0;
   } else if (op == CQ_OP_GEMM) {
-    if (batch < 0 || batch > CQ_MAX_DIM) return CQ_ERR_SHAPE;
+    if (batch < 0 || batch > CQ_MAX_DIM || padded(W->cols) > CQ_MAX_GEMM_COLS) return CQ_ERR_SHAPE;
     *bytes = 0;
   } else if (op == CQ_OP_W2A8) {
     if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
@@ -164,6 +169,7 @@ cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y
   cq_status st = check_matrix(W, &lev);
   if (st != CQ_OK) return st;
   if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+  if ((st = check_matvec_cols(W)) != CQ_OK) return st;
   if (batch == 0 || W->rows == 0) return CQ_OK;
   if (!y) return CQ_ERR_NULL;
   if (!aligned(y, 4)) return CQ_ERR_ALIGN;
@@ -193,6 +199,7 @@ cq_status cq_rotate_matvec(const cq_matrix *W, const float *x, int64_t batch, fl
   cq_status st = check_matrix(W, &lev);
   if (st != CQ_OK) return st;
   if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+  if ((st = check_matvec_cols(W)) != CQ_OK) return st;
   if (batch == 0 || W->rows == 0) return CQ_OK;
   if (!y) return CQ_ERR_NULL;
   if (!aligned(y, 4)) return CQ_ERR_ALIGN;
@@ -229,7 +236,7 @@ cq_status check_multi(const cq_matrix *W, int32_t n, int64_t batch, cq::MultiIte
   for (int i = 0; i < n; ++i) {
     cq_status st = check_matrix(&W[i], &items[i].lev);
     if (st != CQ_OK) return st;
-    if (W[i].cols != W[0].cols) return CQ_ERR_SHAPE;
+    if (W[i].cols != W[0].cols || check_matvec_cols(&W[i]) != CQ_OK) return CQ_ERR_SHAPE;
     items[i].blob = static_cast<const uint8_t *>(W[i].blob);
     items[i].bits = W[i].bits;
     items[i].rows = W[i].rows;
@@ -342,6 +349,7 @@ static cq_status check_w2a8(const cq_matrix *W, int64_t batch, float *y, cq::Cod
   cq_status st = check_matrix(W, lev);
   if (st != CQ_OK) return st;
   if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+  if ((st = check_matvec_cols(W)) != CQ_OK) return st;
   if (batch == 0 || W->rows == 0) return CQ_OK;
   *kpad = padded(W->cols);
   if (*kpad > 0 && !cq::w2a8_fits(W->bits, *kpad, batch)) return CQ_ERR_SHAPE;
@@ -418,7 +426,7 @@ cq_status cq_gather_rows(const cq_matrix *W, const int64_t *ids, int64_t n, void
 
 cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c, void *workspace,
                   uint64_t workspace_bytes, void *stream) {
-  (void)workspace;
+  (void)workspace;  // no scratch: cq_workspace_bytes(CQ_OP_GEMM) is 0
   (void)workspace_bytes;
   cq::CodeLevels lev;
   cq_status st = check_matrix(W, &lev);
@@ -430,6 +438,7 @@ cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c, void 
   const uint64_t cbytes = static_cast<uint64_t>(m) * W->rows * 4;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t kpad = padded(W->cols);
+  if (kpad > CQ_MAX_GEMM_COLS) return CQ_ERR_SHAPE;
   if (kpad == 0) return hip_status(cq::launch_zero_f32(c, m * W->rows, s));
   if (!xr) return CQ_ERR_NULL;
   if (!aligned(xr, 16)) return CQ_ERR_ALIGN;

@@ -67,6 +67,12 @@ typedef enum cq_dtype { CQ_F32 = 0, CQ_F16 = 1, CQ_BF16 = 2 } cq_dtype;
 #define CQ_GROUP 128
 /* Most matrices in one cq_rotate_multi_matvec call. */
 #define CQ_MAX_MULTI 64
+/* Widest cols_pad of the matvec calls (cq_matvec, cq_rotate_matvec,
+ * cq_rotate_multi_matvec, their workspace queries) and of cq_gemm: the
+ * kernels address a tile of rows with 32-bit offsets.  Wider matrices are
+ * refused with CQ_ERR_SHAPE before anything is launched. */
+#define CQ_MAX_MATVEC_COLS ((int64_t)1 << 24)
+#define CQ_MAX_GEMM_COLS ((int64_t)1 << 22)
 
 /*
  * A CQ matrix as the ".cact" blob stores it (needle.js tutorial, "Anatomy of a
@@ -161,7 +167,8 @@ cq_status cq_rotate_acts(const void *x, int32_t x_dtype, int64_t batch, int64_t 
  *
  *   y[b][r] = sum_g float(norm[r][g]) * sum_j c[q[r][g*128+j]] * xr[b][g*128+j]
  *
- *   W        matrix descriptor (its blob is read, never expanded)
+ *   W        matrix descriptor (its blob is read, never expanded);
+ *            W.cols_pad <= CQ_MAX_MATVEC_COLS, else CQ_ERR_SHAPE
  *   xr       device fp32 [batch][W.cols_pad], 16-byte aligned, as written by
  *            cq_rotate_acts(..., CQ_F32, ...)
  *   batch    0 <= batch <= CQ_MAX_MATVEC_BATCH
@@ -360,8 +367,10 @@ cq_status cq_gather_rows(const cq_matrix *W, const int64_t *ids, int64_t n, void
  *   m        0 <= m <= CQ_MAX_DIM
  *   c        device fp32 [m][W.rows], 4-byte aligned, must not overlap xr
  *            or the blob; fully overwritten (0 where cols == 0)
- *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_GEMM)
- *   Errors as cq_matvec.
+ *   workspace, workspace_bytes: unused -- the product needs no scratch and
+ *            cq_workspace_bytes(CQ_OP_GEMM) reports 0; pass NULL, 0 (any
+ *            value is accepted and ignored)
+ *   Errors as cq_matvec; CQ_ERR_SHAPE also for cols_pad > CQ_MAX_GEMM_COLS.
  */
 cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c,
                   void *workspace, uint64_t workspace_bytes, void *stream);

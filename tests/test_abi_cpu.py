@@ -454,3 +454,36 @@ def test_binary_matrices():
     assert _w2a8(wide, batch=3, y=0) == NULL and _w2a8(wide, batch=4) == SHAPE
     assert _w2a8(_matrix(bits=1, rows=4, cols=4096)[0], batch=5, y=0) == NULL
     assert _w2a8(_matrix(bits=1, rows=4, cols=27264)[0], batch=1, y=0) == NULL
+
+
+def test_column_limits_are_shape_errors():
+    # the kernels' 32-bit tile offsets bound cols_pad: a wider matrix is a
+    # CQ_ERR_SHAPE from validation (nothing launched), not a launch failure
+    gemm_max, mv_max = 1 << 22, 1 << 24
+    m, k = _matrix(rows=1, cols=gemm_max + 1)
+    assert _gemm(m) == SHAPE
+    out = ctypes.c_uint64(7)
+    assert lib.cq_workspace_bytes(cq.OP_GEMM, ctypes.byref(m), 8, ctypes.byref(out)) == SHAPE and out.value == 7
+    m, k = _matrix(rows=1, cols=mv_max + 1)
+    assert _matvec(m) == SHAPE and _rotate_matvec(m) == SHAPE
+    for op in (cq.OP_MATVEC, cq.OP_ROTATE_MATVEC):
+        assert lib.cq_workspace_bytes(op, ctypes.byref(m), 1, ctypes.byref(out)) == SHAPE and out.value == 7
+    # at the limits the shape passes and validation goes on to the next check
+    # (outputs placed over the activation: CQ_ERR_OVERLAP, nothing launched)
+    m, k = _matrix(rows=1, cols=gemm_max)
+    assert _gemm(m, c=FAKE + (1 << 30)) == OVERLAP
+    m, k = _matrix(rows=1, cols=mv_max)
+    assert _matvec(m, y=FAKE + (1 << 30)) == OVERLAP
+
+
+def test_gemm_ignores_its_workspace_arguments():
+    # cq_gemm needs no scratch: the workspace query reports 0 and any
+    # workspace pointer and size are accepted (validation reaches the same
+    # overlap error with and without them)
+    m, k = _matrix()
+    out = ctypes.c_uint64(7)
+    assert lib.cq_workspace_bytes(cq.OP_GEMM, ctypes.byref(m), 4096, ctypes.byref(out)) == OK and out.value == 0
+    base = lib.cq_gemm(ctypes.byref(m), ctypes.c_void_p(FAKE + (1 << 30)), 8, ctypes.c_void_p(FAKE), None, 0, None)
+    with_ws = lib.cq_gemm(ctypes.byref(m), ctypes.c_void_p(FAKE + (1 << 30)), 8, ctypes.c_void_p(FAKE),
+                          ctypes.c_void_p(FAKE + 3), 5, None)
+    assert base == with_ws == OVERLAP
