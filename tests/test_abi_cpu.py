@@ -469,11 +469,12 @@ def test_column_limits_are_shape_errors():
     for op in (cq.OP_MATVEC, cq.OP_ROTATE_MATVEC):
         assert lib.cq_workspace_bytes(op, ctypes.byref(m), 1, ctypes.byref(out)) == SHAPE and out.value == 7
     # at the limits the shape passes and validation goes on to the next check
-    # (outputs placed over the activation: CQ_ERR_OVERLAP, nothing launched)
+    # (nothing is launched: the gemm's output overlaps its activation, the
+    # matvec has no workspace for its K slices)
     m, k = _matrix(rows=1, cols=gemm_max)
     assert _gemm(m, c=FAKE + (1 << 30)) == OVERLAP
     m, k = _matrix(rows=1, cols=mv_max)
-    assert _matvec(m, y=FAKE + (1 << 30)) == OVERLAP
+    assert _matvec(m, y=FAKE + (1 << 30)) == WORKSPACE
 
 
 def test_gemm_ignores_its_workspace_arguments():
