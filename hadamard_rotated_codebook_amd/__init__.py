@@ -11,7 +11,7 @@ importing this package without it raises ``ImportError`` -- there is no
 fallback path.
 
 Functions carry the C names: ``cq_blob_bytes``, ``cq_workspace_bytes``,
-``cq_rotate_acts``, ``cq_matvec``, ``cq_rotate_matvec``,
+``cq_rotate_acts``, ``cq_matvec``, ``cq_rotate_matvec``, ``cq_rotate_matvec_noalloc``,
 ``cq_rotate_multi_matvec``, ``cq_rotate_multi_workspace_bytes``,
 ``cq_quantize_acts_int8``, ``cq_matvec_w2a8_quantized``, ``cq_matvec_w2a8``,
 ``cq_gather_rows``, ``cq_gemm``, ``cq_quantize``.
@@ -27,7 +27,7 @@ import torch
 __all__ = [
     "LIB_PATH", "CQError", "CQMatrix", "CQ_GROUP", "CQ_MAX_MATVEC_BATCH", "workspace_for",
     "cq_version", "cq_blob_bytes", "cq_workspace_bytes",
-    "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_multi_matvec",
+    "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_matvec_noalloc", "cq_rotate_multi_matvec",
     "cq_rotate_multi_workspace_bytes", "cq_quantize_acts_int8", "cq_matvec_w2a8_quantized", "cq_matvec_w2a8",
     "cq_gather_rows", "cq_gemm", "cq_quantize",
 ]
@@ -63,6 +63,7 @@ _SIGS = {
     "cq_rotate_acts": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _vp]),
     "cq_matvec": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_rotate_matvec": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
+    "cq_rotate_matvec_noalloc": (_i32, [_MP, _vp, _i64, _vp, _vp]),
     "cq_rotate_multi_matvec": (_i32, [_MP, _i32, _vp, _i64, ctypes.POINTER(_vp), _vp, _u64, _vp]),
     "cq_rotate_multi_workspace_bytes": (_i32, [_MP, _i32, _i64, ctypes.POINTER(_u64)]),
     "cq_quantize_acts_int8": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
@@ -246,6 +247,20 @@ def cq_rotate_matvec(W, x, out=None, workspace=None):
     ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.cq_rotate_matvec(ctypes.byref(m), _dev(x, "x"), b, _dev(out, "out"), ws, wsb, _stream()))
+    return out
+
+
+def cq_rotate_matvec_noalloc(W, x, out):
+    """cq_rotate_matvec with the library's static device scratch instead of
+    a workspace: x float32 [batch, cols] (not rotated), out float32 [batch,
+    rows] (the caller provides it; the call allocates nothing)."""
+    if x.dtype != torch.float32 or x.dim() != 2 or x.shape[1] != W.cols or not x.is_contiguous():
+        raise ValueError("x must be contiguous float32 [batch, cols]")
+    b = x.shape[0]
+    if out.dtype != torch.float32 or tuple(out.shape) != (b, W.rows) or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 [batch, rows]")
+    m, keep = W._struct()
+    _check(_lib.cq_rotate_matvec_noalloc(ctypes.byref(m), _dev(x, "x"), b, _dev(out, "out"), _stream()))
     return out
 
 

@@ -110,6 +110,7 @@ const char *cq_status_string(cq_status status) {
     case CQ_ERR_ALIGN: return "a device pointer is not aligned as documented";
     case CQ_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case CQ_ERR_OVERLAP: return "an output buffer overlaps an input buffer";
+    case CQ_ERR_SCRATCH: return "the call needs more than the static scratch of the no-allocation entry point";
   }
   return "unknown status";
 }

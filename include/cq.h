@@ -53,7 +53,10 @@ typedef enum cq_status {
   CQ_ERR_WORKSPACE = 8, /* workspace smaller than cq_workspace_bytes()          */
   CQ_ERR_ALIGN = 9,     /* a device pointer is not aligned as documented        */
   CQ_ERR_HIP = 10,      /* a HIP runtime call or kernel launch failed           */
-  CQ_ERR_OVERLAP = 11   /* an output buffer overlaps an input buffer            */
+  CQ_ERR_OVERLAP = 11,  /* an output buffer overlaps an input buffer            */
+  CQ_ERR_SCRATCH = 12   /* the call needs more than the static scratch
+                           (CQ_NOALLOC_SCRATCH_BYTES) of the no-allocation
+                           entry point                                        */
 } cq_status;
 
 /* Element types of activation buffers. */
@@ -73,6 +76,8 @@ typedef enum cq_dtype { CQ_F32 = 0, CQ_F16 = 1, CQ_BF16 = 2 } cq_dtype;
  * refused with CQ_ERR_SHAPE before anything is launched. */
 #define CQ_MAX_MATVEC_COLS ((int64_t)1 << 24)
 #define CQ_MAX_GEMM_COLS ((int64_t)1 << 22)
+/* Size of the static device scratch of cq_rotate_matvec_noalloc (16 MiB). */
+#define CQ_NOALLOC_SCRATCH_BYTES ((uint64_t)16 << 20)
 
 /*
  * A CQ matrix as the ".cact" blob stores it (needle.js tutorial, "Anatomy of a
@@ -226,6 +231,25 @@ cq_status cq_matvec(const cq_matrix *W, const float *xr, int64_t batch, float *y
  */
 cq_status cq_rotate_matvec(const cq_matrix *W, const float *x, int64_t batch, float *y,
                            void *workspace, uint64_t workspace_bytes, void *stream);
+
+/*
+ * cq_rotate_matvec without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The call allocates nothing (no hipMalloc,
+ * no hipFree, no allocating library routine); its scratch is a static device
+ * array of CQ_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends.
+ *
+ *   W, x, batch, y, stream: as cq_rotate_matvec (same results, bit for bit)
+ *   Errors: those of cq_rotate_matvec; CQ_ERR_SCRATCH when
+ *   cq_workspace_bytes(CQ_OP_ROTATE_MATVEC, W, batch) exceeds
+ *   CQ_NOALLOC_SCRATCH_BYTES (16 MiB covers 65536 x 16384 at batch 1..8);
+ *   nothing is launched then.
+ *   Every call on one GPU uses the same array and leaves its contents there;
+ *   no call reads what another wrote.  Calls that run at the same time on one
+ *   GPU (several streams or host threads) race on the array: serialise them.
+ */
+cq_status cq_rotate_matvec_noalloc(const cq_matrix *W, const float *x, int64_t batch, float *y, void *stream);
 
 /*
  * Several decode products with one activation: for i < n,

@@ -16,7 +16,7 @@ from conftest import ROOT
 cq = pytest.importorskip("hadamard_rotated_codebook_amd", reason="libcq.so not built")
 lib = cq._lib
 
-OK, NULL, BITS, GROUP, SHAPE, LENGTH, CODEBOOK, DTYPE, WORKSPACE, ALIGN, HIP, OVERLAP = range(12)
+OK, NULL, BITS, GROUP, SHAPE, LENGTH, CODEBOOK, DTYPE, WORKSPACE, ALIGN, HIP, OVERLAP, SCRATCH = range(13)
 FAKE = 1 << 40  # a 256-byte aligned address that is never dereferenced on the host
 
 
@@ -28,7 +28,8 @@ def _declared_functions():
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
     assert set(names) == {"cq_version", "cq_status_string", "cq_blob_bytes", "cq_workspace_bytes",
-                          "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_multi_matvec",
+                          "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_matvec_noalloc",
+                          "cq_rotate_multi_matvec",
                           "cq_rotate_multi_workspace_bytes", "cq_quantize_acts_int8", "cq_matvec_w2a8_quantized",
                           "cq_matvec_w2a8", "cq_gather_rows", "cq_gemm", "cq_quantize"}
     for n in names:
@@ -37,8 +38,8 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     assert cq.cq_version() == 10000
-    for s in range(12):
-        assert lib.cq_status_string(s).decode()
+    for s in range(13):
+        assert lib.cq_status_string(s).decode() != "unknown status"
     assert lib.cq_status_string(LENGTH).decode() == "Inconsistent CQ matrix length"
     assert lib.cq_status_string(99).decode() == "unknown status"
 
@@ -488,3 +489,32 @@ def test_gemm_ignores_its_workspace_arguments():
     with_ws = lib.cq_gemm(ctypes.byref(m), ctypes.c_void_p(FAKE + (1 << 30)), 8, ctypes.c_void_p(FAKE),
                           ctypes.c_void_p(FAKE + 3), 5, None)
     assert base == with_ws == OVERLAP
+
+
+def _noalloc(m, x=FAKE + (1 << 30), batch=1, y=FAKE + (1 << 31)):
+    return lib.cq_rotate_matvec_noalloc(ctypes.byref(m), ctypes.c_void_p(x), batch, ctypes.c_void_p(y), None)
+
+
+def test_noalloc_validation():
+    # the checks of cq_rotate_matvec, then the static scratch's size: a call
+    # that needs more than CQ_NOALLOC_SCRATCH_BYTES is refused before any
+    # device call (65536 x 16384 fits at every batch; 2^20 rows do not)
+    limit = 16 << 20
+    m, k = _matrix(bits=7, nbytes=0, levels=None)
+    assert _noalloc(m) == BITS
+    m, k = _matrix()
+    assert _noalloc(m, batch=9) == SHAPE and _noalloc(m, y=0) == NULL and _noalloc(m, y=FAKE + 64) == OVERLAP
+    need = ctypes.c_uint64(0)
+    for bits in (1, 2, 3, 4, 5):
+        for batch in range(1, 9):
+            m, k = _matrix(bits=bits, rows=65536, cols=16384)
+            assert lib.cq_workspace_bytes(cq.OP_ROTATE_MATVEC, ctypes.byref(m), batch, ctypes.byref(need)) == OK
+            assert need.value <= limit
+    m, k = _matrix(rows=1 << 20, cols=16384)
+    assert lib.cq_workspace_bytes(cq.OP_ROTATE_MATVEC, ctypes.byref(m), 1, ctypes.byref(need)) == OK
+    assert need.value > limit
+    assert _noalloc(m) == SCRATCH
+    assert "static scratch" in lib.cq_status_string(SCRATCH).decode()
+    # nothing to do: no device call at all
+    m, k = _matrix(rows=0)
+    assert _noalloc(m) == OK
