@@ -168,3 +168,113 @@ def test_gather_rows_times_x_is_the_matvec():
     g = oracle.gather_rows(blob, 2, rows, cols, ids, levels)
     y = oracle.matvec(blob, 2, rows, cols, x, levels)
     assert np.allclose(x.astype(np.float64) @ g.T, y[:, ids], rtol=1e-12, atol=1e-12)
+
+
+# --- pins of gemm_bf16's rounding points --------------------------------------
+#
+# gemm_bf16 rounds the rotated activation X' = fp32(H.x) and the weight operand
+# V = fp32(level) * fp32(norm) (the product in fp32) to bf16, nearest even, and
+# sums the products in float64.  The hand-made case below puts X' and V on and
+# off bf16 ties, so that every plausible slip -- rounding only X', only V,
+# neither, V before the norm multiply, or ties away from zero instead of to
+# even -- gives a different, hand-computed result.
+
+def _bf16_by_hand(v):
+    """bf16 round to nearest, ties to even, by way of the significand: v =
+    m * 2^e with m in [0.5, 1); keep 8 significant bits with Python's round
+    (which rounds halves to even).  Normal finite values only."""
+    import math
+    if v == 0.0:
+        return 0.0
+    m, e = math.frexp(v)
+    return math.ldexp(round(m * 256.0), e - 8)
+
+
+def _tie_case():
+    # levels of a 2-bit code book (inputs of the method): 0 for the unused
+    # columns, and two values whose products with the norms sit on or off
+    # bf16 ties (bf16 spacing in [1, 2) is 2^-7)
+    levels = np.array([-1.0, 0.0, 1.00390625, 1.01171875], dtype=np.float32)
+    rows, cols = 2, 128
+    codes = np.ones((rows, cols), dtype=np.uint8)  # level 0
+    codes[:, 0], codes[:, 1] = 2, 3
+    norms = np.array([[1.5], [1.0]], dtype=np.float16)
+    blob = oracle.make_blob(oracle.pack_codes(codes, 2), norms)
+    # x = H v, so that the rotated activation is v (exact in fp32 after the
+    # float64 rotation: x is constant on the Hadamard columns' signs)
+    v = np.zeros(cols)
+    v[0], v[1] = 1.005859375, 1.00390625  # 128.75 ulps (rounds up); an exact tie (to even: down)
+    x = (oracle.hadamard() @ v)[None, :]
+    return blob, levels, rows, cols, x
+
+
+def test_gemm_bf16_tie_case_by_hand():
+    blob, levels, rows, cols, x = _tie_case()
+    C = oracle.gemm_bf16(blob, 2, rows, cols, x, levels)
+    # X' = bf16(1.005859375) = 1.0078125, bf16(1.00390625) = 1.0 (tie to even)
+    # row 0 (norm 1.5): V = bf16(1.505859375) = 1.5078125, bf16(1.517578125) = 1.515625
+    # row 1 (norm 1.0): V = bf16(1.00390625) = 1.0 (tie, even), bf16(1.01171875) = 1.015625 (tie, even)
+    want = [1.0078125 * 1.5078125 + 1.0 * 1.515625, 1.0078125 * 1.0 + 1.0 * 1.015625]
+    assert C.shape == (1, 2) and C[0].tolist() == want
+
+
+def test_gemm_bf16_rounding_slips_all_differ():
+    blob, levels, rows, cols, x = _tie_case()
+    got = oracle.gemm_bf16(blob, 2, rows, cols, x, levels)[0]
+    c = [1.00390625, 1.01171875]
+    v = [1.005859375, 1.00390625]
+    n = [1.5, 1.0]
+
+    def product(rx, rv, v_before_norm=False, rnd=_bf16_by_hand):
+        out = []
+        for r in range(2):
+            acc = 0.0
+            for k in range(2):
+                xk = rnd(v[k]) if rx else v[k]
+                if v_before_norm:
+                    vk = rnd(c[k]) * n[r]
+                else:
+                    vk = rnd(float(np.float32(c[k]) * np.float32(n[r]))) if rv else c[k] * n[r]
+                acc += xk * vk
+            out.append(acc)
+        return out
+
+    variants = {
+        "both": product(True, True),
+        "x only": product(True, False),
+        "v only": product(False, True),
+        "neither": product(False, False),
+        "v before norm": product(True, True, v_before_norm=True),
+        "ties away": product(True, True, rnd=math_half_up),
+    }
+    vals = [tuple(v_) for v_ in variants.values()]
+    assert len(set(vals)) == len(vals), variants
+    assert got.tolist() == variants["both"]
+
+
+def math_half_up(v):
+    """bf16 rounding with ties away from zero (positive values): the slip
+    the tie case must catch."""
+    import math
+    m, e = math.frexp(v)
+    return math.ldexp(math.floor(m * 256.0 + 0.5), e - 8)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+def test_gemm_bf16_equals_an_explicit_loop(bits):
+    rows, cols, M = 3, 256, 2
+    blob, levels, _ = _blob(101, bits, rows, cols)
+    X = cq_inputs.activations(101, bits, M, cols, "f16")
+    got = oracle.gemm_bf16(blob, bits, rows, cols, X, levels)
+    packed, norms = oracle.split_blob(blob, bits, rows, cols)
+    vals = oracle.level_values(oracle.unpack_codes(packed, bits, cols), bits, levels)
+    S = oracle.sylvester(128)
+    for m in range(M):
+        xr = [sum(float(X[m, 128 * (k // 128) + j]) * S[k % 128, j] for j in range(128)) / np.sqrt(128)
+              for k in range(cols)]
+        for r in range(rows):
+            acc = 0.0
+            for k in range(cols):
+                w = float(np.float32(vals[r, k]) * np.float32(norms[r, k // 128]))
+                acc += _bf16_by_hand(float(np.float32(xr[k]))) * _bf16_by_hand(w)
+            assert abs(acc - got[m, r]) <= 1e-12 * max(1.0, abs(acc)), (m, r)
