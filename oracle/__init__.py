@@ -21,7 +21,7 @@ format.  Citations use these page names:
   Chinese, no headings; cited by topic: "CQ quantisation steps", "codebook
   generation", "file layout", "byte accounting table", "idempotence note",
   "rotated-activation identity", "Cactus 2-bit kernel", "activation
-  fake-quant note").
+  fake-quant note", "numeric-paths note", "attention note").
 
 Readings taken where the pages are silent or garbled are stated next to the
 code they affect (each is also listed in the design notes of the repository).
@@ -34,6 +34,7 @@ input of every product call, so this affects no parity claim).
 
 from .cq import *  # noqa: F401,F403
 from .w2a8 import *  # noqa: F401,F403
-from . import cq as _cq, w2a8 as _w2a8
+from .kv import *  # noqa: F401,F403
+from . import cq as _cq, w2a8 as _w2a8, kv as _kv
 
-__all__ = list(_cq.__all__) + list(_w2a8.__all__)
+__all__ = list(_cq.__all__) + list(_w2a8.__all__) + list(_kv.__all__)
