@@ -29,7 +29,8 @@ __all__ = [
     "cq_version", "cq_blob_bytes", "cq_workspace_bytes",
     "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_matvec_noalloc", "cq_rotate_multi_matvec",
     "cq_rotate_multi_workspace_bytes", "cq_quantize_acts_int8", "cq_matvec_w2a8_quantized", "cq_matvec_w2a8",
-    "cq_gather_rows", "cq_gemm", "cq_quantize",
+    "cq_gather_rows", "cq_gemm", "cq_quantize", "cq_quantize_rows", "cq_kv_scores_workspace_bytes",
+    "cq_kv_scores", "cq_matvec_t",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcq.so")
@@ -41,7 +42,7 @@ CQ_GROUP = 128
 CQ_MAX_MATVEC_BATCH = 8
 _F32, _F16, _BF16 = 0, 1, 2
 _DTYPES = {torch.float32: _F32, torch.float16: _F16, torch.bfloat16: _BF16}
-OP_MATVEC, OP_GEMM, OP_ROTATE_MATVEC, OP_W2A8 = 0, 1, 2, 3
+OP_MATVEC, OP_GEMM, OP_ROTATE_MATVEC, OP_W2A8, OP_MATVEC_T = 0, 1, 2, 3, 4
 
 
 class _Matrix(ctypes.Structure):
@@ -72,6 +73,10 @@ _SIGS = {
     "cq_gather_rows": (_i32, [_MP, _vp, _i64, _vp, _i32, _vp]),
     "cq_gemm": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_quantize": (_i32, [_vp, _i64, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_float), _vp, _u64, _vp]),
+    "cq_quantize_rows": (_i32, [_vp, _i64, _MP, _i64, _vp]),
+    "cq_kv_scores_workspace_bytes": (_i32, [_MP, _i32, _i32, _i32, ctypes.POINTER(_u64)]),
+    "cq_kv_scores": (_i32, [_MP, _vp, _i32, _i32, _i32, _vp, _vp, _u64, _vp]),
+    "cq_matvec_t": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -423,3 +428,65 @@ def cq_quantize(w, bits, levels=None, group=CQ_GROUP, out=None):
     arr, ptr = _levels_array(levels)
     _check(_lib.cq_quantize(_dev(w, "w"), rows, cols, bits, group, ptr, _dev(out, "out"), nbytes, _stream()))
     return CQMatrix(bits, rows, cols, out, arr, group)
+
+
+def cq_quantize_rows(W, w, row0):
+    """Encode w (float32 device [n, W.cols]) into rows row0 .. row0+n-1 of the
+    existing matrix W (its blob is overwritten there): the append of new
+    tokens to a CQ-quantised KV cache."""
+    if w.dtype != torch.float32 or w.dim() != 2 or w.shape[1] != W.cols:
+        raise ValueError("w must be float32 [n, cols]")
+    m, keep = W._struct()
+    _check(_lib.cq_quantize_rows(_dev(w.contiguous(), "w"), w.shape[0], ctypes.byref(m), row0, _stream()))
+    return W
+
+
+def cq_kv_scores_workspace_bytes(K, n_q_heads, n_kv_heads, head_dim):
+    m, keep = K._struct()
+    out = _u64(0)
+    _check(_lib.cq_kv_scores_workspace_bytes(ctypes.byref(m), n_q_heads, n_kv_heads, head_dim, ctypes.byref(out)))
+    return int(out.value)
+
+
+def cq_kv_scores(K, q, n_kv_heads, out=None, workspace=None):
+    """Scores of query heads q (float32 [n_q_heads, head_dim]) against the CQ
+    key cache K [tokens, n_kv_heads * head_dim]; returns float32 [n_q_heads,
+    tokens] (consecutive query heads share a KV head)."""
+    if q.dtype != torch.float32 or q.dim() != 2:
+        raise ValueError("q must be float32 [n_q_heads, head_dim]")
+    nq, hd = q.shape
+    if out is None:
+        out = torch.empty((nq, K.rows), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (nq, K.rows):
+        raise ValueError("out must be float32 [n_q_heads, tokens]")
+    if workspace is None:
+        workspace = workspace_for(cq_kv_scores_workspace_bytes(K, nq, n_kv_heads, hd) + 256, q.device)
+    ws, wsb = ctypes.c_void_p(0), 0
+    if workspace is not None:
+        base = workspace.data_ptr()
+        pad = (-base) % 256  # the call wants a 256-byte aligned workspace
+        ws, wsb = ctypes.c_void_p(base + pad), workspace.numel() * workspace.element_size() - pad
+    m, keep = K._struct()
+    _check(_lib.cq_kv_scores(ctypes.byref(m), _dev(q.contiguous(), "q"), nq, n_kv_heads, hd, _dev(out, "out"),
+                             ws, wsb, _stream()))
+    return out
+
+
+def cq_matvec_t(W, p, out=None, workspace=None):
+    """out[b, k] = sum_r p[b, r] * w_hat[r, k]: p float32 [batch, rows];
+    returns float32 [batch, cols] (the value side of attention over a CQ
+    value cache)."""
+    if p.dtype != torch.float32 or p.dim() != 2 or p.shape[1] != W.rows:
+        raise ValueError("p must be float32 [batch, rows]")
+    b = p.shape[0]
+    if out is None:
+        out = torch.empty((b, W.cols), dtype=torch.float32, device=p.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (b, W.cols):
+        raise ValueError("out must be float32 [batch, cols]")
+    if workspace is None and b > 0:
+        workspace = workspace_for(cq_workspace_bytes(OP_MATVEC_T, W, b), p.device)
+    ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    m, keep = W._struct()
+    _check(_lib.cq_matvec_t(ctypes.byref(m), _dev(p.contiguous(), "p"), b, _dev(out, "out"), ws, wsb, _stream()))
+    return out

@@ -73,7 +73,45 @@ cq_status check_matrix(const cq_matrix *W, cq::CodeLevels *lev) {
   return code_levels(W->bits, W->levels, lev);
 }
 
+// Decision table of the encoder: exact midpoints of adjacent ascending
+// levels.  For fp32 levels whose magnitudes are within 2^29 of each other the
+// double sum is exact, so "u > mid" is the exact "nearer to the upper level"
+// test and a tie keeps the smaller index (OpenNeedle reference notes, CQ
+// quantisation steps).  levels are valid (code_levels accepted them).
+cq::EncodeTable encode_table(int32_t bits, const float *levels) {
+  cq::EncodeTable tab;
+  std::memset(&tab, 0, sizeof tab);
+  if (bits == 5) {
+    const double a = static_cast<double>(cq::ternary_level_f32());
+    tab.nlevels = 3;
+    tab.mid[0] = -a * 0.5;
+    tab.mid[1] = a * 0.5;
+    tab.code_of_index[0] = 3;  // -a -> crumb 11
+    tab.code_of_index[1] = 0;  //  0 -> crumb 00
+    tab.code_of_index[2] = 1;  // +a -> crumb 01
+  } else if (bits == 1) {
+    tab.nlevels = 2;
+    tab.mid[0] = 0.0;  // the midpoint of -c and +c
+    tab.code_of_index[0] = 0;
+    tab.code_of_index[1] = 1;
+  } else {
+    tab.nlevels = 1 << bits;
+    for (int j = 0; j + 1 < tab.nlevels; ++j)
+      tab.mid[j] = (static_cast<double>(levels[j]) + static_cast<double>(levels[j + 1])) * 0.5;
+    for (int j = 0; j < tab.nlevels; ++j) tab.code_of_index[j] = static_cast<uint32_t>(j);
+  }
+  return tab;
+}
+
 size_t dtype_size(int32_t dt) { return dt == CQ_F32 ? 4 : 2; }
+
+// Sizes of cq_matvec_t: its kernel addresses the packed rows with 32-bit
+// offsets.
+bool matvec_t_shape_ok(const cq_matrix *W) {
+  if (W->rows > CQ_MAX_MATVEC_T_ROWS || W->cols > CQ_MAX_MATVEC_COLS) return false;
+  const int64_t row_bytes = padded(W->cols) * cq::storage_bits(W->bits) / 8;
+  return W->rows * row_bytes < (int64_t{1} << 31);
+}
 
 // The matvec kernels' 32-bit tile offsets bound cols_pad.
 cq_status check_matvec_cols(const cq_matrix *W) {
@@ -134,6 +172,9 @@ cq_status cq_workspace_bytes(int32_t op, const cq_matrix *W, int64_t batch, uint
   } else if (op == CQ_OP_ROTATE_MATVEC) {
     if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH || check_matvec_cols(W) != CQ_OK) return CQ_ERR_SHAPE;
     *bytes = W->rows ? cq::rotate_matvec_workspace_bytes(W->bits, W->rows, padded(W->cols), batch) : 0;
+  } else if (op == CQ_OP_MATVEC_T) {
+    if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH || !matvec_t_shape_ok(W)) return CQ_ERR_SHAPE;
+    *bytes = W->rows && W->cols && batch ? cq::matvec_t_workspace_bytes(W->rows, W->cols, batch) : 0;
   } else if (op == CQ_OP_GEMM) {
     if (batch < 0 || batch > CQ_MAX_DIM || padded(W->cols) > CQ_MAX_GEMM_COLS) return CQ_ERR_SHAPE;
     *bytes = 0;
@@ -464,34 +505,131 @@ cq_status cq_quantize(const float *w, int64_t rows, int64_t cols, int32_t bits, 
   if (!aligned(w, 4) || !aligned(blob, 16)) return CQ_ERR_ALIGN;
   if (overlaps(blob, need, w, static_cast<uint64_t>(rows) * cols * 4)) return CQ_ERR_OVERLAP;
 
-  // Decision table: exact midpoints of adjacent ascending levels.  For fp32
-  // levels whose magnitudes are within 2^29 of each other the double sum is
-  // exact, so "u > mid" is the exact "nearer to the upper level" test and a
-  // tie keeps the smaller index (OpenNeedle reference notes, CQ quantisation
-  // steps).
-  cq::EncodeTable tab;
-  std::memset(&tab, 0, sizeof tab);
-  if (bits == 5) {
-    const double a = static_cast<double>(cq::ternary_level_f32());
-    tab.nlevels = 3;
-    tab.mid[0] = -a * 0.5;
-    tab.mid[1] = a * 0.5;
-    tab.code_of_index[0] = 3;  // -a -> crumb 11
-    tab.code_of_index[1] = 0;  //  0 -> crumb 00
-    tab.code_of_index[2] = 1;  // +a -> crumb 01
-  } else if (bits == 1) {
-    tab.nlevels = 2;
-    tab.mid[0] = 0.0;  // the midpoint of -c and +c
-    tab.code_of_index[0] = 0;
-    tab.code_of_index[1] = 1;
-  } else {
-    tab.nlevels = 1 << bits;
-    for (int j = 0; j + 1 < tab.nlevels; ++j)
-      tab.mid[j] = (static_cast<double>(levels[j]) + static_cast<double>(levels[j + 1])) * 0.5;
-    for (int j = 0; j < tab.nlevels; ++j) tab.code_of_index[j] = static_cast<uint32_t>(j);
+  const cq::EncodeTable tab = encode_table(bits, levels);
+  const int64_t kpad = padded(cols);
+  uint8_t *packed = static_cast<uint8_t *>(blob);
+  uint16_t *norms = reinterpret_cast<uint16_t *>(packed + rows * (kpad * cq::storage_bits(bits) / 8));
+  return hip_status(cq::launch_quantize(w, rows, cols, kpad, bits, tab, packed, norms,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+cq_status cq_quantize_rows(const float *w, int64_t n, const cq_matrix *dst, int64_t row0, void *stream) {
+  cq::CodeLevels lev;
+  cq_status st = check_matrix(dst, &lev);
+  if (st != CQ_OK) return st;
+  if (n < 0 || row0 < 0 || n > dst->rows || row0 > dst->rows - n) return CQ_ERR_SHAPE;
+  if (n == 0 || dst->cols == 0) return CQ_OK;
+  if (!w) return CQ_ERR_NULL;
+  if (!aligned(w, 4)) return CQ_ERR_ALIGN;
+  if (overlaps(dst->blob, dst->blob_bytes, w, static_cast<uint64_t>(n) * dst->cols * 4)) return CQ_ERR_OVERLAP;
+  const int64_t kpad = padded(dst->cols);
+  const int64_t row_bytes = kpad * cq::storage_bits(dst->bits) / 8;
+  uint8_t *blob = static_cast<uint8_t *>(const_cast<void *>(dst->blob));
+  uint8_t *packed = blob + row0 * row_bytes;
+  uint16_t *norms = reinterpret_cast<uint16_t *>(blob + dst->rows * row_bytes) + row0 * (kpad / CQ_GROUP);
+  return hip_status(cq::launch_quantize(w, n, dst->cols, kpad, dst->bits, encode_table(dst->bits, dst->levels),
+                                        packed, norms, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks of a score call; *xbytes: the padded queries' bytes.
+cq_status check_kv(const cq_matrix *K, int32_t nq, int32_t n_kv, int32_t head_dim, cq::CodeLevels *lev) {
+  cq_status st = check_matrix(K, lev);
+  if (st != CQ_OK) return st;
+  if ((st = check_matvec_cols(K)) != CQ_OK) return st;
+  if (nq < 1 || n_kv < 1 || head_dim < 1 || nq > CQ_MAX_KV_HEADS || nq % n_kv != 0 ||
+      static_cast<int64_t>(n_kv) * head_dim != K->cols)
+    return CQ_ERR_SHAPE;
+  return CQ_OK;
+}
+
+uint64_t kv_scores_ws(const cq_matrix *K, int32_t nq) {
+  const int64_t b = nq < CQ_MAX_MATVEC_BATCH ? nq : CQ_MAX_MATVEC_BATCH;
+  const uint64_t x = (static_cast<uint64_t>(nq) * K->cols * 4 + 255) / 256 * 256;
+  return x + cq::rotate_matvec_workspace_bytes(K->bits, K->rows, padded(K->cols), b);
+}
+
+}  // namespace
+
+extern "C" {
+
+cq_status cq_kv_scores_workspace_bytes(const cq_matrix *K, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                       uint64_t *bytes) {
+  if (!bytes) return CQ_ERR_NULL;
+  cq::CodeLevels lev;
+  cq_status st = check_kv(K, n_q_heads, n_kv_heads, head_dim, &lev);
+  if (st != CQ_OK) return st;
+  *bytes = K->rows ? kv_scores_ws(K, n_q_heads) : 0;
+  return CQ_OK;
+}
+
+cq_status cq_kv_scores(const cq_matrix *K, const float *q, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                       float *scores, void *workspace, uint64_t workspace_bytes, void *stream) {
+  cq::CodeLevels lev;
+  cq_status st = check_kv(K, n_q_heads, n_kv_heads, head_dim, &lev);
+  if (st != CQ_OK) return st;
+  if (K->rows == 0) return CQ_OK;
+  if (!q || !scores) return CQ_ERR_NULL;
+  if (!aligned(q, 4) || !aligned(scores, 4)) return CQ_ERR_ALIGN;
+  const uint64_t need = kv_scores_ws(K, n_q_heads);
+  if (!workspace || workspace_bytes < need) return CQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return CQ_ERR_ALIGN;
+  const uint64_t qbytes = static_cast<uint64_t>(n_q_heads) * head_dim * 4;
+  const uint64_t sbytes = static_cast<uint64_t>(n_q_heads) * K->rows * 4;
+  if (overlaps(scores, sbytes, q, qbytes) || overlaps(scores, sbytes, K->blob, K->blob_bytes) ||
+      overlaps(workspace, need, scores, sbytes) || overlaps(workspace, need, q, qbytes) ||
+      overlaps(workspace, need, K->blob, K->blob_bytes))
+    return CQ_ERR_OVERLAP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float *x = static_cast<float *>(workspace);
+  const uint64_t xb = (static_cast<uint64_t>(n_q_heads) * K->cols * 4 + 255) / 256 * 256;
+  void *ws = static_cast<uint8_t *>(workspace) + xb;
+  hipError_t e = cq::launch_kv_pad_queries(q, n_q_heads, n_kv_heads, head_dim, x, s);
+  const int64_t kpad = padded(K->cols);
+  for (int32_t h0 = 0; h0 < n_q_heads && e == hipSuccess; h0 += CQ_MAX_MATVEC_BATCH) {
+    const int64_t b = n_q_heads - h0 < CQ_MAX_MATVEC_BATCH ? n_q_heads - h0 : CQ_MAX_MATVEC_BATCH;
+    const bool need_ws = cq::rotate_matvec_workspace_bytes(K->bits, K->rows, kpad, b) > 0;
+    e = cq::launch_rotate_matvec(static_cast<const uint8_t *>(K->blob), K->bits, K->rows, kpad, lev,
+                                 x + static_cast<int64_t>(h0) * K->cols, K->cols, b,
+                                 scores + static_cast<int64_t>(h0) * K->rows, need_ws ? ws : nullptr, s);
   }
-  return hip_status(cq::launch_quantize(w, rows, cols, padded(cols), bits, tab,
-                                        static_cast<uint8_t *>(blob), static_cast<hipStream_t>(stream)));
+  return hip_status(e);
+}
+
+cq_status cq_matvec_t(const cq_matrix *W, const float *p, int64_t batch, float *out, void *workspace,
+                      uint64_t workspace_bytes, void *stream) {
+  cq::CodeLevels lev;
+  cq_status st = check_matrix(W, &lev);
+  if (st != CQ_OK) return st;
+  if (batch < 0 || batch > CQ_MAX_MATVEC_BATCH) return CQ_ERR_SHAPE;
+  if (!matvec_t_shape_ok(W)) return CQ_ERR_SHAPE;
+  if (batch == 0 || W->cols == 0) return CQ_OK;
+  if (!out) return CQ_ERR_NULL;
+  if (!aligned(out, 4)) return CQ_ERR_ALIGN;
+  const uint64_t obytes = static_cast<uint64_t>(batch) * W->cols * 4;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (W->rows == 0) return hip_status(cq::launch_zero_f32(out, batch * W->cols, s));
+  if (!p) return CQ_ERR_NULL;
+  if (!aligned(p, 4)) return CQ_ERR_ALIGN;
+  const uint64_t need = cq::matvec_t_workspace_bytes(W->rows, W->cols, batch);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return CQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return CQ_ERR_ALIGN;
+  }
+  const uint64_t pbytes = static_cast<uint64_t>(batch) * W->rows * 4;
+  if (overlaps(out, obytes, p, pbytes) || overlaps(out, obytes, W->blob, W->blob_bytes) ||
+      overlaps(workspace, need, out, obytes) || overlaps(workspace, need, p, pbytes) ||
+      overlaps(workspace, need, W->blob, W->blob_bytes))
+    return CQ_ERR_OVERLAP;
+  return hip_status(cq::launch_matvec_t(static_cast<const uint8_t *>(W->blob), W->bits, W->rows, W->cols,
+                                        padded(W->cols), lev, p, batch, out, need ? workspace : nullptr, s));
 }
 
 }  // extern "C"

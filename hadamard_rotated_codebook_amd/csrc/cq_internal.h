@@ -150,8 +150,20 @@ hipError_t launch_combine(const float *partial, int64_t n, int nslice, float *y,
 hipError_t launch_gemm(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
                        const CodeLevels &lev, const void *xr, int64_t m, float *c, hipStream_t s);
 
+// Encodes rows x cols of w into the codes at packed (rows of kpad * b' / 8
+// bytes) and the fp16 norms at norms ([rows][kpad / 128]).
 hipError_t launch_quantize(const float *w, int64_t rows, int64_t cols, int64_t kpad, int bits,
-                           const EncodeTable &tab, uint8_t *blob, hipStream_t s);
+                           const EncodeTable &tab, uint8_t *packed, uint16_t *norms, hipStream_t s);
+
+// KV-cache products (csrc/kv.hip).  Query padding: x[h][c] = q[h][c - c0(h)]
+// for c in the columns of query head h's KV head, 0 elsewhere (x [nq][cols]).
+hipError_t launch_kv_pad_queries(const float *q, int nq, int n_kv, int head_dim, float *x, hipStream_t s);
+// Transposed product out[b][k] = sum_r p[b][r] w_hat[r][k] (k < cols); the
+// workspace holds the row chunks' partial sums when there is more than one.
+uint64_t matvec_t_workspace_bytes(int64_t rows, int64_t cols, int64_t batch);
+hipError_t launch_matvec_t(const uint8_t *blob, int bits, int64_t rows, int64_t cols, int64_t kpad,
+                           const CodeLevels &lev, const float *p, int64_t batch, float *out, void *workspace,
+                           hipStream_t s);
 
 // Fills n floats with +0.0 (a kernel, so that it can sit in a captured graph).
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s);

@@ -1,0 +1,199 @@
+// Products with a CQ-quantised KV cache (".cact" format post, "Five regions":
+// the header's kv_bits is the cache precision the model was trained for, 8
+// or 2, 3, 4; "How the kernel reads it": the same path serves the KV cache).
+// A cache is a CQ matrix [tokens][n_kv_heads * head_dim]: one token's whole
+// key (or value) vector per row, quantised in 128-groups like a weight row,
+// so a group may hold several heads.
+//
+// Scores: query head h against every cached key, restricted to its KV head's
+// columns, is the decode matvec of the cache with the query written into a
+// zero row of the cache's width (launch_kv_pad_queries, then the matvec
+// kernels, up to 8 heads per launch).
+//
+// Values: out[b][k] = sum_r p[b][r] * w_hat[r][k], the product with the
+// transposed matrix (launch_matvec_t).  By the rotated-activation identity
+// (OpenNeedle reference notes) sum_r p_r w_hat[r, g] = (sum_r p_r n[r, g]
+// c[q[r, g]]) . H: the kernel sums the weighted levels of the codes in the
+// rotated domain and rotates each group back once with the shared butterfly.
+#include "cq_decode.h"
+#include "cq_fwht.h"
+#include "cq_internal.h"
+
+namespace {
+
+using namespace cqdev;
+
+__global__ __launch_bounds__(256) void kv_pad_kernel(const float *__restrict__ q, int nq, int n_kv, int head_dim,
+                                                    float *__restrict__ x) {
+  const int cols = n_kv * head_dim;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(nq) * cols) return;
+  const int h = static_cast<int>(i / cols), c = static_cast<int>(i % cols);
+  const int kvh = h / (nq / n_kv);  // consecutive query heads share a KV head
+  const int d = c - kvh * head_dim;
+  x[i] = (d >= 0 && d < head_dim) ? q[static_cast<int64_t>(h) * head_dim + d] : 0.0f;
+}
+
+constexpr int kTThreads = 512;  // 128 columns of a group x 4 row phases
+constexpr int kTPhases = kTThreads / CQ_GROUP;
+constexpr int kTChunk = 64;     // rows per workgroup: 16 per phase
+constexpr int kTMaxBatch = 8;
+
+struct TArgs {
+  const uint8_t *packed;
+  const uint16_t *norms;  // fp16 bits [rows][ngroups]
+  const float *p;         // [batch][rows]
+  float *out;             // [batch][cols] (one chunk) or partial [nchunk][batch][cols]
+  int64_t rows, cols, kpad, row_bytes, ngroups;
+  int32_t batch, nchunk;
+  cq::CodeLevels lev;
+};
+
+// Workgroup (group g, row chunk c): thread (phase ph, column j) adds
+// p[b][r] * (float(norm[r][g]) * level(code[r][g*128+j])) over rows r = c*64 +
+// 4i + ph of the chunk; the phases are added in order through LDS, the group
+// is rotated back (FWHT, times 1/sqrt(128)) and stored.
+template <int SB>
+__global__ __launch_bounds__(kTThreads) void matvec_t_kernel(TArgs a) {
+  __shared__ float lev[16];
+  __shared__ float pch[kTMaxBatch][kTChunk];
+  __shared__ float red[kTPhases][kTMaxBatch][CQ_GROUP];
+  const int tid = threadIdx.x, j = tid % CQ_GROUP, ph = tid / CQ_GROUP;
+  const int64_t g = blockIdx.x;
+  const int chunk = blockIdx.y;
+  const int64_t r0 = static_cast<int64_t>(chunk) * kTChunk;
+  const int nr = static_cast<int>(a.rows - r0 < kTChunk ? a.rows - r0 : kTChunk);
+  if (tid < 16) lev[tid] = a.lev.v[tid];
+  for (int i = tid; i < a.batch * kTChunk; i += kTThreads) {
+    const int b = i / kTChunk, r = i % kTChunk;
+    pch[b][r] = r < nr ? a.p[static_cast<int64_t>(b) * a.rows + r0 + r] : 0.0f;
+  }
+  __syncthreads();
+
+  // the code of column j of group g: bits [SB*j, SB*j + SB) of the group's
+  // bytes, read from the dword holding the first bit and the next one (only
+  // 3-bit codes cross a dword; bytes past the packed region read as zero)
+  const uint32_t bit = static_cast<uint32_t>(SB * j);
+  const uint32_t goff = static_cast<uint32_t>(g * (CQ_GROUP * SB / 8)) + (bit >> 5) * 4;
+  const __amdgpu_buffer_rsrc_t pk =
+      buffer_rsrc(a.packed, static_cast<uint32_t>(a.rows * a.row_bytes));
+  const __amdgpu_buffer_rsrc_t nb = buffer_rsrc(a.norms, static_cast<uint32_t>(a.rows * a.ngroups * 2));
+  float acc[kTMaxBatch];
+#pragma unroll
+  for (int b = 0; b < kTMaxBatch; ++b) acc[b] = 0.0f;
+  constexpr int PER = kTChunk / kTPhases;  // 16 rows per thread
+  uint32_t w0[PER], w1[PER];
+  uint16_t nrm[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int rl = kTPhases * i + ph;
+    const bool live = rl < nr;
+    const int64_t r = r0 + rl;
+    const uint32_t off = live ? static_cast<uint32_t>(r * a.row_bytes) + goff : 0xffff0000u;
+    // two 4-byte loads, each checked against the range on its own
+    w0[i] = __builtin_amdgcn_raw_buffer_load_b32(pk, off, 0, 0);
+    w1[i] = __builtin_amdgcn_raw_buffer_load_b32(pk, off + 4, 0, 0);
+    nrm[i] = __builtin_amdgcn_raw_buffer_load_b16(nb, live ? static_cast<uint32_t>((r * a.ngroups + g) * 2) : 0xffff0000u,
+                                                  0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int rl = kTPhases * i + ph;
+    const uint32_t code = static_cast<uint32_t>(
+        ((static_cast<uint64_t>(w1[i]) << 32 | w0[i]) >> (bit & 31)) & ((1u << SB) - 1));
+    const float w = static_cast<float>(__builtin_bit_cast(_Float16, nrm[i])) * lev[code];
+#pragma unroll
+    for (int b = 0; b < kTMaxBatch; ++b)
+      if (b < a.batch) acc[b] = __builtin_fmaf(pch[b][rl], w, acc[b]);
+  }
+
+  // the phases in order, then the group's rotation back: thread j of phase
+  // 0 holds column j; the butterfly runs in LDS, one stage per step
+#pragma unroll
+  for (int b = 0; b < kTMaxBatch; ++b)
+    if (b < a.batch) red[ph][b][j] = acc[b];
+  __syncthreads();
+  if (ph == 0) {
+#pragma unroll
+    for (int b = 0; b < kTMaxBatch; ++b) {
+      if (b >= a.batch) break;
+      float s = red[0][b][j];
+#pragma unroll
+      for (int k = 1; k < kTPhases; ++k) s += red[k][b][j];
+      red[0][b][j] = s;
+    }
+  }
+  __syncthreads();
+  for (int h = 1; h < CQ_GROUP; h <<= 1) {
+    float nv[kTMaxBatch];
+    if (ph == 0) {
+      const bool upper = (j & h) != 0;
+#pragma unroll
+      for (int b = 0; b < kTMaxBatch; ++b)
+        if (b < a.batch) nv[b] = upper ? red[0][b][j ^ h] - red[0][b][j] : red[0][b][j] + red[0][b][j ^ h];
+    }
+    __syncthreads();
+    if (ph == 0) {
+#pragma unroll
+      for (int b = 0; b < kTMaxBatch; ++b)
+        if (b < a.batch) red[0][b][j] = nv[b];
+    }
+    __syncthreads();
+  }
+  const int64_t k = g * CQ_GROUP + j;
+  if (ph != 0 || k >= a.cols) return;
+  for (int b = 0; b < a.batch; ++b) {
+    const float v = red[0][b][j] * kInvSqrt128;
+    a.out[(static_cast<int64_t>(chunk) * a.batch + b) * a.cols + k] = v;
+  }
+}
+
+}  // namespace
+
+namespace cq {
+
+hipError_t launch_kv_pad_queries(const float *q, int nq, int n_kv, int head_dim, float *x, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(nq) * n_kv * head_dim;
+  kv_pad_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), 256, 0, s>>>(q, nq, n_kv, head_dim, x);
+  return hipGetLastError();
+}
+
+uint64_t matvec_t_workspace_bytes(int64_t rows, int64_t cols, int64_t batch) {
+  const int64_t nchunk = (rows + kTChunk - 1) / kTChunk;
+  if (nchunk <= 1 || cols <= 0 || batch <= 0) return 0;
+  return static_cast<uint64_t>(nchunk) * batch * cols * 4;
+}
+
+hipError_t launch_matvec_t(const uint8_t *blob, int bits, int64_t rows, int64_t cols, int64_t kpad,
+                           const CodeLevels &lev, const float *p, int64_t batch, float *out, void *workspace,
+                           hipStream_t s) {
+  if (batch < 1 || batch > kTMaxBatch || rows < 1 || kpad % CQ_GROUP != 0) return hipErrorInvalidValue;
+  const int sb = storage_bits(bits);
+  TArgs a;
+  a.row_bytes = kpad * sb / 8;
+  a.packed = blob;
+  a.norms = reinterpret_cast<const uint16_t *>(blob + rows * a.row_bytes);
+  a.p = p;
+  a.rows = rows;
+  a.cols = cols;
+  a.kpad = kpad;
+  a.ngroups = kpad / CQ_GROUP;
+  a.batch = static_cast<int32_t>(batch);
+  a.nchunk = static_cast<int32_t>((rows + kTChunk - 1) / kTChunk);
+  a.lev = lev;
+  a.out = a.nchunk > 1 ? static_cast<float *>(workspace) : out;
+  // 32-bit buffer offsets over the packed region and the norms
+  if (rows * a.row_bytes >= (int64_t{1} << 31) || a.nchunk > 65535) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(a.ngroups), static_cast<unsigned>(a.nchunk));
+  switch (sb) {
+    case 1: matvec_t_kernel<1><<<grid, kTThreads, 0, s>>>(a); break;
+    case 2: matvec_t_kernel<2><<<grid, kTThreads, 0, s>>>(a); break;
+    case 3: matvec_t_kernel<3><<<grid, kTThreads, 0, s>>>(a); break;
+    default: matvec_t_kernel<4><<<grid, kTThreads, 0, s>>>(a); break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nchunk <= 1) return e;
+  return launch_combine(a.out, batch * cols, a.nchunk, out, s);
+}
+
+}  // namespace cq

@@ -19,10 +19,13 @@ namespace {
 
 constexpr double kSqrtInv128 = 0.08838834764831845;  // sqrt(1/128) in double
 
+// packed: the first output row's codes (rows of kpad * SB / 8 bytes follow);
+// norms: its fp16 norms (rows of kpad / 128 follow) -- the rows of a whole
+// blob, or a row range of a larger one.
 template <int SB, bool VEC>
 __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__ w, int64_t rows,
                                                       int64_t cols, int64_t kpad, cq::EncodeTable tab,
-                                                      uint8_t *__restrict__ blob) {
+                                                      uint8_t *__restrict__ packed, uint16_t *__restrict__ norms) {
   const int64_t ngroups = kpad / CQ_GROUP;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int j = threadIdx.x & 15;
@@ -88,7 +91,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
   if (!valid) return;
 
   const int64_t row_bytes = kpad * SB / 8;
-  uint8_t *dst = blob + r * row_bytes + g * (16 * SB) + j * SB;
+  uint8_t *dst = packed + r * row_bytes + g * (16 * SB) + j * SB;
   if (SB == 1) {
     dst[0] = static_cast<uint8_t>(word);
   } else if (SB == 2) {
@@ -100,23 +103,20 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
     dst[1] = static_cast<uint8_t>(word >> 8);
     dst[2] = static_cast<uint8_t>(word >> 16);
   }
-  if (j == 0) {
-    _Float16 *norms = reinterpret_cast<_Float16 *>(blob + rows * row_bytes);
-    norms[r * ngroups + g] = static_cast<_Float16>(n32);
-  }
+  if (j == 0) norms[r * ngroups + g] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(n32));
 }
 
 template <int SB>
 hipError_t launch_sb(const float *w, int64_t rows, int64_t cols, int64_t kpad, const cq::EncodeTable &tab,
-                     uint8_t *blob, hipStream_t s) {
+                     uint8_t *packed, uint16_t *norms, hipStream_t s) {
   const int64_t groups = rows * (kpad / CQ_GROUP);
   const int64_t blocks = (groups + 15) / 16;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const bool vec = (cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0);
   if (vec)
-    quantize_kernel<SB, true><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(w, rows, cols, kpad, tab, blob);
+    quantize_kernel<SB, true><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(w, rows, cols, kpad, tab, packed, norms);
   else
-    quantize_kernel<SB, false><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(w, rows, cols, kpad, tab, blob);
+    quantize_kernel<SB, false><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(w, rows, cols, kpad, tab, packed, norms);
   return hipGetLastError();
 }
 
@@ -125,12 +125,12 @@ hipError_t launch_sb(const float *w, int64_t rows, int64_t cols, int64_t kpad, c
 namespace cq {
 
 hipError_t launch_quantize(const float *w, int64_t rows, int64_t cols, int64_t kpad, int bits,
-                           const EncodeTable &tab, uint8_t *blob, hipStream_t s) {
+                           const EncodeTable &tab, uint8_t *packed, uint16_t *norms, hipStream_t s) {
   switch (storage_bits(bits)) {
-    case 1: return launch_sb<1>(w, rows, cols, kpad, tab, blob, s);
-    case 2: return launch_sb<2>(w, rows, cols, kpad, tab, blob, s);
-    case 3: return launch_sb<3>(w, rows, cols, kpad, tab, blob, s);
-    default: return launch_sb<4>(w, rows, cols, kpad, tab, blob, s);
+    case 1: return launch_sb<1>(w, rows, cols, kpad, tab, packed, norms, s);
+    case 2: return launch_sb<2>(w, rows, cols, kpad, tab, packed, norms, s);
+    case 3: return launch_sb<3>(w, rows, cols, kpad, tab, packed, norms, s);
+    default: return launch_sb<4>(w, rows, cols, kpad, tab, packed, norms, s);
   }
 }
 

@@ -76,6 +76,10 @@ typedef enum cq_dtype { CQ_F32 = 0, CQ_F16 = 1, CQ_BF16 = 2 } cq_dtype;
  * refused with CQ_ERR_SHAPE before anything is launched. */
 #define CQ_MAX_MATVEC_COLS ((int64_t)1 << 24)
 #define CQ_MAX_GEMM_COLS ((int64_t)1 << 22)
+/* Most query heads of one cq_kv_scores call; most rows of cq_matvec_t (whose
+ * packed rows must also stay below 2 GiB). */
+#define CQ_MAX_KV_HEADS 256
+#define CQ_MAX_MATVEC_T_ROWS ((int64_t)1 << 20)
 /* Size of the static device scratch of cq_rotate_matvec_noalloc (16 MiB). */
 #define CQ_NOALLOC_SCRATCH_BYTES ((uint64_t)16 << 20)
 
@@ -131,7 +135,13 @@ cq_status cq_blob_bytes(int32_t bits, int32_t group, int64_t rows, int64_t cols,
                         uint64_t *bytes);
 
 /* Operations that may take a workspace. */
-typedef enum cq_op { CQ_OP_MATVEC = 0, CQ_OP_GEMM = 1, CQ_OP_ROTATE_MATVEC = 2, CQ_OP_W2A8 = 3 } cq_op;
+typedef enum cq_op {
+  CQ_OP_MATVEC = 0,
+  CQ_OP_GEMM = 1,
+  CQ_OP_ROTATE_MATVEC = 2,
+  CQ_OP_W2A8 = 3,
+  CQ_OP_MATVEC_T = 4
+} cq_op;
 
 /*
  * Device workspace (bytes) that `op` needs for `W` and the given batch (M for
@@ -422,6 +432,90 @@ cq_status cq_gemm(const cq_matrix *W, const void *xr, int64_t m, float *c,
  */
 cq_status cq_quantize(const float *w, int64_t rows, int64_t cols, int32_t bits, int32_t group,
                       const float *levels, void *blob, uint64_t blob_bytes, void *stream);
+
+/*
+ * ---- CQ-quantised KV cache ------------------------------------------------
+ *
+ * The header's kv_bits is the precision the KV cache was post-trained for:
+ * 8 (int8), else 2, 3 or 4 (".cact" format post, "Five regions"), and the CQ
+ * path serves the cache at that width (".cact" format post, "How the kernel
+ * reads it"; OpenNeedle reference notes: below 8 bits the cache is simulated
+ * by CQ fake quantisation).  Reading taken here: a cached key or value row
+ * is one token's whole KV vector (n_kv_heads * head_dim values) quantised
+ * like a weight row, in 128-groups along it -- so a group can hold several
+ * heads (Needle 2: four KV heads of 64, two per group) -- and the cache is a
+ * CQ matrix [tokens][n_kv_heads * head_dim] of any storage width.  A sliding
+ * window of W tokens is a matrix of W rows used as a ring.
+ */
+
+/*
+ * Encodes n rows (fp32 [n][dst.cols], 4-byte aligned) into rows row0 ..
+ * row0 + n - 1 of an existing matrix, exactly as cq_quantize would encode
+ * them (rows are encoded on their own: OpenNeedle reference notes, CQ
+ * quantisation steps).  The codes and fp16 norms of those rows in dst.blob
+ * are overwritten; nothing else is touched.  This is the append of new
+ * tokens' keys or values to a cache.
+ *   dst      the matrix (rows = its capacity); its blob is written although
+ *            the descriptor holds a const pointer
+ *   Errors: those of cq_matvec's descriptor checks; CQ_ERR_SHAPE unless
+ *   0 <= row0 and row0 + n <= dst.rows; CQ_ERR_NULL, CQ_ERR_ALIGN,
+ *   CQ_ERR_OVERLAP (w inside the blob), CQ_ERR_HIP.  A norm above the fp16
+ *   range is stored as +inf, as by cq_quantize.
+ */
+cq_status cq_quantize_rows(const float *w, int64_t n, const cq_matrix *dst, int64_t row0, void *stream);
+
+/*
+ * Attention scores against a CQ key cache K [tokens][n_kv_heads * head_dim]:
+ *
+ *   scores[h][t] = sum_{d < head_dim} q[h][d] * k_hat[t][kv(h) * head_dim + d]
+ *
+ * with kv(h) = h / (n_q_heads / n_kv_heads) (consecutive query heads share a
+ * KV head; OpenNeedle reference notes, attention: two query heads map to one
+ * KV head).  No 1/sqrt(head_dim) factor and no mask: those belong to the
+ * attention around it.  Computed as the decode matvec (cq_rotate_matvec) of
+ * K with each query head written into a zero row of K's width: the same
+ * kernels and the same fp32 arithmetic, at most 8 heads per launch.
+ *   q        device fp32 [n_q_heads][head_dim], 4-byte aligned
+ *   n_q_heads 1 <= n_q_heads <= CQ_MAX_KV_HEADS, a multiple of n_kv_heads;
+ *            n_kv_heads * head_dim == K.cols
+ *   scores   device fp32 [n_q_heads][K.rows], 4-byte aligned, must not
+ *            overlap q, the blob or the workspace
+ *   workspace 256-byte aligned, at least cq_kv_scores_workspace_bytes(): the
+ *            padded queries, then the matvec's scratch (any contents on entry)
+ *   Errors: the descriptor checks of cq_matvec, CQ_ERR_SHAPE for head counts
+ *   or widths that do not fit, CQ_ERR_NULL, CQ_ERR_ALIGN, CQ_ERR_WORKSPACE,
+ *   CQ_ERR_OVERLAP, CQ_ERR_HIP.  K.rows == 0 does nothing.
+ */
+cq_status cq_kv_scores_workspace_bytes(const cq_matrix *K, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                       uint64_t *bytes);
+cq_status cq_kv_scores(const cq_matrix *K, const float *q, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                       float *scores, void *workspace, uint64_t workspace_bytes, void *stream);
+
+/*
+ * Product with the transposed matrix (the value side of attention over a CQ
+ * value cache: o = sum_t p_t v_hat_t):
+ *
+ *   out[b][k] = sum_r p[b][r] * w_hat[r][k],   k < W.cols
+ *
+ * By the rotated-activation identity (OpenNeedle reference notes) the
+ * weighted sum is taken on the codes in the rotated domain,
+ * sum_r p[b][r] * float(norm[r][g]) * c[q[r][g*128+j]], and each group is
+ * rotated back once (the butterfly of cq_rotate_acts, times 1/sqrt(128)).
+ * fp32 throughout: each term is fp32(float(norm) * c) times p, summed in
+ * rows of 64 in a fixed order, the row chunks added in order.
+ *   p        device fp32 [batch][W.rows], 4-byte aligned
+ *   batch    0 <= batch <= CQ_MAX_MATVEC_BATCH
+ *   out      device fp32 [batch][W.cols], 4-byte aligned, must not overlap
+ *            p, the blob or the workspace; fully overwritten (0 where W.rows
+ *            == 0)
+ *   workspace, workspace_bytes: at least cq_workspace_bytes(CQ_OP_MATVEC_T)
+ *            (the row chunks' partial sums; NULL, 0 when that is 0)
+ *   W.rows <= CQ_MAX_MATVEC_T_ROWS with the packed rows below 2 GiB, and
+ *   W.cols <= CQ_MAX_MATVEC_COLS, else CQ_ERR_SHAPE.  Other errors as
+ *   cq_matvec.
+ */
+cq_status cq_matvec_t(const cq_matrix *W, const float *p, int64_t batch, float *out, void *workspace,
+                      uint64_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

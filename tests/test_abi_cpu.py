@@ -31,7 +31,8 @@ def test_every_declared_symbol_is_exported():
                           "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_matvec_noalloc",
                           "cq_rotate_multi_matvec",
                           "cq_rotate_multi_workspace_bytes", "cq_quantize_acts_int8", "cq_matvec_w2a8_quantized",
-                          "cq_matvec_w2a8", "cq_gather_rows", "cq_gemm", "cq_quantize"}
+                          "cq_matvec_w2a8", "cq_gather_rows", "cq_gemm", "cq_quantize", "cq_quantize_rows",
+                          "cq_kv_scores_workspace_bytes", "cq_kv_scores", "cq_matvec_t"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -406,7 +407,8 @@ def test_workspace_bytes():
     assert lib.cq_workspace_bytes(1, ctypes.byref(m), 4096, ctypes.byref(out)) == OK
     assert lib.cq_workspace_bytes(0, ctypes.byref(m), 9, ctypes.byref(out)) == SHAPE
     assert lib.cq_workspace_bytes(5, ctypes.byref(m), 1, ctypes.byref(out)) == SHAPE
-    assert lib.cq_workspace_bytes(4, ctypes.byref(m), 1, ctypes.byref(out)) == SHAPE
+    assert lib.cq_workspace_bytes(6, ctypes.byref(m), 1, ctypes.byref(out)) == SHAPE
+    assert lib.cq_workspace_bytes(-1, ctypes.byref(m), 1, ctypes.byref(out)) == SHAPE
     # empty K or no rows: nothing is launched, so no workspace (and no division by zero)
     for rows, cols in ((5, 0), (0, 256), (0, 0)):
         e, _ = _matrix(rows=rows, cols=cols)
@@ -518,3 +520,45 @@ def test_noalloc_validation():
     # nothing to do: no device call at all
     m, k = _matrix(rows=0)
     assert _noalloc(m) == OK
+
+
+def test_kv_cache_calls_validation():
+    # cq_quantize_rows: the row range must lie inside the matrix
+    m, k = _matrix(rows=256, cols=256)
+    w = FAKE + (1 << 33)
+    assert lib.cq_quantize_rows(ctypes.c_void_p(w), 1, ctypes.byref(m), 256, None) == SHAPE
+    assert lib.cq_quantize_rows(ctypes.c_void_p(w), 2, ctypes.byref(m), 255, None) == SHAPE
+    assert lib.cq_quantize_rows(ctypes.c_void_p(w), -1, ctypes.byref(m), 0, None) == SHAPE
+    assert lib.cq_quantize_rows(ctypes.c_void_p(w), 1, ctypes.byref(m), -1, None) == SHAPE
+    assert lib.cq_quantize_rows(ctypes.c_void_p(w), 0, ctypes.byref(m), 256, None) == OK  # nothing to do
+    assert lib.cq_quantize_rows(None, 1, ctypes.byref(m), 0, None) == NULL
+    assert lib.cq_quantize_rows(ctypes.c_void_p(w + 2), 1, ctypes.byref(m), 0, None) == ALIGN
+    assert lib.cq_quantize_rows(ctypes.c_void_p(FAKE + 64), 1, ctypes.byref(m), 0, None) == OVERLAP
+    bad, _ = _matrix(bits=7, nbytes=0, levels=None)
+    assert lib.cq_quantize_rows(ctypes.c_void_p(w), 1, ctypes.byref(bad), 0, None) == BITS
+    # cq_kv_scores: head geometry must match the cache width
+    out = ctypes.c_uint64(7)
+    for nq, nkv, hd in ((8, 4, 64), (12, 2, 128), (4, 4, 64)):
+        assert lib.cq_kv_scores_workspace_bytes(ctypes.byref(m), nq, nkv, hd, ctypes.byref(out)) == (
+            OK if nkv * hd == 256 else SHAPE)
+    assert lib.cq_kv_scores_workspace_bytes(ctypes.byref(m), 8, 4, 64, ctypes.byref(out)) == OK
+    assert out.value >= 8 * 256 * 4
+    for nq, nkv, hd in ((6, 4, 64), (0, 4, 64), (8, 0, 64), (8, 4, 32), (512, 4, 64)):
+        assert lib.cq_kv_scores_workspace_bytes(ctypes.byref(m), nq, nkv, hd, ctypes.byref(out)) == SHAPE
+    q, sc, ws = FAKE + (1 << 33), FAKE + (1 << 34), FAKE + (1 << 35)
+    call = lambda **kw: lib.cq_kv_scores(ctypes.byref(m), ctypes.c_void_p(kw.get("q", q)), 8, 4, 64,
+                                         ctypes.c_void_p(kw.get("sc", sc)), ctypes.c_void_p(kw.get("ws", ws)),
+                                         kw.get("wsb", 1 << 20), None)
+    assert call(wsb=16) == WORKSPACE and call(ws=ws + 16) == ALIGN and call(sc=0) == NULL
+    assert call(sc=q) == OVERLAP and call(ws=FAKE) == OVERLAP
+    # cq_matvec_t: sizes and the workspace query
+    assert lib.cq_workspace_bytes(cq.OP_MATVEC_T, ctypes.byref(m), 8, ctypes.byref(out)) == OK
+    assert out.value == 4 * 8 * 256 * 4  # 256 rows: four chunks of 64 rows
+    assert lib.cq_workspace_bytes(cq.OP_MATVEC_T, ctypes.byref(m), 9, ctypes.byref(out)) == SHAPE
+    big, _ = _matrix(rows=(1 << 20) + 1, cols=128)
+    assert lib.cq_workspace_bytes(cq.OP_MATVEC_T, ctypes.byref(big), 1, ctypes.byref(out)) == SHAPE
+    mt = lambda **kw: lib.cq_matvec_t(ctypes.byref(m), ctypes.c_void_p(kw.get("p", q)), kw.get("b", 2),
+                                      ctypes.c_void_p(kw.get("o", sc)), ctypes.c_void_p(kw.get("ws", ws)),
+                                      kw.get("wsb", 1 << 20), None)
+    assert mt(b=9) == SHAPE and mt(o=0) == NULL and mt(p=0) == NULL and mt(wsb=4) == WORKSPACE
+    assert mt(o=q) == OVERLAP and mt(o=sc + 2) == ALIGN
