@@ -20,7 +20,7 @@ __all__ = [
     "rotate_fp32", "nearest_level", "encode", "quantize",
     "pack_codes", "unpack_codes", "make_blob", "split_blob",
     "level_values", "dequantize", "gather_rows", "rotate_acts",
-    "matvec", "gemm", "bf16_round", "gemm_bf16",
+    "matvec", "matvec_rotated", "gemm", "bf16_round", "gemm_bf16",
 ]
 
 GROUP = 128
@@ -477,6 +477,30 @@ def matvec(blob, bits, rows, cols, x, levels=None, group=GROUP, row_ids=None):
     [batch, rows] (or [batch, len(row_ids)])."""
     w_hat = dequantize(blob, bits, rows, cols, levels, group, row_ids)
     return _pad(x, group) @ w_hat.T
+
+
+def matvec_rotated(blob, bits, rows, cols, x, levels=None, group=GROUP, row0=0, row1=None, row_norms=False):
+    """y[b, r] for rows r in [row0, row1), float64, by the rotated-activation
+    identity [OpenNeedle reference, rotated-activation identity]: for every
+    group, dot(w_hat_g, x_g) = n_store * dot(codebook[q], H x_g), so
+
+        y[b, r] = sum_g float32(n[r, g]) * sum_j c[q[r, g, j]] * (H x_g)[j]
+
+    with H x_g computed once for all rows.  The same value as ``matvec`` up to
+    float64 rounding order, without the dense reconstruction (the rows at
+    full size are far too many for it).  With ``row_norms`` also returns
+    ||w_hat_r||_2, which equals the norm of the rotated row (H is
+    orthogonal: Parseval)."""
+    packed, norms = split_blob(blob, bits, rows, cols, group)
+    row1 = rows if row1 is None else row1
+    kpad = padded_cols(cols, group)
+    xr = rotate_acts(x, group)                      # [batch, kpad]
+    vals = level_values(unpack_codes(packed[row0:row1], bits, kpad), bits, levels, group)
+    wrot = vals * np.repeat(norms[row0:row1].astype(np.float32).astype(np.float64), group, axis=1)
+    y = xr @ wrot.T
+    if row_norms:
+        return y, np.sqrt(np.sum(wrot * wrot, axis=1))
+    return y
 
 
 def gemm(blob, bits, rows, cols, X, levels=None, group=GROUP, row_ids=None):

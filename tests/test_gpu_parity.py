@@ -214,24 +214,40 @@ def test_matvec_very_long_rows(bits, batch):
     _check_fp32_product(y, ref, w_hat, np.linalg.norm(x.astype(np.float64), axis=1))
 
 
+def _oracle_rows_parallel(fn, rows, chunk=1024, threads=16):
+    """fn(r0, r1) over row chunks in a thread pool (the oracle's NumPy work
+    releases the GIL); results concatenated along the last axis."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda r0: fn(r0, min(rows, r0 + chunk)), range(0, rows, chunk)))
+    return parts
+
+
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
-def test_matvec_full_size_sampled_rows(bits):
+def test_matvec_full_size_all_rows(bits):
     # the 65536 x 16384 workload in the launch configuration the benchmark
-    # times; the oracle computes sampled rows one by one
+    # times, every row against the oracle (its rotated-activation route, in
+    # row chunks); CQ2 also at batch 8, binary at batch 3
     rows, cols = 65536, 16384
     say("matvec full size", bits)
     W, blob = _random_cq(bits, rows, cols, 60)
     levels = _levels(bits)
-    pick = cq_inputs.sample_rows(60, bits, rows, 48)
-    sub = _row_subset(blob, bits, rows, cols, pick)
-    w_hat = np.linalg.norm(oracle.dequantize(sub, bits, len(pick), cols, levels), axis=1)
-    for batch in {2: (1, 8), 1: (1, 3)}.get(bits, (1,)):  # binary batches: one table pass per vector
-        x = cq_inputs.activations(60, 100 * batch + bits, batch, cols)
-        y = cq.cq_matvec(W, cq.cq_rotate_acts(_to_dev(x))).cpu().numpy()
-        ref = oracle.matvec(sub, bits, len(pick), cols, x, levels)
-        _check_fp32_product(y[:, pick], ref, w_hat, np.linalg.norm(x.astype(np.float64), axis=1))
+    batches = {2: (1, 8), 1: (1, 3)}.get(bits, (1,))
+    xs = [cq_inputs.activations(60, 100 * b + bits, b, cols) for b in batches]
+    ys = [cq.cq_matvec(W, cq.cq_rotate_acts(_to_dev(x))).cpu().numpy() for x in xs]
     del W
     torch.cuda.empty_cache()
+    xall = np.concatenate(xs)
+    parts = _oracle_rows_parallel(
+        lambda r0, r1: oracle.matvec_rotated(blob, bits, rows, cols, xall, levels, row0=r0, row1=r1,
+                                             row_norms=True), rows)
+    ref = np.concatenate([p[0] for p in parts], axis=1)
+    w_hat = np.concatenate([p[1] for p in parts])
+    say("  oracle done")
+    at = 0
+    for x, y in zip(xs, ys):
+        _check_fp32_product(y, ref[at:at + x.shape[0]], w_hat, np.linalg.norm(x.astype(np.float64), axis=1))
+        at += x.shape[0]
 
 
 def test_matvec_is_deterministic():
@@ -637,8 +653,11 @@ def test_gemm(bits, m, rows, cols):
 
 
 @pytest.mark.parametrize("bits", [4, 3])
-def test_gemm_full_size_sampled(bits):
-    # M = 4096, N = K = 16384: sampled rows of C against the oracle
+def test_gemm_full_size_every_tile(bits):
+    # M = 4096, N = K = 16384: C on a strided grid of 241 x 713 outputs (steps
+    # 17 and 23, prime to the 256 x 256 tile, the 128 x 64 wave tile and the
+    # 16 x 16 MFMA block, so every tile and every position class in them is
+    # hit; every output runs through all K stages) against the oracle
     m, rows, cols = 4096, 16384, 16384
     say("gemm full size", bits)
     W, blob = _random_cq(bits, rows, cols, 61)
@@ -646,11 +665,12 @@ def test_gemm_full_size_sampled(bits):
     X = cq_inputs.activations(61, bits, m, cols, "bf16")
     xr = cq.cq_rotate_acts(_to_dev(X, torch.bfloat16), torch.bfloat16)
     C = cq.cq_gemm(W, xr)
-    pick = cq_inputs.sample_rows(61, bits, rows, 24)
-    mp = cq_inputs.sample_rows(62, bits, m, 12)
+    mp = np.arange(0, m, 17)
+    pick = np.arange(0, rows, 23)
     got = C[torch.from_numpy(mp).to(DEV)][:, torch.from_numpy(pick).to(DEV)].cpu().numpy().astype(np.float64)
     del C, W, xr
     torch.cuda.empty_cache()
+    assert {(int(a) // 256, int(b) // 256) for a in mp for b in pick} == {(i, j) for i in range(16) for j in range(64)}
     sub = _row_subset(blob, bits, rows, cols, pick)
     w_hat = np.linalg.norm(oracle.dequantize(sub, bits, len(pick), cols, levels), axis=1)
     xn = np.linalg.norm(X[mp].astype(np.float64), axis=1)
@@ -714,8 +734,9 @@ def test_quantize(bits, kind, rows, cols):
 
 
 @pytest.mark.parametrize("bits", [4, 3])
-def test_quantize_full_size_sampled_rows(bits):
-    # the 16384 x 16384 encode: sampled rows of the blob against the oracle encoder
+def test_quantize_full_size_all_rows(bits):
+    # the 16384 x 16384 encode: every row of the blob against the oracle
+    # encoder (in row chunks: rows are encoded independently)
     rows, cols = 16384, 16384
     say("quantize full size", bits)
     levels = _levels(bits)
@@ -724,9 +745,10 @@ def test_quantize_full_size_sampled_rows(bits):
     blob_g = W.blob.cpu().numpy()
     del W
     torch.cuda.empty_cache()
-    pick = cq_inputs.sample_rows(63, bits, rows, 32)
-    frac = _encoder_agreement(bits, w[pick], _row_subset(blob_g, bits, rows, cols, pick), levels)
-    say("  identical index fraction", frac)
+    fracs = _oracle_rows_parallel(
+        lambda r0, r1: _encoder_agreement(bits, w[r0:r1], _row_subset(blob_g, bits, rows, cols, np.arange(r0, r1)),
+                                          levels), rows)
+    say("  identical index fraction", min(fracs))
 
 
 def test_quantize_special_groups():

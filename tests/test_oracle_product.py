@@ -278,3 +278,26 @@ def test_gemm_bf16_equals_an_explicit_loop(bits):
                 w = float(np.float32(vals[r, k]) * np.float32(norms[r, k // 128]))
                 acc += _bf16_by_hand(float(np.float32(xr[k]))) * _bf16_by_hand(w)
             assert abs(acc - got[m, r]) <= 1e-12 * max(1.0, abs(acc)), (m, r)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
+def test_matvec_rotated_equals_the_dense_product(bits):
+    # the rotated-activation route (used for full-size parity) against the
+    # dense reconstruction, on every row range
+    rows, cols = 40, 700
+    blob, levels, _ = _blob(102, bits, rows, cols)
+    x = cq_inputs.activations(102, bits, 3, cols)
+    dense = oracle.matvec(blob, bits, rows, cols, x, levels)
+    for r0, r1 in [(0, rows), (0, 1), (13, 29), (39, 40)]:
+        got = oracle.matvec_rotated(blob, bits, rows, cols, x, levels, row0=r0, row1=r1)
+        assert np.allclose(got, dense[:, r0:r1], rtol=0, atol=1e-13 * np.max(np.abs(dense)))
+
+
+@pytest.mark.parametrize("bits", [2, 4, 5])
+def test_matvec_rotated_row_norms_are_the_dense_row_norms(bits):
+    rows, cols = 20, 500
+    blob, levels, _ = _blob(103, bits, rows, cols)
+    x = cq_inputs.activations(103, bits, 1, cols)
+    _, rn = oracle.matvec_rotated(blob, bits, rows, cols, x, levels, row0=4, row1=17, row_norms=True)
+    dense = np.linalg.norm(oracle.dequantize(blob, bits, rows, cols, levels), axis=1)
+    assert np.allclose(rn, dense[4:17], rtol=1e-13, atol=0)
