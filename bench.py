@@ -53,7 +53,8 @@ def _events(torch, n):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
 
-def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen, fused=True, w2a8=False):
+def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen, fused=True, w2a8=False,
+                 read_ceiling=False):
     """One step = the rotation and the product of one batch: cq_rotate_matvec
     (fused=True), cq_rotate_acts + cq_matvec, or the int8 product
     cq_matvec_w2a8 (w2a8=True).  Three copies of the matrix take turns, so no
@@ -102,10 +103,34 @@ def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen, 
     torch.cuda.synchronize()
     times = sorted(a.elapsed_time(b) / 1e3 for a, b in ev)
     nbytes = W0.blob.numel()
+    res = {"bits": bits, "batch": batch, "bytes": nbytes, "step_s": wall, "kernel_s": sum(times) / steps,
+           "kernel_median_s": times[steps // 2], "flop": 2.0 * rows * cols * batch,
+           "call": "cq_matvec_w2a8" if w2a8 else ("cq_rotate_matvec" if fused else "cq_rotate_acts + cq_matvec")}
+    if read_ceiling:
+        res["read_ceiling"] = bench_read_ceiling(torch, cq, [W.blob for W in mats], steps, warmup)
     del mats, W0
-    return {"bits": bits, "batch": batch, "bytes": nbytes, "step_s": wall, "kernel_s": sum(times) / steps,
-            "kernel_median_s": times[steps // 2], "flop": 2.0 * rows * cols * batch,
-            "call": "cq_matvec_w2a8" if w2a8 else ("cq_rotate_matvec" if fused else "cq_rotate_acts + cq_matvec")}
+    return res
+
+
+def bench_read_ceiling(torch, cq, bufs, steps, warmup):
+    """The streaming-read ceiling on the same bytes: cq_read_probe (plain
+    16-byte loads, 32 KB contiguous tiles per workgroup) over the same three
+    copies of the matrix in turn, timed between HIP events."""
+    sink = torch.empty(2048 * 256, dtype=torch.int32, device=bufs[0].device)
+    for i in range(warmup):
+        cq.cq_read_probe(bufs[i % 3], sink)
+    torch.cuda.synchronize()
+    ev = _events(torch, steps)
+    for i in range(steps):
+        ev[i][0].record()
+        cq.cq_read_probe(bufs[i % 3], sink)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) / 1e3 for a, b in ev)
+    nbytes = bufs[0].numel()
+    return {"bytes": nbytes, "median_s": t[steps // 2], "gbs": nbytes / t[steps // 2] / 1e9,
+            "frac_hbm_peak": nbytes / t[steps // 2] / 1e9 / HBM_PEAK_GBS,
+            "probe": "cq_read_probe: 2048 workgroups x 256 threads, 16-byte loads, 8 in flight per thread"}
 
 
 def bench_needle_decode(torch, cq, cq_inputs, steps, gen):
@@ -264,6 +289,54 @@ def bench_small_and_prefill(torch, cq, cq_inputs, gen, steps=100):
     return out
 
 
+def bench_kv_attention(torch, cq, cq_inputs, gen, steps=50):
+    """One layer's decode attention over a CQ-quantised KV cache, Needle 2
+    shape: a 256-token window of keys and values (4 KV heads of 64, the ring
+    full) at kv_bits 2, 3 and 4; a step appends the new token's key and value
+    (cq_quantize_rows), scores 8 query heads (cq_kv_scores), softmax (torch),
+    and the weighted values (cq_matvec_t).  Per step from HIP graph replays."""
+    dev = torch.device("cuda:0")
+    out = {}
+    for bits in (2, 3, 4):
+        lv = cq_inputs.codebook(bits)
+        K = cq.cq_quantize(torch.randn((256, 256), generator=gen, device=dev), bits, lv)
+        V = cq.cq_quantize(torch.randn((256, 256), generator=gen, device=dev), bits, lv)
+        kn = torch.randn((steps, 256), generator=gen, device=dev)
+        vn = torch.randn((steps, 256), generator=gen, device=dev)
+        q = torch.randn((8, 64), generator=gen, device=dev)
+        s = torch.empty((8, 256), device=dev)
+        o = torch.empty((8, 256), device=dev)
+        ws = torch.empty(cq.cq_kv_scores_workspace_bytes(K, 8, 4, 64) + 256, dtype=torch.uint8, device=dev)
+        wt = cq.workspace_for(cq.cq_workspace_bytes(cq.OP_MATVEC_T, V, 8), dev)
+
+        def step(i):
+            cq.cq_quantize_rows(K, kn[i:i + 1], i % 256)
+            cq.cq_quantize_rows(V, vn[i:i + 1], i % 256)
+            cq.cq_kv_scores(K, q, 4, out=s, workspace=ws)
+            p = torch.softmax(s * 0.125, dim=1)
+            cq.cq_matvec_t(V, p, out=o, workspace=wt)
+
+        for i in range(5):
+            step(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(5):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        out[f"kv{bits}"] = {"graph_us_per_step": t0.elapsed_time(t1) * 1e3 / (5 * steps),
+                            "cache_bytes": 2 * K.blob.numel()}
+        del g
+    return out
+
+
 def bench_gemm(torch, cq, cq_inputs, master, bits, m, steps, warmup, gen):
     rows, cols = master.shape
     levels = cq_inputs.codebook(bits)
@@ -393,8 +466,9 @@ def main():
         log("generating the 65536 x 16384 fp32 master on the GPU")
         master = torch.randn((ROWS, COLS), generator=gen, device=dev).mul_(0.02)
     if args.only in ("all", "matvec"):
-        head = bench_matvec(torch, cq, cq_inputs, master, 2, 1, args.steps, args.warmup, gen)
-        log(f"CQ2 b1: step {head['step_s']*1e6:.1f} us, matvec kernel {head['kernel_s']*1e6:.1f} us")
+        head = bench_matvec(torch, cq, cq_inputs, master, 2, 1, args.steps, args.warmup, gen, read_ceiling=True)
+        log(f"CQ2 b1: step {head['step_s']*1e6:.1f} us, matvec kernel {head['kernel_s']*1e6:.1f} us; "
+            f"read ceiling {head['read_ceiling']['gbs']:.0f} GB/s")
         result["head"] = head
         if args.only == "all":
             two = bench_matvec(torch, cq, cq_inputs, master, 2, 1, args.steps, args.warmup, gen, fused=False)
@@ -435,6 +509,9 @@ def main():
         r = bench_gather(torch, cq, cq_inputs, gen)
         secondary["gather_cq4_8192x512_2048_rows"] = r
         log(f"gather 2048 rows of 8192x512 CQ4: {r['kernel_median_s']*1e6:.1f} us, {r['gbs']:.0f} GB/s")
+        r = bench_kv_attention(torch, cq, cq_inputs, gen)
+        secondary["kv_attention_step_needle2"] = r
+        log("kv attention step: " + ", ".join(f"{k} {v['graph_us_per_step']:.1f} us" for k, v in r.items()))
         r = bench_small_and_prefill(torch, cq, cq_inputs, gen)
         secondary.update(r)
         s5 = r["matvec_cq2_512x512_b1"]
@@ -462,7 +539,8 @@ def main():
 
     line = {"metric": "CQ2 batch-1 matvec GB/s of packed weights (% HBM peak); CQ GEMM TFLOP/s",
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32 activations, f16 lookup-table entries, f32 accumulation",
             "data": "synthetic: seeded N(0,0.02^2) master encoded on the GPU; activations N(0,1)"}
     if "head" in result:
         h = result["head"]
@@ -474,7 +552,9 @@ def main():
         line["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": ach / HBM_PEAK_GBS, "traffic": stored_traffic(),
                             "kernel": "cq_rotate_matvec call: matvec_kernel<2, true> + combine_kernel",
-                            "kernel_us": h["kernel_s"] * 1e6, "algorithmic_bytes": h["bytes"]}
+                            "kernel_us": h["kernel_s"] * 1e6, "algorithmic_bytes": h["bytes"],
+                            "read_ceiling_gbs": h["read_ceiling"]["gbs"],
+                            "frac_of_read_ceiling": ach / h["read_ceiling"]["gbs"]}
     else:
         line["value"] = None
         line["ms_per_step"] = None

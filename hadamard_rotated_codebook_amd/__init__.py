@@ -30,7 +30,7 @@ __all__ = [
     "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_matvec_noalloc", "cq_rotate_multi_matvec",
     "cq_rotate_multi_workspace_bytes", "cq_quantize_acts_int8", "cq_matvec_w2a8_quantized", "cq_matvec_w2a8",
     "cq_gather_rows", "cq_gemm", "cq_quantize", "cq_quantize_rows", "cq_kv_scores_workspace_bytes",
-    "cq_kv_scores", "cq_matvec_t",
+    "cq_kv_scores", "cq_matvec_t", "cq_read_probe",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcq.so")
@@ -77,6 +77,7 @@ _SIGS = {
     "cq_kv_scores_workspace_bytes": (_i32, [_MP, _i32, _i32, _i32, ctypes.POINTER(_u64)]),
     "cq_kv_scores": (_i32, [_MP, _vp, _i32, _i32, _i32, _vp, _vp, _u64, _vp]),
     "cq_matvec_t": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
+    "cq_read_probe": (_i32, [_vp, _u64, _vp, _u64, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -490,3 +491,11 @@ def cq_matvec_t(W, p, out=None, workspace=None):
     m, keep = W._struct()
     _check(_lib.cq_matvec_t(ctypes.byref(m), _dev(p.contiguous(), "p"), b, _dev(out, "out"), ws, wsb, _stream()))
     return out
+
+
+def cq_read_probe(buf, sink):
+    """Read every byte of ``buf`` (a device tensor) once with plain wide loads
+    (the streaming-read ceiling); ``sink`` is a uint32/int32 device tensor of
+    a multiple of 256 words (one workgroup per 256)."""
+    _check(_lib.cq_read_probe(_dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink"),
+                              sink.numel() * sink.element_size() // 4, _stream()))

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcq.so")
-SOURCES = ["api.hip", "rotate.hip", "matvec.hip", "matvec_mma.hip", "multi_matvec.hip", "w2a8.hip", "gather.hip", "gemm.hip", "quantize.hip", "noalloc.hip", "kv.hip"]
+SOURCES = ["api.hip", "rotate.hip", "matvec.hip", "matvec_mma.hip", "multi_matvec.hip", "w2a8.hip", "gather.hip", "gemm.hip", "quantize.hip", "noalloc.hip", "kv.hip", "probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

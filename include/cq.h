@@ -517,6 +517,17 @@ cq_status cq_kv_scores(const cq_matrix *K, const float *q, int32_t n_q_heads, in
 cq_status cq_matvec_t(const cq_matrix *W, const float *p, int64_t batch, float *out, void *workspace,
                       uint64_t workspace_bytes, void *stream);
 
+/*
+ * Measurement helper (not part of the product): reads `bytes` bytes at p once
+ * with the widest plain loads (32 KB contiguous tiles per workgroup) and
+ * writes one checksum word per thread to sink.  Its rate is the streaming-read
+ * ceiling the HBM-bound products are reported against beside the published
+ * peak.  sink_words / 256 workgroups are launched (at most 65535), so sink
+ * must hold a multiple of 256 words; CQ_ERR_WORKSPACE when it holds fewer
+ * than 256.
+ */
+cq_status cq_read_probe(const void *p, uint64_t bytes, uint32_t *sink, uint64_t sink_words, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

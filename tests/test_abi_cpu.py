@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
                           "cq_rotate_multi_matvec",
                           "cq_rotate_multi_workspace_bytes", "cq_quantize_acts_int8", "cq_matvec_w2a8_quantized",
                           "cq_matvec_w2a8", "cq_gather_rows", "cq_gemm", "cq_quantize", "cq_quantize_rows",
-                          "cq_kv_scores_workspace_bytes", "cq_kv_scores", "cq_matvec_t"}
+                          "cq_kv_scores_workspace_bytes", "cq_kv_scores", "cq_matvec_t", "cq_read_probe"}
     for n in names:
         assert hasattr(lib, n), n
 
