@@ -439,7 +439,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--only", choices=["all", "matvec", "w2a8", "decode", "gemm", "encode"], default="all")
+    ap.add_argument("--only", choices=["all", "matvec", "batch8", "w2a8", "decode", "gemm", "encode"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
@@ -462,7 +462,7 @@ def main():
     result = {}
     secondary = {}
 
-    if args.only in ("all", "matvec", "w2a8"):
+    if args.only in ("all", "matvec", "batch8", "w2a8"):
         log("generating the 65536 x 16384 fp32 master on the GPU")
         master = torch.randn((ROWS, COLS), generator=gen, device=dev).mul_(0.02)
     if args.only in ("all", "matvec"):
@@ -475,18 +475,20 @@ def main():
             two["gbs"] = two["bytes"] / two["step_s"] / 1e9
             secondary["matvec_cq2_b1_two_calls"] = two
             log(f"CQ2 b1 as rotate + matvec: step {two['step_s']*1e6:.1f} us, matvec {two['kernel_s']*1e6:.1f} us")
-            for bits, batch in [(3, 1), (4, 1), (5, 1), (1, 1), (2, 8), (4, 8), (1, 8)]:
-                r = bench_matvec(torch, cq, cq_inputs, master, bits, batch, max(args.steps // 3, 20),
-                                 args.warmup, gen)
-                key = f"matvec_cq{ {5: 't', 1: 'b'}.get(bits, bits) }_b{batch}"
-                # rates from the median call: a stall of the launching thread
-                # shows up in the events of the call it delays
-                r["gbs"] = r["bytes"] / r["kernel_median_s"] / 1e9
-                r["frac_hbm_peak"] = r["gbs"] / HBM_PEAK_GBS
-                if batch > 1:
-                    r["tflops"] = r["flop"] / r["kernel_median_s"] / 1e12  # fp16 matrix cores, fp32 sums
-                secondary[key] = r
-                log(key, f"{r['kernel_median_s']*1e6:.1f} us (median)", f"{r['gbs']:.0f} GB/s")
+    if args.only in ("all", "batch8"):
+        legs = ([(3, 1), (4, 1), (5, 1), (1, 1)] if args.only == "all" else []) + [(2, 8), (4, 8), (1, 8)]
+        for bits, batch in legs:
+            r = bench_matvec(torch, cq, cq_inputs, master, bits, batch, max(args.steps // 3, 20),
+                             args.warmup, gen)
+            key = f"matvec_cq{ {5: 't', 1: 'b'}.get(bits, bits) }_b{batch}"
+            # rates from the median call: a stall of the launching thread
+            # shows up in the events of the call it delays
+            r["gbs"] = r["bytes"] / r["kernel_median_s"] / 1e9
+            r["frac_hbm_peak"] = r["gbs"] / HBM_PEAK_GBS
+            if batch > 1:
+                r["tflops"] = r["flop"] / r["kernel_median_s"] / 1e12  # fp16 matrix cores, fp32 sums
+            secondary[key] = r
+            log(key, f"{r['kernel_median_s']*1e6:.1f} us (median)", f"{r['gbs']:.0f} GB/s")
     if args.only in ("all", "w2a8"):
         # the pages' deployment numerics: int8 activations and code book
         for bits, batch in [(2, 1), (4, 1), (1, 1), (2, 2)]:
@@ -497,7 +499,7 @@ def main():
             r["frac_hbm_peak"] = r["gbs"] / HBM_PEAK_GBS
             secondary[key] = r
             log(key, f"{r['kernel_median_s']*1e6:.1f} us (median)", f"{r['gbs']:.0f} GB/s")
-    if args.only in ("all", "matvec", "w2a8"):
+    if args.only in ("all", "matvec", "batch8", "w2a8"):
         del master
         torch.cuda.empty_cache()
     if args.only in ("all", "decode"):
