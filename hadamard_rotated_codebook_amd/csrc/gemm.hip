@@ -13,15 +13,16 @@
 //    waves per SIMD so that one's barrier waits and decode hide behind the
 //    other's matrix work.
 //  * K advances 64 columns per stage through double-buffered LDS (2 x 64 KB).
-//    At the start of stage s every thread issues the loads of stage s+2 (Xr
-//    chunks, its part of the W codes and, at group starts, the norm) into one
-//    of two register sets; while the matrix cores work on stage s it writes
-//    stage s+1, Xr chunks and decoded W values, into the other LDS buffer, the
-//    decode interleaved among the MFMAs (sched_group_barrier) so that VALU and
-//    matrix cores overlap: one barrier per stage.  All loads are
-//    unconditional buffer loads; rows past the end of Xr or W fall outside the
-//    tile's buffer range and read as zeros, so no select ties a load to its
-//    issue point.
+//    At the start of stage s every thread issues the Xr tile of stage s+1 as
+//    buffer loads straight into LDS (16 bytes per lane, no registers, into the
+//    buffer stage s-1 used) and the loads of stage s+2's W codes (and, at
+//    group starts, the norm) into one of two register sets; while the matrix
+//    cores work on stage s it decodes stage s+1's W into the other LDS
+//    buffer, the decode interleaved among the MFMAs (sched_group_barrier) so
+//    that VALU and matrix cores overlap; the stage ends waiting for its direct
+//    loads, then one barrier.  All loads are unconditional buffer loads; rows
+//    past the end of Xr or W fall outside the tile's buffer range and read as
+//    zeros, so no select ties a load to its issue point.
 //  * Decode: a pair of threads owns a row of the W tile.  Per (row, group) it
 //    builds the table bf16(level[c] * norm) for every code c
 //    (v_cvt_pk_bf16_f32, round to nearest even) as byte planes, and turns
@@ -66,6 +67,13 @@ struct GemmArgs {
 
 __device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
 // T: the workgroup's tile is T x T (256, or 128 for products too small to
 // give every CU a 256 x 256 tile); WN waves along N.
 template <int SB, int WN, int T>
@@ -79,7 +87,12 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
   constexpr int TPR = kThreads / BN;           // threads per W row
   constexpr int CODES = BK / TPR;              // codes a thread decodes per stage
   constexpr int CODE_DW = CODES * SB / 32;     // their packed dwords
-  __shared__ uint4 As[2][BM * 8];              // [stage][row][chunk], 16-byte chunks
+  // the two stage buffers of the Xr tile as separate arrays: a direct load
+  // into one then provably does not alias reads of the other
+  __shared__ uint4 As0[BM * 8], As1[BM * 8];   // [row][chunk], 16-byte chunks
+  auto as_buf = [&](auto b_c) -> uint4 * {
+    if constexpr (decltype(b_c)::value == 0) return As0; else return As1;
+  };
   __shared__ uint4 Bs[2][BN * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -97,10 +110,9 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
   const int tn = (t % per_group) / gsize;
   const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
 
-  // Global sources of this thread: Xr chunk (tid & 7) of rows (tid >> 3) +
-  // (kThreads / 8) p, and part `half` of row `wr` of the W tile.  Offsets are
-  // relative to the tile's first row and fit 32 bits (the host bounds kpad).
-  const int xch = tid & 7;
+  // Global sources of this thread: part `half` of row `wr` of the W tile (the
+  // Xr tile goes straight to LDS, below).  Offsets are relative to the tile's
+  // first row and fit 32 bits (the host bounds kpad).
   const int wr = tid / TPR, half = tid % TPR;
   const int64_t mrows = a.m - m0 < BM ? a.m - m0 : BM, nrows = a.rows - n0 < BN ? a.rows - n0 : BN;
   const __amdgpu_buffer_rsrc_t xbuf = buffer_rsrc(a.xr + m0 * a.kpad, static_cast<uint32_t>(mrows * a.kpad * 2));
@@ -108,18 +120,14 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
       buffer_rsrc(a.packed + n0 * a.row_bytes, static_cast<uint32_t>(nrows * a.row_bytes));
   const __amdgpu_buffer_rsrc_t nbuf =
       buffer_rsrc(a.norms + n0 * a.ngroups, static_cast<uint32_t>(nrows * a.ngroups * 2));
-  const uint32_t xoff = static_cast<uint32_t>((tid >> 3) * a.kpad * 2 + xch * 16);
-  const uint32_t xstep = static_cast<uint32_t>((kThreads / 8) * a.kpad * 2);  // between a thread's rows
   const uint32_t woff = static_cast<uint32_t>(wr * a.row_bytes + half * (CODES * SB / 8));
   const uint32_t noff = static_cast<uint32_t>(wr * a.ngroups * 2);
 
   // The W codes of stage s+2 (from HBM) are loaded while stage s is
-  // multiplied, into one of two register sets; the Xr chunks of stage s+1
-  // (mostly cache hits: every N-tile reads them) into a single set.  Even
-  // stages start a group (BK is half a group), so only set 0 carries a norm
-  // and only its stores build a table.  Rows past the end load zeros: an Xr
-  // row directly, a W row through a zero norm (an all-zero decode table).
-  uint4 xa[2][XPT];
+  // multiplied, into one of two register sets.  Even stages start a group
+  // (BK is half a group), so only set 0 carries a norm and only its stores
+  // build a table.  Rows past the end load zeros: an Xr row directly, a W
+  // row through a zero norm (an all-zero decode table).
   uint32_t wc[2][CODE_DW];
   uint16_t wn16 = 0;
   auto load = [&](int64_t k0, auto set_c) {
@@ -127,26 +135,31 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
     load_dwords<CODE_DW>(wbuf, woff + static_cast<uint32_t>(k0 * SB / 8), wc[S]);
     if constexpr (S == 0)
       wn16 = __builtin_amdgcn_raw_buffer_load_b16(nbuf, noff + static_cast<uint32_t>(k0 / CQ_GROUP * 2), 0, 0);
+  };
+  // Xr tile of a stage straight into LDS: instruction p of wave w fills rows
+  // 8 (w XPT + p) .. +7 (1 KB), lane -> row + lane / 8, physical chunk
+  // lane % 8, i.e. logical chunk (lane % 8) ^ (row & 7).
+  const int dwave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t dma_off = static_cast<uint32_t>((lane >> 3) * a.kpad * 2 + (((lane & 7) ^ ((lane >> 3) & 7)) * 16));
+  auto dma = [&](int64_t k0, auto buf_c) {
 #pragma unroll
-    for (int p = 0; p < XPT; ++p)
-      xa[S][p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               xbuf, xoff + p * xstep + static_cast<uint32_t>(k0 * 2), 0, 0));
+    for (int p = 0; p < XPT; ++p) {
+      const int row0 = 8 * (dwave * XPT + p);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xbuf, (lds_ptr_t)(as_buf(buf_c) + row0 * 8), 16, dma_off,
+          static_cast<uint32_t>(row0 * a.kpad * 2 + k0 * 2), 0, 0);
+    }
   };
 
-  // Writing the stage held in register set S into LDS buffer buf, in two
-  // parts: part 0 writes the Xr chunks, builds the group's table (set 0: even
-  // stages start a group) and decodes the first half of this thread's codes;
-  // part 1 decodes the second half.  Each half is two 16-byte chunks of W.
+  // Writing the W stage held in register set S into LDS buffer buf, in two
+  // parts: part 0 builds the group's table (set 0: even stages start a group)
+  // and decodes the first half of this thread's codes; part 1 decodes the
+  // second half.  Each half is two 16-byte chunks of W.
   typename std::conditional<SB == 1, BinTable<__bf16>, Table<SB, __bf16>>::type tab;
   auto store_part = [&](int buf, auto set_c, auto part_c) {
     constexpr int S = decltype(set_c)::value, PART = decltype(part_c)::value;
     const uint32_t *wcs = wc[S];
     if constexpr (PART == 0) {
-#pragma unroll
-      for (int p = 0; p < XPT; ++p) {
-        const int row = (tid >> 3) + (kThreads / 8) * p;
-        As[buf][row * 8 + swz(row, xch)] = xa[S][p];
-      }
       if constexpr (S == 0) tab.build(a.lev, static_cast<float>(__builtin_bit_cast(_Float16, wn16)));
     }
     static_assert(CODES / 8 == 4, "four 8-code chunks per thread and stage");
@@ -196,7 +209,7 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
       const int row = wm * WTM + i * 16 + (lane & 15);
-      af[i] = __builtin_bit_cast(bf16x8, As[cur][row * 8 + swz(row, ch)]);
+      af[i] = __builtin_bit_cast(bf16x8, as_buf(cur_c)[row * 8 + swz(row, ch)]);
     }
     store_part(cur ^ 1, set_c, kk_c);
 #pragma unroll
@@ -230,10 +243,12 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
   using Part1 = std::integral_constant<int, 1>;
   // kpad is a multiple of the group size, so the stage count is even.
   const int nstages = static_cast<int>(a.kpad / BK);
+  dma(0, std::integral_constant<int, 0>{});
   load(0, Set0{});
   load(BK, Set1{});
   store_part(0, Set0{}, Part0{});
   store_part(0, Set0{}, Part1{});
+  wait_vmcnt<0>();
   __syncthreads();
   // Stage s: loads of stage s+2 into register set s%2, then the matrix cores
   // on LDS buffer s%2 while stage s+1 (register set (s+1)%2) is written into
@@ -243,18 +258,24 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
   // the compiler wait for the newer loads too, or sink the loads to the use.
   auto stage = [&](int s, auto par_c) {
     constexpr int P = decltype(par_c)::value;  // s % 2
+    // Xr of stage s+1 into the buffer stage s-1 used (every wave is past it)
+    dma(static_cast<int64_t>(s + 1 < nstages ? s + 1 : nstages - 1) * BK, std::integral_constant<int, 1 - P>{});
     load(static_cast<int64_t>(s + 2 < nstages ? s + 2 : nstages - 1) * BK, par_c);
     __builtin_amdgcn_sched_barrier(0);
     using Cur = std::integral_constant<int, P>;
     using Next = std::integral_constant<int, 1 - P>;
     kstep(Cur{}, Part0{}, Next{});
     kstep(Cur{}, Part1{}, Next{});
+    // the direct loads of stage s+1 have landed (only this stage's W loads,
+    // issued after them, may still be in flight)
+    wait_vmcnt<P == 0 ? 2 : 1>();
     __syncthreads();
   };
   for (int s = 0; s < nstages; s += 2) {
     stage(s, Set0{});
     stage(s + 1, Set1{});
   }
+  wait_vmcnt<0>();
 
   // C fragment layout: lane l, register e -> row 4*(l/16) + e, column l%16.
 #pragma unroll
