@@ -34,9 +34,10 @@ __global__ __launch_bounds__(256) void kv_pad_kernel(const float *__restrict__ q
   x[i] = (d >= 0 && d < head_dim) ? q[static_cast<int64_t>(h) * head_dim + d] : 0.0f;
 }
 
-constexpr int kTThreads = 512;  // 128 columns of a group x 4 row phases
+constexpr int kTThreads = 1024;  // 128 columns of a group x 8 row phases
 constexpr int kTPhases = kTThreads / CQ_GROUP;
-constexpr int kTChunk = 64;     // rows per workgroup: 16 per phase
+constexpr int kTChunk = 1024;     // rows per workgroup (a cache of up to 1024 rows needs no combine)
+constexpr int kTInFlight = 8;     // rows whose loads a thread has in flight
 constexpr int kTMaxBatch = 8;
 
 struct TArgs {
@@ -50,13 +51,14 @@ struct TArgs {
 };
 
 // Workgroup (group g, row chunk c): thread (phase ph, column j) adds
-// p[b][r] * (float(norm[r][g]) * level(code[r][g*128+j])) over rows r = c*64 +
-// 4i + ph of the chunk; the phases are added in order through LDS, the group
-// is rotated back (FWHT, times 1/sqrt(128)) and stored.
+// p[b][r] * (float(norm[r][g]) * level(code[r][g*128+j])) over the chunk's
+// rows r = c*1024 + 8i + ph, in order of i; the eight phases are added in
+// order through LDS and the group's 128 sums of each batch row are rotated
+// back with the register butterfly of the rotation (times 1/sqrt(128)).
 template <int SB>
 __global__ __launch_bounds__(kTThreads) void matvec_t_kernel(TArgs a) {
   __shared__ float lev[16];
-  __shared__ float pch[kTMaxBatch][kTChunk];
+  __shared__ float4 pch[kTChunk][2];                       // p of the chunk's rows, [row][batch]
   __shared__ float red[kTPhases][kTMaxBatch][CQ_GROUP];
   const int tid = threadIdx.x, j = tid % CQ_GROUP, ph = tid / CQ_GROUP;
   const int64_t g = blockIdx.x;
@@ -64,87 +66,86 @@ __global__ __launch_bounds__(kTThreads) void matvec_t_kernel(TArgs a) {
   const int64_t r0 = static_cast<int64_t>(chunk) * kTChunk;
   const int nr = static_cast<int>(a.rows - r0 < kTChunk ? a.rows - r0 : kTChunk);
   if (tid < 16) lev[tid] = a.lev.v[tid];
-  for (int i = tid; i < a.batch * kTChunk; i += kTThreads) {
-    const int b = i / kTChunk, r = i % kTChunk;
-    pch[b][r] = r < nr ? a.p[static_cast<int64_t>(b) * a.rows + r0 + r] : 0.0f;
+  for (int rl = tid; rl < kTChunk; rl += kTThreads) {
+    float v[kTMaxBatch];
+#pragma unroll
+    for (int b = 0; b < kTMaxBatch; ++b)
+      v[b] = (rl < nr && b < a.batch) ? a.p[static_cast<int64_t>(b) * a.rows + r0 + rl] : 0.0f;
+    pch[rl][0] = make_float4(v[0], v[1], v[2], v[3]);
+    pch[rl][1] = make_float4(v[4], v[5], v[6], v[7]);
   }
   __syncthreads();
 
   // the code of column j of group g: bits [SB*j, SB*j + SB) of the group's
-  // bytes, read from the dword holding the first bit and the next one (only
-  // 3-bit codes cross a dword; bytes past the packed region read as zero)
+  // bytes, read from the dword holding the first bit (and, for 3-bit codes,
+  // the next one; bytes past the packed region read as zero)
   const uint32_t bit = static_cast<uint32_t>(SB * j);
   const uint32_t goff = static_cast<uint32_t>(g * (CQ_GROUP * SB / 8)) + (bit >> 5) * 4;
-  const __amdgpu_buffer_rsrc_t pk =
-      buffer_rsrc(a.packed, static_cast<uint32_t>(a.rows * a.row_bytes));
+  const __amdgpu_buffer_rsrc_t pk = buffer_rsrc(a.packed, static_cast<uint32_t>(a.rows * a.row_bytes));
   const __amdgpu_buffer_rsrc_t nb = buffer_rsrc(a.norms, static_cast<uint32_t>(a.rows * a.ngroups * 2));
   float acc[kTMaxBatch];
 #pragma unroll
   for (int b = 0; b < kTMaxBatch; ++b) acc[b] = 0.0f;
-  constexpr int PER = kTChunk / kTPhases;  // 16 rows per thread
-  uint32_t w0[PER], w1[PER];
-  uint16_t nrm[PER];
+  const int steps = (nr + kTPhases - 1) / kTPhases;  // rows per thread, the last ones possibly past the chunk
+  for (int i0 = 0; i0 < steps; i0 += kTInFlight) {
+    uint32_t w0[kTInFlight], w1[kTInFlight];
+    uint16_t nrm[kTInFlight];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int rl = kTPhases * i + ph;
-    const bool live = rl < nr;
-    const int64_t r = r0 + rl;
-    const uint32_t off = live ? static_cast<uint32_t>(r * a.row_bytes) + goff : 0xffff0000u;
-    // two 4-byte loads, each checked against the range on its own
-    w0[i] = __builtin_amdgcn_raw_buffer_load_b32(pk, off, 0, 0);
-    w1[i] = __builtin_amdgcn_raw_buffer_load_b32(pk, off + 4, 0, 0);
-    nrm[i] = __builtin_amdgcn_raw_buffer_load_b16(nb, live ? static_cast<uint32_t>((r * a.ngroups + g) * 2) : 0xffff0000u,
-                                                  0, 0);
-  }
+    for (int u = 0; u < kTInFlight; ++u) {
+      const int rl = kTPhases * (i0 + u) + ph;
+      const bool live = rl < nr;
+      const int64_t r = r0 + rl;
+      const uint32_t off = live ? static_cast<uint32_t>(r * a.row_bytes) + goff : 0xffff0000u;
+      w0[u] = __builtin_amdgcn_raw_buffer_load_b32(pk, off, 0, 0);
+      w1[u] = SB == 3 ? __builtin_amdgcn_raw_buffer_load_b32(pk, off + 4, 0, 0) : 0u;
+      nrm[u] = __builtin_amdgcn_raw_buffer_load_b16(
+          nb, live ? static_cast<uint32_t>((r * a.ngroups + g) * 2) : 0xffff0000u, 0, 0);
+    }
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int rl = kTPhases * i + ph;
-    const uint32_t code = static_cast<uint32_t>(
-        ((static_cast<uint64_t>(w1[i]) << 32 | w0[i]) >> (bit & 31)) & ((1u << SB) - 1));
-    const float w = static_cast<float>(__builtin_bit_cast(_Float16, nrm[i])) * lev[code];
-#pragma unroll
-    for (int b = 0; b < kTMaxBatch; ++b)
-      if (b < a.batch) acc[b] = __builtin_fmaf(pch[b][rl], w, acc[b]);
+    for (int u = 0; u < kTInFlight; ++u) {
+      const int rl = kTPhases * (i0 + u) + ph;
+      const uint32_t code = static_cast<uint32_t>(
+          ((static_cast<uint64_t>(w1[u]) << 32 | w0[u]) >> (bit & 31)) & ((1u << SB) - 1));
+      const float w = static_cast<float>(__builtin_bit_cast(_Float16, nrm[u])) * lev[code];
+      // rows past the chunk: p reads the zero padding of pch (rl < kTChunk) or
+      // is skipped
+      if (rl < kTChunk) {
+        const float4 pa = pch[rl][0], pb = pch[rl][1];
+        acc[0] = __builtin_fmaf(pa.x, w, acc[0]);
+        acc[1] = __builtin_fmaf(pa.y, w, acc[1]);
+        acc[2] = __builtin_fmaf(pa.z, w, acc[2]);
+        acc[3] = __builtin_fmaf(pa.w, w, acc[3]);
+        acc[4] = __builtin_fmaf(pb.x, w, acc[4]);
+        acc[5] = __builtin_fmaf(pb.y, w, acc[5]);
+        acc[6] = __builtin_fmaf(pb.z, w, acc[6]);
+        acc[7] = __builtin_fmaf(pb.w, w, acc[7]);
+      }
+    }
   }
 
-  // the phases in order, then the group's rotation back: thread j of phase
-  // 0 holds column j; the butterfly runs in LDS, one stage per step
+  // the phases in order, then the rotation back: waves 0 and 1, 16 lanes per
+  // batch row, lane jj holding sums 8 jj .. 8 jj + 7
 #pragma unroll
-  for (int b = 0; b < kTMaxBatch; ++b)
-    if (b < a.batch) red[ph][b][j] = acc[b];
+  for (int b = 0; b < kTMaxBatch; ++b) red[ph][b][j] = acc[b];
   __syncthreads();
-  if (ph == 0) {
+  if (tid < 2 * 64) {
+    const int b = tid >> 4, jj = tid & 15;
+    float v[8];
 #pragma unroll
-    for (int b = 0; b < kTMaxBatch; ++b) {
-      if (b >= a.batch) break;
-      float s = red[0][b][j];
+    for (int e = 0; e < 8; ++e) {
+      float s = red[0][b][8 * jj + e];
 #pragma unroll
-      for (int k = 1; k < kTPhases; ++k) s += red[k][b][j];
-      red[0][b][j] = s;
+      for (int k = 1; k < kTPhases; ++k) s += red[k][b][8 * jj + e];
+      v[e] = s;
     }
-  }
-  __syncthreads();
-  for (int h = 1; h < CQ_GROUP; h <<= 1) {
-    float nv[kTMaxBatch];
-    if (ph == 0) {
-      const bool upper = (j & h) != 0;
+    fwht128_unscaled(v, jj);
+    if (b < a.batch) {
 #pragma unroll
-      for (int b = 0; b < kTMaxBatch; ++b)
-        if (b < a.batch) nv[b] = upper ? red[0][b][j ^ h] - red[0][b][j] : red[0][b][j] + red[0][b][j ^ h];
+      for (int e = 0; e < 8; ++e) {
+        const int64_t k = g * CQ_GROUP + 8 * jj + e;
+        if (k < a.cols) a.out[(static_cast<int64_t>(chunk) * a.batch + b) * a.cols + k] = v[e] * kInvSqrt128;
+      }
     }
-    __syncthreads();
-    if (ph == 0) {
-#pragma unroll
-      for (int b = 0; b < kTMaxBatch; ++b)
-        if (b < a.batch) red[0][b][j] = nv[b];
-    }
-    __syncthreads();
-  }
-  const int64_t k = g * CQ_GROUP + j;
-  if (ph != 0 || k >= a.cols) return;
-  for (int b = 0; b < a.batch; ++b) {
-    const float v = red[0][b][j] * kInvSqrt128;
-    a.out[(static_cast<int64_t>(chunk) * a.batch + b) * a.cols + k] = v;
   }
 }
 

@@ -501,8 +501,9 @@ cq_status cq_kv_scores(const cq_matrix *K, const float *q, int32_t n_q_heads, in
  * weighted sum is taken on the codes in the rotated domain,
  * sum_r p[b][r] * float(norm[r][g]) * c[q[r][g*128+j]], and each group is
  * rotated back once (the butterfly of cq_rotate_acts, times 1/sqrt(128)).
- * fp32 throughout: each term is fp32(float(norm) * c) times p, summed in
- * rows of 64 in a fixed order, the row chunks added in order.
+ * fp32 throughout: each term is fp32(float(norm) * c) times p, summed over
+ * chunks of 1024 rows in a fixed order, the chunks added in order (a
+ * matrix of at most 1024 rows needs no workspace).
  *   p        device fp32 [batch][W.rows], 4-byte aligned
  *   batch    0 <= batch <= CQ_MAX_MATVEC_BATCH
  *   out      device fp32 [batch][W.cols], 4-byte aligned, must not overlap

@@ -551,13 +551,17 @@ def test_kv_cache_calls_validation():
                                          kw.get("wsb", 1 << 20), None)
     assert call(wsb=16) == WORKSPACE and call(ws=ws + 16) == ALIGN and call(sc=0) == NULL
     assert call(sc=q) == OVERLAP and call(ws=FAKE) == OVERLAP
-    # cq_matvec_t: sizes and the workspace query
+    # cq_matvec_t: sizes and the workspace query (row chunks of 1024: a
+    # 256-row cache needs none, 2500 rows three chunks of partial sums)
     assert lib.cq_workspace_bytes(cq.OP_MATVEC_T, ctypes.byref(m), 8, ctypes.byref(out)) == OK
-    assert out.value == 4 * 8 * 256 * 4  # 256 rows: four chunks of 64 rows
+    assert out.value == 0
+    m3, lv3 = _matrix(rows=2500, cols=256)  # lv3 keeps the levels array alive
+    assert lib.cq_workspace_bytes(cq.OP_MATVEC_T, ctypes.byref(m3), 8, ctypes.byref(out)) == OK
+    assert out.value == 3 * 8 * 256 * 4
     assert lib.cq_workspace_bytes(cq.OP_MATVEC_T, ctypes.byref(m), 9, ctypes.byref(out)) == SHAPE
     big, _ = _matrix(rows=(1 << 20) + 1, cols=128)
     assert lib.cq_workspace_bytes(cq.OP_MATVEC_T, ctypes.byref(big), 1, ctypes.byref(out)) == SHAPE
-    mt = lambda **kw: lib.cq_matvec_t(ctypes.byref(m), ctypes.c_void_p(kw.get("p", q)), kw.get("b", 2),
+    mt = lambda **kw: lib.cq_matvec_t(ctypes.byref(m3), ctypes.c_void_p(kw.get("p", q)), kw.get("b", 2),
                                       ctypes.c_void_p(kw.get("o", sc)), ctypes.c_void_p(kw.get("ws", ws)),
                                       kw.get("wsb", 1 << 20), None)
     assert mt(b=9) == SHAPE and mt(o=0) == NULL and mt(p=0) == NULL and mt(wsb=4) == WORKSPACE

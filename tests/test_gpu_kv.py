@@ -92,7 +92,11 @@ def test_kv_scores(bits, nq, nkv, hd, tokens):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 1])
-@pytest.mark.parametrize("rows,cols,batch", [(256, 256, 8), (1000, 384, 3), (64, 128, 1), (65, 200, 2), (300, 4096, 5)])
+@pytest.mark.parametrize(
+    "rows,cols,batch",
+    # one row chunk of the kernel (up to 1024 rows), then 2 and 3 chunks (partial sums + combine)
+    [(256, 256, 8), (1000, 384, 3), (64, 128, 1), (65, 200, 2), (300, 4096, 5), (1025, 128, 1), (2048, 256, 8), (2500, 384, 3)],
+)
 def test_matvec_t(bits, rows, cols, batch):
     say("matvec_t", bits, rows, cols, batch)
     levels = _levels(bits)
