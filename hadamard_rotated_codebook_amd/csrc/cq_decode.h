@@ -295,6 +295,38 @@ __device__ inline void decode_piece(const MmaTable<SB> &tab, const uint32_t *cod
   }
 }
 
+// 2-bit, two tables at once (the level's high and low fp16 parts): codes
+// 8h..8h+7 of dword d (h = 0 or 1) as the pairs (8h + i, 8h + i + 4), i < 4
+// -- the slot order of decode2_planes.  One selector per pair serves both
+// tables: bytes (c, c | 4, c', c' | 4) pick each code's low-plane byte (the
+// second source) and high-plane byte (the first), so each table takes one
+// permute per pair.  Per four codes (both halves h): 9 instructions for both
+// tables, against 10 with decode2_planes per table sharing the extraction.
+template <typename T16>
+__device__ inline void decode2_pair2(const PlaneTable<2, T16> &ta, const PlaneTable<2, T16> &tb, uint32_t d, int h,
+                                     uint32_t *oa, uint32_t *ob) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t m = (d >> (2 * i)) & 0x03030303u;  // codes i, i+4, i+8, i+12 in bytes 0..3
+    const uint32_t mo = m | 0x04040404u;                // the same, as high-plane byte indices
+    const uint32_t s = perm(mo, m, h ? 0x07030602u : 0x05010400u);
+    oa[i] = perm(ta.hi[0], ta.lo[0], s);
+    ob[i] = perm(tb.hi[0], tb.lo[0], s);
+  }
+}
+
+// decode_piece for the high and low tables of the same codes.
+template <int SB>
+__device__ inline void decode_piece2(const MmaTable<SB> &thi, const MmaTable<SB> &tlo, const uint32_t *codes, int t,
+                                     uint32_t (&ohi)[4], uint32_t (&olo)[4]) {
+  if constexpr (SB == 2) {
+    decode2_pair2(thi, tlo, codes[t >> 1], t & 1, ohi, olo);
+  } else {
+    decode_piece<SB>(thi, codes, t, ohi);
+    decode_piece<SB>(tlo, codes, t, olo);
+  }
+}
+
 // The pieces of a chunk of four groups, from whole groups: lane quarter q
 // (lanes 16q..16q+15) holds group q of the chunk as four pieces of SB dwords
 // (d[p*SB + i]: piece p), and afterwards holds piece q of every group (d[j*SB

@@ -221,15 +221,16 @@ __global__ __launch_bounds__(kThreads) void matvec_mma_kernel(MmArgs a) {
           const f16x8 af = *reinterpret_cast<const f16x8 *>(a_chunk + j * CQ_GROUP * 2 + t * 16);
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
-            uint32_t o[4];
-            decode_piece<SB>(thi, codes[S][b] + j * SB, t, o);
+            uint32_t o[4], ol[4];
+            if constexpr (SPLIT)
+              decode_piece2<SB>(thi, tlo, codes[S][b] + j * SB, t, o, ol);
+            else
+              decode_piece<SB>(thi, codes[S][b] + j * SB, t, o);
             gs[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                 af, __builtin_bit_cast(f16x8, make_uint4(o[0], o[1], o[2], o[3])), gs[b][j], 0, 0, 0);
-            if constexpr (SPLIT) {
-              decode_piece<SB>(tlo, codes[S][b] + j * SB, t, o);
+            if constexpr (SPLIT)
               gs[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                  af, __builtin_bit_cast(f16x8, make_uint4(o[0], o[1], o[2], o[3])), gs[b][j], 0, 0, 0);
-            }
+                  af, __builtin_bit_cast(f16x8, make_uint4(ol[0], ol[1], ol[2], ol[3])), gs[b][j], 0, 0, 0);
           }
         }
       }

@@ -276,15 +276,16 @@ __global__ __launch_bounds__(kThreads) void small_matvec_kernel(const float *x, 
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const f16x8 af = *reinterpret_cast<const f16x8 *>(a_grp + t * 16);
-      uint32_t o[4];
-      decode_piece<SB>(thi, codes[S], t, o);
+      uint32_t o[4], ol[4];
+      if constexpr (SPLIT)
+        decode_piece2<SB>(thi, tlo, codes[S], t, o, ol);
+      else
+        decode_piece<SB>(thi, codes[S], t, o);
       gh = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, __builtin_bit_cast(f16x8, make_uint4(o[0], o[1], o[2], o[3])), gh,
                                                   0, 0, 0);
-      if constexpr (SPLIT) {
-        decode_piece<SB>(tlo, codes[S], t, o);
-        gl = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, __builtin_bit_cast(f16x8, make_uint4(o[0], o[1], o[2], o[3])),
-                                                    gl, 0, 0, 0);
-      }
+      if constexpr (SPLIT)
+        gl = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            af, __builtin_bit_cast(f16x8, make_uint4(ol[0], ol[1], ol[2], ol[3])), gl, 0, 0, 0);
     }
     // the group's sum times its norm (times lscale), in fp32
     const float nf = static_cast<float>(__builtin_bit_cast(_Float16, nrm[S])) * lscale;
