@@ -3,6 +3,7 @@
 // a rejected call launches nothing and writes nothing.
 #include <cmath>
 #include <cstring>
+#include <limits>
 
 #include "cq_internal.h"
 
@@ -78,6 +79,64 @@ cq_status check_matrix(const cq_matrix *W, cq::CodeLevels *lev) {
 // double sum is exact, so "u > mid" is the exact "nearer to the upper level"
 // test and a tie keeps the smaller index (OpenNeedle reference notes, CQ
 // quantisation steps).  levels are valid (code_levels accepted them).
+// The bucket lookup of the encoder's decision (cq::EncodeTable): fp32
+// thresholds, a scale and offset that spread them over the buckets, and a
+// check that no bucket holds two of them.  The bucket map is evaluated here
+// with the same fp32 operations as in the kernel (a product rounded to
+// nearest, clamps, floor), and it is monotone in u, so a u in bucket b lies
+// above every threshold of a lower bucket and below every one of a higher.
+void build_decision_lut(cq::EncodeTable &tab) {
+  tab.lut = 0;
+  const int nt = tab.nlevels - 1;
+  // up to three midpoints, counting them is cheaper than the lookup
+  if (nt < 4) return;
+  float thr[15];
+  for (int m = 0; m < nt; ++m) {
+    float f = static_cast<float>(tab.mid[m]);
+    if (!(static_cast<double>(f) > tab.mid[m])) f = std::nextafter(f, std::numeric_limits<float>::infinity());
+    if (!std::isfinite(f) || f == 0.0f) return;  // a zero threshold: +-0 keys differ, values do not
+    thr[m] = f;
+  }
+  const double span = static_cast<double>(thr[nt - 1]) - static_cast<double>(thr[0]);
+  const float scale = span > 0.0 ? static_cast<float>((cq::kLutBuckets - 4) / span) : 1.0f;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return;
+  auto raw = [&](float u) {
+    const float x = std::fmin(std::fmax(u * scale, -1e6f), 1e6f);
+    return static_cast<int>(std::floor(x));
+  };
+  const int off = 2 - raw(thr[0]);
+  auto bucket = [&](float u) {
+    const int b = raw(u) + off;
+    return b < 0 ? 0 : (b > cq::kLutBuckets - 1 ? cq::kLutBuckets - 1 : b);
+  };
+  int bm[15];
+  for (int m = 0; m < nt; ++m) {
+    // a negative threshold whose product is subnormal: a kernel flushing
+    // subnormals would floor it to 0, not -1
+    const float x = thr[m] * scale;
+    if (x < 0.0f && x > -std::numeric_limits<float>::min()) return;
+    bm[m] = bucket(thr[m]);
+    if (m > 0 && bm[m] <= bm[m - 1]) return;  // two thresholds in one bucket
+  }
+  for (int b = 0; b < cq::kLutBuckets; ++b) {
+    int below = 0;
+    int32_t key = std::numeric_limits<int32_t>::max();
+    for (int m = 0; m < nt; ++m) {
+      if (bm[m] < b) ++below;
+      if (bm[m] == b) {
+        uint32_t tb;
+        std::memcpy(&tb, &thr[m], sizeof tb);
+        key = cq::float_key(tb);
+      }
+    }
+    tab.lut_base[b] = static_cast<uint8_t>(below);
+    tab.lut_key[b] = key;
+  }
+  tab.lut_scale = scale;
+  tab.lut_off = off;
+  tab.lut = 1;
+}
+
 cq::EncodeTable encode_table(int32_t bits, const float *levels) {
   cq::EncodeTable tab;
   std::memset(&tab, 0, sizeof tab);
@@ -100,6 +159,7 @@ cq::EncodeTable encode_table(int32_t bits, const float *levels) {
       tab.mid[j] = (static_cast<double>(levels[j]) + static_cast<double>(levels[j + 1])) * 0.5;
     for (int j = 0; j < tab.nlevels; ++j) tab.code_of_index[j] = static_cast<uint32_t>(j);
   }
+  build_decision_lut(tab);
   return tab;
 }
 

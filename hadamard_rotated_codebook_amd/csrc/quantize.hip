@@ -13,19 +13,55 @@
 //   rounded once, which is exact rounding for fp32 operands); the nearest level
 //   is decided by exact comparison against the midpoints of adjacent levels,
 //   ties to the smaller index; the stored norm is fp16, round to nearest even.
+//   The comparison runs as a bucket lookup (cq::EncodeTable: one fp32
+//   threshold per bucket, compared by order keys of the bit patterns, the
+//   same decisions) or, for code books whose thresholds are too close for
+//   the buckets, as a count of the midpoints.
+// The 16 lanes of a group exchange values with DPP (two 32-bit moves per
+// double), not through LDS.
+#include "cq_fwht.h"
 #include "cq_internal.h"
 
 namespace {
 
 constexpr double kSqrtInv128 = 0.08838834764831845;  // sqrt(1/128) in double
 
+// The double of lane j ^ D within each 16-lane row, both halves moved by DPP.
+template <int D>
+__device__ inline double xor_lane_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __float_as_uint(cqdev::xor_lane<D>(__uint_as_float(static_cast<uint32_t>(b))));
+  const uint32_t hi = __float_as_uint(cqdev::xor_lane<D>(__uint_as_float(static_cast<uint32_t>(b >> 32))));
+  return __builtin_bit_cast(double, static_cast<uint64_t>(hi) << 32 | lo);
+}
+// -v for the upper lane of a pair (sign flip, exact), v otherwise
+__device__ inline double signed_f64(double v, bool upper) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v) ^ (upper ? 0x8000000000000000ull : 0ull);
+  return __builtin_bit_cast(double, b);
+}
+template <int D>
+__device__ inline void lane_stage_f64(double (&t)[8], int j) {
+  const bool upper = (j & D) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = xor_lane_f64<D>(t[i]) + signed_f64(t[i], upper);
+}
+
 // packed: the first output row's codes (rows of kpad * SB / 8 bytes follow);
 // norms: its fp16 norms (rows of kpad / 128 follow) -- the rows of a whole
 // blob, or a row range of a larger one.
-template <int SB, bool VEC>
+template <int SB, bool VEC, bool LUT>
 __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__ w, int64_t rows,
                                                       int64_t cols, int64_t kpad, cq::EncodeTable tab,
                                                       uint8_t *__restrict__ packed, uint16_t *__restrict__ norms) {
+  __shared__ int32_t lut_key[cq::kLutBuckets];
+  __shared__ int32_t lut_base[cq::kLutBuckets];
+  if constexpr (LUT) {
+    if (threadIdx.x < cq::kLutBuckets) {
+      lut_key[threadIdx.x] = tab.lut_key[threadIdx.x];
+      lut_base[threadIdx.x] = tab.lut_base[threadIdx.x];
+    }
+    __syncthreads();
+  }
   const int64_t ngroups = kpad / CQ_GROUP;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int j = threadIdx.x & 15;
@@ -57,15 +93,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
       t[i + h] = a - c;
     }
   }
-#pragma unroll
-  for (int d = 1; d < 16; d <<= 1) {
-    const bool upper = (j & d) != 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const double p = __shfl_xor(t[i], d, 16);
-      t[i] = upper ? (p - t[i]) : (t[i] + p);
-    }
-  }
+  lane_stage_f64<1>(t, j);
+  lane_stage_f64<2>(t, j);
+  lane_stage_f64<4>(t, j);
+  lane_stage_f64<8>(t, j);
 
   float r32[8];
   double ss = 0.0;
@@ -75,17 +106,27 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
     const double rd = static_cast<double>(r32[i]);
     ss += rd * rd;  // each square is exact in double
   }
-#pragma unroll
-  for (int d = 1; d < 16; d <<= 1) ss += __shfl_xor(ss, d, 16);
+  ss += xor_lane_f64<1>(ss);
+  ss += xor_lane_f64<2>(ss);
+  ss += xor_lane_f64<4>(ss);
+  ss += xor_lane_f64<8>(ss);
   const float n32 = static_cast<float>(sqrt(ss));
   const double den = static_cast<double>(fmaxf(n32, 1e-12f));
 
   uint32_t word = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const double u = static_cast<double>(static_cast<float>(static_cast<double>(r32[i]) / den));
+    const float u32 = static_cast<float>(static_cast<double>(r32[i]) / den);
     int q = 0;
-    for (int m = 0; m + 1 < tab.nlevels; ++m) q += (u > tab.mid[m]) ? 1 : 0;
+    if constexpr (LUT) {
+      const float x = fminf(fmaxf(u32 * tab.lut_scale, -1e6f), 1e6f);
+      const int b = min(max(static_cast<int>(floorf(x)) + tab.lut_off, 0), cq::kLutBuckets - 1);
+      q = lut_base[b] + (cq::float_key(__float_as_uint(u32)) >= lut_key[b] ? 1 : 0);
+      q = u32 == u32 ? q : 0;  // NaN: no midpoint is below it
+    } else {
+      const double u = static_cast<double>(u32);
+      for (int m = 0; m + 1 < tab.nlevels; ++m) q += (u > tab.mid[m]) ? 1 : 0;
+    }
     word |= tab.code_of_index[q] << (i * SB);
   }
   if (!valid) return;
@@ -113,10 +154,18 @@ hipError_t launch_sb(const float *w, int64_t rows, int64_t cols, int64_t kpad, c
   const int64_t blocks = (groups + 15) / 16;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const bool vec = (cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0);
-  if (vec)
-    quantize_kernel<SB, true><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(w, rows, cols, kpad, tab, packed, norms);
-  else
-    quantize_kernel<SB, false><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(w, rows, cols, kpad, tab, packed, norms);
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (tab.lut) {
+    if (vec)
+      quantize_kernel<SB, true, true><<<grid, 256, 0, s>>>(w, rows, cols, kpad, tab, packed, norms);
+    else
+      quantize_kernel<SB, false, true><<<grid, 256, 0, s>>>(w, rows, cols, kpad, tab, packed, norms);
+  } else {
+    if (vec)
+      quantize_kernel<SB, true, false><<<grid, 256, 0, s>>>(w, rows, cols, kpad, tab, packed, norms);
+    else
+      quantize_kernel<SB, false, false><<<grid, 256, 0, s>>>(w, rows, cols, kpad, tab, packed, norms);
+  }
   return hipGetLastError();
 }
 

@@ -763,6 +763,18 @@ def test_quantize_special_groups():
     assert np.array_equal(blob_g, oracle.quantize(w, 2, levels))
 
 
+def test_quantize_close_levels_count_the_midpoints():
+    # a code book with two midpoints 1e-6 / sqrt(128) apart: too close for the
+    # encoder's bucket lookup of the decision (one threshold per bucket), so
+    # it counts the midpoints; the decisions are the oracle's either way
+    say("quantize close levels")
+    s = 1.0 / np.sqrt(128.0)
+    levels = (np.array([-1.0, -0.5, -0.25, 0.0, 1e-6, 2e-6, 0.5, 1.0]) * s).astype(np.float32)
+    w = cq_inputs.master(64, 3, 64, 512)
+    W = cq.cq_quantize(_to_dev(w), 3, levels)
+    _encoder_agreement(3, w, W.blob.cpu().numpy(), levels)
+
+
 def test_concurrent_host_threads_on_their_own_streams():
     # the launchers' host-side caches are shared by every thread: calls from
     # several threads at once, each on its own stream, give the results of
