@@ -199,6 +199,22 @@ __device__ inline void decode1(const BinTable<T16> &t, uint32_t b, uint32_t *o) 
   }
 }
 
+// Binary codes as fp16 -1 / +1 (code 0 / 1; the level is applied in fp32 by
+// the caller), for the batched matrix-core kernel: the four fp16 pairs of k
+// step t (t < 4) of a 32-code piece x, pair u holding codes 4t + u and
+// 4t + u + 16.  Bits i and i + 16 of ~x are 16 apart, so one shift puts them
+// on the sign bits 15 and 31 of 0x3c003c00: two instructions per pair, no
+// table.  The activation slots follow the same order (slot 8t + 2u + h holds
+// column 4t + u + 16h of the piece).
+__device__ inline void decode1_sign(uint32_t x, int t, uint32_t (&o)[4]) {
+  const uint32_t nx = ~x;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = 4 * t + u;
+    o[u] = ((nx & (0x00010001u << i)) << (15 - i)) | 0x3c003c00u;
+  }
+}
+
 // Slot order of the permuted decoders: position t of an 8-value operand holds
 // code perm_code<SB>(t) of its 8 consecutive codes (3-bit: natural order).
 template <int SB>

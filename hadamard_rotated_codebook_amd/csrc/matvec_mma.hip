@@ -134,19 +134,34 @@ __global__ __launch_bounds__(kThreads) void matvec_mma_kernel(MmArgs a) {
       if (lane == 0) unscale[m] = ldexpf(1.0f, -e);
       _Float16 *dhi = xs + m * xsr, *dlo = xs + (batch + m) * xsr;
       for (int k = lane * 8; k < staged; k += 64 * 8) {
+        // v: the block's 8 slots in the decoder's order.  Binary: slots
+        // 2u, 2u + 1 of block t of a 32-column piece are columns 4t + u and
+        // 4t + u + 16 (decode1_sign); otherwise perm_code within the block.
         float v[8];
         float4 u0 = make_float4(0.f, 0.f, 0.f, 0.f), u1 = u0;
         if (k < ncols) {
-          u0 = *reinterpret_cast<const float4 *>(src + k);
-          u1 = *reinterpret_cast<const float4 *>(src + k + 4);
+          if constexpr (SB == 1) {
+            const int pc = (k & ~31) + 4 * ((k >> 3) & 3);
+            u0 = *reinterpret_cast<const float4 *>(src + pc);
+            u1 = *reinterpret_cast<const float4 *>(src + pc + 16);
+          } else {
+            u0 = *reinterpret_cast<const float4 *>(src + k);
+            u1 = *reinterpret_cast<const float4 *>(src + k + 4);
+          }
         }
-        v[0] = u0.x, v[1] = u0.y, v[2] = u0.z, v[3] = u0.w, v[4] = u1.x, v[5] = u1.y, v[6] = u1.z, v[7] = u1.w;
+        if constexpr (SB == 1) {
+          v[0] = u0.x, v[1] = u1.x, v[2] = u0.y, v[3] = u1.y, v[4] = u0.z, v[5] = u1.z, v[6] = u0.w, v[7] = u1.w;
+        } else {
+          const float n8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = n8[perm_code<SB>(e)];
+        }
         uint32_t wh[4], wl[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           _Float16 h0, l0, h1, l1;
-          split_f16(v[perm_code<SB>(2 * t)] * scale, h0, l0);
-          split_f16(v[perm_code<SB>(2 * t + 1)] * scale, h1, l1);
+          split_f16(v[2 * t] * scale, h0, l0);
+          split_f16(v[2 * t + 1] * scale, h1, l1);
           wh[t] = pack_h2(h0, h1);
           wl[t] = pack_h2(l0, l1);
         }
@@ -224,6 +239,8 @@ __global__ __launch_bounds__(kThreads) void matvec_mma_kernel(MmArgs a) {
             uint32_t o[4], ol[4];
             if constexpr (SPLIT)
               decode_piece2<SB>(thi, tlo, codes[S][b] + j * SB, t, o, ol);
+            else if constexpr (SB == 1)
+              decode1_sign(codes[S][b][j], t, o);
             else
               decode_piece<SB>(thi, codes[S][b] + j * SB, t, o);
             gs[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
