@@ -9,8 +9,9 @@
 //   w . S is summed in double by the butterfly (exact for fp32 inputs that do
 //   not span more than ~2^22 in magnitude), scaled by sqrt(1/128) in double and
 //   rounded once to the fp32 coordinate r; the norm is the double norm of the
-//   fp32 r rounded to fp32; u is the IEEE fp32 quotient (formed in double and
-//   rounded once, which is exact rounding for fp32 operands); the nearest level
+//   fp32 r rounded to fp32; u is the IEEE fp32 quotient (formed in double --
+//   as r times the group's double reciprocal, see below -- and rounded once,
+//   which is exact rounding for fp32 operands); the nearest level
 //   is decided by exact comparison against the midpoints of adjacent levels,
 //   ties to the smaller index; the stored norm is fp16, round to nearest even.
 //   The comparison runs as a bucket lookup (cq::EncodeTable: one fp32
@@ -113,10 +114,30 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
   const float n32 = static_cast<float>(sqrt(ss));
   const double den = static_cast<double>(fmaxf(n32, 1e-12f));
 
+  // u = fp32(r / den): r * (1 / den) in double rounds to the same fp32.  The
+  // double product is within ~2^-52 of the quotient, and a quotient of two
+  // fp32 values lies at least ~2^-49 (relative) from an fp32 rounding
+  // boundary unless it is exactly one -- impossible for a normal result (it
+  // would need 25 significant bits in r), possible among subnormal results,
+  // so a wave with such a quotient divides exactly.
+  const double inv = 1.0 / den;
+  float uq[8];
+  bool sub = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double ud = static_cast<double>(r32[i]) * inv;
+    uq[i] = static_cast<float>(ud);
+    sub |= ud != 0.0 && fabs(ud) < 1.1754943508222875e-38;  // below the smallest normal fp32
+  }
+  if (__builtin_amdgcn_ballot_w64(sub) != 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) uq[i] = static_cast<float>(static_cast<double>(r32[i]) / den);
+  }
+
   uint32_t word = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float u32 = static_cast<float>(static_cast<double>(r32[i]) / den);
+    const float u32 = uq[i];
     int q = 0;
     if constexpr (LUT) {
       const float x = fminf(fmaxf(u32 * tab.lut_scale, -1e6f), 1e6f);
