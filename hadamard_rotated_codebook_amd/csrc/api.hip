@@ -80,86 +80,90 @@ cq_status check_matrix(const cq_matrix *W, cq::CodeLevels *lev) {
 // test and a tie keeps the smaller index (OpenNeedle reference notes, CQ
 // quantisation steps).  levels are valid (code_levels accepted them).
 // The bucket lookup of the encoder's decision (cq::EncodeTable): fp32
-// thresholds, a scale and offset that spread them over the buckets, and a
+// thresholds, a scale and bias that spread them over the buckets, and a
 // check that no bucket holds two of them.  The bucket map is evaluated here
-// with the same fp32 operations as in the kernel (a product rounded to
-// nearest, clamps, floor), and it is monotone in u, so a u in bucket b lies
-// above every threshold of a lower bucket and below every one of a higher.
-void build_decision_lut(cq::EncodeTable &tab) {
+// with the same fp32 operation as in the kernel (one fused multiply-add,
+// correctly rounded on both sides, then integer clamps of its bit pattern);
+// it is monotone in u, so a u in bucket b lies above every threshold of a
+// lower bucket and below every one of a higher.  Only for code books whose
+// codes are their level indices; up to two midpoints are counted instead.
+void build_decision_lut(cq::EncodeTable &tab, bool codes_are_indices) {
   tab.lut = 0;
   const int nt = tab.nlevels - 1;
-  // up to three midpoints, counting them is cheaper than the lookup
-  if (nt < 4) return;
+  if (nt < 3 || !codes_are_indices) return;
   float thr[15];
   for (int m = 0; m < nt; ++m) {
     float f = static_cast<float>(tab.mid[m]);
     if (!(static_cast<double>(f) > tab.mid[m])) f = std::nextafter(f, std::numeric_limits<float>::infinity());
-    if (!std::isfinite(f) || f == 0.0f) return;  // a zero threshold: +-0 keys differ, values do not
+    // finite and clear of the subnormal range (a tiny threshold: the kernel's
+    // u may then be off by a subnormal step where it matters)
+    if (!std::isfinite(f) || !(std::fabs(f) >= 0x1p-125f)) return;
     thr[m] = f;
   }
   const double span = static_cast<double>(thr[nt - 1]) - static_cast<double>(thr[0]);
   const float scale = span > 0.0 ? static_cast<float>((cq::kLutBuckets - 4) / span) : 1.0f;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return;
-  auto raw = [&](float u) {
-    const float x = std::fmin(std::fmax(u * scale, -1e6f), 1e6f);
-    return static_cast<int>(std::floor(x));
-  };
-  const int off = 2 - raw(thr[0]);
+  // the lowest threshold near bucket 2
+  const double lo = std::floor(static_cast<double>(thr[0]) * static_cast<double>(scale));
+  if (!(std::fabs(lo) < 1e6)) return;
+  const float bias = static_cast<float>(0x1.8p23 + (2.0 - lo));  // exact: an integer below 2^24
   auto bucket = [&](float u) {
-    const int b = raw(u) + off;
-    return b < 0 ? 0 : (b > cq::kLutBuckets - 1 ? cq::kLutBuckets - 1 : b);
+    const float y = std::fmaf(u, scale, bias);
+    int32_t yb;
+    std::memcpy(&yb, &y, sizeof yb);
+    const int32_t b = std::min(std::max(yb, cq::kLutMagicBits), cq::kLutMagicBits + cq::kLutBuckets - 1);
+    return static_cast<int>(b - cq::kLutMagicBits);
   };
   int bm[15];
   for (int m = 0; m < nt; ++m) {
-    // a negative threshold whose product is subnormal: a kernel flushing
-    // subnormals would floor it to 0, not -1
-    const float x = thr[m] * scale;
-    if (x < 0.0f && x > -std::numeric_limits<float>::min()) return;
     bm[m] = bucket(thr[m]);
     if (m > 0 && bm[m] <= bm[m - 1]) return;  // two thresholds in one bucket
   }
   for (int b = 0; b < cq::kLutBuckets; ++b) {
     int below = 0;
-    int32_t key = std::numeric_limits<int32_t>::max();
+    float t = std::numeric_limits<float>::quiet_NaN();
     for (int m = 0; m < nt; ++m) {
       if (bm[m] < b) ++below;
-      if (bm[m] == b) {
-        uint32_t tb;
-        std::memcpy(&tb, &thr[m], sizeof tb);
-        key = cq::float_key(tb);
-      }
+      if (bm[m] == b) t = thr[m];
     }
     tab.lut_base[b] = static_cast<uint8_t>(below);
-    tab.lut_key[b] = key;
+    tab.lut_thr[b] = t;
   }
   tab.lut_scale = scale;
-  tab.lut_off = off;
+  tab.lut_bias = bias;
   tab.lut = 1;
 }
 
 cq::EncodeTable encode_table(int32_t bits, const float *levels) {
   cq::EncodeTable tab;
   std::memset(&tab, 0, sizeof tab);
+  uint32_t code_of_index[16] = {};
   if (bits == 5) {
     const double a = static_cast<double>(cq::ternary_level_f32());
     tab.nlevels = 3;
     tab.mid[0] = -a * 0.5;
     tab.mid[1] = a * 0.5;
-    tab.code_of_index[0] = 3;  // -a -> crumb 11
-    tab.code_of_index[1] = 0;  //  0 -> crumb 00
-    tab.code_of_index[2] = 1;  // +a -> crumb 01
+    code_of_index[0] = 3;  // -a -> crumb 11
+    code_of_index[1] = 0;  //  0 -> crumb 00
+    code_of_index[2] = 1;  // +a -> crumb 01
   } else if (bits == 1) {
     tab.nlevels = 2;
     tab.mid[0] = 0.0;  // the midpoint of -c and +c
-    tab.code_of_index[0] = 0;
-    tab.code_of_index[1] = 1;
+    code_of_index[0] = 0;
+    code_of_index[1] = 1;
   } else {
     tab.nlevels = 1 << bits;
     for (int j = 0; j + 1 < tab.nlevels; ++j)
       tab.mid[j] = (static_cast<double>(levels[j]) + static_cast<double>(levels[j + 1])) * 0.5;
-    for (int j = 0; j < tab.nlevels; ++j) tab.code_of_index[j] = static_cast<uint32_t>(j);
+    for (int j = 0; j < tab.nlevels; ++j) code_of_index[j] = static_cast<uint32_t>(j);
   }
-  build_decision_lut(tab);
+  bool ident = true;
+  for (int j = 0; j < tab.nlevels; ++j) {
+    ident = ident && code_of_index[j] == static_cast<uint32_t>(j);
+    if (j < 4) tab.code_bytes |= code_of_index[j] << (8 * j);
+  }
+  tab.code_ident = ident ? 1 : 0;
+  build_decision_lut(tab, ident);
   return tab;
 }
 

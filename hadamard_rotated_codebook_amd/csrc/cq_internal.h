@@ -19,29 +19,30 @@ struct CodeLevels {
 // Decision thresholds of the encoder: exact midpoints of adjacent ascending
 // levels (held exactly in double), and the stored code of each level index.
 // The decision q = #{m : u > mid[m]} for an fp32 u equals #{m : u >= T[m]}
-// with T[m] the smallest fp32 above mid[m], compared as order keys of the
-// fp32 bit patterns (float_key: exact whatever the denormal mode).  When
-// every bucket of the map b(u) = clamp(floor(clamp(u * lut_scale, +-1e6)) +
-// lut_off, 0, 127) (fp32 arithmetic, monotone in u) holds at most one T[m],
-// q = lut_base[b] + (key(u) >= lut_key[b]) (lut = 1, used from 8 levels);
-// otherwise the encoder counts the midpoints.
+// with T[m] the smallest fp32 above mid[m].  With at least 3 thresholds, all
+// of magnitude >= 2^-125 (so an fp32 compare with them is exact in any
+// denormal mode, and a u anywhere in the subnormal range lies on the same
+// side of each), and codes equal to level indices, the encoder looks the
+// decision up (lut = 1): bucket b(u) = clamp(bits(fma(u, lut_scale,
+// lut_bias)) - bits(1.5 * 2^23), 0, 127) (one fp32 fused multiply-add
+// rounded to nearest, whose result's low bits hold round(u * lut_scale +
+// off) in [2^23, 2^24); monotone in u), at most one threshold per bucket, and
+// q = lut_base[b] + (u >= lut_thr[b]) (NaN for a bucket without one).
+// Otherwise it counts the midpoints in double and stores code byte q of
+// code_bytes (up to 4 levels) or q itself (codes are level indices).
 constexpr int kLutBuckets = 128;
+constexpr int32_t kLutMagicBits = 0x4b400000;  // bits of 1.5 * 2^23
 struct EncodeTable {
   double mid[15];
-  uint32_t code_of_index[16];
+  uint32_t code_bytes;  // byte q: the stored code of level index q (nlevels <= 4)
+  int32_t code_ident;   // 1 when every code is its level index
   int32_t nlevels;
   int32_t lut;
   float lut_scale;
-  int32_t lut_off;
-  int32_t lut_key[kLutBuckets];   // order key of the bucket's threshold, INT32_MAX if none
-  uint8_t lut_base[kLutBuckets];  // thresholds below the bucket
+  float lut_bias;                  // 1.5 * 2^23 + an integer offset
+  float lut_thr[kLutBuckets];      // the bucket's threshold, NaN if none
+  uint8_t lut_base[kLutBuckets];   // thresholds below the bucket
 };
-
-// Order key of an fp32 bit pattern: signed-integer order equals the order of
-// the values (non-NaN; -0 sorts below +0).
-__host__ __device__ inline int32_t float_key(uint32_t bits) {
-  return static_cast<int32_t>(bits ^ ((static_cast<uint32_t>(static_cast<int32_t>(bits) >> 31)) & 0x7fffffffu));
-}
 
 // Storage width of one index: 2 for ternary crumbs, else bits (1 for binary).
 inline int storage_bits(int bits) { return bits == 5 ? 2 : bits; }
