@@ -28,7 +28,9 @@
 //  * The group norms of a wave's unit of 32 rows (16 bytes per row at 2 bits,
 //    4 KB apart) come in a few 2-byte loads per lane when the loads move on
 //    to the unit, and are staged in a per-wave LDS buffer: one load per row
-//    cost 11 % of the kernel's time, the unit loads cut that by a third.
+//    cost 11 % of the kernel's time, the unit loads cut that by a third.  The
+//    buffer holds each group's 32 norms side by side, so one 16-byte LDS read
+//    serves 8 rows (v_fma_mix selects the half).
 //  * Rows are read through buffer descriptors rebased per row in scalar
 //    registers.  A row past the end of its block or of the matrix gets a
 //    zero-length descriptor and reads zeros, as do lanes past the end of K (their
@@ -195,7 +197,8 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
   using G = Geom<SB>;
   __shared__ __align__(16) uint8_t lds[G::LDS_BYTES];
   __shared__ __align__(16) float xrot[ROT ? G::SLICE_COLS : 4];  // the slice's rotated activations
-  __shared__ __align__(16) uint16_t nbuf[kWaves][kRowsPerWave * G::SLICE_GROUPS];  // each wave's unit norms
+  constexpr int NBS = kRowsPerWave + 8;  // halves per group row of the norm buffer (padded)
+  __shared__ __align__(16) uint16_t nbuf[kWaves][G::SLICE_GROUPS * NBS];  // each wave's unit norms, [group][row]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps row addressing scalar
@@ -435,6 +438,7 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
     float racc[kRowsPerWave];
     _Float16 tv[2][G::LOOKUPS];
     _Float16 nv[2];
+    uint4 nb8;
     auto accumulate = [&](int m) {
       float acc = 0.0f;
 #pragma unroll
@@ -451,9 +455,17 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
       for (int d = 0; d < G::DWORDS; ++d) cur[d] = dw[slot][d];
       if (m == 0) {  // this unit's norms into the wave's buffer (written and read as uint16_t)
 #pragma unroll
-        for (int h = 0; h < G::NORM_H; ++h) nbuf[wave][64 * h + lane] = static_cast<uint16_t>(nun[h]);
+        for (int h = 0; h < G::NORM_H; ++h) {
+          const int jn = 64 * h + lane;
+          nbuf[wave][(jn % G::SLICE_GROUPS) * NBS + jn / G::SLICE_GROUPS] = static_cast<uint16_t>(nun[h]);
+        }
       }
-      nv[m & 1] = __builtin_bit_cast(_Float16, nbuf[wave][m * G::SLICE_GROUPS + norm_group]);
+      // one 16-byte read brings the norms of 8 rows; the fma picks its half
+      if (m % 8 == 0) nb8 = *reinterpret_cast<const uint4 *>(&nbuf[wave][norm_group * NBS + m]);
+      {
+        const uint32_t d = (m % 8) / 2 == 0 ? nb8.x : ((m % 8) / 2 == 1 ? nb8.y : ((m % 8) / 2 == 2 ? nb8.z : nb8.w));
+        nv[m & 1] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(d >> (16 * (m % 2))));
+      }
       if (m == 0 && lane == 0) grabbed = static_cast<uint32_t>(atomicAdd(&next_local, 1));
       if (m + AH == kRowsPerWave) {  // the loads move on to the next unit
         un = unit_of(static_cast<int>(__builtin_amdgcn_readfirstlane(grabbed)));
