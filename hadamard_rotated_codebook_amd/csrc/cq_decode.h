@@ -108,13 +108,21 @@ __device__ inline void decode4(const Table<4, T16> &t, uint32_t d, uint32_t *o) 
   o[3] = perm(h47, l47, 0x07030602u);
 }
 
-// 3-bit: 8 codes in the low 24 bits of b -> 4 dwords of 16-bit pairs.
+// 3-bit: 8 codes in the low 24 bits of b (higher bits ignored) -> 4 dwords of
+// 16-bit pairs.
 template <typename T16>
 __device__ inline void decode3(const Table<3, T16> &t, uint32_t b, uint32_t *o) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint32_t f = b >> (12 * h);  // four codes in bits 0..11
-    const uint32_t s = (f & 7u) | ((f << 5) & 0x700u) | ((f << 10) & 0x70000u) | ((f << 15) & 0x7000000u);
+    // four codes in bits 0..11 of f, spread to one per byte: the low 16 bits
+    // in both halves, each half shifted by its own amount (packed 16-bit
+    // shifts), then the bytes that hold codes 0, 1, 2, 3 in their low bits
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t f = b >> (12 * h);
+    const u16x2 ff = __builtin_bit_cast(u16x2, perm(f, f, 0x01000100u));
+    const uint32_t t02 = __builtin_bit_cast(uint32_t, ff >> u16x2{0, 6});  // codes 0 and 2 at bits 0 and 16
+    const uint32_t t13 = __builtin_bit_cast(uint32_t, ff >> u16x2{3, 9});  // codes 1 and 3
+    const uint32_t s = perm(t13, t02, 0x06020400u) & 0x07070707u;
     const uint32_t l = perm(t.lo[1], t.lo[0], s), hh = perm(t.hi[1], t.hi[0], s);
     o[2 * h] = perm(hh, l, 0x05010400u);
     o[2 * h + 1] = perm(hh, l, 0x07030602u);
@@ -278,7 +286,7 @@ __device__ inline void decode_step(const MmaTable<SB> &tab, const uint32_t *code
     constexpr int DW = 3 * 128 / 32;
     const int bit = 24 * s, w = bit >> 5, sh = bit & 31;
     const uint32_t f = sh <= 8 ? (codes[w] >> sh) : __builtin_amdgcn_alignbit(codes[(w + 1) % DW], codes[w], sh);
-    decode3(tab, f & 0xffffffu, o);
+    decode3(tab, f, o);
   } else {
     uint32_t o8[8];
     decode2_planes(tab, codes[s >> 1], o8);
@@ -302,7 +310,7 @@ __device__ inline void decode_piece(const MmaTable<SB> &tab, const uint32_t *cod
                      : t == 1 ? __builtin_amdgcn_alignbit(codes[1], codes[0], 24)
                      : t == 2 ? __builtin_amdgcn_alignbit(codes[2], codes[1], 16)
                               : codes[2] >> 8;
-    decode3(tab, f & 0xffffffu, o);
+    decode3(tab, f, o);
   } else {
     uint32_t o8[8];
     decode2_planes(tab, codes[t >> 1], o8);

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(64 * kWavesM * WN, 1) void gemm_kernel(GemmArgs a) 
       for (int q = 2 * PART; q < 2 * PART + 2; ++q) {  // 24 bits per 8 codes: byte offset 3 q
         const int bit = 24 * q, w = bit >> 5, sh = bit & 31;
         const uint32_t b = sh <= 8 ? (wcs[w] >> sh) : __builtin_amdgcn_alignbit(wcs[(w + 1) % CODE_DW], wcs[w], sh);
-        decode3(tab, b & 0xffffffu, o + 4 * (q - 2 * PART));
+        decode3(tab, b, o + 4 * (q - 2 * PART));
       }
     } else {
       decode2(tab, wcs[PART], o);

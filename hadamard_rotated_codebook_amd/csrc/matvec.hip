@@ -83,13 +83,14 @@ struct Geom {
   static constexpr int SLICE_BYTES = 64 * LANE_BYTES;            // 256, 768, 256
   static constexpr int SLICE_GROUPS = SLICE_COLS / CQ_GROUP;     // 8, 16, 4
   static constexpr int LANES_PER_GROUP = CQ_GROUP / LANE_COLS;   // 8, 4, 16
-  static constexpr int AHEAD = SB == 3 ? 8 : CQ_MV_AHEAD;        // rows of loads in flight per wave
+  // rows of loads in flight per wave (measured per width: 32 helps binary by ~4 %, not CQ2/CQ4)
+  static constexpr int AHEAD = SB == 3 ? 8 : (SB == 1 ? kRowsPerWave : CQ_MV_AHEAD);
   static constexpr int DWORDS = LANE_BYTES / 4;
   static constexpr int LOOKUPS = LANE_BYTES * 8 / IDX_BITS;     // table reads per lane and row
   static constexpr int NORM_BYTES = SLICE_GROUPS * 2;            // a row chunk's norms: 16, 32, 8 (32 at 1 bit)
   static constexpr int NORM_H = kRowsPerWave * SLICE_GROUPS / 64;  // a lane's norms of a unit: 4, 8, 2 (8)
   static_assert(LDS_BYTES == 128 * 1024, "tables fill 128 KB");
-  static_assert(kRowsPerWave % AHEAD == 0 && AHEAD < kRowsPerWave, "prefetch ring: divides the row slots");
+  static_assert(kRowsPerWave % AHEAD == 0 && AHEAD <= kRowsPerWave, "prefetch ring: divides the row slots");
 };
 
 struct MvArgs {
@@ -467,7 +468,9 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
         nv[m & 1] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(d >> (16 * (m % 2))));
       }
       if (m == 0 && lane == 0) grabbed = static_cast<uint32_t>(atomicAdd(&next_local, 1));
-      if (m + AH == kRowsPerWave) {  // the loads move on to the next unit
+      // the loads move on to the next unit (with AH = kRowsPerWave at row 0,
+      // right after the grab and after this unit's norms went to the buffer)
+      if (m + AH == kRowsPerWave) {
         un = unit_of(static_cast<int>(__builtin_amdgcn_readfirstlane(grabbed)));
         start_unit(un);
       }
