@@ -25,13 +25,18 @@ Readings (also listed in the design notes):
   those belong to the attention around the product).
 * R26 -- the value side is o_h = sum_t p[h, t] v_hat_t over the KV head's
   columns, p given.
+* R27 -- one decode attention step over the first n cached rows (the rows
+  filled so far; a full ring is every row): p[h] = softmax_t(scale *
+  scores[h, t]) for t < n, no mask, then R26's sum with that p
+  [OpenNeedle reference, attention note: softmax of the scaled scores of
+  the cached keys, then the weighted values].
 """
 
 import numpy as np
 
 from .cq import dequantize
 
-__all__ = ["kv_head_of", "kv_scores", "matvec_t", "kv_weighted_values"]
+__all__ = ["kv_head_of", "kv_scores", "matvec_t", "kv_weighted_values", "kv_attention"]
 
 
 def kv_head_of(h, n_q_heads, n_kv_heads):
@@ -74,3 +79,20 @@ def kv_weighted_values(blob, bits, tokens, n_kv_heads, head_dim, p, levels=None)
         c0 = kv_head_of(h, p.shape[0], n_kv_heads) * head_dim
         out[h] = full[h, c0:c0 + head_dim]
     return out
+
+
+def kv_attention(kblob, vblob, bits, rows, tokens, n_kv_heads, head_dim, q, scale, klevels=None, vlevels=None):
+    """One decode attention step (R27), float64 [n_q_heads, head_dim]:
+    o[h] = sum_{t < tokens} p[h, t] v_hat[t, kv(h) head columns] with p[h] the
+    softmax over t < tokens of scale * scores[h, t].  Both caches are CQ
+    matrices of ``rows`` rows (their capacity) and n_kv_heads * head_dim
+    columns at the same width ``bits``; only their first ``tokens`` rows are
+    read."""
+    if not 1 <= tokens <= rows:
+        raise ValueError("tokens must be in 1..rows")
+    s = float(scale) * kv_scores(kblob, bits, rows, n_kv_heads, head_dim, q, klevels)[:, :tokens]
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    full = np.zeros((p.shape[0], rows))
+    full[:, :tokens] = p
+    return kv_weighted_values(vblob, bits, rows, n_kv_heads, head_dim, full, vlevels)

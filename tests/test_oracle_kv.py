@@ -139,3 +139,56 @@ def test_rows_encode_independently(bits):
     for a, b in [(0, 1), (3, 11), (19, 20)]:
         part = oracle.split_blob(oracle.quantize(k[a:b], bits, levels), bits, b - a, cols)
         assert np.array_equal(part[0], whole[0][a:b]) and np.array_equal(part[1], whole[1][a:b])
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_kv_attention_by_loops(bits):
+    # the step written out: scaled scores from the loop-dequantised caches,
+    # math.exp softmax over the first `tokens` rows only, weighted value rows
+    import math
+    rows, tokens, n_kv, hd, nq, scale = 9, 6, 4, 32, 8, 0.3
+    kblob, levels, _ = _cache(66, bits, rows, n_kv * hd)
+    vblob, _, _ = _cache(67, bits, rows, n_kv * hd)
+    q = cq_inputs.activations(66, bits, nq, hd)
+    kd = _dense_by_loops(kblob, bits, rows, n_kv * hd, levels)
+    vd = _dense_by_loops(vblob, bits, rows, n_kv * hd, levels)
+    got = oracle.kv_attention(kblob, vblob, bits, rows, tokens, n_kv, hd, q, scale, levels, levels)
+    assert got.shape == (nq, hd)
+    for h in range(nq):
+        c0 = (h // (nq // n_kv)) * hd
+        z = [scale * sum(float(q[h, d]) * kd[t, c0 + d] for d in range(hd)) for t in range(tokens)]
+        zmax = max(z)
+        e = [math.exp(v - zmax) for v in z]
+        tot = sum(e)
+        for d in range(hd):
+            want = sum(e[t] / tot * vd[t, c0 + d] for t in range(tokens))
+            assert abs(got[h, d] - want) <= 1e-12 * (1 + abs(want))
+
+
+def test_kv_attention_special_cases():
+    rows, n_kv, hd, nq = 12, 2, 64, 4
+    kblob, levels, _ = _cache(68, 3, rows, n_kv * hd)
+    vblob, _, _ = _cache(69, 3, rows, n_kv * hd)
+    vd = oracle.dequantize(vblob, 3, rows, n_kv * hd, levels)
+    q = cq_inputs.activations(68, 3, nq, hd)
+    for tokens in (1, 5, rows):
+        # a zero scale (or a zero query) weighs the first `tokens` rows equally
+        flat = oracle.kv_attention(kblob, vblob, 3, rows, tokens, n_kv, hd, q, 0.0, levels, levels)
+        zq = oracle.kv_attention(kblob, vblob, 3, rows, tokens, n_kv, hd, np.zeros_like(q), 1.0, levels, levels)
+        for h in range(nq):
+            c0 = (h // 2) * hd
+            mean = vd[:tokens, c0:c0 + hd].mean(axis=0)
+            assert np.allclose(flat[h], mean, rtol=0, atol=1e-12)
+            assert np.allclose(zq[h], mean, rtol=0, atol=1e-12)
+    # one token: its value row, whatever the query
+    one = oracle.kv_attention(kblob, vblob, 3, rows, 1, n_kv, hd, q, 5.0, levels, levels)
+    for h in range(nq):
+        assert np.allclose(one[h], vd[0, (h // 2) * hd:(h // 2 + 1) * hd], rtol=0, atol=1e-12)
+    # a scale large enough for a hard maximum picks the best-scoring row
+    s = oracle.kv_scores(kblob, 3, rows, n_kv, hd, q, levels)
+    hard = oracle.kv_attention(kblob, vblob, 3, rows, rows, n_kv, hd, q, 1e6, levels, levels)
+    for h in range(nq):
+        t = int(np.argmax(s[h]))
+        assert np.allclose(hard[h], vd[t, (h // 2) * hd:(h // 2 + 1) * hd], rtol=0, atol=1e-9)
+    with pytest.raises(ValueError):
+        oracle.kv_attention(kblob, vblob, 3, rows, 0, n_kv, hd, q, 1.0, levels, levels)
