@@ -294,7 +294,8 @@ def bench_kv_attention(torch, cq, cq_inputs, gen, steps=50):
     shape: a 256-token window of keys and values (4 KV heads of 64, the ring
     full) at kv_bits 2, 3 and 4; a step appends the new token's key and value
     (cq_quantize_rows), scores 8 query heads (cq_kv_scores), softmax (torch),
-    and the weighted values (cq_matvec_t).  Per step from HIP graph replays."""
+    and the weighted values (cq_matvec_t); the fused step replaces the last
+    three with one cq_kv_attention call.  Per step from HIP graph replays."""
     dev = torch.device("cuda:0")
     out = {}
     for bits in (2, 3, 4):
@@ -309,6 +310,8 @@ def bench_kv_attention(torch, cq, cq_inputs, gen, steps=50):
         ws = torch.empty(cq.cq_kv_scores_workspace_bytes(K, 8, 4, 64) + 256, dtype=torch.uint8, device=dev)
         wt = cq.workspace_for(cq.cq_workspace_bytes(cq.OP_MATVEC_T, V, 8), dev)
 
+        of = torch.empty((8, 64), device=dev)
+
         def step(i):
             cq.cq_quantize_rows(K, kn[i:i + 1], i % 256)
             cq.cq_quantize_rows(V, vn[i:i + 1], i % 256)
@@ -316,24 +319,31 @@ def bench_kv_attention(torch, cq, cq_inputs, gen, steps=50):
             p = torch.softmax(s * 0.125, dim=1)
             cq.cq_matvec_t(V, p, out=o, workspace=wt)
 
-        for i in range(5):
-            step(i)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(steps):
-                step(i)
-        g.replay()
-        torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(5):
+        def fused(i):
+            cq.cq_quantize_rows(K, kn[i:i + 1], i % 256)
+            cq.cq_quantize_rows(V, vn[i:i + 1], i % 256)
+            cq.cq_kv_attention(K, V, q, 4, scale=0.125, out=of)
+
+        res = {"cache_bytes": 2 * K.blob.numel()}
+        for name, fn in (("graph_us_per_step", step), ("fused_graph_us_per_step", fused)):
+            for i in range(5):
+                fn(i)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    fn(i)
             g.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        out[f"kv{bits}"] = {"graph_us_per_step": t0.elapsed_time(t1) * 1e3 / (5 * steps),
-                            "cache_bytes": 2 * K.blob.numel()}
-        del g
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(5):
+                g.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            res[name] = t0.elapsed_time(t1) * 1e3 / (5 * steps)
+            del g
+        out[f"kv{bits}"] = res
     return out
 
 
@@ -513,7 +523,9 @@ def main():
         log(f"gather 2048 rows of 8192x512 CQ4: {r['kernel_median_s']*1e6:.1f} us, {r['gbs']:.0f} GB/s")
         r = bench_kv_attention(torch, cq, cq_inputs, gen)
         secondary["kv_attention_step_needle2"] = r
-        log("kv attention step: " + ", ".join(f"{k} {v['graph_us_per_step']:.1f} us" for k, v in r.items()))
+        log("kv attention step: " + ", ".join(f"{k} {v['graph_us_per_step']:.1f} us" for k, v in r.items())
+            + "; fused (append + cq_kv_attention): "
+            + ", ".join(f"{k} {v['fused_graph_us_per_step']:.1f} us" for k, v in r.items()))
         r = bench_small_and_prefill(torch, cq, cq_inputs, gen)
         secondary.update(r)
         s5 = r["matvec_cq2_512x512_b1"]

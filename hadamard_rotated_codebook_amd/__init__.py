@@ -17,6 +17,7 @@ Functions carry the C names: ``cq_blob_bytes``, ``cq_workspace_bytes``,
 ``cq_gather_rows``, ``cq_gemm``, ``cq_quantize``.
 """
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -30,7 +31,7 @@ __all__ = [
     "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_matvec_noalloc", "cq_rotate_multi_matvec",
     "cq_rotate_multi_workspace_bytes", "cq_quantize_acts_int8", "cq_matvec_w2a8_quantized", "cq_matvec_w2a8",
     "cq_gather_rows", "cq_gemm", "cq_quantize", "cq_quantize_rows", "cq_kv_scores_workspace_bytes",
-    "cq_kv_scores", "cq_matvec_t", "cq_read_probe",
+    "cq_kv_scores", "cq_matvec_t", "cq_kv_attention", "cq_read_probe",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcq.so")
@@ -76,6 +77,7 @@ _SIGS = {
     "cq_quantize_rows": (_i32, [_vp, _i64, _MP, _i64, _vp]),
     "cq_kv_scores_workspace_bytes": (_i32, [_MP, _i32, _i32, _i32, ctypes.POINTER(_u64)]),
     "cq_kv_scores": (_i32, [_MP, _vp, _i32, _i32, _i32, _vp, _vp, _u64, _vp]),
+    "cq_kv_attention": (_i32, [_MP, _MP, _i64, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp]),
     "cq_matvec_t": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_read_probe": (_i32, [_vp, _u64, _vp, _u64, _vp]),
 }
@@ -490,6 +492,28 @@ def cq_matvec_t(W, p, out=None, workspace=None):
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     m, keep = W._struct()
     _check(_lib.cq_matvec_t(ctypes.byref(m), _dev(p.contiguous(), "p"), b, _dev(out, "out"), ws, wsb, _stream()))
+    return out
+
+
+def cq_kv_attention(K, V, q, n_kv_heads, tokens=None, scale=None, out=None):
+    """One decode attention step: query heads q (float32 [n_q_heads,
+    head_dim]) against the first ``tokens`` rows (default: all) of the CQ key
+    and value caches K, V [rows, n_kv_heads * head_dim]; softmax of ``scale``
+    (default 1/sqrt(head_dim)) times the scores, then the weighted value rows.
+    Returns float32 [n_q_heads, head_dim]."""
+    if q.dtype != torch.float32 or q.dim() != 2:
+        raise ValueError("q must be float32 [n_q_heads, head_dim]")
+    nq, hd = q.shape
+    tokens = K.rows if tokens is None else int(tokens)
+    scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((nq, hd), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (nq, hd):
+        raise ValueError("out must be float32 [n_q_heads, head_dim]")
+    mk, keep_k = K._struct()
+    mv, keep_v = V._struct()
+    _check(_lib.cq_kv_attention(ctypes.byref(mk), ctypes.byref(mv), tokens, _dev(q.contiguous(), "q"), nq,
+                                n_kv_heads, hd, scale, _dev(out, "out"), _stream()))
     return out
 
 

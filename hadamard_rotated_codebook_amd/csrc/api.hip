@@ -667,6 +667,29 @@ cq_status cq_kv_scores(const cq_matrix *K, const float *q, int32_t n_q_heads, in
   return hip_status(e);
 }
 
+cq_status cq_kv_attention(const cq_matrix *K, const cq_matrix *V, int64_t n_tokens, const float *q,
+                          int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale, float *out,
+                          void *stream) {
+  cq::CodeLevels klev, vlev;
+  cq_status st = check_kv(K, n_q_heads, n_kv_heads, head_dim, &klev);
+  if (st != CQ_OK) return st;
+  if ((st = check_kv(V, n_q_heads, n_kv_heads, head_dim, &vlev)) != CQ_OK) return st;
+  if (V->bits != K->bits || V->rows != K->rows || head_dim > 128 || 128 % head_dim != 0 || n_tokens < 1 ||
+      n_tokens > K->rows || n_tokens > CQ_MAX_KV_TOKENS)
+    return CQ_ERR_SHAPE;
+  const int64_t row_bytes = padded(K->cols) * cq::storage_bits(K->bits) / 8;
+  if (n_tokens * row_bytes >= (int64_t{1} << 31)) return CQ_ERR_SHAPE;
+  if (!q || !out) return CQ_ERR_NULL;
+  if (!aligned(q, 4) || !aligned(out, 4)) return CQ_ERR_ALIGN;
+  const uint64_t qbytes = static_cast<uint64_t>(n_q_heads) * head_dim * 4;
+  if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, K->blob, K->blob_bytes) ||
+      overlaps(out, qbytes, V->blob, V->blob_bytes))
+    return CQ_ERR_OVERLAP;
+  return hip_status(cq::launch_kv_attention(static_cast<const uint8_t *>(K->blob), static_cast<const uint8_t *>(V->blob),
+                                            K->bits, K->rows, padded(K->cols), klev, vlev, n_tokens, q, n_q_heads,
+                                            n_kv_heads, head_dim, scale, out, static_cast<hipStream_t>(stream)));
+}
+
 cq_status cq_matvec_t(const cq_matrix *W, const float *p, int64_t batch, float *out, void *workspace,
                       uint64_t workspace_bytes, void *stream) {
   cq::CodeLevels lev;

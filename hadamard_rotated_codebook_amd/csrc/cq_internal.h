@@ -185,6 +185,15 @@ hipError_t launch_matvec_t(const uint8_t *blob, int bits, int64_t rows, int64_t 
                            const CodeLevels &lev, const float *p, int64_t batch, float *out, void *workspace,
                            hipStream_t s);
 
+// One decode attention step (csrc/kv.hip): per query head, softmax over the
+// first `tokens` rows of the scaled scores against K, then the weighted rows
+// of V (both caches [rows][n_kv * head_dim] at width `bits`, head_dim
+// dividing 128, tokens <= kMaxKvTokens).
+constexpr int kMaxKvTokens = 16384;
+hipError_t launch_kv_attention(const uint8_t *kblob, const uint8_t *vblob, int bits, int64_t rows, int64_t kpad,
+                               const CodeLevels &klev, const CodeLevels &vlev, int64_t tokens, const float *q,
+                               int nq, int n_kv, int head_dim, float scale, float *out, hipStream_t s);
+
 // Fills n floats with +0.0 (a kernel, so that it can sit in a captured graph).
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s);
 

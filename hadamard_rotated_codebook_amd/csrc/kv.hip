@@ -15,6 +15,10 @@
 // (OpenNeedle reference notes) sum_r p_r w_hat[r, g] = (sum_r p_r n[r, g]
 // c[q[r, g]]) . H: the kernel sums the weighted levels of the codes in the
 // rotated domain and rotates each group back once with the shared butterfly.
+//
+// Attention step (launch_kv_attention): scores, softmax and values of one
+// query head in one workgroup; a head whose width divides 128 lies inside one
+// group g of both caches, so the step needs only that group's codes and norms.
 #include "cq_decode.h"
 #include "cq_fwht.h"
 #include "cq_internal.h"
@@ -149,6 +153,239 @@ __global__ __launch_bounds__(kTThreads) void matvec_t_kernel(TArgs a) {
   }
 }
 
+// ---- one decode attention step, a workgroup per query head --------------
+
+constexpr int kAThreads = 1024;
+constexpr int kASlots = kAThreads / 4;  // tokens scored at once: 4 threads per token
+constexpr int kABlocks = 4;             // token blocks whose loads a thread has in flight
+constexpr int kAQuads = CQ_GROUP / 4;   // value side: threads per row, 4 codes each
+constexpr int kAPhases = kAThreads / kAQuads;  // row phases (32)
+constexpr int kAVRows = 8;              // rows per value batch per thread
+
+struct AArgs {
+  const uint8_t *kpacked, *vpacked;
+  const uint16_t *knorms, *vnorms;  // fp16 bits [rows][ngroups]
+  const float *q;                   // [nq][hd]
+  float *out;                       // [nq][hd]
+  int64_t row_bytes, ngroups;
+  int32_t tokens, nq, nkv, hd;
+  float scale;
+  cq::CodeLevels klev, vlev;
+};
+
+// v combined over the 64 lanes with op (every lane gets the same value: the
+// lane exchanges pair each lane with one partner per step, in a fixed order).
+template <typename Op>
+__device__ inline float wave_all(float v, Op op) {
+  v = op(v, xor_lane<1>(v));
+  v = op(v, xor_lane<2>(v));
+  v = op(v, xor_lane<4>(v));
+  v = op(v, xor_lane<8>(v));
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return v;
+}
+
+// Query head h = blockIdx.x, KV head kv(h), columns c0 .. c0 + hd - 1 of
+// group g at offset off.
+//  1. x = the query written into a zero 128-vector at off, rotated (the
+//     butterfly of cq_rotate_acts times 1/sqrt(128)).
+//  2. scores: thread (slot, quarter qj) takes codes 32 qj .. 32 qj + 31 of
+//     group g of key row t = blk * 256 + slot: sum of level(code) * x in
+//     order, the four quarters added pairwise, times float(norm) and scale
+//     (R25 by the rotated-activation identity).
+//  3. softmax weights e_t = exp(z_t - max z) and their sum S, in LDS.
+//  4. values: thread (phase ph, column j) adds e_t * (float(norm) *
+//     level(code j)) over rows t = ph, ph + 8, ... in order; the phases are
+//     added in order, the group is rotated back and scaled by 1/(sqrt(128) S);
+//     columns off .. off + hd - 1 are the head's output (R26, R27).
+template <int SB>
+__global__ __launch_bounds__(kAThreads) void kv_attention_kernel(AArgs a) {
+  __shared__ float z[cq::kMaxKvTokens];  // scaled scores, then their exp weights
+  __shared__ float xr[CQ_GROUP];
+  __shared__ float klv[16], vlv[16];
+  __shared__ float wred[kAThreads / 64];
+  __shared__ float vph[kAPhases][CQ_GROUP];
+  __shared__ float vsum[kAThreads / CQ_GROUP][CQ_GROUP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x;
+  const int c0 = (h / (a.nq / a.nkv)) * a.hd;
+  const int64_t g = c0 / CQ_GROUP;
+  const int off = c0 % CQ_GROUP;
+  const int n = a.tokens;
+
+  // The first key and value loads go out before anything waits: none of
+  // them depends on the query.
+  const __amdgpu_buffer_rsrc_t kb = buffer_rsrc(a.kpacked, static_cast<uint32_t>(n * a.row_bytes));
+  const __amdgpu_buffer_rsrc_t kn = buffer_rsrc(a.knorms, static_cast<uint32_t>(n * a.ngroups * 2));
+  const __amdgpu_buffer_rsrc_t vb = buffer_rsrc(a.vpacked, static_cast<uint32_t>(n * a.row_bytes));
+  const __amdgpu_buffer_rsrc_t vn = buffer_rsrc(a.vnorms, static_cast<uint32_t>(n * a.ngroups * 2));
+  const int qj = tid & 3, slot = tid >> 2;
+  const uint32_t qoff = static_cast<uint32_t>(g * (16 * SB) + qj * (4 * SB));
+  uint32_t d[kABlocks][SB];
+  uint16_t nn[kABlocks];
+  auto kload = [&](int b0) {
+#pragma unroll
+    for (int u = 0; u < kABlocks; ++u) {
+      const int t = b0 + u * kASlots + slot;
+      const bool live = t < n;
+      load_dwords<SB>(kb, live ? static_cast<uint32_t>(t * a.row_bytes) + qoff : 0xffff0000u, d[u]);
+      nn[u] = __builtin_amdgcn_raw_buffer_load_b16(
+          kn, live ? static_cast<uint32_t>((t * a.ngroups + g) * 2) : 0xffff0000u, 0, 0);
+    }
+  };
+  // value side: thread (phase vp, code quad vq) takes codes 4 vq .. 4 vq + 3
+  // of rows vp, vp + 32, ..., kAVRows rows per batch
+  const int vq = tid % kAQuads, vp = tid / kAQuads;
+  const uint32_t vbit = static_cast<uint32_t>(4 * SB * vq);
+  const uint32_t goff = static_cast<uint32_t>(g * (CQ_GROUP * SB / 8)) + (vbit >> 5) * 4;
+  uint32_t w0[kAVRows], w1[kAVRows];
+  uint16_t nrm[kAVRows];
+  auto vload = [&](int t0) {  // rows t0, t0 + 32, ...
+#pragma unroll
+    for (int u = 0; u < kAVRows; ++u) {
+      const int t = t0 + kAPhases * u;
+      const bool live = t < n;
+      const uint32_t o = live ? static_cast<uint32_t>(t * a.row_bytes) + goff : 0xffff0000u;
+      w0[u] = __builtin_amdgcn_raw_buffer_load_b32(vb, o, 0, 0);
+      w1[u] = SB == 3 ? __builtin_amdgcn_raw_buffer_load_b32(vb, o + 4, 0, 0) : 0u;
+      nrm[u] = __builtin_amdgcn_raw_buffer_load_b16(
+          vn, live ? static_cast<uint32_t>((t * a.ngroups + g) * 2) : 0xffff0000u, 0, 0);
+    }
+  };
+  kload(0);
+  vload(vp);
+
+  if (tid < 16) {
+    klv[tid] = a.klev.v[tid];
+    vlv[tid] = a.vlev.v[tid];
+  }
+  if (wave == 0) {  // lanes 0..15 hold elements 8 jj .. 8 jj + 7; the other rows rotate zeros
+    const int jj = lane & 15;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int dd = 8 * jj + e - off;
+      v[e] = (lane < 16 && dd >= 0 && dd < a.hd) ? a.q[static_cast<int64_t>(h) * a.hd + dd] : 0.0f;
+    }
+    fwht128_unscaled(v, jj);
+    if (lane < 16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xr[8 * jj + e] = v[e] * kInvSqrt128;
+    }
+  }
+  __syncthreads();
+
+  // ---- scores (blocks of 256 tokens; a block past the end is skipped by
+  // the whole workgroup)
+  {
+    const float *xq = xr + 32 * qj;  // read in the loop (a broadcast LDS read), not held
+    for (int b0 = 0; b0 < n; b0 += kABlocks * kASlots) {
+      if (b0 > 0) kload(b0);
+#pragma unroll
+      for (int u = 0; u < kABlocks; ++u) {
+        if (b0 + u * kASlots >= n) break;
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int bit = SB * i, w = bit / 32, sh = bit % 32;
+          uint32_t c = d[u][w] >> sh;
+          if (sh + SB > 32) c |= d[u][(w + 1) % SB] << (32 - sh);
+          part = __builtin_fmaf(klv[c & ((1u << SB) - 1)], xq[i], part);
+        }
+        part += xor_lane<1>(part);
+        part += xor_lane<2>(part);
+        const int t = b0 + u * kASlots + slot;
+        if (qj == 0 && t < n) z[t] = a.scale * (part * static_cast<float>(__builtin_bit_cast(_Float16, nn[u])));
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- softmax weights
+  float mx = -__builtin_inff();
+  for (int t = tid; t < n; t += kAThreads) mx = fmaxf(mx, z[t]);
+  mx = wave_all(mx, [](float x, float y) { return fmaxf(x, y); });
+  if (lane == 0) wred[wave] = mx;
+  __syncthreads();
+  mx = wred[0];
+#pragma unroll
+  for (int w = 1; w < kAThreads / 64; ++w) mx = fmaxf(mx, wred[w]);
+  __syncthreads();  // every wave has read wred
+  float se = 0.0f;
+  for (int t = tid; t < n; t += kAThreads) {
+    const float e = expf(z[t] - mx);
+    z[t] = e;
+    se += e;
+  }
+  se = wave_all(se, [](float x, float y) { return x + y; });
+  if (lane == 0) wred[wave] = se;
+  __syncthreads();
+  se = wred[0];
+#pragma unroll
+  for (int w = 1; w < kAThreads / 64; ++w) se += wred[w];
+
+  // ---- values: thread (phase vp, quad vq) adds e_t * (float(norm) *
+  // level(code)) for its 4 codes over rows vp, vp + 32, ... in order (a
+  // cache of up to 256 rows is one batch, loaded at the start)
+  {
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int kStep = kAPhases * kAVRows;
+    for (int t0 = vp; t0 < n; t0 += kStep) {
+      if (t0 != vp) vload(t0);
+#pragma unroll
+      for (int u = 0; u < kAVRows; ++u) {
+        const int t = t0 + kAPhases * u;
+        if (t < n) {
+          const uint64_t bits = (static_cast<uint64_t>(w1[u]) << 32 | w0[u]) >> (vbit & 31);
+          const float nv = static_cast<float>(__builtin_bit_cast(_Float16, nrm[u]));
+          const float p = z[t];
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc[c] = __builtin_fmaf(p, nv * vlv[(bits >> (SB * c)) & ((1u << SB) - 1)], acc[c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vph[vp][4 * vq + c] = acc[c];
+  }
+  __syncthreads();
+  {  // the phases in order, in two levels: 8 parts of 4 phases, then the parts
+    const int k = tid % CQ_GROUP, part = tid / CQ_GROUP;
+    float s4 = vph[4 * part][k];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) s4 += vph[4 * part + i][k];
+    vsum[part][k] = s4;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int jj = lane & 15;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float sum = vsum[0][8 * jj + e];
+#pragma unroll
+      for (int k = 1; k < kAThreads / CQ_GROUP; ++k) sum += vsum[k][8 * jj + e];
+      v[e] = sum;
+    }
+    fwht128_unscaled(v, jj);
+    const float f = kInvSqrt128 / se;
+    if (lane < 16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int dd = 8 * jj + e - off;
+        if (dd >= 0 && dd < a.hd) a.out[static_cast<int64_t>(h) * a.hd + dd] = v[e] * f;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 namespace cq {
@@ -195,6 +432,40 @@ hipError_t launch_matvec_t(const uint8_t *blob, int bits, int64_t rows, int64_t 
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nchunk <= 1) return e;
   return launch_combine(a.out, batch * cols, a.nchunk, out, s);
+}
+
+hipError_t launch_kv_attention(const uint8_t *kblob, const uint8_t *vblob, int bits, int64_t rows, int64_t kpad,
+                               const CodeLevels &klev, const CodeLevels &vlev, int64_t tokens, const float *q,
+                               int nq, int n_kv, int head_dim, float scale, float *out, hipStream_t s) {
+  const int sb = storage_bits(bits);
+  AArgs a;
+  a.row_bytes = kpad * sb / 8;
+  a.ngroups = kpad / CQ_GROUP;
+  if (tokens < 1 || tokens > kMaxKvTokens || tokens > rows || nq < 1 || n_kv < 1 || nq % n_kv != 0 ||
+      head_dim < 1 || CQ_GROUP % head_dim != 0 || kpad % CQ_GROUP != 0 ||
+      tokens * a.row_bytes >= (int64_t{1} << 31) || tokens * a.ngroups * 2 >= (int64_t{1} << 31))
+    return hipErrorInvalidValue;
+  a.kpacked = kblob;
+  a.vpacked = vblob;
+  a.knorms = reinterpret_cast<const uint16_t *>(kblob + rows * a.row_bytes);
+  a.vnorms = reinterpret_cast<const uint16_t *>(vblob + rows * a.row_bytes);
+  a.q = q;
+  a.out = out;
+  a.tokens = static_cast<int32_t>(tokens);
+  a.nq = nq;
+  a.nkv = n_kv;
+  a.hd = head_dim;
+  a.scale = scale;
+  a.klev = klev;
+  a.vlev = vlev;
+  const dim3 grid(static_cast<unsigned>(nq));
+  switch (sb) {
+    case 1: kv_attention_kernel<1><<<grid, kAThreads, 0, s>>>(a); break;
+    case 2: kv_attention_kernel<2><<<grid, kAThreads, 0, s>>>(a); break;
+    case 3: kv_attention_kernel<3><<<grid, kAThreads, 0, s>>>(a); break;
+    default: kv_attention_kernel<4><<<grid, kAThreads, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace cq

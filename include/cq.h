@@ -79,6 +79,8 @@ typedef enum cq_dtype { CQ_F32 = 0, CQ_F16 = 1, CQ_BF16 = 2 } cq_dtype;
 /* Most query heads of one cq_kv_scores call; most rows of cq_matvec_t (whose
  * packed rows must also stay below 2 GiB). */
 #define CQ_MAX_KV_HEADS 256
+/* Most cached tokens one cq_kv_attention call attends to. */
+#define CQ_MAX_KV_TOKENS 16384
 #define CQ_MAX_MATVEC_T_ROWS ((int64_t)1 << 20)
 /* Size of the static device scratch of cq_rotate_matvec_noalloc (16 MiB). */
 #define CQ_NOALLOC_SCRATCH_BYTES ((uint64_t)16 << 20)
@@ -517,6 +519,39 @@ cq_status cq_kv_scores(const cq_matrix *K, const float *q, int32_t n_q_heads, in
  */
 cq_status cq_matvec_t(const cq_matrix *W, const float *p, int64_t batch, float *out, void *workspace,
                       uint64_t workspace_bytes, void *stream);
+
+/*
+ * One decode attention step over a CQ key cache K and value cache V, both
+ * [rows][n_kv_heads * head_dim] at the same width, reading their first
+ * n_tokens rows (the rows filled so far; a full ring is every row):
+ *
+ *   out[h] = sum_{t < n_tokens} p[h][t] * v_hat[t][kv(h) * head_dim + d],
+ *   p[h]   = softmax_t(scale * scores[h][t]),   d < head_dim,
+ *
+ * scores and kv(h) as in cq_kv_scores, no mask (OpenNeedle reference notes,
+ * attention: the softmax of the scaled scores of the cached keys weighs the
+ * cached values).  One launch: each query head's workgroup rotates its
+ * zero-padded query once, scores every token on the codes of its group
+ * (fp32 sums of level * rotated query, times the fp32 norm and scale), takes
+ * the softmax in fp32 (expf; the weights' sum added in a fixed order), sums
+ * the weighted levels of the value codes in the rotated domain and rotates
+ * them back (the rotated-activation identity), as cq_matvec_t.
+ *   q        device fp32 [n_q_heads][head_dim], 4-byte aligned
+ *   head_dim divides 128 (a head lies inside one 128-group); n_q_heads a
+ *            multiple of n_kv_heads, at most CQ_MAX_KV_HEADS; n_kv_heads *
+ *            head_dim == K.cols == V.cols; K.rows == V.rows
+ *   n_tokens 1 <= n_tokens <= min(K.rows, CQ_MAX_KV_TOKENS)
+ *   scale    factor on the scores (e.g. 1/sqrt(head_dim))
+ *   out      device fp32 [n_q_heads][head_dim], 4-byte aligned, must not
+ *            overlap q or either blob; fully overwritten
+ *   Errors: the descriptor checks of cq_matvec on K and V, CQ_ERR_SHAPE for
+ *   shapes outside the above (the composed cq_kv_scores + softmax +
+ *   cq_matvec_t path takes any head_dim), CQ_ERR_NULL, CQ_ERR_ALIGN,
+ *   CQ_ERR_OVERLAP, CQ_ERR_HIP.  No workspace.
+ */
+cq_status cq_kv_attention(const cq_matrix *K, const cq_matrix *V, int64_t n_tokens, const float *q,
+                          int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale, float *out,
+                          void *stream);
 
 /*
  * Measurement helper (not part of the product): reads `bytes` bytes at p once

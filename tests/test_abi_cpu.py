@@ -32,7 +32,8 @@ def test_every_declared_symbol_is_exported():
                           "cq_rotate_multi_matvec",
                           "cq_rotate_multi_workspace_bytes", "cq_quantize_acts_int8", "cq_matvec_w2a8_quantized",
                           "cq_matvec_w2a8", "cq_gather_rows", "cq_gemm", "cq_quantize", "cq_quantize_rows",
-                          "cq_kv_scores_workspace_bytes", "cq_kv_scores", "cq_matvec_t", "cq_read_probe"}
+                          "cq_kv_scores_workspace_bytes", "cq_kv_scores", "cq_matvec_t", "cq_kv_attention",
+                          "cq_read_probe"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -566,3 +567,32 @@ def test_kv_cache_calls_validation():
                                       kw.get("wsb", 1 << 20), None)
     assert mt(b=9) == SHAPE and mt(o=0) == NULL and mt(p=0) == NULL and mt(wsb=4) == WORKSPACE
     assert mt(o=q) == OVERLAP and mt(o=sc + 2) == ALIGN
+
+
+def test_kv_attention_validation():
+    # the fused step: both caches alike, a head inside one 128-group, 1 <= n <= rows
+    K, kk = _matrix(rows=256, cols=256, blob=FAKE)
+    V, kv = _matrix(rows=256, cols=256, blob=FAKE + (1 << 32))
+    q, o = FAKE + (1 << 33), FAKE + (1 << 34)
+    lib.cq_kv_attention.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+
+    def call(k=K, v=V, n=256, qq=q, nq=8, nkv=4, hd=64, out=o):
+        return lib.cq_kv_attention(ctypes.addressof(k), ctypes.addressof(v), n, qq, nq, nkv, hd, 0.125, out, None)
+
+    for n in (0, -1, 257):
+        assert call(n=n) == SHAPE
+    assert call(nq=6) == SHAPE and call(nq=0) == SHAPE and call(nkv=0) == SHAPE and call(nq=512, nkv=4) == SHAPE
+    assert call(nkv=4, hd=32) == SHAPE  # 4 x 32 != 256 columns
+    W, kw = _matrix(rows=64, cols=96 * 2, blob=FAKE)
+    W2, kw2 = _matrix(rows=64, cols=96 * 2, blob=FAKE + (1 << 32))
+    assert call(k=W, v=W2, n=8, nq=2, nkv=2, hd=96) == SHAPE  # 96 does not divide 128
+    K3, k3 = _matrix(bits=3, rows=256, cols=256, blob=FAKE)
+    assert call(k=K3) == SHAPE  # different widths
+    K2, k2 = _matrix(rows=128, cols=256, blob=FAKE)
+    assert call(k=K2, n=100) == SHAPE  # different row counts
+    assert call(qq=0) == NULL and call(out=0) == NULL
+    assert call(qq=q + 2) == ALIGN and call(out=o + 2) == ALIGN
+    assert call(out=q) == OVERLAP and call(out=FAKE + 64) == OVERLAP and call(out=FAKE + (1 << 32) + 64) == OVERLAP
+    bad, _ = _matrix(bits=7, nbytes=0, levels=None)
+    assert call(k=bad) == BITS

@@ -168,3 +168,59 @@ def test_decode_attention_step(kv_bits):
         c0 = oracle.kv_head_of(h, nq, nkv) * hd
         got = o[h, c0:c0 + hd].astype(np.float64)
         assert np.max(np.abs(got - oref[h])) <= 1e-4 * np.max(np.abs(oref[h])) + 1e-6, h
+
+
+@pytest.mark.parametrize("bits,rows,tokens,nq,nkv,hd", [
+    (2, 256, 256, 8, 4, 64),      # Needle 2 geometry, ring full
+    (3, 256, 256, 8, 4, 64),
+    (4, 256, 256, 8, 4, 64),
+    (5, 256, 100, 8, 4, 64),      # ternary, partly filled
+    (1, 256, 256, 8, 4, 64),      # binary
+    (4, 3000, 2500, 4, 2, 128),   # several token blocks per workgroup, one head per group
+    (2, 640, 1, 16, 8, 32),       # one token; four heads per group
+    (3, 1100, 1027, 6, 3, 16),    # ragged block tails, eight heads per group
+])
+def test_kv_attention_against_oracle(bits, rows, tokens, nq, nkv, hd):
+    # the fused step (scores, softmax, values in one launch) against the
+    # oracle's step on the same blobs, and against the composed calls
+    say("kv attention", bits, rows, tokens, nq, nkv, hd)
+    cols = nkv * hd
+    lv = _levels(bits)
+    K = cq.cq_quantize(torch.from_numpy(cq_inputs.master(80, bits, rows, cols, sigma=1.0)).to(DEV), bits, lv)
+    V = cq.cq_quantize(torch.from_numpy(cq_inputs.master(81, bits, rows, cols, sigma=1.0)).to(DEV), bits, lv)
+    q = cq_inputs.activations(82, bits, nq, hd)
+    scale = 1.0 / np.sqrt(hd)
+    got = cq.cq_kv_attention(K, V, torch.from_numpy(q).to(DEV), nkv, tokens=tokens, scale=scale).cpu().numpy()
+    kb, vb = K.blob.cpu().numpy(), V.blob.cpu().numpy()
+    ref = oracle.kv_attention(kb, vb, bits, rows, tokens, nkv, hd, q, scale, lv, lv)
+    for h in range(nq):
+        err = np.max(np.abs(got[h].astype(np.float64) - ref[h]))
+        assert err <= 1e-4 * np.max(np.abs(ref[h])) + 1e-6, (h, err)
+    # the composed path (cq_kv_scores, softmax, cq_matvec_t) agrees too
+    s = cq.cq_kv_scores(K, torch.from_numpy(q).to(DEV), nkv)[:, :tokens]
+    p = torch.zeros((nq, rows), device=DEV)
+    p[:, :tokens] = torch.softmax(s * scale, dim=1)
+    o = torch.cat([cq.cq_matvec_t(V, p[b:b + 8]) for b in range(0, nq, 8)]).cpu().numpy()  # batches of 8
+    for h in range(nq):
+        c0 = oracle.kv_head_of(h, nq, nkv) * hd
+        assert np.max(np.abs(got[h] - o[h, c0:c0 + hd])) <= 2e-4 * np.max(np.abs(ref[h])) + 1e-6, h
+
+
+def test_kv_attention_special_inputs():
+    # a zero query weighs the rows equally (the mean of the value rows), and
+    # a repeated call gives the same bytes
+    bits, rows, nq, nkv, hd = 2, 512, 8, 4, 64
+    lv = _levels(bits)
+    K = cq.cq_quantize(torch.from_numpy(cq_inputs.master(83, bits, rows, nkv * hd, sigma=1.0)).to(DEV), bits, lv)
+    V = cq.cq_quantize(torch.from_numpy(cq_inputs.master(84, bits, rows, nkv * hd, sigma=1.0)).to(DEV), bits, lv)
+    z = torch.zeros((nq, hd), device=DEV)
+    got = cq.cq_kv_attention(K, V, z, nkv, tokens=300).cpu().numpy()
+    vd = oracle.dequantize(V.blob.cpu().numpy(), bits, rows, nkv * hd, lv)
+    for h in range(nq):
+        c0 = (h // 2) * hd
+        mean = vd[:300, c0:c0 + hd].mean(axis=0)
+        assert np.max(np.abs(got[h] - mean)) <= 1e-4 * np.max(np.abs(mean)) + 1e-6, h
+    q = torch.from_numpy(cq_inputs.activations(85, bits, nq, hd)).to(DEV)
+    a = cq.cq_kv_attention(K, V, q, nkv)
+    b = cq.cq_kv_attention(K, V, q, nkv)
+    assert torch.equal(a, b)
