@@ -294,8 +294,9 @@ def bench_kv_attention(torch, cq, cq_inputs, gen, steps=50):
     shape: a 256-token window of keys and values (4 KV heads of 64, the ring
     full) at kv_bits 2, 3 and 4; a step appends the new token's key and value
     (cq_quantize_rows), scores 8 query heads (cq_kv_scores), softmax (torch),
-    and the weighted values (cq_matvec_t); the fused step replaces the last
-    three with one cq_kv_attention call.  Per step from HIP graph replays."""
+    and the weighted values (cq_matvec_t); the fused step is one cq_kv_append
+    (both appends in one launch) and one cq_kv_attention.  Per step from HIP
+    graph replays."""
     dev = torch.device("cuda:0")
     out = {}
     for bits in (2, 3, 4):
@@ -320,8 +321,7 @@ def bench_kv_attention(torch, cq, cq_inputs, gen, steps=50):
             cq.cq_matvec_t(V, p, out=o, workspace=wt)
 
         def fused(i):
-            cq.cq_quantize_rows(K, kn[i:i + 1], i % 256)
-            cq.cq_quantize_rows(V, vn[i:i + 1], i % 256)
+            cq.cq_kv_append(K, V, kn[i:i + 1], vn[i:i + 1], i % 256)
             cq.cq_kv_attention(K, V, q, 4, scale=0.125, out=of)
 
         res = {"cache_bytes": 2 * K.blob.numel()}
@@ -524,7 +524,7 @@ def main():
         r = bench_kv_attention(torch, cq, cq_inputs, gen)
         secondary["kv_attention_step_needle2"] = r
         log("kv attention step: " + ", ".join(f"{k} {v['graph_us_per_step']:.1f} us" for k, v in r.items())
-            + "; fused (append + cq_kv_attention): "
+            + "; fused (cq_kv_append + cq_kv_attention): "
             + ", ".join(f"{k} {v['fused_graph_us_per_step']:.1f} us" for k, v in r.items()))
         r = bench_small_and_prefill(torch, cq, cq_inputs, gen)
         secondary.update(r)

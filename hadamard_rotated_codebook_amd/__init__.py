@@ -31,7 +31,7 @@ __all__ = [
     "cq_rotate_acts", "cq_matvec", "cq_rotate_matvec", "cq_rotate_matvec_noalloc", "cq_rotate_multi_matvec",
     "cq_rotate_multi_workspace_bytes", "cq_quantize_acts_int8", "cq_matvec_w2a8_quantized", "cq_matvec_w2a8",
     "cq_gather_rows", "cq_gemm", "cq_quantize", "cq_quantize_rows", "cq_kv_scores_workspace_bytes",
-    "cq_kv_scores", "cq_matvec_t", "cq_kv_attention", "cq_read_probe",
+    "cq_kv_scores", "cq_matvec_t", "cq_kv_append", "cq_kv_attention", "cq_read_probe",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcq.so")
@@ -78,6 +78,7 @@ _SIGS = {
     "cq_kv_scores_workspace_bytes": (_i32, [_MP, _i32, _i32, _i32, ctypes.POINTER(_u64)]),
     "cq_kv_scores": (_i32, [_MP, _vp, _i32, _i32, _i32, _vp, _vp, _u64, _vp]),
     "cq_kv_attention": (_i32, [_MP, _MP, _i64, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp]),
+    "cq_kv_append": (_i32, [_MP, _MP, _vp, _vp, _i64, _i64, _vp]),
     "cq_matvec_t": (_i32, [_MP, _vp, _i64, _vp, _vp, _u64, _vp]),
     "cq_read_probe": (_i32, [_vp, _u64, _vp, _u64, _vp]),
 }
@@ -493,6 +494,22 @@ def cq_matvec_t(W, p, out=None, workspace=None):
     m, keep = W._struct()
     _check(_lib.cq_matvec_t(ctypes.byref(m), _dev(p.contiguous(), "p"), b, _dev(out, "out"), ws, wsb, _stream()))
     return out
+
+
+def cq_kv_append(K, V, k, v, row0):
+    """Append n new tokens' keys k and values v (float32 [n, cols]) to the CQ
+    caches K and V at rows row0 .. row0 + n - 1 (one launch when they share
+    the code book).  Returns (K, V)."""
+    for name, t, M in (("k", k, K), ("v", v, V)):
+        if t.dtype != torch.float32 or t.dim() != 2 or t.shape[1] != M.cols:
+            raise ValueError(f"{name} must be float32 [n, cols]")
+    if k.shape[0] != v.shape[0]:
+        raise ValueError("k and v must hold the same number of rows")
+    mk, keep_k = K._struct()
+    mv, keep_v = V._struct()
+    _check(_lib.cq_kv_append(ctypes.byref(mk), ctypes.byref(mv), _dev(k.contiguous(), "k"), _dev(v.contiguous(), "v"),
+                             k.shape[0], row0, _stream()))
+    return K, V
 
 
 def cq_kv_attention(K, V, q, n_kv_heads, tokens=None, scale=None, out=None):

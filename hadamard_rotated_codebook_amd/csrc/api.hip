@@ -573,8 +573,8 @@ cq_status cq_quantize(const float *w, int64_t rows, int64_t cols, int32_t bits, 
   const int64_t kpad = padded(cols);
   uint8_t *packed = static_cast<uint8_t *>(blob);
   uint16_t *norms = reinterpret_cast<uint16_t *>(packed + rows * (kpad * cq::storage_bits(bits) / 8));
-  return hip_status(cq::launch_quantize(w, rows, cols, kpad, bits, tab, packed, norms,
-                                        static_cast<hipStream_t>(stream)));
+  const cq::QuantizeJob job{w, rows, cols, kpad, packed, norms};
+  return hip_status(cq::launch_quantize(job, nullptr, tab, bits, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"
@@ -595,8 +595,9 @@ cq_status cq_quantize_rows(const float *w, int64_t n, const cq_matrix *dst, int6
   uint8_t *blob = static_cast<uint8_t *>(const_cast<void *>(dst->blob));
   uint8_t *packed = blob + row0 * row_bytes;
   uint16_t *norms = reinterpret_cast<uint16_t *>(blob + dst->rows * row_bytes) + row0 * (kpad / CQ_GROUP);
-  return hip_status(cq::launch_quantize(w, n, dst->cols, kpad, dst->bits, encode_table(dst->bits, dst->levels),
-                                        packed, norms, static_cast<hipStream_t>(stream)));
+  const cq::QuantizeJob job{w, n, dst->cols, kpad, packed, norms};
+  return hip_status(cq::launch_quantize(job, nullptr, encode_table(dst->bits, dst->levels), dst->bits,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"
@@ -664,6 +665,42 @@ cq_status cq_kv_scores(const cq_matrix *K, const float *q, int32_t n_q_heads, in
                                  x + static_cast<int64_t>(h0) * K->cols, K->cols, b,
                                  scores + static_cast<int64_t>(h0) * K->rows, need_ws ? ws : nullptr, s);
   }
+  return hip_status(e);
+}
+
+cq_status cq_kv_append(const cq_matrix *K, const cq_matrix *V, const float *k, const float *v, int64_t n,
+                       int64_t row0, void *stream) {
+  cq::CodeLevels klev, vlev;
+  cq_status st = check_matrix(K, &klev);
+  if (st != CQ_OK) return st;
+  if ((st = check_matrix(V, &vlev)) != CQ_OK) return st;
+  if (V->bits != K->bits) return CQ_ERR_SHAPE;
+  if (n < 0 || row0 < 0 || n > K->rows || row0 > K->rows - n || n > V->rows || row0 > V->rows - n)
+    return CQ_ERR_SHAPE;
+  if (n == 0) return CQ_OK;
+  if (!k || !v) return CQ_ERR_NULL;
+  if (!aligned(k, 4) || !aligned(v, 4)) return CQ_ERR_ALIGN;
+  if (overlaps(K->blob, K->blob_bytes, V->blob, V->blob_bytes) ||
+      overlaps(K->blob, K->blob_bytes, k, static_cast<uint64_t>(n) * K->cols * 4) ||
+      overlaps(K->blob, K->blob_bytes, v, static_cast<uint64_t>(n) * V->cols * 4) ||
+      overlaps(V->blob, V->blob_bytes, k, static_cast<uint64_t>(n) * K->cols * 4) ||
+      overlaps(V->blob, V->blob_bytes, v, static_cast<uint64_t>(n) * V->cols * 4))
+    return CQ_ERR_OVERLAP;
+  auto job = [&](const cq_matrix *M, const float *w) {
+    const int64_t kpad = padded(M->cols);
+    const int64_t row_bytes = kpad * cq::storage_bits(M->bits) / 8;
+    uint8_t *blob = static_cast<uint8_t *>(const_cast<void *>(M->blob));
+    return cq::QuantizeJob{w, n, M->cols, kpad, blob + row0 * row_bytes,
+                           reinterpret_cast<uint16_t *>(blob + M->rows * row_bytes) + row0 * (kpad / CQ_GROUP)};
+  };
+  const cq::QuantizeJob jk = job(K, k), jv = job(V, v);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool same_book = std::memcmp(&klev, &vlev, sizeof klev) == 0;
+  if (same_book && K->cols > 0 && V->cols > 0)
+    return hip_status(cq::launch_quantize(jk, &jv, encode_table(K->bits, K->levels), K->bits, s));
+  hipError_t e = K->cols > 0 ? cq::launch_quantize(jk, nullptr, encode_table(K->bits, K->levels), K->bits, s)
+                             : hipSuccess;
+  if (e == hipSuccess && V->cols > 0) e = cq::launch_quantize(jv, nullptr, encode_table(V->bits, V->levels), V->bits, s);
   return hip_status(e);
 }
 

@@ -170,10 +170,16 @@ hipError_t launch_combine(const float *partial, int64_t n, int nslice, float *y,
 hipError_t launch_gemm(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
                        const CodeLevels &lev, const void *xr, int64_t m, float *c, hipStream_t s);
 
-// Encodes rows x cols of w into the codes at packed (rows of kpad * b' / 8
-// bytes) and the fp16 norms at norms ([rows][kpad / 128]).
-hipError_t launch_quantize(const float *w, int64_t rows, int64_t cols, int64_t kpad, int bits,
-                           const EncodeTable &tab, uint8_t *packed, uint16_t *norms, hipStream_t s);
+// Encoding job: rows x cols of w into the codes at packed (rows of kpad * b'
+// / 8 bytes) and the fp16 norms at norms ([rows][kpad / 128]).
+struct QuantizeJob {
+  const float *w;
+  int64_t rows, cols, kpad;
+  uint8_t *packed;
+  uint16_t *norms;
+};
+// Encodes job a, and job b if not null, in one launch with one code book.
+hipError_t launch_quantize(const QuantizeJob &a, const QuantizeJob *b, const EncodeTable &tab, int bits, hipStream_t s);
 
 // KV-cache products (csrc/kv.hip).  Query padding: x[h][c] = q[h][c - c0(h)]
 // for c in the columns of query head h's KV head, 0 elsewhere (x [nq][cols]).

@@ -20,6 +20,8 @@
 //   fp32 threshold per bucket, the same decisions) or, for binary, ternary
 //   and code books whose thresholds are too close for the buckets, as a
 //   count of the midpoints.
+#include <algorithm>
+
 #include "cq_fwht.h"
 #include "cq_internal.h"
 
@@ -51,14 +53,22 @@ __device__ inline void lane_stage_f64(double (&t)[kPer], int j) {
   for (int i = 0; i < kPer; ++i) t[i] = __builtin_fma(t[i], sgn, xor_lane_f64<D>(t[i]));
 }
 
-// packed: the first output row's codes (rows of kpad * SB / 8 bytes follow);
-// norms: its fp16 norms (rows of kpad / 128 follow) -- the rows of a whole
-// blob, or a row range of a larger one.  16-byte aligned (blob layout).
+// Job blockIdx.y of one launch (a launch may encode two matrices' rows with
+// one code book, e.g. a new key and value row of a KV cache): job.packed is the first output
+// row's codes (rows of kpad * SB / 8 bytes follow), job.norms its fp16 norms
+// (rows of kpad / 128 follow) -- the rows of a whole blob, or a row range of
+// a larger one.  16-byte aligned (blob layout).
+// Both jobs use the one code book of `tab` (a by-value table chosen per
+// block would be copied to scratch).
 template <int SB, bool VEC, bool LUT>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(const float *__restrict__ w, int64_t rows,
-                                                           int64_t cols, int64_t kpad, cq::EncodeTable tab,
-                                                           uint8_t *__restrict__ packed,
-                                                           uint16_t *__restrict__ norms) {
+__global__ __launch_bounds__(kThreads) void quantize_kernel(cq::QuantizeJob j0, cq::QuantizeJob j1,
+                                                           cq::EncodeTable tab) {
+  const bool second = blockIdx.y != 0;
+  const float *__restrict__ w = second ? j1.w : j0.w;
+  const int64_t rows = second ? j1.rows : j0.rows, cols = second ? j1.cols : j0.cols;
+  const int64_t kpad = second ? j1.kpad : j0.kpad;
+  uint8_t *__restrict__ packed = second ? j1.packed : j0.packed;
+  uint16_t *__restrict__ norms = second ? j1.norms : j0.norms;
   __shared__ float lut_thr[cq::kLutBuckets];
   __shared__ int32_t lut_base[cq::kLutBuckets];
   if constexpr (LUT) {
@@ -197,23 +207,29 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const float *__restr
 }
 
 template <int SB>
-hipError_t launch_sb(const float *w, int64_t rows, int64_t cols, int64_t kpad, const cq::EncodeTable &tab,
-                     uint8_t *packed, uint16_t *norms, hipStream_t s) {
-  const int64_t groups = rows * (kpad / CQ_GROUP);
-  const int64_t blocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
+hipError_t launch_sb(const cq::QuantizeJob &a, const cq::QuantizeJob *b, const cq::EncodeTable &tab, hipStream_t s) {
+  auto blocks_of = [](const cq::QuantizeJob &j) {
+    return (j.rows * (j.kpad / CQ_GROUP) + kGroupsPerBlock - 1) / kGroupsPerBlock;
+  };
+  auto vec_of = [](const cq::QuantizeJob &j) {
+    return (j.cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(j.w) & 15) == 0);
+  };
+  const int64_t blocks = b ? std::max(blocks_of(a), blocks_of(*b)) : blocks_of(a);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const bool vec = (cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0);
-  const dim3 grid(static_cast<unsigned>(blocks));
+  if (blocks == 0) return hipSuccess;
+  const bool vec = vec_of(a) && (!b || vec_of(*b));
+  const dim3 grid(static_cast<unsigned>(blocks), b ? 2u : 1u);
+  const cq::QuantizeJob &jb = b ? *b : a;
   if (tab.lut) {
     if (vec)
-      quantize_kernel<SB, true, true><<<grid, kThreads, 0, s>>>(w, rows, cols, kpad, tab, packed, norms);
+      quantize_kernel<SB, true, true><<<grid, kThreads, 0, s>>>(a, jb, tab);
     else
-      quantize_kernel<SB, false, true><<<grid, kThreads, 0, s>>>(w, rows, cols, kpad, tab, packed, norms);
+      quantize_kernel<SB, false, true><<<grid, kThreads, 0, s>>>(a, jb, tab);
   } else {
     if (vec)
-      quantize_kernel<SB, true, false><<<grid, kThreads, 0, s>>>(w, rows, cols, kpad, tab, packed, norms);
+      quantize_kernel<SB, true, false><<<grid, kThreads, 0, s>>>(a, jb, tab);
     else
-      quantize_kernel<SB, false, false><<<grid, kThreads, 0, s>>>(w, rows, cols, kpad, tab, packed, norms);
+      quantize_kernel<SB, false, false><<<grid, kThreads, 0, s>>>(a, jb, tab);
   }
   return hipGetLastError();
 }
@@ -222,13 +238,12 @@ hipError_t launch_sb(const float *w, int64_t rows, int64_t cols, int64_t kpad, c
 
 namespace cq {
 
-hipError_t launch_quantize(const float *w, int64_t rows, int64_t cols, int64_t kpad, int bits,
-                           const EncodeTable &tab, uint8_t *packed, uint16_t *norms, hipStream_t s) {
+hipError_t launch_quantize(const QuantizeJob &a, const QuantizeJob *b, const EncodeTable &tab, int bits, hipStream_t s) {
   switch (storage_bits(bits)) {
-    case 1: return launch_sb<1>(w, rows, cols, kpad, tab, packed, norms, s);
-    case 2: return launch_sb<2>(w, rows, cols, kpad, tab, packed, norms, s);
-    case 3: return launch_sb<3>(w, rows, cols, kpad, tab, packed, norms, s);
-    default: return launch_sb<4>(w, rows, cols, kpad, tab, packed, norms, s);
+    case 1: return launch_sb<1>(a, b, tab, s);
+    case 2: return launch_sb<2>(a, b, tab, s);
+    case 3: return launch_sb<3>(a, b, tab, s);
+    default: return launch_sb<4>(a, b, tab, s);
   }
 }
 

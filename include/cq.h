@@ -521,6 +521,19 @@ cq_status cq_matvec_t(const cq_matrix *W, const float *p, int64_t batch, float *
                       uint64_t workspace_bytes, void *stream);
 
 /*
+ * The append of n new tokens to a key cache K and a value cache V at once:
+ * k (fp32 [n][K.cols]) into rows row0 .. row0 + n - 1 of K and v (fp32
+ * [n][V.cols]) into the same rows of V, each exactly as cq_quantize_rows
+ * encodes them, in one launch when K and V share the code book (same width
+ * and levels; else one launch each).
+ *   Errors: those of cq_quantize_rows on either cache; CQ_ERR_SHAPE when
+ *   the widths differ or the rows do not fit either cache; CQ_ERR_OVERLAP
+ *   when the blobs overlap each other or an input.
+ */
+cq_status cq_kv_append(const cq_matrix *K, const cq_matrix *V, const float *k, const float *v, int64_t n,
+                       int64_t row0, void *stream);
+
+/*
  * One decode attention step over a CQ key cache K and value cache V, both
  * [rows][n_kv_heads * head_dim] at the same width, reading their first
  * n_tokens rows (the rows filled so far; a full ring is every row):

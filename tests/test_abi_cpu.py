@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
                           "cq_rotate_multi_matvec",
                           "cq_rotate_multi_workspace_bytes", "cq_quantize_acts_int8", "cq_matvec_w2a8_quantized",
                           "cq_matvec_w2a8", "cq_gather_rows", "cq_gemm", "cq_quantize", "cq_quantize_rows",
-                          "cq_kv_scores_workspace_bytes", "cq_kv_scores", "cq_matvec_t", "cq_kv_attention",
+                          "cq_kv_scores_workspace_bytes", "cq_kv_scores", "cq_matvec_t", "cq_kv_append", "cq_kv_attention",
                           "cq_read_probe"}
     for n in names:
         assert hasattr(lib, n), n
@@ -596,3 +596,28 @@ def test_kv_attention_validation():
     assert call(out=q) == OVERLAP and call(out=FAKE + 64) == OVERLAP and call(out=FAKE + (1 << 32) + 64) == OVERLAP
     bad, _ = _matrix(bits=7, nbytes=0, levels=None)
     assert call(k=bad) == BITS
+
+
+def test_kv_append_validation():
+    K, kk = _matrix(rows=256, cols=256, blob=FAKE)
+    V, kv = _matrix(rows=256, cols=256, blob=FAKE + (1 << 32))
+    k, v = FAKE + (1 << 33), FAKE + (1 << 34)
+    lib.cq_kv_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_void_p]
+
+    def call(kk_=K, vv=V, ka=k, va=v, n=1, row0=0):
+        return lib.cq_kv_append(ctypes.addressof(kk_), ctypes.addressof(vv), ka, va, n, row0, None)
+
+    assert call(n=0, row0=256) == OK  # nothing to do
+    assert call(row0=256) == SHAPE and call(n=2, row0=255) == SHAPE and call(n=-1) == SHAPE and call(row0=-1) == SHAPE
+    V3, k3 = _matrix(bits=3, rows=256, cols=256, blob=FAKE + (1 << 32))
+    assert call(vv=V3) == SHAPE  # widths differ
+    Vs, ks = _matrix(rows=100, cols=256, blob=FAKE + (1 << 32))
+    assert call(vv=Vs, row0=100) == SHAPE  # does not fit the smaller cache
+    assert call(ka=0) == NULL and call(va=0) == NULL
+    assert call(ka=k + 2) == ALIGN and call(va=v + 2) == ALIGN
+    Vo, ko = _matrix(rows=256, cols=256, blob=FAKE + 64)
+    assert call(vv=Vo) == OVERLAP  # the two blobs overlap
+    assert call(ka=FAKE + 128) == OVERLAP and call(va=FAKE + (1 << 32) + 128) == OVERLAP
+    bad, _ = _matrix(bits=7, nbytes=0, levels=None)
+    assert call(kk_=bad) == BITS

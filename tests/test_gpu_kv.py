@@ -224,3 +224,48 @@ def test_kv_attention_special_inputs():
     a = cq.cq_kv_attention(K, V, q, nkv)
     b = cq.cq_kv_attention(K, V, q, nkv)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 1])
+def test_kv_append_equals_two_row_appends(bits):
+    # the joint append (one launch) writes exactly what two cq_quantize_rows
+    # calls write, across the ring's wrap; caches of different widths too
+    say("kv joint append", bits)
+    rows, kc, vc = 256, 256, 384
+    lv = _levels(bits)
+    K1, V1, K2, V2 = _empty(bits, rows, kc), _empty(bits, rows, vc), _empty(bits, rows, kc), _empty(bits, rows, vc)
+    kk = torch.from_numpy(cq_inputs.master(86, bits, 300, kc, sigma=1.0)).to(DEV)
+    vv = torch.from_numpy(cq_inputs.master(87, bits, 300, vc, sigma=1.0)).to(DEV)
+    pos = 0
+    for n in (1, 60, 3, 150, 86):  # 300 tokens
+        a = pos % rows
+        first = min(n, rows - a)
+        cq.cq_kv_append(K1, V1, kk[pos:pos + first], vv[pos:pos + first], a)
+        cq.cq_quantize_rows(K2, kk[pos:pos + first], a)
+        cq.cq_quantize_rows(V2, vv[pos:pos + first], a)
+        if first < n:
+            cq.cq_kv_append(K1, V1, kk[pos + first:pos + n], vv[pos + first:pos + n], 0)
+            cq.cq_quantize_rows(K2, kk[pos + first:pos + n], 0)
+            cq.cq_quantize_rows(V2, vv[pos + first:pos + n], 0)
+        pos += n
+    torch.cuda.synchronize()
+    assert torch.equal(K1.blob, K2.blob) and torch.equal(V1.blob, V2.blob)
+
+
+def test_kv_append_with_two_code_books():
+    # different levels for keys and values: one launch each, same bytes as
+    # the row appends
+    rows, cols = 64, 256
+    lk = cq_inputs.codebook(2)
+    lvv = (lk * np.float32(1.5)).astype(np.float32)
+    K1 = cq.CQMatrix(2, rows, cols, torch.zeros(cq.cq_blob_bytes(2, rows, cols), dtype=torch.uint8, device=DEV), lk)
+    V1 = cq.CQMatrix(2, rows, cols, torch.zeros(cq.cq_blob_bytes(2, rows, cols), dtype=torch.uint8, device=DEV), lvv)
+    K2 = cq.CQMatrix(2, rows, cols, torch.zeros_like(K1.blob), lk)
+    V2 = cq.CQMatrix(2, rows, cols, torch.zeros_like(V1.blob), lvv)
+    kk = torch.from_numpy(cq_inputs.master(88, 2, 10, cols, sigma=1.0)).to(DEV)
+    vv = torch.from_numpy(cq_inputs.master(89, 2, 10, cols, sigma=1.0)).to(DEV)
+    cq.cq_kv_append(K1, V1, kk, vv, 7)
+    cq.cq_quantize_rows(K2, kk, 7)
+    cq.cq_quantize_rows(V2, vv, 7)
+    torch.cuda.synchronize()
+    assert torch.equal(K1.blob, K2.blob) and torch.equal(V1.blob, V2.blob)
