@@ -3,8 +3,9 @@
 // elements.  Stages of element distance 1, 2, 4 run inside a lane; distances
 // 8..64 are lane distances 1..8, exchanged with DPP ("cact-format" post, "How
 // the kernel reads it": a fast Walsh-Hadamard butterfly per group).  Every
-// kernel that rotates uses this one routine, so they all produce the same
-// fp32 values.
+// kernel that rotates activations (or rotates sums back) uses this one
+// routine, so they all produce the same fp32 values; the encoder rotates
+// weights in double with a butterfly of its own (quantize.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
