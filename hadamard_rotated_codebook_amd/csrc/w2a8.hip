@@ -197,15 +197,52 @@ __device__ inline void to_slot_order(const uint4 *src, uint4 *dst) {
 
 // The quantised activation into LDS: xq [batch][kpad] in slot order and the
 // scales at sxs[g * 8 + b].  All threads of the workgroup call it.
-template <int SB, int NT>
+// Bit planes of a 32-code binary block (two uint4 of int8 in column order):
+// plane p (dword p of the output) has bit i = bit p of activation i, so that
+// sum_i bit_i * x_i = sum_p (p < 7 ? 2^p : -2^7) * popcount(bits & plane_p).
+// Each 8 bytes are one 8 x 8 bit transpose (three delta swaps: byte p of the
+// result holds bit p of bytes 0..7).
+__device__ inline uint64_t transpose8x8(uint64_t x) {
+  uint64_t t = (x ^ (x >> 7)) & 0x00AA00AA00AA00AAull;
+  x = x ^ t ^ (t << 7);
+  t = (x ^ (x >> 14)) & 0x0000CCCC0000CCCCull;
+  x = x ^ t ^ (t << 14);
+  t = (x ^ (x >> 28)) & 0x00000000F0F0F0F0ull;
+  return x ^ t ^ (t << 28);
+}
+__device__ inline void to_planes(const uint4 *src, uint4 *dst) {
+  const uint4 lo = src[0], hi = src[1];
+  const uint64_t w[4] = {lo.x | static_cast<uint64_t>(lo.y) << 32, lo.z | static_cast<uint64_t>(lo.w) << 32,
+                         hi.x | static_cast<uint64_t>(hi.y) << 32, hi.z | static_cast<uint64_t>(hi.w) << 32};
+  uint64_t t[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) t[a] = transpose8x8(w[a]);
+  uint32_t pl[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {  // byte a of plane q: byte q of t[a]
+    pl[q] = 0u;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) pl[q] |= static_cast<uint32_t>((t[a] >> (8 * q)) & 0xffu) << (8 * a);
+  }
+  dst[0] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+  dst[1] = make_uint4(pl[4], pl[5], pl[6], pl[7]);
+}
+
+template <int SB, int NT, bool PLANES = false>
 __device__ inline void fill_int8(const int8_t *xq, const float *sx, int batch, int ngroups, uint8_t *lxq,
                                  float *sxs) {
+  static_assert(!PLANES || SB == 1, "bit planes: binary blocks");
   const int tid = threadIdx.x;
   constexpr int Q = slot_block<SB>() / 16;  // uint4 per decoder block
   const int blocks = batch * ngroups * (CQ_GROUP / slot_block<SB>());
   const uint4 *src = reinterpret_cast<const uint4 *>(xq);
   uint4 *dst = reinterpret_cast<uint4 *>(lxq);
-  for (int t = tid; t < blocks; t += NT) to_slot_order<SB>(src + Q * t, dst + Q * t);
+  for (int t = tid; t < blocks; t += NT) {
+    if constexpr (PLANES)
+      to_planes(src + Q * t, dst + Q * t);
+    else
+      to_slot_order<SB>(src + Q * t, dst + Q * t);
+  }
   for (int t = tid; t < batch * ngroups; t += NT) {
     const int b = t / ngroups, g = t - b * ngroups;
     sxs[g * 8 + b] = sx[t];
@@ -415,7 +452,11 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
   const int s_begin = static_cast<int>(blockIdx.x) * spw;
   const int s_end = min(s_begin + spw, a.nsteps);
   if (tid == 0) next_step = s_begin;
-  fill_int8<SB, kRowThreads>(a.xq, a.sx, B, ngroups, xq, sxs);
+  // Binary at batch 1 with the activations in registers: the lane holds the
+  // activations' bit planes instead of their bytes (the same 32 dwords per
+  // piece), and a group's masked sum is 32 popcounts of code & plane.
+  constexpr bool PLANES = SB == 1 && XREG && B == 1;
+  fill_int8<SB, kRowThreads, PLANES>(a.xq, a.sx, B, ngroups, xq, sxs);
   __syncthreads();
 
   const int lps = a.lpr_shift, lpr = 1 << lps, li = lane & (lpr - 1), rsub = lane >> lps;
@@ -449,14 +490,29 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
   constexpr bool MASKED = SB == 1 && XREG;
   const int c0 = static_cast<int8_t>(tab[0] & 0xffu), dc = static_cast<int8_t>((tab[0] >> 8) & 0xffu) - c0;
   int xsum[MASKED ? B : 1][MASKED ? NPL : 1];
+  // sum_p (p < 7 ? 2^p : -2^7) * cnt[p]: the signed int8 sum the planes encode
+  auto plane_sum = [](const int (&cnt)[8]) {
+    int v = -(cnt[7] << 7);
+#pragma unroll
+    for (int q = 0; q < 7; ++q) v += cnt[q] << q;
+    return v;
+  };
   if constexpr (MASKED) {
 #pragma unroll
     for (int b = 0; b < B; ++b)
 #pragma unroll
       for (int i = 0; i < NPL; ++i) {
         int t = 0;
+        if constexpr (PLANES) {
+          int cnt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int w = 0; w < G::XDW; ++w) t = __builtin_amdgcn_sdot4(0x01010101, static_cast<int>(xr8[b][i][w]), t, false);
+          for (int w = 0; w < G::XDW; ++w) cnt[w & 7] += __builtin_popcount(xr8[b][i][w]);
+          t = plane_sum(cnt);
+        } else {
+#pragma unroll
+          for (int w = 0; w < G::XDW; ++w)
+            t = __builtin_amdgcn_sdot4(0x01010101, static_cast<int>(xr8[b][i][w]), t, false);
+        }
         xsum[b][i] = t;
       }
   }
@@ -501,7 +557,9 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
       if (i >= a.npl) break;  // uniform
       const uint32_t *cd = codes[S][i];
       int32x4 dq[G::XDW / 4];
-      if constexpr (MASKED) {
+      if constexpr (PLANES) {
+        // (the planes' dot replaces the bit bytes below)
+      } else if constexpr (MASKED) {
         // bit bytes: selector k of code dword w is slot dword 8w + k
 #pragma unroll
         for (int w = 0; w < 4; ++w)
@@ -526,7 +584,14 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         int dot = 0;
-        if constexpr (XREG) {
+        if constexpr (PLANES) {  // code dword w against planes 8w .. 8w + 7
+          int cnt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) cnt[q] += __builtin_popcount(cd[w] & xr8[b][i][8 * w + q]);
+          dot = plane_sum(cnt);
+        } else if constexpr (XREG) {
 #pragma unroll
           for (int w = 0; w < G::XDW; ++w)
             dot = __builtin_amdgcn_sdot4(dq[w >> 2][w & 3], static_cast<int>(xr8[b][i][w]), dot, false);
