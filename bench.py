@@ -113,8 +113,8 @@ def bench_matvec(torch, cq, cq_inputs, master, bits, batch, steps, warmup, gen, 
 
 
 def bench_read_ceiling(torch, cq, bufs, steps, warmup):
-    """The streaming-read ceiling on the same bytes: cq_read_probe (plain
-    16-byte loads, 32 KB contiguous tiles per workgroup) over the same three
+    """The streaming-read ceiling on the same bytes: cq_read_probe (16-byte
+    loads with the nt streaming hint, 32 KB contiguous tiles per workgroup) over the same three
     copies of the matrix in turn, timed between HIP events."""
     sink = torch.empty(2048 * 256, dtype=torch.int32, device=bufs[0].device)
     for i in range(warmup):
@@ -130,7 +130,7 @@ def bench_read_ceiling(torch, cq, bufs, steps, warmup):
     nbytes = bufs[0].numel()
     return {"bytes": nbytes, "median_s": t[steps // 2], "gbs": nbytes / t[steps // 2] / 1e9,
             "frac_hbm_peak": nbytes / t[steps // 2] / 1e9 / HBM_PEAK_GBS,
-            "probe": "cq_read_probe: 2048 workgroups x 256 threads, 16-byte loads, 8 in flight per thread"}
+            "probe": "cq_read_probe: 2048 workgroups x 256 threads, 16-byte nt loads, 8 in flight per thread"}
 
 
 def bench_needle_decode(torch, cq, cq_inputs, steps, gen):

@@ -23,23 +23,24 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// N consecutive dwords at byte offset off, in as few loads as possible.
-template <int N>
+// N consecutive dwords at byte offset off, in as few loads as possible, with
+// cache policy POLICY (0, or cq::kStreamLoad for data read once).
+template <int N, int POLICY = 0>
 __device__ inline void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *d) {
 #pragma unroll
   for (int q = 0; q + 4 <= N; q += 4) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * q, 0, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * q, 0, POLICY);
     d[q] = v.x, d[q + 1] = v.y, d[q + 2] = v.z, d[q + 3] = v.w;
   }
   constexpr int q = N / 4 * 4;
   if constexpr (N - q == 3) {
-    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off + 4 * q, 0, 0);
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off + 4 * q, 0, POLICY);
     d[q] = v.x, d[q + 1] = v.y, d[q + 2] = v.z;
   } else if constexpr (N - q == 2) {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * q, 0, 0);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * q, 0, POLICY);
     d[q] = v.x, d[q + 1] = v.y;
   } else if constexpr (N - q == 1) {
-    d[q] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * q, 0, 0);
+    d[q] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * q, 0, POLICY);
   }
 }
 

@@ -9,6 +9,14 @@
 
 namespace cq {
 
+// Cache-policy operand of the buffer-load builtins with the nt (non-temporal)
+// bit set.  A batch-1 product reads each packed code once per call, and a
+// large matrix is gone from every cache before the next call reaches it; the
+// nt hint marks such loads as streaming data for L2 and the Infinity Cache.
+// Measured on the table kernel (CQ2, 65536 x 16384, batch 1): 65.2 -> 57.9 us
+// per call, outputs unchanged.
+constexpr int kStreamLoad = 2;
+
 // Level selected by each *stored* code: levels[code] for 2/3/4-bit matrices;
 // for the ternary marker the crumb's sign extension times a, i.e.
 // {0, a, -2a, -a} for crumbs 00, 01, 10, 11.  Passed to kernels by value.

@@ -1,8 +1,10 @@
 // Streaming-read probe: the rate at which one kernel can read a buffer from
-// HBM with the widest plain loads, the ceiling the HBM-bound products are
-// measured against beside the published peak.  Each workgroup reads 32 KB
-// tiles (256 threads x 8 loads of 16 bytes, contiguous), tiles dealt out
-// round robin; loads past the end read zeros through the buffer range.
+// HBM with the widest loads, the ceiling the HBM-bound products are measured
+// against beside the published peak.  Each workgroup reads 32 KB tiles (256
+// threads x 8 loads of 16 bytes, contiguous), tiles dealt out round robin;
+// loads past the end read zeros through the buffer range.  The loads carry
+// the nt (streaming) cache hint, as the products' code loads do: on the
+// 285 MB CQ2 blob it reads ~6.4 TB/s against ~5.8 TB/s with plain loads.
 #include "cq_decode.h"
 #include "cq_internal.h"
 
@@ -23,7 +25,7 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const uint8_t
     cqdev::u32x4 v[kProbeLoads];
 #pragma unroll
     for (int l = 0; l < kProbeLoads; ++l)
-      v[l] = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<uint32_t>((l * kProbeThreads + threadIdx.x) * 16), 0, 0);
+      v[l] = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<uint32_t>((l * kProbeThreads + threadIdx.x) * 16), 0, cq::kStreamLoad);
 #pragma unroll
     for (int l = 0; l < kProbeLoads; ++l) acc ^= v[l].x ^ v[l].y ^ v[l].z ^ v[l].w;
   }

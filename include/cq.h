@@ -568,7 +568,8 @@ cq_status cq_kv_attention(const cq_matrix *K, const cq_matrix *V, int64_t n_toke
 
 /*
  * Measurement helper (not part of the product): reads `bytes` bytes at p once
- * with the widest plain loads (32 KB contiguous tiles per workgroup) and
+ * with the widest loads, nt (streaming) cache hint as the products' code
+ * loads have it (32 KB contiguous tiles per workgroup), and
  * writes one checksum word per thread to sink.  Its rate is the streaming-read
  * ceiling the HBM-bound products are reported against beside the published
  * peak.  sink_words / 256 workgroups are launched (at most 65535), so sink
