@@ -121,8 +121,10 @@ __device__ inline _Float16 lds_half(const uint8_t *lds, uint32_t byte_addr) {
 
 // Two floats rounded to nearest-even fp16, a in the low half.
 __device__ inline uint32_t pack_half2(float a, float b) {
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(a))) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(b))) << 16);
+  // one v_cvt_pk_f16_f32 (round to nearest even, as two scalar conversions)
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
 __device__ inline __amdgpu_buffer_rsrc_t buffer(uint64_t addr, uint32_t nbytes) {
@@ -395,35 +397,39 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) out[i * 64] = pack_half2(a2[0][i & 3] + b3[0][i >> 2], a2[1][i & 3] + b3[1][i >> 2]);
     } else if constexpr (SB == 2) {
-      // position h of the pair: codes (v&3, v>>2&3, v>>4&3, v>>6) of columns 4h..4h+3
-      const int c2hi = (vb >> 5) & 1, c3 = vb >> 6;  // fixed for this thread
-      float hi[2][2];
+      // position h of the pair: codes (v&3, v>>2&3, v>>4&3, v>>6) of columns 4h..4h+3.
+      // entry = lo[v & 15] + hi[bit 4 of v], each half summed in a fixed order
+      // (one rounded product, then a fused multiply-add); bits 5..7 of v are
+      // fixed for this thread.
+      const int c2hi = (vb >> 5) & 1, c3 = vb >> 6;
+      float lo[2][16], hi[2][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) hi[h][b] = lev[2 * c2hi + b] * xq[4 * h + 2] + lev[c3] * xq[4 * h + 3];
+        for (int c = 0; c < 16; ++c) lo[h][c] = __builtin_fmaf(lev[c >> 2], xq[4 * h + 1], lev[c & 3] * xq[4 * h]);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float t0 = lev[i & 3] * xq[0] + lev[(i >> 2) & 3] * xq[1] + hi[0][i >> 4];
-        const float t1 = lev[i & 3] * xq[4] + lev[(i >> 2) & 3] * xq[5] + hi[1][i >> 4];
-        out[i * 64] = pack_half2(t0, t1);
+        for (int b = 0; b < 2; ++b) hi[h][b] = __builtin_fmaf(lev[c3], xq[4 * h + 3], lev[2 * c2hi + b] * xq[4 * h + 2]);
       }
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        out[i * 64] = pack_half2(lo[0][i & 15] + hi[0][i >> 4], lo[1][i & 15] + hi[1][i >> 4]);
     } else if constexpr (SB == 4) {
-      // position h: codes (v&15, v>>4) of columns 2h, 2h+1
+      // position h: codes (v&15, v>>4) of columns 2h, 2h+1 (the high code's
+      // rounded product, then a fused multiply-add with the low code's level)
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int v = vb + i;
-        const float t0 = lev[v & 15] * xq[0] + lev[v >> 4] * xq[1];
-        const float t1 = lev[v & 15] * xq[2] + lev[v >> 4] * xq[3];
+        const float t0 = __builtin_fmaf(lev[v & 15], xq[0], lev[v >> 4] * xq[1]);
+        const float t1 = __builtin_fmaf(lev[v & 15], xq[2], lev[v >> 4] * xq[3]);
         out[i * 64] = pack_half2(t0, t1);
       }
     } else {
-      // position h: codes (v&7, v>>3) of columns 2h, 2h+1
+      // position h: codes (v&7, v>>3) of columns 2h, 2h+1, as at 4 bits
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int v = vb + i;
-        const float t0 = lev[v & 7] * xq[0] + lev[v >> 3] * xq[1];
-        const float t1 = lev[v & 7] * xq[2] + lev[v >> 3] * xq[3];
+        const float t0 = __builtin_fmaf(lev[v & 7], xq[0], lev[v >> 3] * xq[1]);
+        const float t1 = __builtin_fmaf(lev[v & 7], xq[2], lev[v >> 3] * xq[3]);
         out[i * 64] = pack_half2(t0, t1);
       }
     }
