@@ -381,18 +381,19 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
     if constexpr (SB == 1) {
       // position h of the pair: bit m of v selects -c or +c for column 8h + m;
       // bits 5..7 are fixed for this thread, bits 0..1 and 2..4 are summed
-      // from small tables
+      // from small tables, each sum in a fixed order (one rounded product,
+      // then fused multiply-adds)
       float a2[2][4], b3[2][8];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const float fixed = lev[(vb >> 5) & 1] * xq[8 * h + 5] + lev[(vb >> 6) & 1] * xq[8 * h + 6] +
-                            lev[(vb >> 7) & 1] * xq[8 * h + 7];
+        const float fixed = __builtin_fmaf(lev[(vb >> 7) & 1], xq[8 * h + 7],
+                                           __builtin_fmaf(lev[(vb >> 6) & 1], xq[8 * h + 6], lev[(vb >> 5) & 1] * xq[8 * h + 5]));
 #pragma unroll
-        for (int t = 0; t < 4; ++t) a2[h][t] = lev[t & 1] * xq[8 * h] + lev[(t >> 1) & 1] * xq[8 * h + 1];
+        for (int t = 0; t < 4; ++t) a2[h][t] = __builtin_fmaf(lev[(t >> 1) & 1], xq[8 * h + 1], lev[t & 1] * xq[8 * h]);
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-          b3[h][t] = lev[t & 1] * xq[8 * h + 2] + lev[(t >> 1) & 1] * xq[8 * h + 3] +
-                     lev[(t >> 2) & 1] * xq[8 * h + 4] + fixed;
+          b3[h][t] = __builtin_fmaf(lev[(t >> 2) & 1], xq[8 * h + 4],
+                                    __builtin_fmaf(lev[(t >> 1) & 1], xq[8 * h + 3], __builtin_fmaf(lev[t & 1], xq[8 * h + 2], fixed)));
       }
 #pragma unroll
       for (int i = 0; i < 32; ++i) out[i * 64] = pack_half2(a2[0][i & 3] + b3[0][i >> 2], a2[1][i & 3] + b3[1][i >> 2]);
