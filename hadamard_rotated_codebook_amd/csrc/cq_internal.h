@@ -16,6 +16,13 @@ namespace cq {
 // Measured on the table kernel (CQ2, 65536 x 16384, batch 1): 65.2 -> 57.9 us
 // per call, outputs unchanged.
 constexpr int kStreamLoad = 2;
+// Blob size from which the batch-1 products (table and W2A8 kernels) load
+// the packed codes with kStreamLoad: half the 256 MB Infinity Cache.  A
+// smaller matrix may stay in that cache from one call to the next, which nt
+// loads forgo: per call at CQ2 (plain / nt), 71 MB 18.2 / 18.8 us; 143 MB
+// 28.8 / 31.7 us on one matrix called again and again but 36.0 / 31.9 us on
+// three matrices in turn; 285 MB 68.3 / 58.2 us on three in turn.
+constexpr int64_t kStreamMinBytes = int64_t{128} << 20;
 
 // Level selected by each *stored* code: levels[code] for 2/3/4-bit matrices;
 // for the ternary marker the crumb's sign extension times a, i.e.

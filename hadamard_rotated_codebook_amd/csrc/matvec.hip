@@ -31,10 +31,14 @@
 //    cost 11 % of the kernel's time, the unit loads cut that by a third.  The
 //    buffer holds each group's 32 norms side by side, so one 16-byte LDS read
 //    serves 8 rows (v_fma_mix selects the half).
-//  * The code rows are loaded with the nt (streaming) cache hint: each byte
-//    is read once per call.  11 % faster at CQ2 and 14 % at CQ4 than plain
-//    loads; the norms, which the K-slices of a row share through L2, keep
-//    plain loads (nt on them measured slower).
+//  * Matrices of cq::kStreamMinBytes and more load their code rows with the nt
+//    (streaming) cache hint: each byte is read once per call, and such a
+//    matrix does not stay in the 256 MB Infinity Cache between calls.  11 %
+//    faster at CQ2 and 14 % at CQ4 on the 65536 x 16384 matrices than plain
+//    loads; smaller matrices keep plain loads, which let a matrix that fits
+//    the cache be read from it on the next call (nt measured up to 10 %
+//    slower there).  The norms, which the K-slices of a row share through
+//    L2, always take plain loads (nt on them measured slower).
 //  * Rows are read through buffer descriptors rebased per row in scalar
 //    registers.  A row past the end of its block or of the matrix gets a
 //    zero-length descriptor and reads zeros, as do lanes past the end of K (their
@@ -199,7 +203,7 @@ __device__ inline int table_exponent(float bound) {
 
 // ROT: the kernel rotates its slice of x itself (the fused call) instead of
 // reading the rotated activation xr.
-template <int SB, bool ROT>
+template <int SB, bool ROT, int POL>
 __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
   using G = Geom<SB>;
   __shared__ __align__(16) uint8_t lds[G::LDS_BYTES];
@@ -282,12 +286,12 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(MvArgs a) {
     // a different order there makes the compiler drain the prefetch ring.
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (SB == 3) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b96(rd, voff_data, 0, cq::kStreamLoad);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b96(rd, voff_data, 0, POL);
       d[0] = v[0];
       d[1 % G::DWORDS] = v[1];
       d[2 % G::DWORDS] = v[2];
     } else {
-      d[0] = __builtin_amdgcn_raw_buffer_load_b32(rd, voff_data, 0, cq::kStreamLoad);
+      d[0] = __builtin_amdgcn_raw_buffer_load_b32(rd, voff_data, 0, POL);
     }
     __builtin_amdgcn_sched_barrier(0);
     ++lk;
@@ -541,12 +545,16 @@ int slice_cols(int sb) {
 
 typedef void (*MvKernel)(MvArgs);
 
-MvKernel pick_kernel(int sb, bool rot = false) {
-  if (rot)
-    return sb == 1 ? matvec_kernel<1, true>
-                   : (sb == 2 ? matvec_kernel<2, true> : (sb == 3 ? matvec_kernel<3, true> : matvec_kernel<4, true>));
-  return sb == 1 ? matvec_kernel<1, false>
-                 : (sb == 2 ? matvec_kernel<2, false> : (sb == 3 ? matvec_kernel<3, false> : matvec_kernel<4, false>));
+template <bool ROT, int POL>
+MvKernel pick_sb(int sb) {
+  return sb == 1 ? matvec_kernel<1, ROT, POL>
+                 : (sb == 2 ? matvec_kernel<2, ROT, POL> : (sb == 3 ? matvec_kernel<3, ROT, POL> : matvec_kernel<4, ROT, POL>));
+}
+
+// stream: the code rows' loads carry the nt hint (cq::kStreamLoad)
+MvKernel pick_kernel(int sb, bool rot = false, bool stream = false) {
+  if (stream) return rot ? pick_sb<true, cq::kStreamLoad>(sb) : pick_sb<false, cq::kStreamLoad>(sb);
+  return rot ? pick_sb<true, 0>(sb) : pick_sb<false, 0>(sb);
 }
 
 int max_grid(int sb) {
@@ -671,7 +679,8 @@ hipError_t launch_lut(const uint8_t *blob, int bits, int64_t rows, int64_t kpad,
   a.per_slice = sh.per_slice;
   a.partial = sh.nslice > 1 ? static_cast<float *>(workspace) : nullptr;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(sh.nslice) * sh.per_slice));
-  pick_kernel(sb, x != nullptr)<<<grid, kThreads, 0, s>>>(a);
+  const bool stream = rows * (a.row_bytes + 2 * a.ngroups) >= cq::kStreamMinBytes;
+  pick_kernel(sb, x != nullptr, stream)<<<grid, kThreads, 0, s>>>(a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || sh.nslice <= 1) return e;
   return launch_combine(a.partial, rows, sh.nslice, y, s);

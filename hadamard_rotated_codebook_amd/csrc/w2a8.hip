@@ -37,8 +37,10 @@
 //    many workgroups as fit the chip).  Chunks of 4 groups, two in flight per
 //    wave; with 2+ chunks, 2 or 4 waves split a block's K and add their
 //    accumulators through LDS in wave order.
-// Both product kernels load the packed codes with the nt (streaming) cache
-// hint: 3-5 % faster at CQ2 and CQ4 than plain loads.
+// Both product kernels load the packed codes of matrices of
+// cq::kStreamMinBytes and more with the nt (streaming) cache hint: 3-10 %
+// faster on the 285 and 554 MB matrices than plain loads, which smaller
+// matrices keep (they may stay in the Infinity Cache between calls).
 #include <atomic>
 #include <mutex>
 
@@ -253,7 +255,7 @@ __device__ inline void fill_int8(const int8_t *xq, const float *sx, int batch, i
 
 // LDS: int8 activations [kMaxBatch + 1 rows][kpad] (row `batch` is zero for
 // the padding lanes), then the group scales [ngroups][8] (fp32).
-template <int SB>
+template <int SB, int POL>
 __global__ __launch_bounds__(kThreads) void w2a8_kernel(W8Args a) {
   constexpr int GROUP_BYTES = CQ_GROUP * SB / 8;  // 16, 32, 48, 64
   constexpr int QB = GROUP_BYTES / 4;              // a quarter's bytes: 4, 8, 12, 16
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void w2a8_kernel(W8Args a) {
       const int g = CG * c + gi;
       const uint32_t off = live && g < ngroups ? static_cast<uint32_t>(n * a.row_bytes + g * GROUP_BYTES + q * QB)
                                                : kOutOfRange;
-      load_dwords<QDW, cq::kStreamLoad>(wbuf, off, codes[S][gi]);
+      load_dwords<QDW, POL>(wbuf, off, codes[S][gi]);
       const uint32_t noff = live && g < ngroups ? static_cast<uint32_t>((n * ngroups + g) * 2) : kOutOfRange;
       nrm[S][gi] = __builtin_amdgcn_raw_buffer_load_b16(nbuf, noff, 0, 0);
     }
@@ -437,7 +439,7 @@ struct W8RowArgs {
 
 // XREG: the lane's activation bytes live in registers (B * NPL * XDW <= 64
 // dwords); otherwise each piece reads them from LDS.
-template <int SB, int B, int NPL, bool XREG>
+template <int SB, int B, int NPL, bool XREG, int POL>
 __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
   using G = RowGeom<SB>;
   static_assert(!XREG || B * NPL * G::XDW <= kRowMaxXdw, "activation registers");
@@ -545,7 +547,7 @@ __global__ __launch_bounds__(kRowThreads) void w2a8_row_kernel(W8RowArgs a) {
         buffer_rsrc(a.norms + r0 * ngroups, static_cast<uint32_t>(live_rows * ngroups * 2));
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
-      load_dwords<G::PDW, cq::kStreamLoad>(rb, coff[i], codes[S][i]);
+      load_dwords<G::PDW, POL>(rb, coff[i], codes[S][i]);
       nrm[S][i] = __builtin_amdgcn_raw_buffer_load_b16(nb, noff[i], 0, 0);
     }
   };
@@ -669,22 +671,29 @@ constexpr int kRowMaxBatch = 4;
 
 // The row kernel for (storage bits, batch, pieces per lane): registers when
 // they hold the lane's activations, else LDS; nullptr past its limits.
-template <int SB>
+template <int SB, int POL>
 W8RowKernel pick_row_sb(int batch, int npl) {
-  if (batch == 1 && npl <= row_npl_reg<SB, 1>()) return w2a8_row_kernel<SB, 1, row_npl_reg<SB, 1>(), true>;
-  if (batch == 2 && npl <= row_npl_reg<SB, 2>()) return w2a8_row_kernel<SB, 2, row_npl_reg<SB, 2>(), true>;
+  if (batch == 1 && npl <= row_npl_reg<SB, 1>()) return w2a8_row_kernel<SB, 1, row_npl_reg<SB, 1>(), true, POL>;
+  if (batch == 2 && npl <= row_npl_reg<SB, 2>()) return w2a8_row_kernel<SB, 2, row_npl_reg<SB, 2>(), true, POL>;
   if (npl > row_npl_lds<SB>()) return nullptr;
   switch (batch) {  // batch 1 always fits registers
-    case 2: return w2a8_row_kernel<SB, 2, row_npl_lds<SB>(), false>;
-    case 3: return w2a8_row_kernel<SB, 3, row_npl_lds<SB>(), false>;
-    case 4: return w2a8_row_kernel<SB, 4, row_npl_lds<SB>(), false>;
+    case 2: return w2a8_row_kernel<SB, 2, row_npl_lds<SB>(), false, POL>;
+    case 3: return w2a8_row_kernel<SB, 3, row_npl_lds<SB>(), false, POL>;
+    case 4: return w2a8_row_kernel<SB, 4, row_npl_lds<SB>(), false, POL>;
     default: return nullptr;
   }
 }
 
-W8RowKernel pick_row(int sb, int batch, int npl) {
-  return sb == 1 ? pick_row_sb<1>(batch, npl)
-                 : (sb == 2 ? pick_row_sb<2>(batch, npl) : (sb == 3 ? pick_row_sb<3>(batch, npl) : pick_row_sb<4>(batch, npl)));
+template <int POL>
+W8RowKernel pick_row_pol(int sb, int batch, int npl) {
+  return sb == 1 ? pick_row_sb<1, POL>(batch, npl)
+                 : (sb == 2 ? pick_row_sb<2, POL>(batch, npl)
+                            : (sb == 3 ? pick_row_sb<3, POL>(batch, npl) : pick_row_sb<4, POL>(batch, npl)));
+}
+
+// stream: the packed codes' loads carry the nt hint (cq::kStreamLoad)
+W8RowKernel pick_row(int sb, int batch, int npl, bool stream) {
+  return stream ? pick_row_pol<cq::kStreamLoad>(sb, batch, npl) : pick_row_pol<0>(sb, batch, npl);
 }
 
 // Resident workgroups per CU of a row kernel at an LDS size, cached per
@@ -705,9 +714,13 @@ int row_occupancy(const void *k, size_t lds, int dev) {
 
 typedef void (*W8Kernel)(W8Args);
 
-W8Kernel pick(int sb) {
-  return sb == 1 ? w2a8_kernel<1> : (sb == 2 ? w2a8_kernel<2> : (sb == 3 ? w2a8_kernel<3> : w2a8_kernel<4>));
+template <int POL>
+W8Kernel pick_pol(int sb) {
+  return sb == 1 ? w2a8_kernel<1, POL>
+                 : (sb == 2 ? w2a8_kernel<2, POL> : (sb == 3 ? w2a8_kernel<3, POL> : w2a8_kernel<4, POL>));
 }
+
+W8Kernel pick(int sb, bool stream) { return stream ? pick_pol<cq::kStreamLoad>(sb) : pick_pol<0>(sb); }
 
 }  // namespace
 
@@ -791,7 +804,7 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t kpad
     for (int i = 0; i < 4; ++i) r.c8[i] = cb.c8[i];
     r.sc = cb.sc;
     const size_t lds = static_cast<size_t>(row_lds_bytes(kpad, batch));
-    const W8RowKernel k = pick_row(sb, static_cast<int>(batch), r.npl);
+    const W8RowKernel k = pick_row(sb, static_cast<int>(batch), r.npl, rows * (r.row_bytes + 2 * r.ngroups) >= kStreamMinBytes);
     if (!k) return hipErrorInvalidValue;
     // one wave of workgroups: as many as the CUs hold at once (registers and
     // LDS), each over a contiguous range of row steps
@@ -827,7 +840,7 @@ hipError_t launch_w2a8(const uint8_t *blob, int bits, int64_t rows, int64_t kpad
   int64_t per_cu = static_cast<int64_t>(160 * 1024) / static_cast<int64_t>(lds + sizeof(float) * 4 * kThreads);
   per_cu = per_cu < 1 ? 1 : (per_cu > 8 ? 8 : per_cu);
   const int64_t grid = ntiles < per_cu * cus ? ntiles : per_cu * cus;
-  const W8Kernel k = pick(sb);
+  const W8Kernel k = pick(sb, rows * (a.row_bytes + 2 * a.ngroups) >= kStreamMinBytes);
   if (!k) return hipErrorInvalidValue;
   k<<<dim3(static_cast<unsigned>(grid)), kThreads, lds, s>>>(a);
   return hipGetLastError();
