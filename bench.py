@@ -565,7 +565,7 @@ def main():
         ach = h["bytes"] / h["kernel_s"] / 1e9
         line["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": ach / HBM_PEAK_GBS, "traffic": stored_traffic(),
-                            "kernel": "cq_rotate_matvec call: matvec_kernel<2, true> + combine_kernel",
+                            "kernel": "cq_rotate_matvec call: matvec_kernel<2, true, 2> (nt code loads) + combine_kernel",
                             "kernel_us": h["kernel_s"] * 1e6, "algorithmic_bytes": h["bytes"],
                             "read_ceiling_gbs": h["read_ceiling"]["gbs"],
                             "frac_of_read_ceiling": ach / h["read_ceiling"]["gbs"]}
