@@ -680,6 +680,22 @@ def test_gemm_full_size_every_tile(bits):
                         tol=1e-4, min_cos=0.99999)
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+def test_gemm_large_tiles_ragged(bits):
+    # 258 tiles of 256 x 256, so the large-tile kernel runs: N = 32900 leaves
+    # a ragged last N-tile (132 of 256 rows), K = 640 five groups (ten stages)
+    m, rows, cols = 512, 32900, 640
+    say("gemm large tiles ragged", bits, m, rows, cols)
+    W, blob, levels, _ = _cq_from_oracle(bits, rows, cols, 90 + bits)
+    X = cq_inputs.activations(91, bits, m, cols, "f16")
+    xr = cq.cq_rotate_acts(_to_dev(X, torch.float16), torch.bfloat16)
+    got = cq.cq_gemm(W, xr).cpu().numpy().astype(np.float64)
+    w_hat = np.linalg.norm(oracle.dequantize(blob, bits, rows, cols, levels), axis=1)
+    xn = np.linalg.norm(X.astype(np.float64), axis=1)
+    _check_fp32_product(got, oracle.gemm(blob, bits, rows, cols, X, levels), w_hat, xn, tol=1e-2, min_cos=0.9999)
+    _check_fp32_product(got, oracle.gemm_bf16(blob, bits, rows, cols, X, levels), w_hat, xn, tol=1e-4, min_cos=0.99999)
+
+
 def test_gemm_degenerate_shapes():
     levels = cq_inputs.codebook(4)
     W = cq.CQMatrix(4, 6, 0, torch.zeros(0, dtype=torch.uint8, device=DEV), levels)
